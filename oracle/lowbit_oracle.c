@@ -1,0 +1,494 @@
+/*
+ * lowbit_oracle.c -- plain, scalar CPU oracle for the packed low-bit weight x int8 activation product.
+ *
+ * TEST INFRASTRUCTURE.  Only tests/, __graft_entry__.smoke() and bench.py's cpu_baseline leg may load,
+ * link or call this library.  It shares no code, header, table or helper with the HIP library under
+ * bit_quantized_matvec_q1_amd/: it is written from the pages' definitions alone, one loop per index,
+ * no intrinsics, single-threaded, built with -O2 -ffp-contract=off (no fused multiply-add is formed
+ * where the source does not write one).
+ *
+ * Sources (cited by page title and section):
+ *   [TR]  "bankml: verified low-bit inference on commodity CPUs -- a technical report"
+ *         (bankml docs/TECHNICAL.md), sections III.2, III.3, III.5, III.8.
+ *   [ARCH] tritium "Architecture" page, sections 1, 2, 4.1, 5, 8.
+ *   [BH]  bankml BUILD_HISTORY.md, checklist "P2 -- own the kernels".
+ *
+ * What it computes, and in which precision:
+ *   - block decode to one small integer per weight (the tritsim approach: one i8 per weight, [ARCH] s.5);
+ *   - the q8_0 activation quantiser in fp32, multiplier 127/amax, round-half-to-even ([TR] III.2,
+ *     [BH]); the per-token int8 quantiser in fp32 with the same rule;
+ *   - exact integer per-block sums (int64 arithmetic, checked to fit int32), computed three ways
+ *     (multiply, select, offset) that must agree ([TR] III.8; [BH]);
+ *   - the ggml-format outputs y = sum_b d_w[b] * sum_{j in b} d_x[j] * isum[j] in fp64 (every term is
+ *     exact in fp64; only the additions round);
+ *   - the planar output ((float)acc * s_x) * s_w in fp32 with two roundings ([ARCH] s.5 names the
+ *     twice-multiplied order);
+ *   - the dense bf16 head y = sum_k bf16(W) * x in fp64 (every product exact).
+ *
+ * Parity pins live in tests/test_oracle_*.py.  Parity unpinned: ggml's exact fp32 operation order (only
+ * recoverable from a compiled binary) and the absolute Q1_0 sign polarity relative to ggml; this oracle
+ * reads bit 1 as +1 (the "+" selector of the {0,1} form in [BH]).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#define QK1 128 /* weights per Q1_0 block   ([TR] III.2) */
+#define QK2 64  /* weights per Q2_0_g64 block ([TR] III.5) */
+#define QKP 64  /* columns per planar beat  ([ARCH] s.2) */
+#define QK8 32  /* activations per q8_0 block ([TR] III.2) */
+
+enum { FMT_Q1_0 = 1, FMT_Q2_0_G64 = 2, FMT_PLANAR = 3 };
+
+/* ------------------------------------------------------------------------------------------------
+ * binary16 and bfloat16 conversions ([TR] III.2: the scale is "a 16-bit IEEE 754 half-precision" value)
+ * ---------------------------------------------------------------------------------------------- */
+
+/* binary16 bits -> float, exactly: sign, 5-bit exponent (bias 15), 10-bit fraction. */
+float lbo_half_to_float(uint16_t h)
+{
+    int sign = (h >> 15) & 1;
+    int e = (h >> 10) & 31;
+    int m = h & 1023;
+    double v;
+    if (e == 0)
+        v = ldexp((double)m, -24); /* subnormal: m * 2^-24 */
+    else if (e == 31)
+        v = m ? (double)NAN : (double)INFINITY;
+    else
+        v = ldexp((double)(1024 + m), e - 25); /* (1 + m/1024) * 2^(e-15) */
+    return (float)(sign ? -v : v);
+}
+
+/* float -> binary16 bits, round to nearest, ties to even. */
+uint16_t lbo_float_to_half_rne(float f)
+{
+    uint32_t bits;
+    memcpy(&bits, &f, 4);
+    uint16_t sign = (uint16_t)((bits >> 16) & 0x8000u);
+    if (isnan(f))
+        return (uint16_t)(sign | 0x7e00u);
+    double a = fabs((double)f);
+    /* the largest finite half is 65504; 65520 lies half way to 65536 and ties to the even (infinite) side */
+    if (a >= 65520.0)
+        return (uint16_t)(sign | 0x7c00u);
+    if (a == 0.0)
+        return sign;
+    int e;
+    frexp(a, &e);              /* a = fr * 2^e, 0.5 <= fr < 1 */
+    int ulp_exp = e - 11;      /* 11 significant bits in a normal half */
+    if (ulp_exp < -24)
+        ulp_exp = -24;         /* subnormal spacing */
+    double r = nearbyint(ldexp(a, -ulp_exp)); /* exact scaling, then round half to even */
+    double v = ldexp(r, ulp_exp);
+    if (v == 0.0)
+        return sign;
+    if (v < ldexp(1.0, -14))
+        return (uint16_t)(sign | (uint16_t)ldexp(v, 24)); /* subnormal fraction */
+    int ee;
+    double fr = frexp(v, &ee); /* v = (2 fr) * 2^(ee-1) */
+    int frac = (int)ldexp(2.0 * fr - 1.0, 10);
+    return (uint16_t)(sign | (uint16_t)((ee - 1 + 15) << 10) | (uint16_t)frac);
+}
+
+/* bfloat16 bits -> float: the top half of the binary32 pattern. */
+float lbo_bf16_to_float(uint16_t b)
+{
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    return f;
+}
+
+static uint16_t le16(const uint8_t *p) { return (uint16_t)(p[0] | (p[1] << 8)); }
+
+static uint64_t le64(const uint8_t *p)
+{
+    uint64_t v = 0;
+    for (int i = 7; i >= 0; i--)
+        v = (v << 8) | p[i];
+    return v;
+}
+
+/* ------------------------------------------------------------------------------------------------
+ * Sizes ([TR] III.2: (16 + 2) * 8 / 128 = 1.125 bits per weight; III.5: 2.25 bits per weight;
+ * [ARCH] s.2: 16 bytes per 64 columns)
+ * ---------------------------------------------------------------------------------------------- */
+
+int64_t lbo_block_weights(int fmt)
+{
+    return fmt == FMT_Q1_0 ? QK1 : fmt == FMT_Q2_0_G64 ? QK2 : fmt == FMT_PLANAR ? QKP : 0;
+}
+
+int64_t lbo_block_bytes(int fmt)
+{
+    return fmt == FMT_Q1_0 ? 2 + QK1 / 8 : fmt == FMT_Q2_0_G64 ? 2 + QK2 / 4 : fmt == FMT_PLANAR ? 16 : 0;
+}
+
+int64_t lbo_weight_bytes(int fmt, int64_t N, int64_t K)
+{
+    int64_t qk = lbo_block_weights(fmt);
+    if (qk == 0 || N < 0 || K < 0 || K % qk)
+        return -1;
+    return N * (K / qk) * lbo_block_bytes(fmt);
+}
+
+/* ------------------------------------------------------------------------------------------------
+ * Decode: one small integer per weight, plus the block scale
+ * ---------------------------------------------------------------------------------------------- */
+
+/* Q1_0 ([TR] III.2; [BH] "f16 d first, 16 sign bytes LSB-first"): weight i of a block is d * s_i with
+ * s_i = +1 when bit (i mod 8) of sign byte floor(i/8) is 1, and -1 when it is 0. */
+static int q1_weight(const uint8_t *blk, int i) { return ((blk[2 + (i >> 3)] >> (i & 7)) & 1) ? +1 : -1; }
+
+/* Q2_0_g64 ([TR] III.5): 2-bit code c of weight i at bits 2*(i mod 4) of code byte floor(i/4),
+ * lowest bits first; the weight is (c - 1) * d, c - 1 in {-1, 0, +1, +2}. */
+static int q2_code(const uint8_t *blk, int i) { return (blk[2 + (i >> 2)] >> (2 * (i & 3))) & 3; }
+
+/* planar ([ARCH] s.2): beat = {u64 pos, u64 neg}; column c is bit c of each plane; weight = pos - neg
+ * (a column with both bits set reads 0 -- the pages leave that pattern undefined). */
+static int planar_weight(const uint8_t *beat, int c)
+{
+    uint64_t pos = le64(beat), neg = le64(beat + 8);
+    return (int)((pos >> c) & 1) - (int)((neg >> c) & 1);
+}
+
+/* Decode a whole tensor: w[N][K] small integers; d[N][K/QK] block scales as floats (ggml formats only,
+ * may be NULL).  Returns 0, or -1 on a bad format or shape. */
+int lbo_decode(int fmt, const uint8_t *raw, int64_t N, int64_t K, int8_t *w, float *d)
+{
+    int64_t qk = lbo_block_weights(fmt), bb = lbo_block_bytes(fmt);
+    if (qk == 0 || K % qk)
+        return -1;
+    int64_t nb = K / qk;
+    for (int64_t r = 0; r < N; r++)
+        for (int64_t b = 0; b < nb; b++) {
+            const uint8_t *blk = raw + (r * nb + b) * bb;
+            for (int i = 0; i < qk; i++) {
+                int v = fmt == FMT_Q1_0 ? q1_weight(blk, i) : fmt == FMT_Q2_0_G64 ? q2_code(blk, i) - 1
+                                                                                  : planar_weight(blk, i);
+                w[r * K + b * qk + i] = (int8_t)v;
+            }
+            if (d && fmt != FMT_PLANAR)
+                d[r * nb + b] = lbo_half_to_float(le16(blk));
+        }
+    return 0;
+}
+
+/* Encode (inverse of decode, for round-trip pins): w[N][K] and binary16 scale bits dh[N][K/QK]. */
+int lbo_encode(int fmt, const int8_t *w, const uint16_t *dh, int64_t N, int64_t K, uint8_t *raw)
+{
+    int64_t qk = lbo_block_weights(fmt), bb = lbo_block_bytes(fmt);
+    if (qk == 0 || K % qk)
+        return -1;
+    int64_t nb = K / qk;
+    for (int64_t r = 0; r < N; r++)
+        for (int64_t b = 0; b < nb; b++) {
+            uint8_t *blk = raw + (r * nb + b) * bb;
+            memset(blk, 0, (size_t)bb);
+            const int8_t *wb = w + r * K + b * qk;
+            if (fmt == FMT_PLANAR) {
+                for (int c = 0; c < QKP; c++) {
+                    if (wb[c] == 1)
+                        blk[c >> 3] |= (uint8_t)(1u << (c & 7));
+                    else if (wb[c] == -1)
+                        blk[8 + (c >> 3)] |= (uint8_t)(1u << (c & 7));
+                    else if (wb[c] != 0)
+                        return -1;
+                }
+                continue;
+            }
+            blk[0] = (uint8_t)(dh[r * nb + b] & 0xff);
+            blk[1] = (uint8_t)(dh[r * nb + b] >> 8);
+            for (int i = 0; i < qk; i++) {
+                if (fmt == FMT_Q1_0) {
+                    if (wb[i] != 1 && wb[i] != -1)
+                        return -1;
+                    if (wb[i] == 1)
+                        blk[2 + (i >> 3)] |= (uint8_t)(1u << (i & 7));
+                } else {
+                    if (wb[i] < -1 || wb[i] > 2)
+                        return -1;
+                    blk[2 + (i >> 2)] |= (uint8_t)((wb[i] + 1) << (2 * (i & 3)));
+                }
+            }
+        }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------------------------------
+ * Activation quantisers
+ * ---------------------------------------------------------------------------------------------- */
+
+/* q8_0 ([TR] III.2: blocks of 32 signed bytes with their own half-precision scale, computed as
+ * 127 / max|x| with round-half-to-even; [BH] "AVX2 quantizer: 127/amax, round-half-even").
+ * Per block: amax = max|x_i| (exact); stored scale = binary16_rne(amax / 127) in fp32;
+ * multiplier id = 127 / amax in fp32 (0 when amax = 0); q_i = round_half_even(x_i * id) (fp32 product).
+ * x[M][K] -> q[M][K], dh[M][K/32] (binary16 bits).  Returns -1 when K is not a multiple of 32. */
+int lbo_quantize_q8_0(const float *x, int64_t M, int64_t K, int8_t *q, uint16_t *dh)
+{
+    if (K % QK8)
+        return -1;
+    for (int64_t m = 0; m < M; m++)
+        for (int64_t j = 0; j < K / QK8; j++) {
+            const float *xb = x + m * K + j * QK8;
+            float amax = 0.0f;
+            for (int i = 0; i < QK8; i++)
+                if (fabsf(xb[i]) > amax)
+                    amax = fabsf(xb[i]);
+            float d = amax / 127.0f;
+            float id = amax > 0.0f ? 127.0f / amax : 0.0f;
+            dh[m * (K / QK8) + j] = lbo_float_to_half_rne(d);
+            for (int i = 0; i < QK8; i++) {
+                float v = xb[i] * id;
+                q[m * K + j * QK8 + i] = (int8_t)nearbyintf(v);
+            }
+        }
+    return 0;
+}
+
+/* Per-token int8 (the planar path's activations, [ARCH] s.1 "activations are int8", one absmax scale per
+ * token): amax over the row, s = amax / 127 (fp32), q = clamp(round_half_even(x * (127/amax)), -128, 127),
+ * all zeros when amax = 0.  x[M][K] -> q[M][K], s[M]. */
+int lbo_quantize_i8_row(const float *x, int64_t M, int64_t K, int8_t *q, float *s)
+{
+    for (int64_t m = 0; m < M; m++) {
+        const float *xr = x + m * K;
+        float amax = 0.0f;
+        for (int64_t k = 0; k < K; k++)
+            if (fabsf(xr[k]) > amax)
+                amax = fabsf(xr[k]);
+        s[m] = amax / 127.0f;
+        float id = amax > 0.0f ? 127.0f / amax : 0.0f;
+        for (int64_t k = 0; k < K; k++) {
+            float v = nearbyintf(xr[k] * id);
+            if (v > 127.0f)
+                v = 127.0f;
+            if (v < -128.0f)
+                v = -128.0f;
+            q[m * K + k] = (int8_t)v;
+        }
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------------------------------
+ * Integer per-block sums for the ggml formats: isum[r][j] = sum over the 32 weights of act block j of
+ * w_i * q_i.  Three exact forms ([TR] III.8 "Operation"; [BH] "y = s * (sum x[w=+1] - sum x[w=-1])").
+ * rows: optional list of row indices (NULL = all N rows, in order); out is [nrows][K/32].
+ * Each returns 0, -1 on a bad shape or format, -2 if a sum does not fit int32 (cannot happen for
+ * int8 activations; checked anyway).
+ * ---------------------------------------------------------------------------------------------- */
+
+static int64_t row_of(const int64_t *rows, int64_t i) { return rows ? rows[i] : i; }
+
+/* multiply form: decode each weight to its integer value and multiply. */
+int lbo_block_sums_multiply(int fmt, const uint8_t *raw, int64_t N, int64_t K, const int8_t *q,
+                            const int64_t *rows, int64_t nrows, int32_t *isum)
+{
+    int64_t qk = lbo_block_weights(fmt), bb = lbo_block_bytes(fmt);
+    if ((fmt != FMT_Q1_0 && fmt != FMT_Q2_0_G64) || K % qk)
+        return -1;
+    int64_t nb = K / qk;
+    for (int64_t t = 0; t < nrows; t++) {
+        int64_t r = row_of(rows, t);
+        if (r < 0 || r >= N)
+            return -1;
+        for (int64_t j = 0; j < K / QK8; j++) {
+            int64_t acc = 0;
+            for (int i = 0; i < QK8; i++) {
+                int64_t k = j * QK8 + i;
+                const uint8_t *blk = raw + (r * nb + k / qk) * bb;
+                int wv = fmt == FMT_Q1_0 ? q1_weight(blk, (int)(k % qk)) : q2_code(blk, (int)(k % qk)) - 1;
+                acc += (int64_t)wv * (int64_t)q[k];
+            }
+            if (acc > INT32_MAX || acc < INT32_MIN)
+                return -2;
+            isum[t * (K / QK8) + j] = (int32_t)acc;
+        }
+    }
+    return 0;
+}
+
+/* select form: add the activation where the weight is +1, subtract it where -1, skip 0, add twice for +2. */
+int lbo_block_sums_select(int fmt, const uint8_t *raw, int64_t N, int64_t K, const int8_t *q,
+                          const int64_t *rows, int64_t nrows, int32_t *isum)
+{
+    int64_t qk = lbo_block_weights(fmt), bb = lbo_block_bytes(fmt);
+    if ((fmt != FMT_Q1_0 && fmt != FMT_Q2_0_G64) || K % qk)
+        return -1;
+    int64_t nb = K / qk;
+    for (int64_t t = 0; t < nrows; t++) {
+        int64_t r = row_of(rows, t);
+        if (r < 0 || r >= N)
+            return -1;
+        for (int64_t j = 0; j < K / QK8; j++) {
+            int64_t plus = 0, minus = 0, two = 0;
+            for (int i = 0; i < QK8; i++) {
+                int64_t k = j * QK8 + i;
+                const uint8_t *blk = raw + (r * nb + k / qk) * bb;
+                int i_in = (int)(k % qk);
+                if (fmt == FMT_Q1_0) {
+                    if ((blk[2 + (i_in >> 3)] >> (i_in & 7)) & 1)
+                        plus += q[k];
+                    else
+                        minus += q[k];
+                } else {
+                    int c = (blk[2 + (i_in >> 2)] >> (2 * (i_in & 3))) & 3;
+                    if (c == 2)
+                        plus += q[k];
+                    else if (c == 0)
+                        minus += q[k];
+                    else if (c == 3)
+                        two += q[k];
+                }
+            }
+            int64_t acc = plus - minus + 2 * two;
+            if (acc > INT32_MAX || acc < INT32_MIN)
+                return -2;
+            isum[t * (K / QK8) + j] = (int32_t)acc;
+        }
+    }
+    return 0;
+}
+
+/* offset form: Q2_0 sum c*q - sum q (stored code c = w + 1); Q1_0 2 * sum_{bit=1} q - sum q. */
+int lbo_block_sums_offset(int fmt, const uint8_t *raw, int64_t N, int64_t K, const int8_t *q,
+                          const int64_t *rows, int64_t nrows, int32_t *isum)
+{
+    int64_t qk = lbo_block_weights(fmt), bb = lbo_block_bytes(fmt);
+    if ((fmt != FMT_Q1_0 && fmt != FMT_Q2_0_G64) || K % qk)
+        return -1;
+    int64_t nb = K / qk;
+    for (int64_t t = 0; t < nrows; t++) {
+        int64_t r = row_of(rows, t);
+        if (r < 0 || r >= N)
+            return -1;
+        for (int64_t j = 0; j < K / QK8; j++) {
+            int64_t sel = 0, sq = 0;
+            for (int i = 0; i < QK8; i++) {
+                int64_t k = j * QK8 + i;
+                const uint8_t *blk = raw + (r * nb + k / qk) * bb;
+                int i_in = (int)(k % qk);
+                sq += q[k];
+                if (fmt == FMT_Q1_0)
+                    sel += ((blk[2 + (i_in >> 3)] >> (i_in & 7)) & 1) * (int64_t)q[k];
+                else
+                    sel += ((blk[2 + (i_in >> 2)] >> (2 * (i_in & 3))) & 3) * (int64_t)q[k];
+            }
+            int64_t acc = fmt == FMT_Q1_0 ? 2 * sel - sq : sel - sq;
+            if (acc > INT32_MAX || acc < INT32_MIN)
+                return -2;
+            isum[t * (K / QK8) + j] = (int32_t)acc;
+        }
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------------------------------
+ * ggml-format matvec output ([TR] III.2: both scales are applied to the integer sums at the end;
+ * III.3: one multiply-add per q8_0 block, then one per Q1_0 block):
+ *   y[r] = sum_b d_w[r][b] * ( sum_{j in b} d_x[j] * isum[r][j] )
+ * computed in fp64 from the exact integer sums and the exact binary16 scales.  Also returns
+ * A[r] = sum_b sum_{j in b} |d_w[r][b] * d_x[j] * isum[r][j]| (the magnitude the terms carry) so that a
+ * reordered fp32 evaluation can be judged against the rounding it must incur.
+ * q: int8 [K]; dxh: binary16 bits [K/32]; rows: NULL or row indices; y, A: [nrows].
+ * ---------------------------------------------------------------------------------------------- */
+int lbo_matvec_q(int fmt, const uint8_t *raw, int64_t N, int64_t K, const int8_t *q, const uint16_t *dxh,
+                 const int64_t *rows, int64_t nrows, double *y, double *A)
+{
+    int64_t qk = lbo_block_weights(fmt), bb = lbo_block_bytes(fmt);
+    if ((fmt != FMT_Q1_0 && fmt != FMT_Q2_0_G64) || K % qk)
+        return -1;
+    int64_t nb = K / qk, per = qk / QK8;
+    int32_t isum_blk[QK1 / QK8];
+    for (int64_t t = 0; t < nrows; t++) {
+        int64_t r = row_of(rows, t);
+        if (r < 0 || r >= N)
+            return -1;
+        double acc = 0.0, mag = 0.0;
+        for (int64_t b = 0; b < nb; b++) {
+            const uint8_t *blk = raw + (r * nb + b) * bb;
+            for (int64_t jj = 0; jj < per; jj++) {
+                int64_t s = 0;
+                for (int i = 0; i < QK8; i++) {
+                    int wi = (int)(jj * QK8 + i);
+                    int wv = fmt == FMT_Q1_0 ? q1_weight(blk, wi) : q2_code(blk, wi) - 1;
+                    s += (int64_t)wv * q[b * qk + wi];
+                }
+                isum_blk[jj] = (int32_t)s;
+            }
+            double dw = (double)lbo_half_to_float(le16(blk));
+            for (int64_t jj = 0; jj < per; jj++) {
+                double dx = (double)lbo_half_to_float(dxh[b * per + jj]);
+                double term = dw * dx * (double)isum_blk[jj]; /* exact: 11 + 11 + 14 significant bits */
+                acc += term;
+                mag += fabs(term);
+            }
+        }
+        y[t] = acc;
+        if (A)
+            A[t] = mag;
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------------------------------
+ * Planar ternary matvec ([ARCH] s.1 select-accumulate; s.2 the plane identity
+ * y[r] = sum_{W=+1} x - sum_{W=-1} x; s.4.1 i32 accumulators; s.5 scales multiplied twice):
+ *   acc[r] = sum_k w[r][k] * q[k]  (exact integer)
+ *   y[r]   = ((float)acc[r] * s_x) * s_w   (fp32, two roundings)
+ * ---------------------------------------------------------------------------------------------- */
+int lbo_matvec_planar(const uint8_t *beats, int64_t N, int64_t K, const int8_t *q, float s_x, float s_w,
+                      const int64_t *rows, int64_t nrows, int32_t *acc_out, float *y)
+{
+    if (K % QKP)
+        return -1;
+    int64_t nb = K / QKP;
+    for (int64_t t = 0; t < nrows; t++) {
+        int64_t r = row_of(rows, t);
+        if (r < 0 || r >= N)
+            return -1;
+        int64_t acc = 0;
+        for (int64_t b = 0; b < nb; b++) {
+            const uint8_t *beat = beats + (r * nb + b) * 16;
+            for (int c = 0; c < QKP; c++)
+                acc += (int64_t)planar_weight(beat, c) * q[b * QKP + c];
+        }
+        if (acc > INT32_MAX || acc < INT32_MIN)
+            return -2;
+        if (acc_out)
+            acc_out[t] = (int32_t)acc;
+        if (y) {
+            float a = (float)acc; /* exact: |acc| < 2^24 for K < 2^17 */
+            float ys = a * s_x;
+            y[t] = ys * s_w;
+        }
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------------------------------
+ * Dense bf16 head ([ARCH] s.3: the dense head is the largest single stream; f32_matvec):
+ *   y[r] = sum_k bf16_to_f32(W[r][k]) * x[k]  in fp64 (each product of an 8-bit and a 24-bit
+ *   significand is exact), A[r] = sum_k |W * x|.
+ * ---------------------------------------------------------------------------------------------- */
+int lbo_head_matvec(const uint16_t *W, int64_t N, int64_t K, const float *x, const int64_t *rows, int64_t nrows,
+                    double *y, double *A)
+{
+    for (int64_t t = 0; t < nrows; t++) {
+        int64_t r = row_of(rows, t);
+        if (r < 0 || r >= N)
+            return -1;
+        double acc = 0.0, mag = 0.0;
+        for (int64_t k = 0; k < K; k++) {
+            double p = (double)lbo_bf16_to_float(W[r * K + k]) * (double)x[k];
+            acc += p;
+            mag += fabs(p);
+        }
+        y[t] = acc;
+        if (A)
+            A[t] = mag;
+    }
+    return 0;
+}

@@ -1,0 +1,191 @@
+"""Seeded synthetic inputs for the packed low-bit x int8 product.
+
+This module only *draws* inputs and lays them out in the weight formats' byte layouts; it holds none
+of the product's arithmetic (no decode, no quantiser, no dot products, no scaling). Both sides of every
+parity check consume the bytes it returns: the CPU oracle under ``oracle/`` and the HIP library.
+
+Formats (byte layouts as the pages define them):
+
+* ggml ``Q1_0`` -- bankml technical report, section III.2 "The Q1_0 format and its arithmetic":
+  18-byte blocks of 128 weights, a little-endian binary16 scale ``d`` first, then 16 bytes of sign
+  bits, least-significant bit first (weight i sits at byte i//8, bit i%8).
+* ggml ``Q2_0_g64`` -- same report, section III.5 "The Q2_0_g64 (ternary) kernel": 18-byte blocks of
+  64 weights, binary16 ``d`` first, then 16 bytes of 2-bit codes, lowest bits first (weight i at byte
+  i//4, bits 2*(i%4)); code c stands for weight c-1.
+* planar ternary ``.trit v1`` beat -- tritium "Architecture", section 2 "The one design commitment: bit
+  planes": 16 bytes per 64 consecutive columns of one row, ``{u64 pos, u64 neg}``, column c at bit c.
+
+Workload shapes and value distributions follow the five workloads this library is measured on: block
+scales fp16(|N(0,1)|*0.02), ternary codes -1/0/+1 at 31/38/31 % (the split the bankml report observed
+in Ternary-Bonsai-8B), 1-bit signs Bernoulli(0.5), activations fp32 N(0,1), head weights N(0,0.02)
+rounded to bfloat16.  Random numbers come from numpy's PCG64 stream seeded per input.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+Q1_0 = 1
+Q2_0_G64 = 2
+TERNARY_PLANAR = 3
+
+QK1 = 128  # weights per Q1_0 block
+QK2 = 64  # weights per Q2_0_g64 block
+QKP = 64  # columns per planar beat
+QK8 = 32  # activations per q8_0 block
+
+BLOCK_BYTES = {Q1_0: 18, Q2_0_G64: 18, TERNARY_PLANAR: 16}
+BLOCK_WEIGHTS = {Q1_0: QK1, Q2_0_G64: QK2, TERNARY_PLANAR: QKP}
+
+# ternary weight distribution of the ggml file the pages measured: P(-1), P(0), P(+1), P(+2)
+TERNARY_P = (0.31, 0.38, 0.31, 0.0)
+
+
+def rng(seed: int) -> np.random.Generator:
+    return np.random.default_rng(np.random.PCG64(seed))
+
+
+def fp16_scales(g: np.random.Generator, n: int) -> np.ndarray:
+    """fp16(|z| * 0.02), z ~ N(0,1): the block-scale recipe of every ggml-format workload."""
+    return (np.abs(g.standard_normal(n)) * 0.02).astype(np.float16)
+
+
+def ternary_weights(g: np.random.Generator, N: int, K: int, p=TERNARY_P) -> np.ndarray:
+    """Dense int8 matrix of weights in {-1, 0, +1, +2} drawn i.i.d. with probabilities ``p``."""
+    return (g.choice(4, size=(N, K), p=np.asarray(p, dtype=np.float64)) - 1).astype(np.int8)
+
+
+def sign_weights(g: np.random.Generator, N: int, K: int) -> np.ndarray:
+    """Dense int8 matrix of weights in {-1, +1}, each sign a fair coin."""
+    return np.where(g.integers(0, 2, size=(N, K), dtype=np.int8) == 1, 1, -1).astype(np.int8)
+
+
+def _bits_lsb_first(bits: np.ndarray) -> np.ndarray:
+    """Pack 0/1 values along the last axis, 8 per byte, least-significant bit first."""
+    return np.packbits(bits.astype(np.uint8), axis=-1, bitorder="little")
+
+
+def lay_out_q1_0(w: np.ndarray, d: np.ndarray) -> np.ndarray:
+    """ggml Q1_0 bytes for sign weights ``w`` [N][K] (+1 -> bit 1, -1 -> bit 0) and fp16 scales ``d``
+    [N][K/128].  Returns uint8 [N][K/128][18]."""
+    N, K = w.shape
+    nb = K // QK1
+    assert K % QK1 == 0 and d.shape == (N, nb)
+    out = np.empty((N, nb, 18), dtype=np.uint8)
+    out[:, :, 0:2] = d.astype("<f2").view(np.uint8).reshape(N, nb, 2)
+    out[:, :, 2:18] = _bits_lsb_first((w > 0).reshape(N, nb, QK1))
+    return out
+
+
+def lay_out_q2_0(w: np.ndarray, d: np.ndarray) -> np.ndarray:
+    """ggml Q2_0_g64 bytes for weights ``w`` [N][K] in {-1,0,1,2} (code = w + 1, lowest bits first)
+    and fp16 scales ``d`` [N][K/64].  Returns uint8 [N][K/64][18]."""
+    N, K = w.shape
+    nb = K // QK2
+    assert K % QK2 == 0 and d.shape == (N, nb)
+    codes = (w.astype(np.int16) + 1).astype(np.uint8).reshape(N, nb, 16, 4)
+    packed = codes[..., 0] | (codes[..., 1] << 2) | (codes[..., 2] << 4) | (codes[..., 3] << 6)
+    out = np.empty((N, nb, 18), dtype=np.uint8)
+    out[:, :, 0:2] = d.astype("<f2").view(np.uint8).reshape(N, nb, 2)
+    out[:, :, 2:18] = packed
+    return out
+
+
+def lay_out_planar(w: np.ndarray) -> np.ndarray:
+    """Planar beats for ternary ``w`` [N][K] in {-1,0,+1}: per 64 columns 8 bytes of the "+1" plane
+    then 8 bytes of the "-1" plane, column c at bit c (little-endian u64).  Returns uint8 [N][K/64][16]."""
+    N, K = w.shape
+    nb = K // QKP
+    assert K % QKP == 0
+    out = np.empty((N, nb, 16), dtype=np.uint8)
+    out[:, :, 0:8] = _bits_lsb_first((w == 1).reshape(N, nb, QKP))
+    out[:, :, 8:16] = _bits_lsb_first((w == -1).reshape(N, nb, QKP))
+    return out
+
+
+def activations(g: np.random.Generator, M: int, K: int) -> np.ndarray:
+    """fp32 N(0,1) activation rows [M][K]."""
+    return g.standard_normal((M, K)).astype(np.float32)
+
+
+def bf16_bits(a: np.ndarray) -> np.ndarray:
+    """Round fp32 values to bfloat16 (round-to-nearest-even, via torch) and return the raw uint16 bits."""
+    import torch
+
+    t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16).copy()
+
+
+class Weights:
+    """One synthetic weight tensor: the format bytes plus the values drawn to make them."""
+
+    def __init__(self, fmt, N, K, raw, w, d=None, s_w=None):
+        self.fmt, self.N, self.K = fmt, N, K
+        self.raw = raw  # uint8, ggml blocks [N][K/QK][18] or planar beats [N][K/64][16]
+        self.w = w  # int8 [N][K], the drawn weight values (before scaling)
+        self.d = d  # fp16 [N][K/QK] block scales (ggml formats)
+        self.s_w = s_w  # fp32 per-tensor scale (planar)
+
+    @property
+    def nbytes(self) -> int:
+        return int(self.raw.size)
+
+
+def make_weights(fmt: int, N: int, K: int, seed: int, p=TERNARY_P) -> Weights:
+    g = rng(seed)
+    if fmt == Q1_0:
+        w = sign_weights(g, N, K)
+        d = fp16_scales(g, N * (K // QK1)).reshape(N, K // QK1)
+        return Weights(fmt, N, K, lay_out_q1_0(w, d), w, d=d)
+    if fmt == Q2_0_G64:
+        w = ternary_weights(g, N, K, p)
+        d = fp16_scales(g, N * (K // QK2)).reshape(N, K // QK2)
+        return Weights(fmt, N, K, lay_out_q2_0(w, d), w, d=d)
+    if fmt == TERNARY_PLANAR:
+        p3 = np.asarray(p[:3], dtype=np.float64)
+        w = ternary_weights(g, N, K, tuple(p3 / p3.sum()) + (0.0,))
+        s_w = np.float32(abs(g.standard_normal()) * 0.02)
+        return Weights(fmt, N, K, lay_out_planar(w), w, s_w=s_w)
+    raise ValueError(f"unknown weight format {fmt}")
+
+
+def head_weights(N: int, K: int, seed: int) -> np.ndarray:
+    """Dense head: N(0, 0.02) rounded to bfloat16, raw uint16 bits [N][K]."""
+    g = rng(seed)
+    return bf16_bits((g.standard_normal((N, K)) * 0.02).astype(np.float32))
+
+
+# --- the measured workloads' shapes -------------------------------------------------------------
+
+# Qwen3-8B-like projections (rows x K) of one transformer block, in file order.
+QWEN3_8B_LAYER = (
+    ("attn_q", 4096, 4096),
+    ("attn_k", 1024, 4096),
+    ("attn_v", 1024, 4096),
+    ("attn_output", 4096, 4096),
+    ("ffn_gate", 12288, 4096),
+    ("ffn_up", 12288, 4096),
+    ("ffn_down", 4096, 12288),
+)
+QWEN3_8B_LAYERS = 36
+QWEN3_8B_OUTPUT = ("output", 151669, 4096)
+
+# BitNet-b1.58-2B-like block with the attention projections as 2560x2560 (the workload as stated).
+BITNET_2B_LAYER = (
+    ("attn_q", 2560, 2560),
+    ("attn_k", 2560, 2560),
+    ("attn_v", 2560, 2560),
+    ("attn_output", 2560, 2560),
+    ("ffn_gate", 6912, 2560),
+    ("ffn_up", 6912, 2560),
+    ("ffn_down", 2560, 6912),
+)
+BITNET_2B_LAYERS = 30
+BITNET_HEAD = (128256, 2560)
+
+PREFILL_M = 512
+PREFILL_SHAPES = ((4096, 4096), (12288, 4096))
+
+
+def format_bytes(fmt: int, N: int, K: int) -> int:
+    """Bytes of a packed weight tensor in its on-disk format (18 B per ggml block, 16 B per beat)."""
+    return N * (K // BLOCK_WEIGHTS[fmt]) * BLOCK_BYTES[fmt]
