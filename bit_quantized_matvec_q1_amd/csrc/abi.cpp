@@ -1,0 +1,403 @@
+// The C ABI of liblowbit.so: argument validation, the device check, and dispatch to the kernels.
+// Every argument is checked on the host before anything is launched; an error launches nothing and
+// there is no fallback path (tritium "Architecture", section 4.2: a pinned kernel errors rather than
+// falling back, so a run never measures a different kernel than the one it names).
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "lowbit_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+lb_status fail(lb_status st, const char *fn, const char *what)
+{
+    g_last_error = std::string(fn) + ": " + what;
+    return st;
+}
+
+lb_status hip_fail(const char *fn, hipError_t e)
+{
+    g_last_error = std::string(fn) + ": " + hipGetErrorName(e) + ": " + hipGetErrorString(e);
+    return LB_EDEVICE;
+}
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+bool is_wfmt(int f) { return f == LB_Q1_0 || f == LB_Q2_0_G64 || f == LB_TERNARY_PLANAR; }
+int64_t block_weights(int f) { return f == LB_Q1_0 ? 128 : 64; }
+int64_t block_bytes(int f) { return f == LB_TERNARY_PLANAR ? 16 : 18; }
+int paired_afmt(int f) { return f == LB_TERNARY_PLANAR ? LB_ACT_I8_ROW : LB_ACT_Q8_0; }
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_dev_state[kMaxDevices]; // 0 unknown, 1 gfx950, 2 other
+
+// The kernels are written for gfx950 only; any other device is refused.
+lb_status check_device(const char *fn)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        (void)hipGetLastError();
+        return fail(LB_EUNSUPPORTED, fn, "no HIP device is available (a gfx950 GPU is required)");
+    }
+    int st = g_dev_state[dev].load(std::memory_order_relaxed);
+    if (st == 0) {
+        hipDeviceProp_t prop;
+        e = hipGetDeviceProperties(&prop, dev);
+        if (e != hipSuccess) {
+            (void)hipGetLastError();
+            return fail(LB_EUNSUPPORTED, fn, "cannot query the current device");
+        }
+        st = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+        g_dev_state[dev].store(st, std::memory_order_relaxed);
+    }
+    if (st != 1)
+        return fail(LB_EUNSUPPORTED, fn, "the current device is not gfx950");
+    return LB_OK;
+}
+
+// Shared checks of a decode product's arguments (lowbit_matvec and each batch entry).
+lb_status check_product(const char *fn, int fmt, const void *W, int64_t N, int64_t K, int afmt, const void *xq,
+                        const void *xscale, const void *y)
+{
+    if (!is_wfmt(fmt) || (afmt != LB_ACT_Q8_0 && afmt != LB_ACT_I8_ROW))
+        return fail(LB_EINVAL, fn, "unknown weight or activation format");
+    if (afmt != paired_afmt(fmt))
+        return fail(LB_EINVAL, fn, "activation format does not match the weight format "
+                                   "(Q1_0/Q2_0_g64 take LB_ACT_Q8_0, planar takes LB_ACT_I8_ROW)");
+    if (N < 0 || K < 0)
+        return fail(LB_ESHAPE, fn, "negative size");
+    if (K % block_weights(fmt))
+        return fail(LB_ESHAPE, fn, "K is not a multiple of the weight block (128 for Q1_0, 64 otherwise)");
+    if (K > 32768 || N > INT32_MAX)
+        return fail(LB_ESHAPE, fn, "K above 32768 or N above 2^31-1");
+    if (N * (K / block_weights(fmt)) * block_bytes(fmt) >= (int64_t(1) << 32))
+        return fail(LB_ESHAPE, fn, "weight tensor of 4 GiB or more");
+    if (N == 0)
+        return LB_OK;
+    if (!W || !xq || !xscale || !y)
+        return fail(LB_EINVAL, fn, "null pointer");
+    if (!aligned(W, 16) || !aligned(xq, 16) || !aligned(xscale, 4) || !aligned(y, 4))
+        return fail(LB_EALIGN, fn, "W and xq need 16-byte alignment, xscale and y 4-byte alignment");
+    return LB_OK;
+}
+
+} // namespace
+
+extern "C" {
+
+const char *lowbit_status_str(lb_status st)
+{
+    switch (st) {
+    case LB_OK:
+        return "LB_OK";
+    case LB_EINVAL:
+        return "LB_EINVAL: invalid argument";
+    case LB_ESHAPE:
+        return "LB_ESHAPE: invalid shape";
+    case LB_EALIGN:
+        return "LB_EALIGN: misaligned pointer";
+    case LB_EUNSUPPORTED:
+        return "LB_EUNSUPPORTED: unsupported device";
+    case LB_EDEVICE:
+        return "LB_EDEVICE: HIP runtime error";
+    }
+    return "unknown lb_status";
+}
+
+const char *lowbit_last_error(void) { return g_last_error.c_str(); }
+
+int64_t lowbit_weight_bytes(int fmt, int64_t N, int64_t K)
+{
+    if (!is_wfmt(fmt) || N < 0 || K < 0 || K % block_weights(fmt))
+        return -1;
+    return N * (K / block_weights(fmt)) * block_bytes(fmt);
+}
+
+static lb_status pack_common(const char *fn, int fmt, const void *src, int64_t N, int64_t K, void *dst,
+                             bool unpack, hipStream_t s)
+{
+    if (!is_wfmt(fmt))
+        return fail(LB_EINVAL, fn, "unknown weight format");
+    if (N < 0 || K < 0 || K % block_weights(fmt))
+        return fail(LB_ESHAPE, fn, "negative size or K not a multiple of the weight block");
+    if (N == 0 || K == 0)
+        return LB_OK;
+    if (!src || !dst)
+        return fail(LB_EINVAL, fn, "null pointer");
+    const void *packed = unpack ? src : dst;
+    if (!aligned(packed, 16))
+        return fail(LB_EALIGN, fn, "the device layout needs 16-byte alignment");
+    lb_status st = check_device(fn);
+    if (st != LB_OK)
+        return st;
+    hipError_t e = lb::launch_pack(fmt, static_cast<const uint8_t *>(unpack ? dst : src), N, K,
+                                   static_cast<uint8_t *>(unpack ? const_cast<void *>(src) : dst), unpack, s);
+    return e == hipSuccess ? LB_OK : hip_fail(fn, e);
+}
+
+lb_status lowbit_pack_weights(int fmt, const void *blocks, int64_t N, int64_t K, void *packed, hipStream_t s)
+{
+    return pack_common("lowbit_pack_weights", fmt, blocks, N, K, packed, false, s);
+}
+
+lb_status lowbit_unpack_weights(int fmt, const void *packed, int64_t N, int64_t K, void *blocks, hipStream_t s)
+{
+    return pack_common("lowbit_unpack_weights", fmt, packed, N, K, blocks, true, s);
+}
+
+lb_status lowbit_quantize_act(int afmt, const float *x, int64_t M, int64_t K, int8_t *xq, void *xscale,
+                              hipStream_t s)
+{
+    const char *fn = "lowbit_quantize_act";
+    if (afmt != LB_ACT_Q8_0 && afmt != LB_ACT_I8_ROW)
+        return fail(LB_EINVAL, fn, "unknown activation format");
+    if (M < 0 || K < 0 || M > INT32_MAX)
+        return fail(LB_ESHAPE, fn, "negative size");
+    if (afmt == LB_ACT_Q8_0 && K % lb::QK8)
+        return fail(LB_ESHAPE, fn, "K is not a multiple of 32");
+    if (M == 0 || K == 0)
+        return LB_OK;
+    if (!x || !xq || !xscale)
+        return fail(LB_EINVAL, fn, "null pointer");
+    if (!aligned(x, 16) || !aligned(xq, 16) || !aligned(xscale, 4))
+        return fail(LB_EALIGN, fn, "x and xq need 16-byte alignment, xscale 4-byte alignment");
+    lb_status st = check_device(fn);
+    if (st != LB_OK)
+        return st;
+    hipError_t e = afmt == LB_ACT_Q8_0
+                       ? lb::launch_quantize_q8_0(x, M, K, xq, static_cast<uint16_t *>(xscale), s)
+                       : lb::launch_quantize_i8_row(x, M, K, xq, static_cast<float *>(xscale), s);
+    return e == hipSuccess ? LB_OK : hip_fail(fn, e);
+}
+
+static lb_status matvec_common(const char *fn, int fmt, const void *W, int64_t N, int64_t K, float w_scale,
+                               int afmt, const int8_t *xq, const void *xscale, float *y, int32_t *sums,
+                               hipStream_t s)
+{
+    lb_status st = check_product(fn, fmt, W, N, K, afmt, xq, xscale, sums ? (const void *)sums : (const void *)y);
+    if (st != LB_OK || N == 0)
+        return st;
+    st = check_device(fn);
+    if (st != LB_OK)
+        return st;
+    hipError_t e;
+    if (K == 0) {
+        // an empty sum: y = 0 (and no per-block sums exist; planar row sums are 0)
+        if (sums)
+            e = fmt == LB_TERNARY_PLANAR ? lb::launch_fill_zero_i32(sums, N, s) : hipSuccess;
+        else
+            e = lb::launch_fill_zero(y, N, s);
+    } else {
+        e = lb::launch_matvec(fmt, static_cast<const uint8_t *>(W), N, K, w_scale, xq, xscale, y, sums, s);
+    }
+    return e == hipSuccess ? LB_OK : hip_fail(fn, e);
+}
+
+lb_status lowbit_matvec(int fmt, const void *W, int64_t N, int64_t K, float w_tensor_scale, int afmt,
+                        const int8_t *xq, const void *xscale, float *y, hipStream_t s)
+{
+    return matvec_common("lowbit_matvec", fmt, W, N, K, w_tensor_scale, afmt, xq, xscale, y, nullptr, s);
+}
+
+static lb_status gemm_common(const char *fn, int fmt, const void *W, int64_t N, int64_t K, float w_scale,
+                             int afmt, const int8_t *Xq, const void *Xscale, int64_t M, float *Y, int32_t *sums,
+                             hipStream_t s)
+{
+    if (M < 0 || M > INT32_MAX)
+        return fail(LB_ESHAPE, fn, "negative M");
+    lb_status st = check_product(fn, fmt, W, N, K, afmt, Xq, Xscale, sums ? (const void *)sums : (const void *)Y);
+    if (st != LB_OK || N == 0 || M == 0)
+        return st;
+    if (N * M >= (int64_t(1) << 31) / ((sums && fmt != LB_TERNARY_PLANAR) ? (K / 32 + 1) : 1))
+        return fail(LB_ESHAPE, fn, "output of 2^31 elements or more");
+    st = check_device(fn);
+    if (st != LB_OK)
+        return st;
+    hipError_t e;
+    if (K == 0) {
+        if (sums)
+            e = fmt == LB_TERNARY_PLANAR ? lb::launch_fill_zero_i32(sums, M * N, s) : hipSuccess;
+        else
+            e = lb::launch_fill_zero(Y, M * N, s);
+    } else {
+        e = lb::launch_gemm(fmt, static_cast<const uint8_t *>(W), N, K, w_scale, Xq, Xscale, M, Y, sums, s);
+    }
+    if (e == hipErrorNotSupported)
+        return fail(LB_EUNSUPPORTED, fn, "this weight format has no prefill kernel yet");
+    return e == hipSuccess ? LB_OK : hip_fail(fn, e);
+}
+
+lb_status lowbit_gemm(int fmt, const void *W, int64_t N, int64_t K, float w_tensor_scale, int afmt,
+                      const int8_t *Xq, const void *Xscale, int64_t M, float *Y, hipStream_t s)
+{
+    return gemm_common("lowbit_gemm", fmt, W, N, K, w_tensor_scale, afmt, Xq, Xscale, M, Y, nullptr, s);
+}
+
+lb_status lowbit_block_sums(int fmt, const void *W, int64_t N, int64_t K, int afmt, const int8_t *Xq,
+                            const void *Xscale, int64_t M, int32_t *sums, hipStream_t s)
+{
+    const char *fn = "lowbit_block_sums";
+    if (!sums && N > 0 && M > 0)
+        return fail(LB_EINVAL, fn, "null pointer");
+    if (M == 1)
+        return matvec_common(fn, fmt, W, N, K, 1.0f, afmt, Xq, Xscale, nullptr, sums, s);
+    return gemm_common(fn, fmt, W, N, K, 1.0f, afmt, Xq, Xscale, M, nullptr, sums, s);
+}
+
+lb_status dense_head_matvec(const uint16_t *W, int64_t N, int64_t K, const float *x, float *y, hipStream_t s)
+{
+    const char *fn = "dense_head_matvec";
+    if (N < 0 || K < 0 || N > INT32_MAX)
+        return fail(LB_ESHAPE, fn, "negative size");
+    if (K % 8 || K > 4096)
+        return fail(LB_ESHAPE, fn, "K must be a multiple of 8 and at most 4096");
+    if (N == 0)
+        return LB_OK;
+    if (!W || !x || !y)
+        return fail(LB_EINVAL, fn, "null pointer");
+    if (!aligned(W, 16) || !aligned(x, 16) || !aligned(y, 4))
+        return fail(LB_EALIGN, fn, "W and x need 16-byte alignment, y 4-byte alignment");
+    lb_status st = check_device(fn);
+    if (st != LB_OK)
+        return st;
+    hipError_t e = K == 0 ? lb::launch_fill_zero(y, N, s) : lb::launch_head(W, N, K, x, y, s);
+    return e == hipSuccess ? LB_OK : hip_fail(fn, e);
+}
+
+// ---- batched decode ------------------------------------------------------------------------------
+
+struct lb_batch {
+    struct Group {
+        lb::BatchGroup g;
+        size_t lds;
+    };
+    std::vector<Group> groups;
+    void *dev = nullptr;
+    int device = -1;
+};
+
+lb_status lowbit_batch_create(const lb_matvec_desc *list, int32_t n, lb_batch **out)
+{
+    const char *fn = "lowbit_batch_create";
+    if (!out)
+        return fail(LB_EINVAL, fn, "null output pointer");
+    *out = nullptr;
+    if (!list || n < 1)
+        return fail(LB_EINVAL, fn, "empty or null work list");
+    for (int32_t i = 0; i < n; i++) {
+        const lb_matvec_desc &d = list[i];
+        lb_status st = check_product(fn, d.fmt, d.W, d.N, d.K, d.afmt, d.xq, d.xscale, d.y);
+        if (st != LB_OK)
+            return st;
+        if (d.K == 0 && d.N > 0)
+            return fail(LB_ESHAPE, fn, "K == 0 in a work list (use lowbit_matvec for empty sums)");
+        if (d.N > 0 && lb::matvec_config(d.fmt, d.K) < 0)
+            return fail(LB_ESHAPE, fn, "K above the batched kernel's limit (16384)");
+    }
+    lb_status st = check_device(fn);
+    if (st != LB_OK)
+        return st;
+
+    // one launch group per weight format present, products in list order
+    std::vector<std::vector<lb::DevDesc>> descs(4);
+    std::vector<std::vector<int32_t>> tiles(4);
+    std::vector<size_t> lds(4, 0);
+    for (int32_t i = 0; i < n; i++) {
+        const lb_matvec_desc &d = list[i];
+        if (d.N == 0)
+            continue;
+        lb::DevDesc dd;
+        dd.W = static_cast<const uint8_t *>(d.W);
+        dd.xq = d.xq;
+        dd.xscale = d.xscale;
+        dd.y = d.y;
+        dd.N = (int32_t)d.N;
+        dd.K = (int32_t)d.K;
+        dd.w_scale = d.w_tensor_scale;
+        dd.cfg = lb::matvec_config(d.fmt, d.K);
+        const int rpi = lb::matvec_config_rows_per_iter(d.fmt, dd.cfg);
+        dd.tile_rows = rpi * ((128 + rpi - 1) / rpi);
+        dd.tile_begin = (int32_t)tiles[d.fmt].size();
+        const int64_t nt = (d.N + dd.tile_rows - 1) / dd.tile_rows;
+        for (int64_t t = 0; t < nt; t++)
+            tiles[d.fmt].push_back((int32_t)descs[d.fmt].size());
+        descs[d.fmt].push_back(dd);
+        lds[d.fmt] = std::max(lds[d.fmt], (size_t)lb::matvec_stage_bytes(d.fmt, d.K));
+    }
+    size_t bytes = 0;
+    for (int f = 1; f <= 3; f++)
+        bytes += (descs[f].size() * sizeof(lb::DevDesc) + 255) / 256 * 256 + (tiles[f].size() * sizeof(int32_t) + 255) / 256 * 256;
+    lb_batch *b = new lb_batch();
+    hipGetDevice(&b->device);
+    hipError_t e = hipMalloc(&b->dev, bytes > 0 ? bytes : 256);
+    if (e != hipSuccess) {
+        delete b;
+        return hip_fail(fn, e);
+    }
+    size_t off = 0;
+    for (int f = 1; f <= 3; f++) {
+        if (descs[f].empty())
+            continue;
+        lb_batch::Group grp;
+        grp.g.fmt = f;
+        grp.g.cfg_a = grp.g.cfg_b = -1;
+        grp.g.ntiles = (int32_t)tiles[f].size();
+        char *base = static_cast<char *>(b->dev);
+        grp.g.desc = reinterpret_cast<const lb::DevDesc *>(base + off);
+        e = hipMemcpy(base + off, descs[f].data(), descs[f].size() * sizeof(lb::DevDesc), hipMemcpyHostToDevice);
+        off += (descs[f].size() * sizeof(lb::DevDesc) + 255) / 256 * 256;
+        if (e == hipSuccess) {
+            grp.g.tile_prod = reinterpret_cast<const int32_t *>(base + off);
+            e = hipMemcpy(base + off, tiles[f].data(), tiles[f].size() * sizeof(int32_t), hipMemcpyHostToDevice);
+            off += (tiles[f].size() * sizeof(int32_t) + 255) / 256 * 256;
+        }
+        if (e != hipSuccess) {
+            hipFree(b->dev);
+            delete b;
+            return hip_fail(fn, e);
+        }
+        grp.lds = lds[f];
+        b->groups.push_back(grp);
+    }
+    *out = b;
+    return LB_OK;
+}
+
+lb_status lowbit_matvec_batched(const lb_batch *b, hipStream_t s)
+{
+    const char *fn = "lowbit_matvec_batched";
+    if (!b)
+        return fail(LB_EINVAL, fn, "null batch");
+    lb_status st = check_device(fn);
+    if (st != LB_OK)
+        return st;
+    int dev = -1;
+    hipGetDevice(&dev);
+    if (dev != b->device)
+        return fail(LB_EINVAL, fn, "the batch was created on another device");
+    for (const auto &grp : b->groups) {
+        hipError_t e = lb::launch_matvec_batched(grp.g, s, grp.lds);
+        if (e != hipSuccess)
+            return hip_fail(fn, e);
+    }
+    return LB_OK;
+}
+
+void lowbit_batch_destroy(lb_batch *b)
+{
+    if (!b)
+        return;
+    if (b->dev)
+        (void)hipFree(b->dev);
+    delete b;
+}
+
+} // extern "C"

@@ -1,0 +1,154 @@
+// Activation quantisers, the one-time weight layout conversion and small fills.
+#include "lowbit_internal.h"
+
+namespace lb {
+
+// q8_0 (bankml technical report, section III.2: blocks of 32 signed bytes with their own half-precision
+// scale, 127 / max|x| with round-half-to-even).  One thread per block of 32: amax is exact, the stored
+// scale is fp16_rne(amax / 127) from the correctly rounded fp32 quotient, the multiplier 127 / amax is a
+// correctly rounded fp32 quotient, and each q is round-half-even of the fp32 product (v_rndne_f32).
+__global__ __launch_bounds__(WG) void quantize_q8_0_kernel(const float *__restrict__ x, int64_t nblocks,
+                                                           int8_t *__restrict__ xq, uint16_t *__restrict__ xs)
+{
+    const int64_t b = (int64_t)blockIdx.x * WG + threadIdx.x;
+    if (b >= nblocks)
+        return;
+    const float4 *src = reinterpret_cast<const float4 *>(x + b * QK8);
+    float v[QK8];
+#pragma unroll
+    for (int i = 0; i < QK8 / 4; i++) {
+        float4 t = src[i];
+        v[4 * i + 0] = t.x;
+        v[4 * i + 1] = t.y;
+        v[4 * i + 2] = t.z;
+        v[4 * i + 3] = t.w;
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < QK8; i++)
+        amax = fmaxf(amax, fabsf(v[i]));
+    const float d = amax / 127.0f;
+    const float id = amax > 0.0f ? 127.0f / amax : 0.0f;
+    xs[b] = __half_as_ushort(__float2half_rn(d));
+    uint32_t packed[QK8 / 4];
+#pragma unroll
+    for (int i = 0; i < QK8 / 4; i++) {
+        uint32_t w = 0;
+#pragma unroll
+        for (int t = 0; t < 4; t++) {
+            const int q = (int)rintf(v[4 * i + t] * id);
+            w |= (uint32_t)(q & 0xff) << (8 * t);
+        }
+        packed[i] = w;
+    }
+    uint4 *dst = reinterpret_cast<uint4 *>(xq + b * QK8);
+    dst[0] = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+    dst[1] = make_uint4(packed[4], packed[5], packed[6], packed[7]);
+}
+
+hipError_t launch_quantize_q8_0(const float *x, int64_t M, int64_t K, int8_t *xq, uint16_t *xs, hipStream_t s)
+{
+    const int64_t nblocks = M * (K / QK8);
+    const int64_t grid = (nblocks + WG - 1) / WG;
+    hipLaunchKernelGGL(quantize_q8_0_kernel, dim3((unsigned)grid), dim3(WG), 0, s, x, nblocks, xq, xs);
+    return hipGetLastError();
+}
+
+// Per-token int8 (tritium "Architecture", section 1: int8 activations; one absmax scale per token).
+// One workgroup per row: amax over the row, s = amax / 127, q = clamp(rne(x * (127 / amax)), -128, 127).
+__global__ __launch_bounds__(WG) void quantize_i8_row_kernel(const float *__restrict__ x, int64_t K,
+                                                             int8_t *__restrict__ xq, float *__restrict__ xs)
+{
+    __shared__ float red[WG / 64];
+    const int64_t m = blockIdx.x;
+    const float *xr = x + m * K;
+    float amax = 0.0f;
+    for (int64_t k = threadIdx.x; k < K; k += WG)
+        amax = fmaxf(amax, fabsf(xr[k]));
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1)
+        amax = fmaxf(amax, __shfl_xor(amax, off, 64));
+    if ((threadIdx.x & 63) == 0)
+        red[threadIdx.x >> 6] = amax;
+    __syncthreads();
+    amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    const float id = amax > 0.0f ? 127.0f / amax : 0.0f;
+    if (threadIdx.x == 0)
+        xs[m] = amax / 127.0f;
+    int8_t *qr = xq + m * K;
+    for (int64_t k = threadIdx.x; k < K; k += WG) {
+        float v = rintf(xr[k] * id);
+        v = fminf(fmaxf(v, -128.0f), 127.0f);
+        qr[k] = (int8_t)(int)v;
+    }
+}
+
+hipError_t launch_quantize_i8_row(const float *x, int64_t M, int64_t K, int8_t *xq, float *xs, hipStream_t s)
+{
+    hipLaunchKernelGGL(quantize_i8_row_kernel, dim3((unsigned)M), dim3(WG), 0, s, x, K, xq, xs);
+    return hipGetLastError();
+}
+
+// ggml blocks [N][nb][2 + 16] <-> device layout [N][nb][16] code records, then [N][nb] binary16 scales.
+// Planar beats are copied unchanged.  One thread per block; byte accesses (the ggml stream has 18-byte
+// records, so nothing in it is aligned).
+__global__ __launch_bounds__(WG) void pack_kernel(int fmt, const uint8_t *__restrict__ src, int64_t nblk,
+                                                  uint8_t *__restrict__ dst, int unpack)
+{
+    const int64_t b = (int64_t)blockIdx.x * WG + threadIdx.x;
+    if (b >= nblk)
+        return;
+    if (fmt == LB_TERNARY_PLANAR) {
+        for (int i = 0; i < 16; i++)
+            dst[b * 16 + i] = src[b * 16 + i];
+        return;
+    }
+    uint8_t *codes = unpack ? nullptr : dst;
+    if (!unpack) {
+        const uint8_t *blk = src + b * 18;
+        for (int i = 0; i < 16; i++)
+            codes[b * 16 + i] = blk[2 + i];
+        dst[nblk * 16 + b * 2 + 0] = blk[0];
+        dst[nblk * 16 + b * 2 + 1] = blk[1];
+    } else {
+        uint8_t *blk = dst + b * 18;
+        for (int i = 0; i < 16; i++)
+            blk[2 + i] = src[b * 16 + i];
+        blk[0] = src[nblk * 16 + b * 2 + 0];
+        blk[1] = src[nblk * 16 + b * 2 + 1];
+    }
+}
+
+hipError_t launch_pack(int fmt, const uint8_t *blocks, int64_t N, int64_t K, uint8_t *packed, bool unpack,
+                       hipStream_t s)
+{
+    const int64_t nblk = N * (K / (fmt == LB_Q1_0 ? 128 : 64));
+    const int64_t grid = (nblk + WG - 1) / WG;
+    if (unpack)
+        hipLaunchKernelGGL(pack_kernel, dim3((unsigned)grid), dim3(WG), 0, s, fmt, (const uint8_t *)packed, nblk,
+                           (uint8_t *)blocks, 1);
+    else
+        hipLaunchKernelGGL(pack_kernel, dim3((unsigned)grid), dim3(WG), 0, s, fmt, blocks, nblk, packed, 0);
+    return hipGetLastError();
+}
+
+template <typename T> __global__ __launch_bounds__(WG) void fill_zero_kernel(T *__restrict__ y, int64_t n)
+{
+    const int64_t i = (int64_t)blockIdx.x * WG + threadIdx.x;
+    if (i < n)
+        y[i] = T(0);
+}
+
+hipError_t launch_fill_zero(float *y, int64_t n, hipStream_t s)
+{
+    hipLaunchKernelGGL(fill_zero_kernel<float>, dim3((unsigned)((n + WG - 1) / WG)), dim3(WG), 0, s, y, n);
+    return hipGetLastError();
+}
+
+hipError_t launch_fill_zero_i32(int32_t *y, int64_t n, hipStream_t s)
+{
+    hipLaunchKernelGGL(fill_zero_kernel<int32_t>, dim3((unsigned)((n + WG - 1) / WG)), dim3(WG), 0, s, y, n);
+    return hipGetLastError();
+}
+
+} // namespace lb

@@ -1,0 +1,168 @@
+/*
+ * lowbit.h -- C ABI of liblowbit.so: products of packed low-bit weights with int8 activations on one
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Weight formats:
+ *   LB_Q1_0           ggml Q1_0: 18-byte blocks of 128 weights, binary16 scale d then 16 bytes of sign
+ *                     bits, least-significant bit first; weight = d * (bit ? +1 : -1).
+ *                     (bankml technical report, section III.2 "The Q1_0 format and its arithmetic".)
+ *   LB_Q2_0_G64       ggml Q2_0 with group 64: 18-byte blocks of 64 weights, binary16 d then 16 bytes of
+ *                     2-bit codes, lowest bits first; weight = (code - 1) * d, code in {0,1,2,3}.
+ *                     (bankml technical report, section III.5 "The Q2_0_g64 (ternary) kernel".)
+ *   LB_TERNARY_PLANAR the planar ternary beat: 16 bytes per 64 consecutive columns of one row,
+ *                     {u64 pos, u64 neg}, column c at bit c; weight = pos_c - neg_c, times one fp32
+ *                     per-tensor scale.  (tritium "Architecture", section 2 "bit planes".)
+ *
+ * Activation formats:
+ *   LB_ACT_Q8_0       ggml q8_0: int8 xq[M][K] plus binary16 scales xscale[M][K/32]; one block of 32
+ *                     activations per scale (bankml technical report, section III.2).  Used with the
+ *                     two ggml weight formats.
+ *   LB_ACT_I8_ROW     int8 xq[M][K] plus one fp32 scale per row (per token), xscale[M] (tritium
+ *                     "Architecture", section 1: activations are int8).  Used with the planar format.
+ *
+ * Conventions for every entry point:
+ *   - Tensor pointers are DEVICE pointers unless stated otherwise; the caller owns every buffer.  No
+ *     entry point below allocates, frees or synchronises, except lowbit_batch_create/destroy, which
+ *     are set-up calls.
+ *   - Work is enqueued asynchronously on the caller's HIP stream `s` (NULL = the null stream).
+ *   - Arguments are validated on the host before anything is launched; an error launches nothing.
+ *     There is no fallback path: an unsupported device or shape is an error, never a slower kernel.
+ *   - Outputs are row-major fp32.  Integer per-block sums are exact; fp32 outputs follow the
+ *     definition  y = sum_b d_w[b] * sum_{j in b} d_x[j] * isum[j]  up to fp32 rounding order.
+ *   - N == 0 or M == 0 is an empty product: LB_OK, nothing launched.  K == 0 writes zeros.
+ */
+#ifndef LOWBIT_H
+#define LOWBIT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { LB_Q1_0 = 1, LB_Q2_0_G64 = 2, LB_TERNARY_PLANAR = 3 } lb_wfmt;
+typedef enum { LB_ACT_Q8_0 = 1, LB_ACT_I8_ROW = 2 } lb_afmt;
+
+typedef enum {
+    LB_OK = 0,
+    LB_EINVAL = 1,       /* null pointer, unknown enum, or a weight/activation format pairing that is not defined */
+    LB_ESHAPE = 2,       /* negative size, K not a multiple of the weight block (128, 64, 64), or over a limit */
+    LB_EALIGN = 3,       /* a pointer is not aligned as its argument requires */
+    LB_EUNSUPPORTED = 4, /* the current device is not gfx950 */
+    LB_EDEVICE = 5       /* a HIP call failed; lowbit_last_error() holds the runtime's message */
+} lb_status;
+
+/* Human-readable name of a status code (static string). */
+const char *lowbit_status_str(lb_status st);
+
+/* Message of the last error raised by this library on the calling thread ("" if none). */
+const char *lowbit_last_error(void);
+
+/*
+ * Bytes of the device layout of an N x K weight tensor in format `fmt`: 18 per ggml block (128 or 64
+ * weights), 16 per planar beat -- the same count as the on-disk format (1.125, 2.25 and 2 bits per
+ * weight; bankml technical report sections III.2 and III.5).  Returns -1 for a bad format or shape.
+ */
+int64_t lowbit_weight_bytes(int fmt, int64_t N, int64_t K);
+
+/*
+ * One-time conversion of a ggml block stream into the device layout the kernels read.
+ *   blocks: device, N rows x K/QK blocks of 18 bytes, row-major, no alignment requirement.
+ *   packed: device, lowbit_weight_bytes(fmt, N, K) bytes, 16-byte aligned.  Layout: all 16-byte code
+ *           records row-major ([N][K/QK][16]), then all binary16 scales row-major ([N][K/QK]).
+ * Lossless (lowbit_unpack_weights is its inverse).  For LB_TERNARY_PLANAR the beat stream already is
+ * the device layout (tritium "Architecture", section 2: the file layout is the beat stream) and pack
+ * copies it unchanged.
+ */
+lb_status lowbit_pack_weights(int fmt, const void *blocks, int64_t N, int64_t K, void *packed, hipStream_t s);
+lb_status lowbit_unpack_weights(int fmt, const void *packed, int64_t N, int64_t K, void *blocks, hipStream_t s);
+
+/*
+ * Quantise fp32 activation rows x[M][K] (device, 16-byte aligned).
+ *   LB_ACT_Q8_0:  per block of 32, amax = max|x|; xscale (uint16 binary16, [M][K/32]) = fp16_rne(amax/127);
+ *                 xq = round_half_even(x * (127/amax)) in fp32, 0 when amax = 0.  K % 32 == 0.
+ *                 (bankml technical report, section III.2: 127 / max|x| with round-half-to-even.)
+ *   LB_ACT_I8_ROW: per row, amax over the row; xscale (fp32, [M]) = amax/127;
+ *                 xq = clamp(round_half_even(x * (127/amax)), -128, 127).
+ *   xq: device int8 [M][K], 16-byte aligned.  xscale: device, 4-byte aligned.
+ */
+lb_status lowbit_quantize_act(int afmt, const float *x, int64_t M, int64_t K, int8_t *xq, void *xscale,
+                              hipStream_t s);
+
+/*
+ * Batch-1 decode product y[N] = W . dequant(xq): the select-accumulate of the weights over the int8
+ * activations, exact integer sums per activation block, scaled per block in fp32
+ * (bankml technical report, sections III.2, III.5 and III.8; tritium "Architecture", sections 1-2).
+ *   W:      device layout of the N x K tensor (lowbit_pack_weights; planar beats as they are), 16-byte aligned.
+ *   w_tensor_scale: planar per-tensor scale s_w (y = ((float)acc * s_x) * s_w); ignored otherwise.
+ *   afmt:   LB_ACT_Q8_0 for the ggml formats, LB_ACT_I8_ROW for planar.
+ *   xq:     device int8 [K], 16-byte aligned.  xscale: binary16 [K/32] or one fp32, 4-byte aligned.
+ *   y:      device fp32 [N], 4-byte aligned.
+ * Limits: K <= 65536; the weight tensor must be smaller than 4 GiB.
+ */
+lb_status lowbit_matvec(int fmt, const void *W, int64_t N, int64_t K, float w_tensor_scale, int afmt,
+                        const int8_t *xq, const void *xscale, float *y, hipStream_t s);
+
+/*
+ * Prefill product Y[M][N] = dequant(Xq) . W^T for M activation rows: the same per-block integer sums
+ * as lowbit_matvec, computed as int8 matrix-core products over weight tiles unpacked to int8 in LDS,
+ * then scaled per block in fp32 (bankml technical report, section III.3: a tile that loads each weight
+ * block once and applies it to several activation columns; tritium "Architecture", section 3:
+ * prefill runs compute-bound).
+ *   Xq: device int8 [M][K], 16-byte aligned; Xscale: binary16 [M][K/32] (ggml formats) or fp32 [M].
+ *   Y:  device fp32 [M][N], 4-byte aligned.
+ */
+lb_status lowbit_gemm(int fmt, const void *W, int64_t N, int64_t K, float w_tensor_scale, int afmt,
+                      const int8_t *Xq, const void *Xscale, int64_t M, float *Y, hipStream_t s);
+
+/*
+ * The exact integer sums the products above are built from, written by the same kernels (M == 1: the
+ * decode kernel; M > 1: the prefill kernel) instantiated with one extra store:
+ *   ggml formats: sums int32 [M][N][K/32], sums[m][n][j] = sum over activation block j of w * q;
+ *   planar:       sums int32 [M][N], the whole row's select-accumulate.
+ */
+lb_status lowbit_block_sums(int fmt, const void *W, int64_t N, int64_t K, int afmt, const int8_t *Xq,
+                            const void *Xscale, int64_t M, int32_t *sums, hipStream_t s);
+
+/*
+ * Dense bf16 head matvec y[N] = sum_k bf16_to_f32(W[n][k]) * x[k], accumulated in fp32
+ * (tritium "Architecture", section 3: the dense head is the largest single stream; bf16 storage).
+ *   W: device uint16 bf16 bits [N][K], 16-byte aligned, K % 8 == 0; x: device fp32 [K], 16-byte aligned;
+ *   y: device fp32 [N].  K <= 16384.
+ */
+lb_status dense_head_matvec(const uint16_t *W, int64_t N, int64_t K, const float *x, float *y, hipStream_t s);
+
+/*
+ * Many independent decode products in ONE launch (a token's work list).  A batch is a set-up object:
+ * lowbit_batch_create validates the host-side list, and copies it with its tile table into device
+ * memory it allocates once; lowbit_matvec_batched then enqueues a single kernel over every product.
+ * (tritium "Architecture", section 7: handing each small matvec to a pool costs more than the matvec
+ * itself -- dispatch, not arithmetic, is what a token's many products must amortise.)
+ */
+typedef struct {
+    int32_t fmt;          /* lb_wfmt */
+    int32_t afmt;         /* lb_afmt, paired with fmt as in lowbit_matvec */
+    int64_t N, K;         /* rows, columns */
+    const void *W;        /* device layout, 16-byte aligned */
+    float w_tensor_scale; /* planar only */
+    const int8_t *xq;     /* device int8 [K] */
+    const void *xscale;   /* device binary16 [K/32] or fp32 [1] */
+    float *y;             /* device fp32 [N] */
+} lb_matvec_desc;
+
+typedef struct lb_batch lb_batch;
+
+/* list: HOST array of n descriptors (n >= 1).  On success *out owns device memory until destroyed.
+ * The buffers the descriptors point to must stay valid while the batch is used. */
+lb_status lowbit_batch_create(const lb_matvec_desc *list, int32_t n, lb_batch **out);
+lb_status lowbit_matvec_batched(const lb_batch *b, hipStream_t s);
+void lowbit_batch_destroy(lb_batch *b);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LOWBIT_H */

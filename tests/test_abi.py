@@ -1,0 +1,100 @@
+"""The C ABI on the host: the library loads, exports every entry point include/lowbit.h declares, and
+rejects bad arguments with its status codes before touching a device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import bit_quantized_matvec_q1_amd.lowbit as L
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "lowbit.h")
+
+A16 = 1 << 20  # a 16-byte-aligned stand-in address; never dereferenced (every call below fails validation)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*\b([a-z_0-9]+)\s*\(", text, flags=re.M)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert "lowbit_matvec" in names and "lowbit_gemm" in names and "dense_head_matvec" in names
+    for n in names:
+        assert hasattr(L.lib, n), n
+        assert n in L.SIGNATURES, f"{n} declared in lowbit.h but not bound in lowbit.py"
+    assert set(L.SIGNATURES) == set(names)
+
+
+def test_status_strings():
+    for st in range(6):
+        assert L.lib.lowbit_status_str(st)
+    assert L.lib.lowbit_status_str(0) == b"LB_OK"
+
+
+def test_weight_bytes():
+    assert L.lowbit_weight_bytes(L.Q1_0, 4096, 4096) == 2_359_296
+    assert L.lowbit_weight_bytes(L.Q2_0_G64, 4096, 4096) == 4_718_592
+    assert L.lowbit_weight_bytes(L.TERNARY_PLANAR, 6912, 2560) == 4_423_680
+    assert L.lowbit_weight_bytes(L.Q1_0, 4, 64) == -1
+    assert L.lowbit_weight_bytes(7, 4, 64) == -1
+    assert L.lowbit_weight_bytes(L.Q2_0_G64, -1, 64) == -1
+
+
+def mv(fmt=L.Q2_0_G64, W=A16, N=8, K=128, afmt=L.ACT_Q8_0, xq=A16, xs=A16, y=A16):
+    return L.lib.lowbit_matvec(fmt, W, N, K, 1.0, afmt, xq, xs, y, None)
+
+
+def test_matvec_validation_codes():
+    assert mv(fmt=9) == L.LB_EINVAL
+    assert mv(afmt=9) == L.LB_EINVAL
+    assert mv(afmt=L.ACT_I8_ROW) == L.LB_EINVAL  # Q2_0 needs q8_0 activations
+    assert mv(fmt=L.TERNARY_PLANAR, afmt=L.ACT_Q8_0) == L.LB_EINVAL
+    assert mv(N=-1) == L.LB_ESHAPE
+    assert mv(K=96) == L.LB_ESHAPE  # not a multiple of 64
+    assert mv(fmt=L.Q1_0, K=192) == L.LB_ESHAPE  # not a multiple of 128
+    assert mv(K=32768 + 64) == L.LB_ESHAPE
+    assert mv(W=None) == L.LB_EINVAL
+    assert mv(y=None) == L.LB_EINVAL
+    assert mv(W=A16 + 8) == L.LB_EALIGN
+    assert mv(xq=A16 + 4) == L.LB_EALIGN
+    assert mv(y=A16 + 2) == L.LB_EALIGN
+    assert mv(N=0, W=None, y=None) == L.LB_OK  # empty product: nothing to do, nothing touched
+    assert b"lowbit_matvec" in L.lib.lowbit_last_error()
+
+
+def test_other_entry_points_validate():
+    lib = L.lib
+    assert lib.lowbit_quantize_act(3, A16, 1, 64, A16, A16, None) == L.LB_EINVAL
+    assert lib.lowbit_quantize_act(L.ACT_Q8_0, A16, 1, 48, A16, A16, None) == L.LB_ESHAPE
+    assert lib.lowbit_quantize_act(L.ACT_Q8_0, A16 + 4, 1, 64, A16, A16, None) == L.LB_EALIGN
+    assert lib.lowbit_quantize_act(L.ACT_Q8_0, A16, 0, 64, None, None, None) == L.LB_OK
+    assert lib.lowbit_pack_weights(L.Q1_0, A16, 2, 64, A16, None) == L.LB_ESHAPE
+    assert lib.lowbit_pack_weights(L.Q2_0_G64, A16, 2, 64, A16 + 8, None) == L.LB_EALIGN
+    assert lib.lowbit_gemm(L.Q2_0_G64, A16, 8, 64, 1.0, L.ACT_Q8_0, A16, A16, -1, A16, None) == L.LB_ESHAPE
+    assert lib.lowbit_gemm(L.Q2_0_G64, A16, 8, 64, 1.0, L.ACT_I8_ROW, A16, A16, 4, A16, None) == L.LB_EINVAL
+    assert lib.lowbit_block_sums(L.Q2_0_G64, A16, 8, 64, L.ACT_Q8_0, A16, A16, 1, None, None) == L.LB_EINVAL
+    assert lib.dense_head_matvec(A16, 8, 12, A16, A16, None) == L.LB_ESHAPE
+    assert lib.dense_head_matvec(A16, 8, 8192, A16, A16, None) == L.LB_ESHAPE
+    assert lib.dense_head_matvec(A16 + 2, 8, 64, A16, A16, None) == L.LB_EALIGN
+    assert lib.lowbit_matvec_batched(None, None) == L.LB_EINVAL
+    h = ctypes.c_void_p()
+    assert lib.lowbit_batch_create(None, 0, ctypes.byref(h)) == L.LB_EINVAL
+    bad = (L.lb_matvec_desc * 1)(L.lb_matvec_desc(L.Q2_0_G64, L.ACT_Q8_0, 8, 100, A16, 1.0, A16, A16, A16))
+    assert lib.lowbit_batch_create(ctypes.cast(bad, ctypes.c_void_p), 1, ctypes.byref(h)) == L.LB_ESHAPE
+
+
+def _has_device():
+    import torch
+
+    return torch.cuda.device_count() > 0
+
+
+@pytest.mark.skipif(_has_device(), reason="checks the no-device refusal; would launch on a real device")
+def test_no_device_is_refused_without_launch():
+    assert mv() == L.LB_EUNSUPPORTED
+    assert b"gfx950" in L.lib.lowbit_last_error()
+    with pytest.raises(L.LowbitError):
+        L.lowbit_matvec(L.Q2_0_G64, A16, 8, 128, 1.0, L.ACT_Q8_0, A16, A16, A16, stream=0)

@@ -1,0 +1,97 @@
+"""GPU parity of the dense bf16 head and of the batched decode launch against the CPU oracle."""
+import numpy as np
+import pytest
+import torch
+
+import bit_quantized_matvec_q1_amd.lowbit as L
+import oracle
+import synth
+from gpu_util import act_for, assert_close, dev, gpu_matvec, host, packed_weights, say
+
+pytestmark = pytest.mark.gpu
+
+
+def gpu_head(W, N, K, x):
+    y = torch.empty(N, dtype=torch.float32, device="cuda")
+    L.dense_head_matvec(dev(W), N, K, dev(x), y)
+    return host(y)
+
+
+@pytest.mark.parametrize("N,K", [(1, 8), (77, 520), (1000, 2560), (300, 4096)])
+def test_head_shapes(N, K):
+    say(f"case head N={N} K={K}")
+    W = synth.head_weights(N, K, 4000 + N)
+    x = synth.activations(synth.rng(4001 + K), 1, K)[0]
+    y = gpu_head(W, N, K, x)
+    y_ref, A = oracle.head_matvec(W, N, K, x)
+    assert_close(y, y_ref, A, K, f"head {N}x{K}")
+
+
+def test_head_full_size_sampled():
+    """The tied 128256 x 2560 head at full size; the oracle checks a seeded sample of rows."""
+    N, K = synth.BITNET_HEAD
+    say(f"case head full {N}x{K}")
+    W = synth.head_weights(N, K, 4100)
+    x = synth.activations(synth.rng(4101), 1, K)[0]
+    y = gpu_head(W, N, K, x)
+    rows = np.unique(np.concatenate([synth.rng(4102).integers(0, N, 2000), [0, N - 1]]))
+    y_ref, A = oracle.head_matvec(W, N, K, x, rows=rows)
+    assert_close(y[rows], y_ref, A, K, "head full size (sampled rows)")
+
+
+def _product(fmt, N, K, seed):
+    Wt = synth.make_weights(fmt, N, K, seed)
+    q, xs, _ = act_for(fmt, K, seed + 1)
+    return Wt, packed_weights(Wt), q, xs
+
+
+@pytest.mark.parametrize("fmt", [synth.Q1_0, synth.Q2_0_G64, synth.TERNARY_PLANAR])
+def test_batched_matches_single_and_oracle(fmt):
+    shapes = [(300, 1024), (1024, 4096), (129, 12288), (1, 128), (517, 2560)]
+    if fmt != synth.Q1_0:
+        shapes.append((70, 6912 // 64 * 64))
+    say(f"case batched fmt={fmt} shapes={shapes}")
+    prods, descs, ys = [], [], []
+    for i, (N, K) in enumerate(shapes):
+        Wt, packed, q, xs = _product(fmt, N, K, 5000 + 10 * i)
+        qd, xsd = dev(q), dev(xs)
+        y = torch.full((N,), float("nan"), dtype=torch.float32, device="cuda")
+        prods.append((Wt, packed, q, xs, qd, xsd))
+        ys.append(y)
+        descs.append(L.desc(fmt, packed, N, K, qd, xsd, y, w_tensor_scale=Wt.s_w if Wt.s_w is not None else 1.0))
+    b = L.Batch(descs)
+    b.run()
+    torch.cuda.synchronize()
+    for (N, K), (Wt, packed, q, xs, _, _), y in zip(shapes, prods, ys):
+        yb = host(y)
+        ys_single = gpu_matvec(fmt, packed, N, K, q, xs, w_scale=Wt.s_w if Wt.s_w is not None else 1.0)
+        assert np.array_equal(yb, ys_single), f"batched != single for {N}x{K}"
+        if fmt == synth.TERNARY_PLANAR:
+            _, y_ref = oracle.matvec_planar(Wt.raw, N, K, q, xs[0], Wt.s_w)
+            assert np.array_equal(yb, y_ref)
+        else:
+            y_ref, A = oracle.matvec_q(fmt, Wt.raw, N, K, q, xs)
+            assert_close(yb, y_ref, A, K // 32, f"batched {N}x{K}")
+    b.run()  # a second launch of the same plan gives the same bits
+    torch.cuda.synchronize()
+    assert np.array_equal(host(ys[1]), gpu_matvec(fmt, prods[1][1], shapes[1][0], shapes[1][1], prods[1][2],
+                                                  prods[1][3], w_scale=prods[1][0].s_w or 1.0))
+    b.close()
+
+
+def test_batched_mixed_formats():
+    say("case batched mixed formats")
+    items = [(synth.Q2_0_G64, 256, 4096), (synth.Q1_0, 256, 4096), (synth.TERNARY_PLANAR, 256, 2560)]
+    descs, keep = [], []
+    for i, (fmt, N, K) in enumerate(items):
+        Wt, packed, q, xs = _product(fmt, N, K, 5500 + i)
+        qd, xsd = dev(q), dev(xs)
+        y = torch.empty(N, dtype=torch.float32, device="cuda")
+        keep.append((fmt, N, K, Wt, packed, q, xs, qd, xsd, y))
+        descs.append(L.desc(fmt, packed, N, K, qd, xsd, y, w_tensor_scale=Wt.s_w if Wt.s_w is not None else 1.0))
+    b = L.Batch(descs)
+    b.run()
+    for fmt, N, K, Wt, packed, q, xs, _, _, y in keep:
+        ref = gpu_matvec(fmt, packed, N, K, q, xs, w_scale=Wt.s_w if Wt.s_w is not None else 1.0)
+        assert np.array_equal(host(y), ref)
+    b.close()

@@ -1,0 +1,203 @@
+"""GPU parity of the decode products (Q1_0, Q2_0_g64, planar) and the activation quantisers against the
+CPU oracle, through the C ABI: per-block integer sums bit-exact, fp32 outputs within 1e-5 relative
+(with the cancellation floor), planar outputs and quantised bytes bit-exact."""
+import numpy as np
+import pytest
+import torch
+
+import bit_quantized_matvec_q1_amd.lowbit as L
+import oracle
+import synth
+from gpu_util import act_for, assert_close, dev, gpu_matvec, gpu_sums, host, packed_weights, say
+
+pytestmark = pytest.mark.gpu
+
+Q_FMTS = [synth.Q1_0, synth.Q2_0_G64]
+ALL_FMTS = Q_FMTS + [synth.TERNARY_PLANAR]
+NAMES = {synth.Q1_0: "Q1_0", synth.Q2_0_G64: "Q2_0_g64", synth.TERNARY_PLANAR: "planar"}
+
+
+def check_product(fmt, N, K, seed, p=synth.TERNARY_P, q_override=None, rows=None):
+    say(f"case {NAMES[fmt]} N={N} K={K} seed={seed}")
+    Wt = synth.make_weights(fmt, N, K, seed, p=p)
+    q, xs, _ = act_for(fmt, K, seed + 1)
+    if q_override is not None:
+        q = q_override(q)
+    packed = packed_weights(Wt)
+    y = gpu_matvec(fmt, packed, N, K, q, xs, w_scale=Wt.s_w if Wt.s_w is not None else 1.0)
+    sums = gpu_sums(fmt, packed, N, K, q[None, :], xs[None, :] if fmt != synth.TERNARY_PLANAR else xs)[0]
+    r = np.arange(N) if rows is None else np.asarray(rows)
+    if fmt == synth.TERNARY_PLANAR:
+        acc, y_ref = oracle.matvec_planar(Wt.raw, N, K, q, xs[0], Wt.s_w, rows=r)
+        assert np.array_equal(sums[r], acc), "planar row sums differ"
+        assert np.array_equal(y[r], y_ref), "planar outputs differ"
+    else:
+        ref_sums = oracle.block_sums(fmt, Wt.raw, N, K, q, rows=r)
+        assert np.array_equal(sums[r], ref_sums), "per-block integer sums differ"
+        y_ref, A = oracle.matvec_q(fmt, Wt.raw, N, K, q, xs, rows=r)
+        assert_close(y[r], y_ref, A, K // 32, f"{NAMES[fmt]} {N}x{K}")
+    return y
+
+
+@pytest.mark.parametrize("fmt", ALL_FMTS, ids=NAMES.get)
+@pytest.mark.parametrize("N,K", [(1, 128), (37, 384), (300, 640), (1000, 1024), (517, 2560), (130, 4096),
+                                 (70, 6912), (33, 12288)])
+def test_matvec_shapes(fmt, N, K):
+    check_product(fmt, N, K, seed=1000 + N + K)
+
+
+@pytest.mark.parametrize("fmt", ALL_FMTS, ids=NAMES.get)
+def test_matvec_odd_block_counts(fmt):
+    # ragged tails: odd numbers of blocks per row, and row counts that leave partial tiles
+    for K in ((128 * 3, 128 * 5, 128 * 9) if fmt == synth.Q1_0 else (64 * 3, 64 * 7, 64 * 33)):
+        check_product(fmt, 129, K, seed=2000 + K)
+
+
+@pytest.mark.parametrize("fmt", ALL_FMTS, ids=NAMES.get)
+def test_matvec_largest_k(fmt):
+    check_product(fmt, 20, 32768, seed=2100)
+
+
+def test_q2_code3_and_minus_128():
+    # every code including 3 (+2), and the activation extremes
+    def extremes(q):
+        q = q.copy()
+        q[::7] = -128
+        q[3::11] = 127
+        return q
+
+    check_product(synth.Q2_0_G64, 257, 4096, seed=2200, p=(0.25, 0.25, 0.25, 0.25), q_override=extremes)
+
+
+@pytest.mark.parametrize("fmt", ALL_FMTS, ids=NAMES.get)
+def test_minus_128_against_all_minus_one(fmt):
+    """The i8-negation trap: q = -128 everywhere, every weight -1 -> +4096 per block of 32."""
+    N, K = 65, 1024
+    say(f"case minus128 {NAMES[fmt]}")
+    w = np.full((N, K), -1, np.int8)
+    if fmt == synth.Q1_0:
+        raw = synth.lay_out_q1_0(w, np.full((N, K // 128), 1.0, np.float16))
+    elif fmt == synth.Q2_0_G64:
+        raw = synth.lay_out_q2_0(w, np.full((N, K // 64), 1.0, np.float16))
+    else:
+        raw = synth.lay_out_planar(w)
+    Wt = synth.Weights(fmt, N, K, raw, w, s_w=np.float32(1.0))
+    q = np.full(K, -128, np.int8)
+    xs = np.array([1.0], np.float32) if fmt == synth.TERNARY_PLANAR else np.full(K // 32, 0x3C00, np.uint16)
+    packed = packed_weights(Wt)
+    sums = gpu_sums(fmt, packed, N, K, q[None, :], xs[None, :] if fmt != synth.TERNARY_PLANAR else xs)[0]
+    y = gpu_matvec(fmt, packed, N, K, q, xs)
+    if fmt == synth.TERNARY_PLANAR:
+        assert np.all(sums == 128 * K)
+    else:
+        assert np.all(sums == 4096)
+    assert np.all(y == 128.0 * K)
+
+
+@pytest.mark.parametrize("fmt", Q_FMTS, ids=NAMES.get)
+def test_unit_scales_bit_exact(fmt):
+    """With every binary16 scale 1.0 each term is an integer below 2^24: y must equal the oracle exactly."""
+    N, K = 300, 4096
+    say(f"case unit-scales {NAMES[fmt]}")
+    Wt = synth.make_weights(fmt, N, K, seed=2300)
+    qk = 128 if fmt == synth.Q1_0 else 64
+    raw = oracle.encode(fmt, Wt.w, np.full((N, K // qk), 0x3C00, np.uint16), N, K)
+    Wu = synth.Weights(fmt, N, K, raw.reshape(N, K // qk, 18), Wt.w)
+    q, _, _ = act_for(fmt, K, 2301)
+    ones = np.full(K // 32, 0x3C00, np.uint16)
+    y = gpu_matvec(fmt, packed_weights(Wu), N, K, q, ones)
+    y_ref, _ = oracle.matvec_q(fmt, raw, N, K, q, ones)
+    assert np.array_equal(y.astype(np.float64), y_ref)
+
+
+@pytest.mark.parametrize("fmt", Q_FMTS, ids=NAMES.get)
+def test_zero_activation_blocks(fmt):
+    """amax = 0 blocks: scale 0, every q 0."""
+    K = 4096
+    x = synth.activations(synth.rng(2400), 1, K)
+    x[0, 64:160] = 0.0
+    q, dh, _ = act_for(fmt, K, 0, x=x)
+    assert np.all(q[64:160] == 0)
+    N = 128
+    Wt = synth.make_weights(fmt, N, K, 2401)
+    packed = packed_weights(Wt)
+    y = gpu_matvec(fmt, packed, N, K, q, dh)
+    y_ref, A = oracle.matvec_q(fmt, Wt.raw, N, K, q, dh)
+    assert_close(y, y_ref, A, K // 32, "zero blocks")
+
+
+def test_empty_and_k0():
+    say("case empty")
+    y = torch.full((5,), 7.0, device="cuda")
+    q = torch.zeros(16, dtype=torch.int8, device="cuda")
+    xs = torch.zeros(8, dtype=torch.uint16, device="cuda")
+    W = torch.zeros(16, dtype=torch.uint8, device="cuda")
+    L.lowbit_matvec(synth.Q2_0_G64, W, 0, 64, 1.0, L.ACT_Q8_0, q, xs, y)  # N = 0: untouched
+    assert np.all(host(y) == 7.0)
+    L.lowbit_matvec(synth.Q2_0_G64, W, 5, 0, 1.0, L.ACT_Q8_0, q, xs, y)  # K = 0: empty sums
+    assert np.all(host(y) == 0.0)
+
+
+@pytest.mark.parametrize("fmt", Q_FMTS, ids=NAMES.get)
+def test_pack_round_trip(fmt):
+    say(f"case pack {NAMES[fmt]}")
+    Wt = synth.make_weights(fmt, 77, 1024, 2500)
+    packed = packed_weights(Wt)
+    back = torch.empty(Wt.raw.size, dtype=torch.uint8, device="cuda")
+    L.lowbit_unpack_weights(fmt, packed, 77, 1024, back)
+    assert np.array_equal(host(back), Wt.raw.reshape(-1))
+    # the device layout is all code records, then all scales
+    p = host(packed)
+    nb = Wt.raw.shape[1]
+    assert np.array_equal(p[: 77 * nb * 16].reshape(77, nb, 16), Wt.raw[:, :, 2:])
+    assert np.array_equal(p[77 * nb * 16:].reshape(77, nb, 2), Wt.raw[:, :, :2])
+
+
+def test_launch_geometry_invariance():
+    """A row's result does not depend on which tile or how many rows the launch covers."""
+    say("case geometry")
+    fmt, N, K = synth.Q2_0_G64, 4096, 4096
+    Wt = synth.make_weights(fmt, N, K, 2600)
+    q, dh, _ = act_for(fmt, K, 2601)
+    packed = packed_weights(Wt)
+    y_full = gpu_matvec(fmt, packed, N, K, q, dh)
+    y_again = gpu_matvec(fmt, packed, N, K, q, dh)
+    assert np.array_equal(y_full, y_again)
+    row_bytes = (K // 64) * 16
+    # rows 512.. as their own tensor: a different tile layout over the same rows
+    sub = Wt.raw[512:1536]
+    Wsub = synth.Weights(fmt, 1024, K, sub, Wt.w[512:1536])
+    y_sub = gpu_matvec(fmt, packed_weights(Wsub), 1024, K, q, dh)
+    assert np.array_equal(y_sub, y_full[512:1536])
+    assert row_bytes > 0
+
+
+# --- quantisers -----------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("M,K", [(1, 32), (1, 4096), (7, 12288), (512, 4096)])
+def test_quantize_q8_0_bytes(M, K):
+    say(f"case quantize q8_0 M={M} K={K}")
+    g = synth.rng(3000 + M + K)
+    x = (g.standard_normal((M, K)) * np.exp(g.uniform(-6, 6, (M, 1)))).astype(np.float32)
+    x[0, :32] = 0.0
+    if K >= 64:
+        x[0, 32:64] = np.array([127.0, 2.5, 3.5, -2.5, -3.5, 0.5, 1.5, -0.5] * 4, np.float32)
+    q_ref, d_ref = oracle.quantize_q8_0(x)
+    xq = torch.empty((M, K), dtype=torch.int8, device="cuda")
+    xs = torch.empty((M, K // 32), dtype=torch.uint16, device="cuda")
+    L.lowbit_quantize_act(L.ACT_Q8_0, dev(x), M, K, xq, xs)
+    assert np.array_equal(host(xq), q_ref)
+    assert np.array_equal(host(xs), d_ref)
+
+
+@pytest.mark.parametrize("M,K", [(1, 2560), (3, 6912), (2, 100)])
+def test_quantize_i8_row_bytes(M, K):
+    say(f"case quantize i8_row M={M} K={K}")
+    x = synth.activations(synth.rng(3100 + K), M, K)
+    x[-1] = 0.0
+    q_ref, s_ref = oracle.quantize_i8_row(x)
+    xq = torch.empty((M, K), dtype=torch.int8, device="cuda")
+    xs = torch.empty(M, dtype=torch.float32, device="cuda")
+    L.lowbit_quantize_act(L.ACT_I8_ROW, dev(x), M, K, xq, xs)
+    assert np.array_equal(host(xq), q_ref)
+    assert np.array_equal(host(xs), s_ref)
