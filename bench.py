@@ -1,0 +1,317 @@
+#!/usr/bin/env python3
+"""Benchmark: one batch-1 decode token of a Qwen3-8B-shape Q2_0_g64 (ternary) model on one MI355X.
+
+A step is one pass of the decode hot path over one token: quantise the token's activations to q8_0
+(the 108 K=4096 rows and 36 K=12288 rows feeding the 252 products) and run all 252 products -- 36
+layers x {q, k, v, o, gate, up, down} with distinct weights per layer, 1,953,497,088 bytes of packed
+weights -- as one batched launch.  Inputs are synthetic (seeded), with the shapes and value
+distributions of the workload, and resident in HBM before timing starts.
+
+Prints ONE JSON line: the effective weight GB/s of the step (weight bytes / step time), the roofline of
+the dominant kernel (the batched decode launch) measured with HIP events on the stream it runs on, and
+the CPU oracle timed on a bounded sample of the same bytes.  ``--gpus`` above 1 exits: this library
+runs on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+MFMA_I8_PEAK_TOPS = 5000.0  # MI355X dense int8, published
+METRIC = "effective weight GB/s & % HBM peak, 8B-shape batch-1 ternary matvec; prefill TOPS"
+PROFILE_PMC = os.path.join(ROOT, "profiles", "matvec_batched_q2_8b_token.pmc.txt")
+KERNEL_SRC = os.path.join(ROOT, "bit_quantized_matvec_q1_amd", "csrc", "matvec.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class DecodeToken:
+    """All products of one decode token of a layered model, batched into one launch plan."""
+
+    def __init__(self, fmt, layer_shapes, layers, seed, keep_blocks_layers=0):
+        import torch
+
+        import bit_quantized_matvec_q1_amd.lowbit as L
+        import synth
+
+        self.fmt, self.layers, self.L = fmt, layers, L
+        planar = fmt == synth.TERNARY_PLANAR
+        # distinct activation vectors per layer: attention input (q, k, v), o input, ffn input (gate, up),
+        # down input -- grouped by K so each group is quantised by one launch
+        names = [n for n, _, _ in layer_shapes]
+        feeds = {"attn_q": 0, "attn_k": 0, "attn_v": 0, "attn_output": 1, "ffn_gate": 2, "ffn_up": 2, "ffn_down": 3}
+        feed_k = {}
+        for n, N, K in layer_shapes:
+            feed_k[feeds[n]] = K
+        self.groups = {}  # K -> list of (layer, feed)
+        for l in range(layers):
+            for f in sorted(feed_k):
+                self.groups.setdefault(feed_k[f], []).append((l, f))
+        g = torch.Generator(device="cuda")
+        g.manual_seed(seed)
+        self.x, self.xq, self.xs, self.row_of = {}, {}, {}, {}
+        for K, rows in self.groups.items():
+            M = len(rows)
+            self.x[K] = torch.randn((M, K), generator=g, device="cuda")
+            self.xq[K] = torch.empty((M, K), dtype=torch.int8, device="cuda")
+            self.xs[K] = torch.empty((M,) if planar else (M, K // 32), dtype=torch.float32 if planar else torch.uint16,
+                                     device="cuda")
+            for i, key in enumerate(rows):
+                self.row_of[key] = (K, i)
+        self.products, descs = [], []
+        self.weight_bytes = self.act_bytes = self.out_bytes = 0
+        self.blocks = {}
+        for l in range(layers):
+            for j, (n, N, K) in enumerate(layer_shapes):
+                s = seed + 1000 * (l + 1) + j
+                if planar:
+                    raw = synth.device_planar_beats(N, K, s)
+                    packed = raw.reshape(-1)
+                    w_scale = float(abs(torch.randn((), generator=g, device="cuda").item()) * 0.02)
+                else:
+                    raw = synth.device_ggml_blocks(fmt, N, K, s)
+                    packed = torch.empty(L.lowbit_weight_bytes(fmt, N, K), dtype=torch.uint8, device="cuda")
+                    L.lowbit_pack_weights(fmt, raw.reshape(-1), N, K, packed)
+                    w_scale = 1.0
+                if l < keep_blocks_layers:
+                    self.blocks[(l, j)] = raw
+                Kx, r = self.row_of[(l, feeds[n])]
+                y = torch.empty(N, dtype=torch.float32, device="cuda")
+                xq = self.xq[Kx][r]
+                xs = self.xs[Kx][r] if not planar else self.xs[Kx][r:r + 1]
+                self.products.append(dict(layer=l, name=n, N=N, K=K, W=packed, y=y, xq=xq, xs=xs, w_scale=w_scale,
+                                          feed=(Kx, r)))
+                descs.append(L.desc(fmt, packed, N, K, xq, xs, y, w_tensor_scale=w_scale))
+                self.weight_bytes += L.lowbit_weight_bytes(fmt, N, K)
+                self.act_bytes += K + (4 if planar else K // 16)
+                self.out_bytes += 4 * N
+        self.batch = L.Batch(descs)
+        self.afmt = L.ACT_I8_ROW if planar else L.ACT_Q8_0
+        torch.cuda.synchronize()
+
+    def quantize(self):
+        for K, x in self.x.items():
+            self.L.lowbit_quantize_act(self.afmt, x, x.shape[0], K, self.xq[K], self.xs[K])
+
+    def products_launch(self):
+        self.batch.run()
+
+    @property
+    def algorithmic_bytes(self):
+        return self.weight_bytes + self.act_bytes + self.out_bytes
+
+
+def time_token(tok, steps, warmup):
+    """Time `steps` whole steps (quantise + batched products) and, inside them, the batched launch alone
+    with HIP events on the stream the kernels run on (torch's current stream)."""
+    import torch
+
+    for _ in range(warmup):
+        tok.quantize()
+        tok.products_launch()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for a, b in ev:
+        tok.quantize()
+        a.record()
+        tok.products_launch()
+        b.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch_ms = [a.elapsed_time(b) for a, b in ev]
+    return wall / steps * 1e3, sum(launch_ms) / len(launch_ms)
+
+
+def stored_traffic(kernel_name, algorithmic_bytes):
+    """HBM bytes per launch from the committed rocprofv3 --pmc summary, if it was taken on the current
+    kernel source; otherwise None."""
+    if not os.path.exists(PROFILE_PMC):
+        return None
+    text = open(PROFILE_PMC).read()
+    src_hash = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
+    m_hash = re.search(r"kernel_source_sha256:\s*([0-9a-f]{64})", text)
+    m_bytes = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m_hash or not m_bytes or m_hash.group(1) != src_hash:
+        return None
+    return float(m_bytes.group(1))
+
+
+def cpu_baseline(tok, budget_s=12.0):
+    """The oracle, as it stands, on the same bytes: layers in order (quantise + all 7 products each) until
+    the time budget is spent.  Single-threaded."""
+    import numpy as np
+    import torch
+
+    import oracle
+
+    t_total, wbytes, layers_done = 0.0, 0, 0
+    for l in range(tok.layers):
+        if (l, 0) not in tok.blocks:
+            break
+        xs_host = {K: x.cpu().numpy() for K, x in tok.x.items()}
+        raws = [(p, tok.blocks[(l, j)].cpu().numpy().reshape(-1))
+                for j, p in enumerate([p for p in tok.products if p["layer"] == l])]
+        t0 = time.perf_counter()
+        qcache = {}
+        for p, raw in raws:
+            K, r = p["feed"]
+            if (K, r) not in qcache:
+                qcache[(K, r)] = oracle.quantize_q8_0(xs_host[K][r:r + 1])
+            q, dh = qcache[(K, r)]
+            oracle.matvec_q(tok.fmt, raw, p["N"], p["K"], q[0], dh[0])
+            wbytes += raw.size
+        t_total += time.perf_counter() - t0
+        layers_done += 1
+        if t_total >= budget_s:
+            break
+    return t_total, wbytes, layers_done
+
+
+def copy_probe_gbs(nbytes=1 << 31, reps=5):
+    """Device-to-device copy of a buffer far larger than the 256 MB last-level cache: read+write GB/s."""
+    import torch
+
+    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    best = 0.0
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        b.copy_(a)
+        e1.record()
+        torch.cuda.synchronize()
+        best = max(best, 2 * nbytes / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+    del a, b
+    torch.cuda.empty_cache()
+    return best
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle leg (profiling runs)")
+    ap.add_argument("--secondary", default="q1,planar", help="comma list of extra workloads: q1, planar, none")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU: this library has no multi-GPU path (asked for --gpus {args.gpus}). "
+              "Each product shards by rows; see the design notes.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import synth
+
+    assert torch.cuda.is_available(), "bench.py needs an MI355X"
+    dev = torch.cuda.get_device_properties(0)
+    log(f"device: {dev.name} ({getattr(dev, 'gcnArchName', '?')}), {dev.multi_processor_count} CUs")
+
+    probe = copy_probe_gbs()
+    log(f"copy probe: {probe:.0f} GB/s (read+write)")
+
+    tok = DecodeToken(synth.Q2_0_G64, synth.QWEN3_8B_LAYER, synth.QWEN3_8B_LAYERS, seed=1003,
+                      keep_blocks_layers=0 if args.no_cpu_baseline else synth.QWEN3_8B_LAYERS)
+    log(f"Q2_0_g64 token: {len(tok.products)} products, {tok.weight_bytes} weight bytes")
+    ms_step, ms_launch = time_token(tok, args.steps, args.warmup)
+    value = tok.weight_bytes / (ms_step * 1e-3) / 1e9
+    achieved = tok.algorithmic_bytes / (ms_launch * 1e-3) / 1e9
+    traffic = stored_traffic("matvec_batched_kernel", tok.algorithmic_bytes)
+    log(f"step {ms_step:.4f} ms, batched launch {ms_launch:.4f} ms -> {value:.0f} GB/s weights, "
+        f"launch {achieved:.0f} GB/s algorithmic")
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {
+            "workload": "Q2_0_g64 decode token, Qwen3-8B shapes: 36 layers x {q 4096x4096, k/v 1024x4096, "
+                        "o 4096x4096, gate/up 12288x4096, down 4096x12288}, batch 1, q8_0 activations",
+            "products": len(tok.products),
+            "weight_bytes": tok.weight_bytes,
+            "parallelism": "single GPU",
+        },
+        "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "tokens_per_s_equiv": round(1e3 / ms_step, 1),
+        "copy_probe_gbs": round(probe, 1),
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "kernel": "matvec_batched_kernel<Q2_0_g64>",
+            "algorithmic_bytes_per_launch": tok.algorithmic_bytes,
+            "launch_ms": round(ms_launch, 5),
+        },
+    }
+
+    if not args.no_cpu_baseline:
+        t_cpu, wb, layers = cpu_baseline(tok)
+        out["cpu_baseline"] = {
+            "value": round(wb / t_cpu / 1e9, 4),
+            "unit": "GB/s",
+            "cores": 1,
+            "kind": "oracle",
+            "sample": f"first {layers} of 36 layers (all 7 products each, q8_0 quantise included), the same "
+                      f"bytes as the GPU run: {wb} weight bytes in {t_cpu:.2f} s on one host thread",
+        }
+    tok.batch.close()
+    del tok
+    torch.cuda.empty_cache()
+
+    secondary = {}
+    for name in [s for s in args.secondary.split(",") if s and s != "none"]:
+        if name == "q1":
+            t1 = DecodeToken(synth.Q1_0, synth.QWEN3_8B_LAYER, synth.QWEN3_8B_LAYERS, seed=1002)
+            ms1, ml1 = time_token(t1, max(10, args.steps // 2), 5)
+            secondary["q1_0_8b_token"] = {
+                "weight_bytes": t1.weight_bytes, "ms_per_step": round(ms1, 5),
+                "gbs": round(t1.weight_bytes / (ms1 * 1e-3) / 1e9, 1),
+                "launch_gbs": round(t1.algorithmic_bytes / (ml1 * 1e-3) / 1e9, 1),
+                "pct_hbm_peak": round(100 * t1.weight_bytes / (ms1 * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+            }
+            t1.batch.close()
+            del t1
+        elif name == "planar":
+            tp = DecodeToken(synth.TERNARY_PLANAR, synth.BITNET_2B_LAYER, synth.BITNET_2B_LAYERS, seed=1005)
+            msp, mlp = time_token(tp, max(10, args.steps // 2), 5)
+            secondary["planar_2b_token"] = {
+                "weight_bytes": tp.weight_bytes, "ms_per_step": round(msp, 5),
+                "gbs": round(tp.weight_bytes / (msp * 1e-3) / 1e9, 1),
+                "launch_gbs": round(tp.algorithmic_bytes / (mlp * 1e-3) / 1e9, 1),
+            }
+            tp.batch.close()
+            del tp
+        torch.cuda.empty_cache()
+    if secondary:
+        out["secondary"] = secondary
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

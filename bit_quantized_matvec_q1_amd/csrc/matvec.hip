@@ -177,8 +177,125 @@ __device__ __forceinline__ int planar_total8(const PlanarAcc &a)
 }
 
 // ------------------------------------------------------------------------------------------------
-// One workgroup, one tile of rows [row0, row0 + nrows) of one product.
+// Cross-lane sum over aligned groups of L lanes with DPP (no LDS round trip).  The total ends up in the
+// group's last lane (li == L - 1); for L <= 16 every lane of the group holds it.
 // ------------------------------------------------------------------------------------------------
+template <int L> __device__ __forceinline__ int group_sum_i(int v)
+{
+    if (L >= 2)
+        v += __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false); // quad_perm [1,0,3,2]
+    if (L >= 4)
+        v += __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false); // quad_perm [2,3,0,1]
+    if (L >= 8)
+        v += __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false); // row_half_mirror
+    if (L >= 16)
+        v += __builtin_amdgcn_update_dpp(0, v, 0x140, 0xF, 0xF, false); // row_mirror
+    if (L >= 32)
+        v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false); // row_bcast:15 into rows 1, 3
+    if (L >= 64)
+        v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false); // row_bcast:31 into rows 2, 3
+    return v;
+}
+
+template <int L> __device__ __forceinline__ float group_sum_f(float v)
+{
+    if (L >= 2)
+        v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
+    if (L >= 4)
+        v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
+    if (L >= 8)
+        v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false));
+    if (L >= 16)
+        v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false));
+    if (L >= 32)
+        v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x142, 0xA, 0xF, false));
+    if (L >= 64)
+        v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x143, 0xC, 0xF, false));
+    return v;
+}
+
+// ------------------------------------------------------------------------------------------------
+// One workgroup, one tile of rows [row0, row0 + nrows) of one product.
+//
+// Loads are unconditional: a lane past the tile's last row re-reads that row and a lane past the row's
+// last slice re-reads that slice (its staged activations are zero, so it adds nothing and its result
+// is never stored).  Offsets are 32-bit from the tensor's base (the ABI keeps tensors under 4 GiB).
+// The next rows' loads are issued before the current rows are computed (ping-pong registers), and the
+// first rows' loads before the activation is staged, so the weight stream never waits on the staging.
+// ------------------------------------------------------------------------------------------------
+template <int FMT, int L, int S> struct RowRegs {
+    uint4 code[S];
+    uint32_t sc[S];
+};
+
+template <int FMT, int L, int S>
+__device__ __forceinline__ void issue_row(RowRegs<FMT, L, S> &r, const uint8_t *__restrict__ W,
+                                          const uint16_t *__restrict__ scales, uint32_t row, int ns, int li)
+{
+    constexpr int CB = F<FMT>::CODE_BYTES;
+    const uint32_t nsr = FMT == LB_Q1_0 ? (uint32_t)ns / 2 : (uint32_t)ns;
+#pragma unroll
+    for (int i = 0; i < S; i++) {
+        const uint32_t sl = (uint32_t)min(li + i * L, ns - 1);
+        const uint32_t off = (row * (uint32_t)ns + sl) * CB;
+        if (CB == 16) {
+            r.code[i] = *reinterpret_cast<const uint4 *>(W + off);
+        } else {
+            const uint2 t = *reinterpret_cast<const uint2 *>(W + off);
+            r.code[i] = make_uint4(t.x, t.y, 0, 0);
+        }
+        if (FMT != LB_TERNARY_PLANAR)
+            r.sc[i] = scales[row * nsr + (FMT == LB_Q1_0 ? sl >> 1 : sl)];
+    }
+}
+
+template <int FMT, int L, int S, bool EMIT>
+__device__ __forceinline__ void compute_row(const RowRegs<FMT, L, S> &r, const uint32_t (&act)[S][F<FMT>::REC],
+                                            int ns, int li, bool valid, int row, float w_scale, float sx,
+                                            float *__restrict__ y, int32_t *__restrict__ sums)
+{
+    if (FMT == LB_TERNARY_PLANAR) {
+        PlanarAcc acc = {};
+#pragma unroll
+        for (int i = 0; i < S; i++)
+            planar_accumulate(r.code[i], act[i], acc);
+        const int t = group_sum_i<L>(planar_total8(acc));
+        if (valid && li == L - 1) {
+            const int a = t >> 3; // exact: the total is a multiple of 8
+            if (EMIT)
+                sums[row] = a;
+            // tritium "Architecture", section 5: activation scale and weight scale are applied as two
+            // fp32 multiplies, in that order
+            const float ys = (float)a * sx;
+            if (!EMIT || y != nullptr) // the sums instantiation may be called without an output vector
+                y[row] = ys * w_scale;
+        }
+    } else {
+        float part = 0.0f;
+#pragma unroll
+        for (int i = 0; i < S; i++) {
+            const int sl = li + i * L;
+            int i0, i1;
+            if (FMT == LB_Q2_0_G64)
+                q2_isums(r.code[i], act[i], i0, i1);
+            else
+                q1_isums(make_uint2(r.code[i].x, r.code[i].y), act[i], i0, i1);
+            const float dx0 = __uint_as_float(act[i][16]), dx1 = __uint_as_float(act[i][17]);
+            const float t = fmaf(dx1, (float)i1, dx0 * (float)i0);
+            const float c = fmaf(half_bits_to_float((uint16_t)r.sc[i]), t, part);
+            part = sl < ns ? c : part;
+            if (EMIT && valid && sl < ns) {
+                int32_t *o = sums + (int64_t)row * (ns * 2) + 2 * sl;
+                o[0] = i0;
+                o[1] = i1;
+            }
+        }
+        part = group_sum_f<L>(part);
+        if (valid && li == L - 1 && (!EMIT || y != nullptr))
+            y[row] = part;
+    }
+}
+
 template <int FMT, int L, int S, bool EMIT>
 __device__ __forceinline__ void matvec_tile(const uint8_t *__restrict__ W, int N, int K, float w_scale,
                                             const int8_t *__restrict__ xq, const void *__restrict__ xscale,
@@ -187,16 +304,22 @@ __device__ __forceinline__ void matvec_tile(const uint8_t *__restrict__ W, int N
 {
     constexpr int REC = F<FMT>::REC;
     constexpr int CB = F<FMT>::CODE_BYTES;
-    constexpr int GROUPS = 64 / L;                // rows per wave per iteration
-    constexpr int ROWS_IT = GROUPS * (WG / 64);   // rows per workgroup per iteration
-    const int ns = K / SLICE;                     // slices per row
+    constexpr int GROUPS = 64 / L;              // rows per wave per iteration
+    constexpr int ROWS_IT = GROUPS * (WG / 64); // rows per workgroup per iteration
+    const int ns = K / SLICE;                   // slices per row
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int g = lane / L, li = lane % L;
+    const uint16_t *scales = reinterpret_cast<const uint16_t *>(W + (int64_t)N * ns * CB);
+    const int rbase = wave * GROUPS + g; // this lane's row within an iteration
+
+    auto row_at = [&](int it) -> uint32_t { return (uint32_t)(row0 + min(it + rbase, nrows - 1)); };
+
+    RowRegs<FMT, L, S> ra, rb;
+    issue_row<FMT, L, S>(ra, W, scales, row_at(0), ns, li);
 
     for (int sl = threadIdx.x; sl < ns; sl += WG)
         stage_slice<FMT>(xq, xscale, sl, lds + sl * REC);
     __syncthreads();
-
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int g = lane / L, li = lane % L;
 
     uint32_t act[S][REC];
 #pragma unroll
@@ -218,95 +341,21 @@ __device__ __forceinline__ void matvec_tile(const uint8_t *__restrict__ W, int N
                 act[i][q] = 0;
         }
     }
-
-    // Q1_0 stores one scale per 128 weights, i.e. per two slices; the other formats one per slice.
-    const int64_t nscale_row = FMT == LB_Q1_0 ? ns / 2 : ns;
-    const uint16_t *scales = reinterpret_cast<const uint16_t *>(W + (int64_t)N * ns * CB);
-
     const float sx = FMT == LB_TERNARY_PLANAR ? *reinterpret_cast<const float *>(xscale) : 0.0f;
 
-    constexpr int U = 2; // rows in flight per lane
-    for (int it = 0; it < nrows; it += U * ROWS_IT) {
-        uint4 code[U][S];
-        uint16_t sc[U][S];
-        bool valid[U];
-        int row[U];
-#pragma unroll
-        for (int u = 0; u < U; u++) {
-            const int rl = it + u * ROWS_IT + wave * GROUPS + g;
-            valid[u] = rl < nrows;
-            row[u] = row0 + rl;
-#pragma unroll
-            for (int i = 0; i < S; i++) {
-                const int sl = li + i * L;
-                code[u][i] = make_uint4(0, 0, 0, 0);
-                sc[u][i] = 0;
-                if (valid[u] && sl < ns) {
-                    const uint8_t *p = W + ((int64_t)row[u] * ns + sl) * CB;
-                    if (CB == 16) {
-                        code[u][i] = *reinterpret_cast<const uint4 *>(p);
-                    } else {
-                        const uint2 t = *reinterpret_cast<const uint2 *>(p);
-                        code[u][i] = make_uint4(t.x, t.y, 0, 0);
-                    }
-                    if (FMT != LB_TERNARY_PLANAR)
-                        sc[u][i] = scales[(int64_t)row[u] * nscale_row + (FMT == LB_Q1_0 ? sl >> 1 : sl)];
-                }
-            }
-        }
-#pragma unroll
-        for (int u = 0; u < U; u++) {
-            if (FMT == LB_TERNARY_PLANAR) {
-                PlanarAcc acc = {};
-#pragma unroll
-                for (int i = 0; i < S; i++)
-                    if (li + i * L < ns)
-                        planar_accumulate(code[u][i], act[i], acc);
-                int t = planar_total8(acc);
-#pragma unroll
-                for (int off = L / 2; off >= 1; off >>= 1)
-                    t += __shfl_xor(t, off, 64);
-                if (valid[u] && li == 0) {
-                    const int a = t >> 3; // exact: the total is a multiple of 8
-                    if (EMIT)
-                        sums[row[u]] = a;
-                    // tritium "Architecture", section 5: activation scale and weight scale are applied
-                    // as two fp32 multiplies, in that order
-                    const float ys = (float)a * sx;
-                    if (!EMIT || y != nullptr) // the sums instantiation is called without an output vector
-                        y[row[u]] = ys * w_scale;
-                }
-            } else {
-                float part = 0.0f;
-#pragma unroll
-                for (int i = 0; i < S; i++) {
-                    const int sl = li + i * L;
-                    if (sl < ns) {
-                        int i0, i1;
-                        if (FMT == LB_Q2_0_G64)
-                            q2_isums(code[u][i], act[i], i0, i1);
-                        else
-                            q1_isums(make_uint2(code[u][i].x, code[u][i].y), act[i], i0, i1);
-                        const float dx0 = __uint_as_float(act[i][16]), dx1 = __uint_as_float(act[i][17]);
-                        const float t = fmaf(dx1, (float)i1, dx0 * (float)i0);
-                        part = fmaf(half_bits_to_float(sc[u][i]), t, part);
-                        if (EMIT && valid[u]) {
-                            int32_t *o = sums + (int64_t)row[u] * (ns * 2) + 2 * sl;
-                            o[0] = i0;
-                            o[1] = i1;
-                        }
-                    }
-                }
-#pragma unroll
-                for (int off = L / 2; off >= 1; off >>= 1)
-                    part += __shfl_xor(part, off, 64);
-                if (valid[u] && li == 0 && (!EMIT || y != nullptr))
-                    y[row[u]] = part;
-            }
-        }
+    for (int it = 0; it < nrows; it += 2 * ROWS_IT) {
+        const bool more1 = it + ROWS_IT < nrows; // uniform across the workgroup
+        if (more1)
+            issue_row<FMT, L, S>(rb, W, scales, row_at(it + ROWS_IT), ns, li);
+        compute_row<FMT, L, S, EMIT>(ra, act, ns, li, it + rbase < nrows, row0 + it + rbase, w_scale, sx, y, sums);
+        if (!more1)
+            break;
+        if (it + 2 * ROWS_IT < nrows)
+            issue_row<FMT, L, S>(ra, W, scales, row_at(it + 2 * ROWS_IT), ns, li);
+        compute_row<FMT, L, S, EMIT>(rb, act, ns, li, it + ROWS_IT + rbase < nrows, row0 + it + ROWS_IT + rbase,
+                                     w_scale, sx, y, sums);
     }
 }
-
 
 // ------------------------------------------------------------------------------------------------
 // Configurations (L lanes per row, S slices per lane).  The host picks, per product, the entry that

@@ -189,3 +189,56 @@ PREFILL_SHAPES = ((4096, 4096), (12288, 4096))
 def format_bytes(fmt: int, N: int, K: int) -> int:
     """Bytes of a packed weight tensor in its on-disk format (18 B per ggml block, 16 B per beat)."""
     return N * (K // BLOCK_WEIGHTS[fmt]) * BLOCK_BYTES[fmt]
+
+
+# --- device-side drawing for the bandwidth workloads --------------------------------------------------
+# The same recipes drawn with torch's seeded generator directly in device memory, for tensors too large
+# to draw on the host in reasonable time (a whole 8B-shape token is 1-2 GB of packed weights).  Parity
+# tests use the host generators above; the bench uses these.
+
+def device_ggml_blocks(fmt: int, N: int, K: int, seed: int, device="cuda"):
+    """ggml Q1_0 / Q2_0_g64 blocks [N][K/QK][18] (uint8) drawn on the device."""
+    import torch
+
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    qk = BLOCK_WEIGHTS[fmt]
+    nb = K // qk
+    d = (torch.randn((N, nb), generator=g, device=device).abs() * 0.02).to(torch.float16)
+    out = torch.empty((N, nb, 18), dtype=torch.uint8, device=device)
+    out[:, :, 0:2] = d.view(torch.uint8).view(N, nb, 2)
+    if fmt == Q1_0:
+        out[:, :, 2:18] = torch.randint(0, 256, (N, nb, 16), generator=g, device=device, dtype=torch.uint8)
+    else:
+        u = torch.rand((N, nb, 16, 4), generator=g, device=device)
+        lo, hi = TERNARY_P[0], TERNARY_P[0] + TERNARY_P[1]
+        c = (u >= lo).to(torch.uint8) + (u >= hi).to(torch.uint8)  # code 0, 1, 2 = weight -1, 0, +1
+        out[:, :, 2:18] = c[..., 0] | (c[..., 1] << 2) | (c[..., 2] << 4) | (c[..., 3] << 6)
+    return out
+
+
+def device_planar_beats(N: int, K: int, seed: int, device="cuda"):
+    """Planar beats [N][K/64][16] (uint8) with weights -1/0/+1 at 31/38/31 %, drawn on the device."""
+    import torch
+
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    nb = K // QKP
+    u = torch.rand((N, nb, 2, 8, 8), generator=g, device=device)
+    lo, hi = TERNARY_P[0], TERNARY_P[0] + TERNARY_P[1]
+    pos = (u >= hi).to(torch.uint8)
+    neg = (u < lo).to(torch.uint8)
+    shifts = torch.arange(8, device=device, dtype=torch.uint8)
+    out = torch.empty((N, nb, 16), dtype=torch.uint8, device=device)
+    out[:, :, 0:8] = (pos[:, :, 0] << shifts).sum(dim=-1, dtype=torch.uint8)
+    out[:, :, 8:16] = (neg[:, :, 0] << shifts).sum(dim=-1, dtype=torch.uint8)
+    return out
+
+
+def device_head_weights(N: int, K: int, seed: int, device="cuda"):
+    """Head weights N(0, 0.02) in bfloat16, returned as int16 bits [N][K], drawn on the device."""
+    import torch
+
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    return (torch.randn((N, K), generator=g, device=device) * 0.02).to(torch.bfloat16).view(torch.int16)
