@@ -179,6 +179,36 @@ def cpu_baseline(tok, budget_s=12.0):
     return t_total, wbytes, layers_done
 
 
+def prefill_tops(fmt, N, K, M, reps=20, seed=1004):
+    """Time the prefill product (M activation rows x N weight rows x K) on inputs resident in HBM."""
+    import torch
+
+    import bit_quantized_matvec_q1_amd.lowbit as L
+    import synth
+
+    raw = synth.device_ggml_blocks(fmt, N, K, seed)
+    W = torch.empty(L.lowbit_weight_bytes(fmt, N, K), dtype=torch.uint8, device="cuda")
+    L.lowbit_pack_weights(fmt, raw.reshape(-1), N, K, W)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed + 1)
+    X = torch.randn((M, K), generator=g, device="cuda")
+    Xq = torch.empty((M, K), dtype=torch.int8, device="cuda")
+    Xs = torch.empty((M, K // 32), dtype=torch.uint16, device="cuda")
+    L.lowbit_quantize_act(L.ACT_Q8_0, X, M, K, Xq, Xs)
+    Y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    for _ in range(3):
+        L.lowbit_gemm(fmt, W, N, K, 1.0, L.ACT_Q8_0, Xq, Xs, M, Y)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        L.lowbit_gemm(fmt, W, N, K, 1.0, L.ACT_Q8_0, Xq, Xs, M, Y)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    return ms, 2.0 * M * N * K / (ms * 1e-3) / 1e12
+
+
 def copy_probe_gbs(nbytes=1 << 31, reps=5):
     """Device-to-device copy of a buffer far larger than the 256 MB last-level cache: read+write GB/s."""
     import torch
@@ -206,7 +236,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle leg (profiling runs)")
-    ap.add_argument("--secondary", default="q1,planar", help="comma list of extra workloads: q1, planar, none")
+    ap.add_argument("--secondary", default="q1,planar,prefill",
+                    help="comma list of extra workloads: q1, planar, prefill, none")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU: this library has no multi-GPU path (asked for --gpus {args.gpus}). "
@@ -307,6 +338,15 @@ def main():
             }
             tp.batch.close()
             del tp
+        elif name == "prefill":
+            pre = {}
+            for fmt, fname in ((synth.Q2_0_G64, "q2_0_g64"), (synth.Q1_0, "q1_0")):
+                for N, K in synth.PREFILL_SHAPES:
+                    ms, tops = prefill_tops(fmt, N, K, synth.PREFILL_M)
+                    pre[f"{fname}_{synth.PREFILL_M}x{N}x{K}"] = {
+                        "ms": round(ms, 4), "tops": round(tops, 1),
+                        "frac_int8_mfma_peak": round(tops / MFMA_I8_PEAK_TOPS, 4)}
+            secondary["prefill"] = pre
         torch.cuda.empty_cache()
     if secondary:
         out["secondary"] = secondary
