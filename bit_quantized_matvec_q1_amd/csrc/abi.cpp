@@ -300,20 +300,34 @@ lb_status lowbit_batch_create(const lb_matvec_desc *list, int32_t n, lb_batch **
         if (d.K == 0 && d.N > 0)
             return fail(LB_ESHAPE, fn, "K == 0 in a work list (use lowbit_matvec for empty sums)");
         if (d.N > 0 && lb::matvec_config(d.fmt, d.K) < 0)
-            return fail(LB_ESHAPE, fn, "K above the batched kernel's limit (16384)");
+            return fail(LB_ESHAPE, fn, "K above the decode kernel's limit");
     }
     lb_status st = check_device(fn);
     if (st != LB_OK)
         return st;
 
-    // one launch group per weight format present, products in list order
-    std::vector<std::vector<lb::DevDesc>> descs(4);
-    std::vector<std::vector<int32_t>> tiles(4);
-    std::vector<size_t> lds(4, 0);
+    // one launch group per (weight format, kernel configuration) present, products in list order
+    struct Key {
+        int fmt, cfg;
+    };
+    std::vector<Key> keys;
+    std::vector<std::vector<lb::DevDesc>> descs;
+    std::vector<std::vector<int32_t>> tiles;
+    std::vector<size_t> lds;
     for (int32_t i = 0; i < n; i++) {
         const lb_matvec_desc &d = list[i];
         if (d.N == 0)
             continue;
+        const int cfg = lb::matvec_config(d.fmt, d.K);
+        size_t gi = 0;
+        while (gi < keys.size() && !(keys[gi].fmt == d.fmt && keys[gi].cfg == cfg))
+            gi++;
+        if (gi == keys.size()) {
+            keys.push_back({d.fmt, cfg});
+            descs.emplace_back();
+            tiles.emplace_back();
+            lds.push_back(0);
+        }
         lb::DevDesc dd;
         dd.W = static_cast<const uint8_t *>(d.W);
         dd.xq = d.xq;
@@ -322,49 +336,53 @@ lb_status lowbit_batch_create(const lb_matvec_desc *list, int32_t n, lb_batch **
         dd.N = (int32_t)d.N;
         dd.K = (int32_t)d.K;
         dd.w_scale = d.w_tensor_scale;
-        dd.cfg = lb::matvec_config(d.fmt, d.K);
-        const int rpi = lb::matvec_config_rows_per_iter(d.fmt, dd.cfg);
-        dd.tile_rows = rpi * ((128 + rpi - 1) / rpi);
-        dd.tile_begin = (int32_t)tiles[d.fmt].size();
+        dd.cfg = cfg;
+        // tiles of about 256 KiB of weights (whole row iterations): enough work to amortise the activation
+        // staging, small enough that long rows still give many workgroups
+        const int rpi = lb::matvec_config_rows_per_iter(d.fmt, cfg);
+        const int64_t row_bytes = lowbit_weight_bytes(d.fmt, 1, d.K);
+        const int64_t want = std::max<int64_t>(1, (262144 + row_bytes - 1) / row_bytes);
+        dd.tile_rows = (int32_t)(rpi * ((want + rpi - 1) / rpi));
+        dd.tile_begin = (int32_t)tiles[gi].size();
         const int64_t nt = (d.N + dd.tile_rows - 1) / dd.tile_rows;
         for (int64_t t = 0; t < nt; t++)
-            tiles[d.fmt].push_back((int32_t)descs[d.fmt].size());
-        descs[d.fmt].push_back(dd);
-        lds[d.fmt] = std::max(lds[d.fmt], (size_t)lb::matvec_stage_bytes(d.fmt, d.K));
+            tiles[gi].push_back((int32_t)descs[gi].size());
+        descs[gi].push_back(dd);
+        lds[gi] = std::max(lds[gi], (size_t)lb::matvec_stage_bytes(d.fmt, d.K));
     }
-    size_t bytes = 0;
-    for (int f = 1; f <= 3; f++)
-        bytes += (descs[f].size() * sizeof(lb::DevDesc) + 255) / 256 * 256 + (tiles[f].size() * sizeof(int32_t) + 255) / 256 * 256;
+    size_t bytes = 256;
+    for (size_t gi = 0; gi < keys.size(); gi++)
+        bytes += (descs[gi].size() * sizeof(lb::DevDesc) + 255) / 256 * 256 +
+                 (tiles[gi].size() * sizeof(int32_t) + 255) / 256 * 256;
     lb_batch *b = new lb_batch();
     hipGetDevice(&b->device);
-    hipError_t e = hipMalloc(&b->dev, bytes > 0 ? bytes : 256);
+    hipError_t e = hipMalloc(&b->dev, bytes);
     if (e != hipSuccess) {
         delete b;
         return hip_fail(fn, e);
     }
     size_t off = 0;
-    for (int f = 1; f <= 3; f++) {
-        if (descs[f].empty())
-            continue;
+    char *base = static_cast<char *>(b->dev);
+    for (size_t gi = 0; gi < keys.size(); gi++) {
         lb_batch::Group grp;
-        grp.g.fmt = f;
-        grp.g.cfg_a = grp.g.cfg_b = -1;
-        grp.g.ntiles = (int32_t)tiles[f].size();
-        char *base = static_cast<char *>(b->dev);
+        grp.g.fmt = keys[gi].fmt;
+        grp.g.cfg_a = keys[gi].cfg;
+        grp.g.cfg_b = -1;
+        grp.g.ntiles = (int32_t)tiles[gi].size();
         grp.g.desc = reinterpret_cast<const lb::DevDesc *>(base + off);
-        e = hipMemcpy(base + off, descs[f].data(), descs[f].size() * sizeof(lb::DevDesc), hipMemcpyHostToDevice);
-        off += (descs[f].size() * sizeof(lb::DevDesc) + 255) / 256 * 256;
+        e = hipMemcpy(base + off, descs[gi].data(), descs[gi].size() * sizeof(lb::DevDesc), hipMemcpyHostToDevice);
+        off += (descs[gi].size() * sizeof(lb::DevDesc) + 255) / 256 * 256;
         if (e == hipSuccess) {
             grp.g.tile_prod = reinterpret_cast<const int32_t *>(base + off);
-            e = hipMemcpy(base + off, tiles[f].data(), tiles[f].size() * sizeof(int32_t), hipMemcpyHostToDevice);
-            off += (tiles[f].size() * sizeof(int32_t) + 255) / 256 * 256;
+            e = hipMemcpy(base + off, tiles[gi].data(), tiles[gi].size() * sizeof(int32_t), hipMemcpyHostToDevice);
+            off += (tiles[gi].size() * sizeof(int32_t) + 255) / 256 * 256;
         }
         if (e != hipSuccess) {
             hipFree(b->dev);
             delete b;
             return hip_fail(fn, e);
         }
-        grp.lds = lds[f];
+        grp.lds = lds[gi];
         b->groups.push_back(grp);
     }
     *out = b;

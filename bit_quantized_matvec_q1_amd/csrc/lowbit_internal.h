@@ -53,7 +53,7 @@ struct DevDesc {
 
 struct BatchGroup {
     int fmt;
-    int cfg_a, cfg_b;        // the (at most two) configurations this launch covers
+    int cfg_a, cfg_b;        // the kernel configuration of this launch group (cfg_b unused)
     int32_t ntiles;          // workgroups in the launch
     const DevDesc *desc;     // device
     const int32_t *tile_prod; // device, product index of each tile

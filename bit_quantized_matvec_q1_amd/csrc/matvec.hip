@@ -5,9 +5,9 @@
 // select-accumulate, and only the block scales are floating point.
 //
 // Mapping to CDNA4:
-//  * The unit of work is a "slice" of 64 consecutive weights of one row: one Q2_0_g64 code record
-//    (16 B), half a Q1_0 block's sign bits (8 B), or one planar beat (16 B).  A slice meets exactly two
-//    q8_0 activation blocks.
+//  * The unit of work is a "slice": one 16-byte code record of one row -- a Q2_0_g64 block (64 weights,
+//    two q8_0 activation blocks), a Q1_0 block (128 weights, four activation blocks) or a planar beat
+//    (64 weights).
 //  * A workgroup owns a tile of rows of one product.  It first stages the activation vector into LDS,
 //    once, in the order the unpack needs (the activation, not the weights, is rearranged -- the bankml
 //    report's ternary kernel does the same once per token).  Each int8 activation q is split into a
@@ -29,12 +29,13 @@
 namespace lb {
 
 template <int FMT> struct F;
-// REC: dwords of staged activation per slice: 16 nibble words, then (ggml formats) dx[2] and sum(q)[2]
-template <> struct F<LB_Q2_0_G64> { enum { REC = 20, CODE_BYTES = 16 }; };
-template <> struct F<LB_Q1_0> { enum { REC = 20, CODE_BYTES = 8 }; };
-template <> struct F<LB_TERNARY_PLANAR> { enum { REC = 16, CODE_BYTES = 16 }; };
+// SW: weights per slice; NAB: q8_0 blocks per slice; REC: dwords of staged activation per slice
+// (SW/4 nibble words, then, for the ggml formats, d_x[NAB] (2 d_x for Q1_0) and -sum(q)[NAB])
+template <> struct F<LB_Q2_0_G64> { enum { SW = 64, NAB = 2, REC = 20 }; };
+template <> struct F<LB_Q1_0> { enum { SW = 128, NAB = 4, REC = 40 }; };
+template <> struct F<LB_TERNARY_PLANAR> { enum { SW = 64, NAB = 0, REC = 16 }; };
 
-constexpr int SLICE = 64; // weights per slice
+constexpr int CODE_BYTES = 16; // every slice is one 16-byte record
 
 // ------------------------------------------------------------------------------------------------
 // Activation staging.  Nibble word (a, b) holds, at bits 4n..4n+3, the low (b = 0) or high (b = 1)
@@ -49,10 +50,11 @@ template <int FMT>
 __device__ __forceinline__ void stage_slice(const int8_t *__restrict__ xq, const void *__restrict__ xscale, int sl,
                                             uint32_t *__restrict__ rec)
 {
-    const uint4 *src = reinterpret_cast<const uint4 *>(xq + (int64_t)sl * SLICE);
-    uint32_t wb[SLICE / 4];
+    constexpr int SW = F<FMT>::SW, NAB = F<FMT>::NAB;
+    const uint4 *src = reinterpret_cast<const uint4 *>(xq + (int64_t)sl * SW);
+    uint32_t wb[SW / 4];
 #pragma unroll
-    for (int i = 0; i < SLICE / 16; i++) {
+    for (int i = 0; i < SW / 16; i++) {
         const uint4 t = src[i];
         wb[4 * i + 0] = t.x;
         wb[4 * i + 1] = t.y;
@@ -61,7 +63,7 @@ __device__ __forceinline__ void stage_slice(const int8_t *__restrict__ xq, const
     }
 #define LB_BYTE(i) ((wb[(i) >> 2] >> (8 * ((i)&3))) & 0xffu)
 #pragma unroll
-    for (int a = 0; a < 8; a++) {
+    for (int a = 0; a < SW / 8; a++) {
         uint32_t lo = 0, hi = 0;
 #pragma unroll
         for (int n = 0; n < 8; n++) {
@@ -73,16 +75,18 @@ __device__ __forceinline__ void stage_slice(const int8_t *__restrict__ xq, const
         rec[2 * a + 0] = lo;
         rec[2 * a + 1] = hi;
     }
-    if (FMT != LB_TERNARY_PLANAR) {
+    if (NAB > 0) {
         const uint16_t *xs = reinterpret_cast<const uint16_t *>(xscale);
 #pragma unroll
-        for (int j = 0; j < 2; j++) {
-            rec[16 + j] = __float_as_uint(half_bits_to_float(xs[2 * sl + j]));
+        for (int j = 0; j < NAB; j++) {
+            // Q1_0 keeps 2 d_x (exact): its sums are formed as 2 * S - sum(q), S = sum of q where the bit is 1
+            const float dx = half_bits_to_float(xs[NAB * sl + j]);
+            rec[SW / 4 + j] = __float_as_uint(FMT == LB_Q1_0 ? 2.0f * dx : dx);
             int sq = 0;
 #pragma unroll
             for (int i = 0; i < 32; i++)
                 sq += (int)(int8_t)LB_BYTE(32 * j + i);
-            rec[18 + j] = (uint32_t)sq;
+            rec[SW / 4 + NAB + j] = (uint32_t)(-sq);
         }
     }
 #undef LB_BYTE
@@ -106,7 +110,8 @@ __device__ __forceinline__ int udot8(uint32_t a, uint32_t b, int c)
 __device__ __forceinline__ void q2_isums(uint4 c, const uint32_t *A, int &i0, int &i1)
 {
     const uint32_t cw[4] = {c.x, c.y, c.z, c.w};
-    int h[2] = {0, 0}, l[2] = {0, 0};
+    // the low-nibble accumulators start at -sum(q) (modular), so each block sum is one shift-add
+    int h[2] = {0, 0}, l[2] = {(int)A[18], (int)A[19]};
 #pragma unroll
     for (int k = 0; k < 4; k++) {
         const uint32_t e0 = cw[k] & 0x33333333u;
@@ -117,17 +122,17 @@ __device__ __forceinline__ void q2_isums(uint4 c, const uint32_t *A, int &i0, in
         h[j] = sdot8(e1, A[(2 * k + 1) * 2 + 1], h[j]);
         l[j] = udot8(e1, A[(2 * k + 1) * 2 + 0], l[j]);
     }
-    i0 = h[0] * 16 + l[0] - (int)A[18];
-    i1 = h[1] * 16 + l[1] - (int)A[19];
+    i0 = h[0] * 16 + l[0];
+    i1 = h[1] * 16 + l[1];
 }
 
-// Q1_0 (half a block): 2 sign dwords, 32 bits each; bit r of nibble n is weight 4n + r.
-__device__ __forceinline__ void q1_isums(uint2 b, const uint32_t *A, int &i0, int &i1)
+// Q1_0: 4 sign dwords, 32 bits each (one q8_0 block each); bit r of nibble n is weight 4n + r.
+// Returns S[k] = sum of q over the weights whose bit is 1; the block sum is 2 S[k] - sum(q).
+__device__ __forceinline__ void q1_sel_sums(uint4 b, const uint32_t *A, int (&S)[4])
 {
-    const uint32_t bw[2] = {b.x, b.y};
-    int s[2];
+    const uint32_t bw[4] = {b.x, b.y, b.z, b.w};
 #pragma unroll
-    for (int k = 0; k < 2; k++) {
+    for (int k = 0; k < 4; k++) {
         int h = 0, l = 0;
 #pragma unroll
         for (int r = 0; r < 4; r++) {
@@ -135,10 +140,8 @@ __device__ __forceinline__ void q1_isums(uint2 b, const uint32_t *A, int &i0, in
             h = sdot8(e, A[(4 * k + r) * 2 + 1], h);
             l = udot8(e, A[(4 * k + r) * 2 + 0], l);
         }
-        s[k] = h * 16 + l; // sum of q where the sign bit is 1
+        S[k] = h * 16 + l;
     }
-    i0 = 2 * s[0] - (int)A[18];
-    i1 = 2 * s[1] - (int)A[19];
 }
 
 // Planar: plane words {pos0, pos1, neg0, neg1}.  Masking without a shift leaves bit r of a nibble in
@@ -223,42 +226,48 @@ template <int L> __device__ __forceinline__ float group_sum_f(float v)
 // The next rows' loads are issued before the current rows are computed (ping-pong registers), and the
 // first rows' loads before the activation is staged, so the weight stream never waits on the staging.
 // ------------------------------------------------------------------------------------------------
-template <int FMT, int L, int S> struct RowRegs {
-    uint4 code[S];
-    uint32_t sc[S];
+// Rows in flight per register buffer (two buffers ping-pong).
+template <int FMT> constexpr int rows_in_flight() { return 1; }
+
+template <int FMT, int S> struct RowRegs {
+    uint4 code[rows_in_flight<FMT>()][S];
+    uint32_t sc[rows_in_flight<FMT>()][S];
 };
 
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
+
+// The code records are read exactly once: non-temporal loads keep the stream from displacing the
+// activations, tables and scales in the caches.
 template <int FMT, int L, int S>
-__device__ __forceinline__ void issue_row(RowRegs<FMT, L, S> &r, const uint8_t *__restrict__ W,
-                                          const uint16_t *__restrict__ scales, uint32_t row, int ns, int li)
+__device__ __forceinline__ void issue_rows(RowRegs<FMT, S> &r, const uint8_t *__restrict__ W,
+                                           const uint16_t *__restrict__ scales, const uint32_t (&row)[rows_in_flight<FMT>()],
+                                           int ns, int li)
 {
-    constexpr int CB = F<FMT>::CODE_BYTES;
-    const uint32_t nsr = FMT == LB_Q1_0 ? (uint32_t)ns / 2 : (uint32_t)ns;
 #pragma unroll
-    for (int i = 0; i < S; i++) {
-        const uint32_t sl = (uint32_t)min(li + i * L, ns - 1);
-        const uint32_t off = (row * (uint32_t)ns + sl) * CB;
-        if (CB == 16) {
-            r.code[i] = *reinterpret_cast<const uint4 *>(W + off);
-        } else {
-            const uint2 t = *reinterpret_cast<const uint2 *>(W + off);
-            r.code[i] = make_uint4(t.x, t.y, 0, 0);
+    for (int u = 0; u < rows_in_flight<FMT>(); u++)
+#pragma unroll
+        for (int i = 0; i < S; i++) {
+            const uint32_t sl = (uint32_t)min(li + i * L, ns - 1);
+            const uint32_t idx = row[u] * (uint32_t)ns + sl;
+            const v4u t = __builtin_nontemporal_load(reinterpret_cast<const v4u *>(W + idx * CODE_BYTES));
+            r.code[u][i] = make_uint4(t.x, t.y, t.z, t.w);
+            if (FMT != LB_TERNARY_PLANAR)
+                r.sc[u][i] = scales[idx]; // small, shared by neighbouring lanes: left cacheable
         }
-        if (FMT != LB_TERNARY_PLANAR)
-            r.sc[i] = scales[row * nsr + (FMT == LB_Q1_0 ? sl >> 1 : sl)];
-    }
 }
 
 template <int FMT, int L, int S, bool EMIT>
-__device__ __forceinline__ void compute_row(const RowRegs<FMT, L, S> &r, const uint32_t (&act)[S][F<FMT>::REC],
-                                            int ns, int li, bool valid, int row, float w_scale, float sx,
-                                            float *__restrict__ y, int32_t *__restrict__ sums)
+__device__ __forceinline__ void compute_row(const uint4 (&code)[S], const uint32_t (&sc)[S],
+                                            const uint32_t (&act)[S][F<FMT>::REC], const float (&cfold)[S], int ns, int li,
+                                            bool valid, int row, float w_scale, float sx, float *__restrict__ y,
+                                            int32_t *__restrict__ sums)
 {
+    constexpr int NAB = F<FMT>::NAB, DX = F<FMT>::SW / 4;
     if (FMT == LB_TERNARY_PLANAR) {
         PlanarAcc acc = {};
 #pragma unroll
         for (int i = 0; i < S; i++)
-            planar_accumulate(r.code[i], act[i], acc);
+            planar_accumulate(code[i], act[i], acc);
         const int t = group_sum_i<L>(planar_total8(acc));
         if (valid && li == L - 1) {
             const int a = t >> 3; // exact: the total is a multiple of 8
@@ -275,19 +284,31 @@ __device__ __forceinline__ void compute_row(const RowRegs<FMT, L, S> &r, const u
 #pragma unroll
         for (int i = 0; i < S; i++) {
             const int sl = li + i * L;
-            int i0, i1;
-            if (FMT == LB_Q2_0_G64)
-                q2_isums(r.code[i], act[i], i0, i1);
-            else
-                q1_isums(make_uint2(r.code[i].x, r.code[i].y), act[i], i0, i1);
-            const float dx0 = __uint_as_float(act[i][16]), dx1 = __uint_as_float(act[i][17]);
-            const float t = fmaf(dx1, (float)i1, dx0 * (float)i0);
-            const float c = fmaf(half_bits_to_float((uint16_t)r.sc[i]), t, part);
+            float t;
+            int is[NAB > 0 ? NAB : 1];
+            if (FMT == LB_Q2_0_G64) {
+                q2_isums(code[i], act[i], is[0], is[1]);
+                // bankml report, section III.3: one multiply-add per q8_0 block, then one per weight block
+                t = fmaf(__uint_as_float(act[i][DX + 1]), (float)is[1], __uint_as_float(act[i][DX]) * (float)is[0]);
+            } else {
+                // t = sum_j d_x[j] (2 S_j - sum q_j): the -sum_j d_x[j] sum q_j part is the slice constant
+                // cfold (computed once per lane), then one multiply-add by 2 d_x[j] per q8_0 block
+                int Ssel[4];
+                q1_sel_sums(code[i], act[i], Ssel);
+                t = cfold[i];
+#pragma unroll
+                for (int j = 0; j < 4; j++) {
+                    t = fmaf(__uint_as_float(act[i][DX + j]), (float)Ssel[j], t);
+                    is[j] = 2 * Ssel[j] + (int)act[i][DX + NAB + j];
+                }
+            }
+            const float c = fmaf(half_bits_to_float((uint16_t)sc[i]), t, part);
             part = sl < ns ? c : part;
             if (EMIT && valid && sl < ns) {
-                int32_t *o = sums + (int64_t)row * (ns * 2) + 2 * sl;
-                o[0] = i0;
-                o[1] = i1;
+                int32_t *o = sums + (int64_t)row * (ns * NAB) + NAB * sl;
+#pragma unroll
+                for (int j = 0; j < NAB; j++)
+                    o[j] = is[j];
             }
         }
         part = group_sum_f<L>(part);
@@ -303,19 +324,28 @@ __device__ __forceinline__ void matvec_tile(const uint8_t *__restrict__ W, int N
                                             uint32_t *__restrict__ lds)
 {
     constexpr int REC = F<FMT>::REC;
-    constexpr int CB = F<FMT>::CODE_BYTES;
     constexpr int GROUPS = 64 / L;              // rows per wave per iteration
     constexpr int ROWS_IT = GROUPS * (WG / 64); // rows per workgroup per iteration
-    const int ns = K / SLICE;                   // slices per row
+    const int ns = K / F<FMT>::SW;              // slices per row
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int g = lane / L, li = lane % L;
-    const uint16_t *scales = reinterpret_cast<const uint16_t *>(W + (int64_t)N * ns * CB);
+    const uint16_t *scales = reinterpret_cast<const uint16_t *>(W + (int64_t)N * ns * CODE_BYTES);
     const int rbase = wave * GROUPS + g; // this lane's row within an iteration
 
-    auto row_at = [&](int it) -> uint32_t { return (uint32_t)(row0 + min(it + rbase, nrows - 1)); };
+    constexpr int U = rows_in_flight<FMT>();
+    constexpr int STEP = U * ROWS_IT; // rows per workgroup per register buffer
+    auto rows_at = [&](int it, uint32_t (&rows)[U]) {
+#pragma unroll
+        for (int u = 0; u < U; u++)
+            rows[u] = (uint32_t)(row0 + min(it + u * ROWS_IT + rbase, nrows - 1));
+    };
 
-    RowRegs<FMT, L, S> ra, rb;
-    issue_row<FMT, L, S>(ra, W, scales, row_at(0), ns, li);
+    RowRegs<FMT, S> ra, rb;
+    {
+        uint32_t rows[U];
+        rows_at(0, rows);
+        issue_rows<FMT, L, S>(ra, W, scales, rows, ns, li);
+    }
 
     for (int sl = threadIdx.x; sl < ns; sl += WG)
         stage_slice<FMT>(xq, xscale, sl, lds + sl * REC);
@@ -342,53 +372,90 @@ __device__ __forceinline__ void matvec_tile(const uint8_t *__restrict__ W, int N
         }
     }
     const float sx = FMT == LB_TERNARY_PLANAR ? *reinterpret_cast<const float *>(xscale) : 0.0f;
+    float cfold[S]; // Q1_0: -sum_j d_x[j] sum(q_j) of each slice (the staged words hold 2 d_x[j] and -sum(q_j))
+#pragma unroll
+    for (int i = 0; i < S; i++) {
+        float c = 0.0f;
+        if (FMT == LB_Q1_0) {
+#pragma unroll
+            for (int j = 0; j < 4; j++)
+                c = fmaf(0.5f * __uint_as_float(act[i][32 + j]), (float)(int)act[i][36 + j], c);
+        }
+        cfold[i] = c;
+    }
+    auto compute = [&](const RowRegs<FMT, S> &r, int it) {
+#pragma unroll
+        for (int u = 0; u < U; u++) {
+            const int rl = it + u * ROWS_IT + rbase;
+            compute_row<FMT, L, S, EMIT>(r.code[u], r.sc[u], act, cfold, ns, li, rl < nrows, row0 + rl, w_scale, sx, y,
+                                         sums);
+        }
+    };
 
-    for (int it = 0; it < nrows; it += 2 * ROWS_IT) {
-        const bool more1 = it + ROWS_IT < nrows; // uniform across the workgroup
-        if (more1)
-            issue_row<FMT, L, S>(rb, W, scales, row_at(it + ROWS_IT), ns, li);
-        compute_row<FMT, L, S, EMIT>(ra, act, ns, li, it + rbase < nrows, row0 + it + rbase, w_scale, sx, y, sums);
+    for (int it = 0; it < nrows; it += 2 * STEP) {
+        const bool more1 = it + STEP < nrows; // uniform across the workgroup
+        if (more1) {
+            uint32_t rows[U];
+            rows_at(it + STEP, rows);
+            issue_rows<FMT, L, S>(rb, W, scales, rows, ns, li);
+        }
+        compute(ra, it);
         if (!more1)
             break;
-        if (it + 2 * ROWS_IT < nrows)
-            issue_row<FMT, L, S>(ra, W, scales, row_at(it + 2 * ROWS_IT), ns, li);
-        compute_row<FMT, L, S, EMIT>(rb, act, ns, li, it + ROWS_IT + rbase < nrows, row0 + it + ROWS_IT + rbase,
-                                     w_scale, sx, y, sums);
+        if (it + 2 * STEP < nrows) {
+            uint32_t rows[U];
+            rows_at(it + 2 * STEP, rows);
+            issue_rows<FMT, L, S>(ra, W, scales, rows, ns, li);
+        }
+        compute(rb, it + STEP);
     }
 }
 
 // ------------------------------------------------------------------------------------------------
-// Configurations (L lanes per row, S slices per lane).  The host picks, per product, the entry that
-// wastes the fewest lane slots for K/64 slices, then the one with fewer lanes per row.
+// Configurations (L lanes per row, S slices per lane), each compiled as its own kernel; the staged
+// activations of a lane (S * REC dwords) must fit a budget of 160 registers.
 // ------------------------------------------------------------------------------------------------
 #define LB_CFGS(X)                                                                                            \
     X(0, 1, 1) X(1, 1, 2) X(2, 2, 2) X(3, 4, 1) X(4, 4, 2) X(5, 4, 4) X(6, 8, 2) X(7, 8, 4) X(8, 8, 5)        \
-    X(9, 16, 1) X(10, 16, 2) X(11, 16, 4) X(12, 32, 2) X(13, 32, 4) X(14, 64, 2) X(15, 64, 3) X(16, 64, 4)    \
-    X(17, 64, 8)
+    X(9, 16, 1) X(10, 16, 2) X(11, 16, 4) X(12, 32, 2) X(13, 32, 3) X(14, 32, 4) X(15, 64, 2) X(16, 64, 3)    \
+    X(17, 64, 4) X(18, 64, 8) X(19, 32, 1) X(20, 64, 1) X(21, 8, 8) X(22, 16, 3) X(23, 32, 6) X(24, 16, 7)
 
 struct CfgLS {
     int L, S;
 };
 #define LB_CFG_ENTRY(i, l, s) {l, s},
-static const CfgLS kCfgs[] = {LB_CFGS(LB_CFG_ENTRY)};
+static constexpr CfgLS kCfgs[] = {LB_CFGS(LB_CFG_ENTRY)};
 #undef LB_CFG_ENTRY
 constexpr int kNumCfgs = sizeof(kCfgs) / sizeof(kCfgs[0]);
-constexpr int kBigCfg = 17; // the only entry kept out of the batched kernel (160 VGPRs of activations)
 
-static int pick_cfg(int64_t ns, bool batched)
+constexpr int rec_of(int fmt) { return fmt == LB_Q1_0 ? F<LB_Q1_0>::REC : fmt == LB_Q2_0_G64 ? F<LB_Q2_0_G64>::REC
+                                                                                            : F<LB_TERNARY_PLANAR>::REC; }
+constexpr int sw_of(int fmt) { return fmt == LB_Q1_0 ? 128 : 64; }
+constexpr bool cfg_allowed(int fmt, int S) { return S * rec_of(fmt) <= 160; }
+
+// Choice (measured on the 8B- and 2B-shape products): fewest idle lane slots; among equals, a light
+// register footprint (at most 80 staged dwords per lane, which keeps 3-4 waves per SIMD) before a
+// heavy one; then fewer lanes per row (a shorter cross-lane reduction per row).
+static int pick_cfg(int fmt, int64_t ns)
 {
     int best = -1;
     int64_t best_waste = 0;
+    bool best_light = false;
     for (int c = 0; c < kNumCfgs; c++) {
-        if (batched && c == kBigCfg)
+        if (!cfg_allowed(fmt, kCfgs[c].S))
             continue;
         const int64_t slots = (int64_t)kCfgs[c].L * kCfgs[c].S;
         if (slots < ns)
             continue;
         const int64_t waste = slots - ns;
-        if (best < 0 || waste < best_waste || (waste == best_waste && kCfgs[c].L < kCfgs[best].L)) {
+        const bool light = kCfgs[c].S * rec_of(fmt) <= 80;
+        const bool better = best < 0 || waste < best_waste ||
+                            (waste == best_waste && light && !best_light) ||
+                            (waste == best_waste && light == best_light && kCfgs[c].L < kCfgs[best].L);
+        if (better) {
             best = c;
             best_waste = waste;
+            best_light = light;
         }
     }
     return best;
@@ -396,23 +463,20 @@ static int pick_cfg(int64_t ns, bool batched)
 
 int matvec_config(int fmt, int64_t K)
 {
-    (void)fmt;
-    if (K <= 0 || K % SLICE)
+    if (K <= 0 || K % sw_of(fmt))
         return -1;
-    return pick_cfg(K / SLICE, true);
+    return pick_cfg(fmt, K / sw_of(fmt));
 }
 
-bool matvec_supported_k(int fmt, int64_t K)
-{
-    (void)fmt;
-    return K > 0 && K % SLICE == 0 && pick_cfg(K / SLICE, false) >= 0;
-}
+bool matvec_supported_k(int fmt, int64_t K) { return matvec_config(fmt, K) >= 0; }
 
 int matvec_config_rows_per_iter(int fmt, int cfg)
 {
     (void)fmt;
     return (64 / kCfgs[cfg].L) * (WG / 64);
 }
+
+int matvec_stage_bytes(int fmt, int64_t K) { return (int)((K / sw_of(fmt)) * rec_of(fmt) * 4); }
 
 template <int FMT, int L, int S, bool EMIT>
 __global__ __launch_bounds__(WG) void matvec_kernel(const uint8_t *__restrict__ W, int N, int K, float w_scale,
@@ -430,12 +494,13 @@ static hipError_t launch_single(int cfg, const uint8_t *W, int N, int K, float w
                                 const void *xscale, float *y, int32_t *sums, int tile_rows, hipStream_t stream)
 {
     const int ntiles = (N + tile_rows - 1) / tile_rows;
-    const size_t lds = (size_t)(K / SLICE) * F<FMT>::REC * 4;
+    const size_t lds = (size_t)matvec_stage_bytes(FMT, K);
     switch (cfg) {
 #define LB_CASE(i, l, s)                                                                                      \
     case i:                                                                                                   \
-        hipLaunchKernelGGL((matvec_kernel<FMT, l, s, EMIT>), dim3(ntiles), dim3(WG), lds, stream, W, N, K,       \
-                           w_scale, xq, xscale, y, sums, tile_rows);                                           \
+        if constexpr (cfg_allowed(FMT, s))                                                                    \
+            hipLaunchKernelGGL((matvec_kernel<FMT, l, s, EMIT>), dim3(ntiles), dim3(WG), lds, stream, W, N, K,   \
+                               w_scale, xq, xscale, y, sums, tile_rows);                                       \
         break;
         LB_CFGS(LB_CASE)
 #undef LB_CASE
@@ -448,7 +513,7 @@ static hipError_t launch_single(int cfg, const uint8_t *W, int N, int K, float w
 hipError_t launch_matvec(int fmt, const uint8_t *W, int64_t N, int64_t K, float w_scale, const int8_t *xq,
                          const void *xscale, float *y, int32_t *sums, hipStream_t s)
 {
-    const int cfg = pick_cfg(K / SLICE, false);
+    const int cfg = matvec_config(fmt, K);
     if (cfg < 0)
         return hipErrorInvalidValue;
     // enough workgroups to cover the device when the product allows it, whole iterations per tile
@@ -476,10 +541,11 @@ hipError_t launch_matvec(int fmt, const uint8_t *W, int64_t N, int64_t K, float 
 }
 
 // ------------------------------------------------------------------------------------------------
-// Batched: one launch over a device table of products of one format.  Each workgroup looks up its
-// product (a uniform, scalar-cached read) and runs the configuration the host chose for it.
+// Batched: one launch per (format, configuration) group of a work list.  Each workgroup looks up its
+// product (a uniform, scalar-cached read); every instantiation is compiled for one configuration, so
+// each gets the registers it needs and no more.
 // ------------------------------------------------------------------------------------------------
-template <int FMT>
+template <int FMT, int L, int S>
 __global__ __launch_bounds__(WG) void matvec_batched_kernel(const DevDesc *__restrict__ desc,
                                                             const int32_t *__restrict__ tile_prod)
 {
@@ -488,41 +554,38 @@ __global__ __launch_bounds__(WG) void matvec_batched_kernel(const DevDesc *__res
     const DevDesc d = desc[tile_prod[t]];
     const int row0 = (t - d.tile_begin) * d.tile_rows;
     const int nrows = min(d.tile_rows, d.N - row0);
-    switch (d.cfg) {
+    matvec_tile<FMT, L, S, false>(d.W, d.N, d.K, d.w_scale, d.xq, d.xscale, d.y, nullptr, row0, nrows, lds);
+}
+
+template <int FMT>
+static hipError_t launch_batched_fmt(const BatchGroup &g, hipStream_t stream, size_t lds_bytes)
+{
+    switch (g.cfg_a) {
 #define LB_BCASE(i, l, s)                                                                                     \
     case i:                                                                                                   \
-        if (i != kBigCfg)                                                                                     \
-            matvec_tile<FMT, l, (i == kBigCfg ? 1 : s), false>(d.W, d.N, d.K, d.w_scale, d.xq, d.xscale, d.y,  \
-                                                               nullptr, row0, nrows, lds);                     \
+        if constexpr (cfg_allowed(FMT, s))                                                                    \
+            hipLaunchKernelGGL((matvec_batched_kernel<FMT, l, s>), dim3(g.ntiles), dim3(WG), lds_bytes, stream,  \
+                               g.desc, g.tile_prod);                                                           \
         break;
         LB_CFGS(LB_BCASE)
 #undef LB_BCASE
-    }
-}
-
-hipError_t launch_matvec_batched(const BatchGroup &g, hipStream_t s, size_t lds_bytes)
-{
-    switch (g.fmt) {
-    case LB_Q1_0:
-        hipLaunchKernelGGL(matvec_batched_kernel<LB_Q1_0>, dim3(g.ntiles), dim3(WG), lds_bytes, s, g.desc, g.tile_prod);
-        break;
-    case LB_Q2_0_G64:
-        hipLaunchKernelGGL(matvec_batched_kernel<LB_Q2_0_G64>, dim3(g.ntiles), dim3(WG), lds_bytes, s, g.desc,
-                           g.tile_prod);
-        break;
-    case LB_TERNARY_PLANAR:
-        hipLaunchKernelGGL(matvec_batched_kernel<LB_TERNARY_PLANAR>, dim3(g.ntiles), dim3(WG), lds_bytes, s, g.desc,
-                           g.tile_prod);
-        break;
     default:
         return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }
 
-int matvec_stage_bytes(int fmt, int64_t K)
+hipError_t launch_matvec_batched(const BatchGroup &g, hipStream_t s, size_t lds_bytes)
 {
-    return (int)((K / SLICE) * (fmt == LB_TERNARY_PLANAR ? F<LB_TERNARY_PLANAR>::REC : F<LB_Q2_0_G64>::REC) * 4);
+    switch (g.fmt) {
+    case LB_Q1_0:
+        return launch_batched_fmt<LB_Q1_0>(g, s, lds_bytes);
+    case LB_Q2_0_G64:
+        return launch_batched_fmt<LB_Q2_0_G64>(g, s, lds_bytes);
+    case LB_TERNARY_PLANAR:
+        return launch_batched_fmt<LB_TERNARY_PLANAR>(g, s, lds_bytes);
+    }
+    return hipErrorInvalidValue;
 }
 
 } // namespace lb
