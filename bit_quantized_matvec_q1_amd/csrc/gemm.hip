@@ -5,31 +5,38 @@
 // tile loads each weight block once and applies it to several activation columns).
 //
 // Mapping to CDNA4:
-//  * A workgroup owns a tile of TN = 128 weight rows x TM = 64 activation rows.  Per K-step of 128
-//    weights it loads the packed codes of its 128 rows once and unpacks them into LDS as int8 weights in
-//    natural column order (shift and mask, a 4x4 byte transpose with v_perm_b32, and a v_perm_b32
-//    table lookup from code to weight byte: Q2_0 c -> c - 1, Q1_0 bit -> +/-1, planar (pos, neg) ->
-//    pos - neg).
-//  * Each of the 4 waves computes 32 weight rows x 64 activation rows: per q8_0 block (32 columns, the
-//    MFMA's K depth) one A operand from LDS and two B operands (activation rows, read straight from the
-//    L2-resident activation matrix), two MFMAs.  Each MFMA result is one exact int32 sum per (row, block).
+//  * A workgroup owns a tile of TN = 128 weight rows x TM = 64 activation rows and walks K in steps of
+//    128 columns.  Each step is software-pipelined: the packed weight codes, activation tile and
+//    activation scales of the step three ahead are loaded into a register ring while the current step
+//    computes; at the top
+//    of a step they are written to double-buffered LDS -- the weights unpacked to int8 in natural column
+//    order (shift and mask, a 4x4 byte transpose with v_perm_b32, and a v_perm_b32 lookup from code to
+//    weight byte: Q2_0 c -> c - 1, Q1_0 bit -> +/-1, planar (pos, neg) -> pos - neg) -- and one barrier
+//    per step separates the writes from the reads.
+//  * A workgroup is 8 waves (512 threads); each wave computes one 32 x 32 tile (32 weight rows x 32
+//    activation rows): per q8_0 block (32 columns, the MFMA's K depth) one A operand (weights) and one B
+//    operand (activations) from LDS, one MFMA.  Each MFMA result is one exact int32 sum per (weight row,
+//    activation row, block).  Small per-wave state keeps about four waves per SIMD resident, so one
+//    wave's rescale arithmetic overlaps another's matrix-core and LDS latency.
 //  * The accumulator input of every MFMA is a constant register tile holding 0x4B400000 (1.5 * 2^23), so
 //    each result, read as fp32, is 1.5 * 2^23 + isum exactly; one FMA with the block's activation scale
-//    and the precomputed -d_x * 1.5 * 2^23 gives round(d_x * isum) without a conversion.  The weight
-//    block scale is then applied with one more FMA (bankml technical report, section III.3: one multiply-
-//    add per q8_0 block, then one per weight block).
+//    and -d_x * 1.5 * 2^23 gives round(d_x * isum) without a conversion.  The weight block scale is then
+//    applied with one more FMA (bankml technical report, section III.3: one multiply-add per q8_0 block,
+//    then one per weight block).
 //  * Planar weights have no block scales: the MFMA accumulates int32 over the whole row and the two
-//    per-row/per-tensor scales are applied once at the end.
+//    per-row / per-tensor scales are applied once at the end.
 #include "lowbit_internal.h"
 
 namespace lb {
 
 namespace {
 
-constexpr int TN = 128; // weight rows per workgroup
-constexpr int TM = 64;  // activation rows per workgroup
-constexpr int KS = 128; // weights per K-step
+constexpr int GT = 512;          // threads per workgroup (8 waves)
+constexpr int TN = 128;          // weight rows per workgroup
+constexpr int TM = 64;           // activation rows per workgroup
+constexpr int KS = 128;          // columns per K-step
 constexpr int WROW = KS / 4 + 4; // LDS dwords per unpacked weight row (padded against bank conflicts)
+constexpr int XROW = KS / 4 + 4; // LDS dwords per activation row
 constexpr uint32_t BIAS = 0x4B400000u; // 1.5 * 2^23 as fp32 bits
 constexpr float BIASF = 12582912.0f;
 
@@ -64,8 +71,8 @@ __device__ __forceinline__ void unpack_q2_dword(uint32_t v, uint32_t *out)
     transpose4(e[0], e[1], e[2], e[3], out);
 }
 
-// Q1_0 / planar: 32 sign bits (or plane bits) -> 8 dwords of int8 weights in order, via an 8-entry
-// byte table indexed by the 0/1 (Q1_0) or pos | neg << 1 (planar) selector of each weight.
+// Q1_0 / planar: 32 sign bits (or plane bits) -> 8 dwords of int8 weights in order, via a byte table
+// indexed by the 0/1 (Q1_0) or pos | neg << 1 (planar) selector of each weight.
 __device__ __forceinline__ void unpack_bits_dword(uint32_t sel_lo_bits, uint32_t sel_hi_bits, bool planar,
                                                   uint32_t *out)
 {
@@ -89,163 +96,245 @@ __device__ __forceinline__ void unpack_bits_dword(uint32_t sel_lo_bits, uint32_t
     }
 }
 
-template <int FMT, bool EMIT>
-__global__ __launch_bounds__(WG) void gemm_kernel(const uint8_t *__restrict__ W, int N, int K, float w_scale,
-                                                  const int8_t *__restrict__ X, const void *__restrict__ Xscale, int M,
-                                                  float *__restrict__ Y, int32_t *__restrict__ sums)
+// What one thread carries from global memory into a K-step: a quarter of one weight row's codes for the
+// step, 16 activation bytes, and (threads < TM) the row's four activation scales.
+struct StepRegs {
+    uint2 wcode;     // Q2_0: 2 code dwords; Q1_0: 1 sign dword (.x); planar: pos dword (.x), neg dword (.y)
+    uint32_t wscale; // the weight block scale (binary16), where this thread stores it
+    uint4 x;         // 16 activation bytes
+    uint2 dx;        // 4 binary16 activation scales
+};
+
+template <int FMT>
+__device__ __forceinline__ void load_step(StepRegs &r, const uint8_t *__restrict__ W, const uint16_t *__restrict__ wsc,
+                                          int N, int K, const int8_t *__restrict__ X, const uint16_t *__restrict__ xsc,
+                                          int M, int n0, int m0, int kk, int tid)
 {
-    __shared__ __attribute__((aligned(16))) uint32_t w_lds[TN * WROW];
-    __shared__ __attribute__((aligned(16))) float dw_lds[2 * TN];
+    const int kab = min(KS, K - kk) / QK8; // activation blocks in this step
+    const int row = min(n0 + (tid >> 2), N - 1), p = tid & 3;
+    if (FMT == LB_Q1_0) {
+        // one 128-weight record per row; thread p takes its sign dword p
+        const int64_t idx = (int64_t)row * (K / 128) + kk / 128;
+        r.wcode.x = *reinterpret_cast<const uint32_t *>(W + idx * 16 + 4 * p);
+        if (p == 0)
+            r.wscale = wsc[idx];
+    } else {
+        // two 64-weight records per row (one on a half step); thread p takes half p & 1 of record p >> 1
+        const int bb = p >> 1, hh = p & 1;
+        if (2 * bb < kab) {
+            const int64_t idx = (int64_t)row * (K / 64) + kk / 64 + bb;
+            if (FMT == LB_TERNARY_PLANAR) {
+                r.wcode.x = *reinterpret_cast<const uint32_t *>(W + idx * 16 + 4 * hh);     // pos
+                r.wcode.y = *reinterpret_cast<const uint32_t *>(W + idx * 16 + 8 + 4 * hh); // neg
+            } else {
+                r.wcode = *reinterpret_cast<const uint2 *>(W + idx * 16 + 8 * hh);
+                if (hh == 0)
+                    r.wscale = wsc[idx];
+            }
+        }
+    }
+    // activation tile: 64 rows x kab * 32 bytes; thread -> (row tid / 8, 16-byte chunk tid % 8)
+    {
+        const int m = min(m0 + (tid >> 3), M - 1), ch = tid & 7;
+        if (ch < 2 * kab)
+            r.x = *reinterpret_cast<const uint4 *>(X + (int64_t)m * K + kk + 16 * ch);
+    }
+    if (FMT != LB_TERNARY_PLANAR && tid < TM) {
+        const int m = min(m0 + tid, M - 1);
+        const uint16_t *pp = xsc + (int64_t)m * (K / QK8) + kk / QK8;
+        uint16_t hs[4] = {0, 0, 0, 0};
+        for (int j = 0; j < kab; j++)
+            hs[j] = pp[j];
+        r.dx = make_uint2((uint32_t)hs[0] | ((uint32_t)hs[1] << 16), (uint32_t)hs[2] | ((uint32_t)hs[3] << 16));
+    }
+}
+
+struct __attribute__((aligned(16))) Lds {
+    uint32_t w[2][TN * WROW];
+    uint32_t x[2][TM * XROW];
+    float dw[2][2 * TN]; // weight block scales: [block within step][row]
+    float dx[2][4 * TM]; // activation scales: [block within step][row]
+};
+
+template <int FMT>
+__device__ __forceinline__ void store_step(Lds &lds, int buf, const StepRegs &r, int K, int kk, int tid)
+{
+    const int kab = min(KS, K - kk) / QK8;
+    const int rr = tid >> 2, p = tid & 3;
+    uint32_t *wrow = lds.w[buf] + rr * WROW;
+    if (FMT == LB_Q1_0) {
+        uint32_t o[8];
+        unpack_bits_dword(r.wcode.x, 0u, false, o);
+        *reinterpret_cast<uint4 *>(wrow + 8 * p) = make_uint4(o[0], o[1], o[2], o[3]);
+        *reinterpret_cast<uint4 *>(wrow + 8 * p + 4) = make_uint4(o[4], o[5], o[6], o[7]);
+        if (p == 0)
+            lds.dw[buf][rr] = half_bits_to_float((uint16_t)r.wscale);
+    } else {
+        const int bb = p >> 1, hh = p & 1;
+        if (2 * bb < kab) {
+            uint32_t *dst = wrow + 16 * bb + 8 * hh;
+            uint32_t o[8];
+            if (FMT == LB_TERNARY_PLANAR) {
+                unpack_bits_dword(r.wcode.x, r.wcode.y, true, o);
+            } else {
+                unpack_q2_dword(r.wcode.x, o);
+                unpack_q2_dword(r.wcode.y, o + 4);
+                if (hh == 0)
+                    lds.dw[buf][bb * TN + rr] = half_bits_to_float((uint16_t)r.wscale);
+            }
+            *reinterpret_cast<uint4 *>(dst) = make_uint4(o[0], o[1], o[2], o[3]);
+            *reinterpret_cast<uint4 *>(dst + 4) = make_uint4(o[4], o[5], o[6], o[7]);
+        }
+    }
+    {
+        const int mr = tid >> 3, ch = tid & 7;
+        if (ch < 2 * kab)
+            *reinterpret_cast<uint4 *>(lds.x[buf] + mr * XROW + 4 * ch) = r.x;
+    }
+    if (FMT != LB_TERNARY_PLANAR && tid < TM) {
+        lds.dx[buf][0 * TM + tid] = half_bits_to_float((uint16_t)(r.dx.x & 0xffffu));
+        lds.dx[buf][1 * TM + tid] = half_bits_to_float((uint16_t)(r.dx.x >> 16));
+        lds.dx[buf][2 * TM + tid] = half_bits_to_float((uint16_t)(r.dx.y & 0xffffu));
+        lds.dx[buf][3 * TM + tid] = half_bits_to_float((uint16_t)(r.dx.y >> 16));
+    }
+}
+
+// One K-step of one wave: NJ activation blocks (compile-time, so the pairing of blocks into weight
+// blocks and every register index are static).
+template <int FMT, bool EMIT, int NJ>
+__device__ __forceinline__ void step_compute(const Lds &lds, int buf, int h, int l32, int wn, int wm, int m0, int n0,
+                                             int M, int N, int nab, int kk, float (&acc)[16], v16i &iacc,
+                                             const v16i &cbias, int32_t *__restrict__ sums)
+{
+    constexpr bool PLANAR = FMT == LB_TERNARY_PLANAR;
+    constexpr int JW = FMT == LB_Q1_0 ? 4 : 2; // activation blocks per weight block
+    const uint32_t *wl = lds.w[buf] + (32 * wn + l32) * WROW + 4 * h;
+    const uint32_t *xl = lds.x[buf] + (32 * wm + l32) * XROW + 4 * h;
+    float t[16];
+#pragma unroll
+    for (int j = 0; j < NJ; j++) {
+        const uint4 a4 = *reinterpret_cast<const uint4 *>(wl + 8 * j);
+        const uint4 b4 = *reinterpret_cast<const uint4 *>(xl + 8 * j);
+        const v4i A = {(int)a4.x, (int)a4.y, (int)a4.z, (int)a4.w};
+        const v4i B = {(int)b4.x, (int)b4.y, (int)b4.z, (int)b4.w};
+        if (PLANAR) {
+            iacc = __builtin_amdgcn_mfma_i32_32x32x32_i8(A, B, iacc, 0, 0, 0);
+            continue;
+        }
+        const v16i D = __builtin_amdgcn_mfma_i32_32x32x32_i8(A, B, cbias, 0, 0, 0);
+        const float dx = lds.dx[buf][j * TM + 32 * wm + l32];
+        const float c = -dx * BIASF; // exact: an 11-bit significand times 3 * 2^22
+#pragma unroll
+        for (int i = 0; i < 16; i++) {
+            const float v = fmaf(dx, __int_as_float(D[i]), c); // round(d_x * isum)
+            t[i] = (j % JW) == 0 ? v : t[i] + v;
+        }
+        if (EMIT) {
+            const int m = m0 + 32 * wm + l32, kb = kk / QK8 + j;
+#pragma unroll
+            for (int i = 0; i < 16; i++) {
+                const int n = n0 + 32 * wn + 8 * (i >> 2) + 4 * h + (i & 3);
+                if (m < M && n < N)
+                    sums[((int64_t)m * N + n) * nab + kb] = D[i] - (int)BIAS;
+            }
+        }
+        if ((j % JW) == JW - 1) {
+            const int b = j / JW;
+#pragma unroll
+            for (int g = 0; g < 4; g++) {
+                const float4 dw = *reinterpret_cast<const float4 *>(lds.dw[buf] + b * TN + 32 * wn + 8 * g + 4 * h);
+                const float dwv[4] = {dw.x, dw.y, dw.z, dw.w};
+#pragma unroll
+                for (int q = 0; q < 4; q++)
+                    acc[4 * g + q] = fmaf(dwv[q], t[4 * g + q], acc[4 * g + q]);
+            }
+        }
+    }
+}
+
+template <int FMT, bool EMIT>
+__global__ __launch_bounds__(GT, 2) void gemm_kernel(const uint8_t *__restrict__ W, int N, int K, float w_scale,
+                                                     const int8_t *__restrict__ X, const void *__restrict__ Xscale,
+                                                     int M, float *__restrict__ Y, int32_t *__restrict__ sums)
+{
+    __shared__ Lds lds;
 
     constexpr bool PLANAR = FMT == LB_TERNARY_PLANAR;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int h = lane >> 5, l32 = lane & 31;
+    const int wn = wave & 3, wm = wave >> 2; // this wave's 32 x 32 tile inside the 128 x 64 workgroup tile
     const int n0 = blockIdx.x * TN, m0 = blockIdx.y * TM;
-    const int ns = K / 64;        // 16-byte records per row (Q2_0, planar) / half that for Q1_0
-    const int nrec = FMT == LB_Q1_0 ? K / 128 : ns;
-    const int nab = K / QK8;      // activation blocks per row
+    const int nrec = FMT == LB_Q1_0 ? K / 128 : K / 64; // 16-byte records per weight row
+    const int nab = K / QK8;                             // activation blocks per row
     const uint16_t *wsc = reinterpret_cast<const uint16_t *>(W + (int64_t)N * nrec * 16);
-
-    // this lane's activation rows (clamped: rows past M are computed and never stored)
-    int mrow[2];
-#pragma unroll
-    for (int s = 0; s < 2; s++)
-        mrow[s] = min(m0 + 32 * s + l32, M - 1);
+    const uint16_t *xsc = reinterpret_cast<const uint16_t *>(Xscale);
 
     v16i cbias;
 #pragma unroll
     for (int i = 0; i < 16; i++)
         cbias[i] = (int)BIAS;
-
-    float acc[2][16];
-    v16i iacc[2];
+    float acc[16];
+    v16i iacc;
 #pragma unroll
-    for (int s = 0; s < 2; s++)
-#pragma unroll
-        for (int i = 0; i < 16; i++) {
-            acc[s][i] = 0.0f;
-            iacc[s][i] = 0;
-        }
-
-    for (int kk = 0; kk < K; kk += KS) {
-        const int kab = min(KS, K - kk) / QK8; // activation blocks in this step (4, or 2 on a Q2_0 / planar tail)
-        // --- unpack this step's weights into LDS ---
-        __syncthreads();
-        if (FMT == LB_Q1_0) {
-            if (tid < TN) {
-                const int row = min(n0 + tid, N - 1);
-                const uint4 c = *reinterpret_cast<const uint4 *>(W + ((int64_t)row * nrec + kk / 128) * 16);
-                const uint32_t cw[4] = {c.x, c.y, c.z, c.w};
-                uint32_t *dst = w_lds + tid * WROW;
-#pragma unroll
-                for (int k = 0; k < 4; k++) {
-                    uint32_t o[8];
-                    unpack_bits_dword(cw[k], 0u, false, o);
-                    *reinterpret_cast<uint4 *>(dst + 8 * k) = make_uint4(o[0], o[1], o[2], o[3]);
-                    *reinterpret_cast<uint4 *>(dst + 8 * k + 4) = make_uint4(o[4], o[5], o[6], o[7]);
-                }
-                dw_lds[tid] = half_bits_to_float(wsc[(int64_t)row * nrec + kk / 128]);
-            }
-        } else {
-            const int r = tid >> 1, bb = tid & 1;
-            if (2 * bb < kab) {
-                const int row = min(n0 + r, N - 1);
-                const uint4 c = *reinterpret_cast<const uint4 *>(W + ((int64_t)row * ns + kk / 64 + bb) * 16);
-                uint32_t *dst = w_lds + r * WROW + 16 * bb;
-                if (PLANAR) {
-                    // beat = {pos lo, pos hi, neg lo, neg hi}
-                    uint32_t o[8];
-                    unpack_bits_dword(c.x, c.z, true, o);
-                    *reinterpret_cast<uint4 *>(dst + 0) = make_uint4(o[0], o[1], o[2], o[3]);
-                    *reinterpret_cast<uint4 *>(dst + 4) = make_uint4(o[4], o[5], o[6], o[7]);
-                    unpack_bits_dword(c.y, c.w, true, o);
-                    *reinterpret_cast<uint4 *>(dst + 8) = make_uint4(o[0], o[1], o[2], o[3]);
-                    *reinterpret_cast<uint4 *>(dst + 12) = make_uint4(o[4], o[5], o[6], o[7]);
-                } else {
-                    const uint32_t cw[4] = {c.x, c.y, c.z, c.w};
-#pragma unroll
-                    for (int k = 0; k < 4; k++) {
-                        uint32_t o[4];
-                        unpack_q2_dword(cw[k], o);
-                        *reinterpret_cast<uint4 *>(dst + 4 * k) = make_uint4(o[0], o[1], o[2], o[3]);
-                    }
-                    dw_lds[bb * TN + r] = half_bits_to_float(wsc[(int64_t)row * ns + kk / 64 + bb]);
-                }
-            }
-        }
-        __syncthreads();
-
-        // --- this wave's 32 weight rows x 64 activation rows ---
-        float t[2][16];
-        for (int j = 0; j < kab; j++) {
-            const int kb = kk / QK8 + j; // activation block index along K
-            const uint4 a4 = *reinterpret_cast<const uint4 *>(w_lds + (32 * wave + l32) * WROW + 8 * j + 4 * h);
-            const v4i A = {(int)a4.x, (int)a4.y, (int)a4.z, (int)a4.w};
-#pragma unroll
-            for (int s = 0; s < 2; s++) {
-                const uint4 b4 = *reinterpret_cast<const uint4 *>(X + (int64_t)mrow[s] * K + kk + 32 * j + 16 * h);
-                const v4i B = {(int)b4.x, (int)b4.y, (int)b4.z, (int)b4.w};
-                if (PLANAR) {
-                    iacc[s] = __builtin_amdgcn_mfma_i32_32x32x32_i8(A, B, iacc[s], 0, 0, 0);
-                } else {
-                    const v16i D = __builtin_amdgcn_mfma_i32_32x32x32_i8(A, B, cbias, 0, 0, 0);
-                    const float dx = half_bits_to_float(reinterpret_cast<const uint16_t *>(Xscale)[(int64_t)mrow[s] * nab + kb]);
-                    const float c = -dx * BIASF; // exact: an 11-bit significand times 3 * 2^22
-                    const int jw = FMT == LB_Q1_0 ? j : (j & 1); // position inside the weight block
-#pragma unroll
-                    for (int i = 0; i < 16; i++) {
-                        const float v = fmaf(dx, __int_as_float(D[i]), c); // round(d_x * isum)
-                        t[s][i] = jw == 0 ? v : t[s][i] + v;
-                    }
-                    if (EMIT) {
-                        const int m = m0 + 32 * s + l32;
-#pragma unroll
-                        for (int i = 0; i < 16; i++) {
-                            const int n = n0 + 32 * wave + 8 * (i >> 2) + 4 * h + (i & 3);
-                            if (m < M && n < N)
-                                sums[((int64_t)m * N + n) * nab + kb] = D[i] - (int)BIAS;
-                        }
-                    }
-                    const bool block_end = FMT == LB_Q1_0 ? j == 3 : (j & 1) == 1;
-                    if (block_end) {
-                        const int b = FMT == LB_Q1_0 ? 0 : (j >> 1);
-#pragma unroll
-                        for (int g = 0; g < 4; g++) {
-                            const float4 dw = *reinterpret_cast<const float4 *>(dw_lds + b * TN + 32 * wave + 8 * g + 4 * h);
-                            const float dwv[4] = {dw.x, dw.y, dw.z, dw.w};
-#pragma unroll
-                            for (int q = 0; q < 4; q++)
-                                acc[s][4 * g + q] = fmaf(dwv[q], t[s][4 * g + q], acc[s][4 * g + q]);
-                        }
-                    }
-                }
-            }
-        }
+    for (int i = 0; i < 16; i++) {
+        acc[i] = 0.0f;
+        iacc[i] = 0;
     }
 
-    // --- store: lane holds rows n = 32 wave + 8 (i / 4) + 4 h + i % 4 of activation row m = 32 s + l32 ---
-    const float *sxp = reinterpret_cast<const float *>(Xscale);
+    // Each workgroup walks its K-steps starting at a different step (rotating with the weight tile), so
+    // at any moment the workgroups read different column ranges of the activation rows: with row strides
+    // that are large powers of two, all workgroups reading the same column range at once pile onto a few
+    // cache channels.  Integer block sums do not depend on the order; only the fp32 accumulation order
+    // of the weight blocks does.
+    const int nsteps = (K + KS - 1) / KS;
+    const int rot = blockIdx.x % nsteps;
+    auto step_k = [&](int s) { return ((s + rot) % nsteps) * KS; };
+
+    // register ring: the loads of step s + PF are issued while step s computes
+    constexpr int PF = 2;
+    StepRegs ring[PF];
 #pragma unroll
-    for (int s = 0; s < 2; s++) {
-        const int m = m0 + 32 * s + l32;
-        if (m >= M)
+    for (int p = 0; p < PF; p++)
+        if (p < nsteps)
+            load_step<FMT>(ring[p], W, wsc, N, K, X, xsc, M, n0, m0, step_k(p), tid);
+
+    int buf = 0;
+    for (int s = 0; s < nsteps; s++, buf ^= 1) {
+        const int kk = step_k(s);
+        const int kab = min(KS, K - kk) / QK8;
+        store_step<FMT>(lds, buf, ring[0], K, kk, tid);
+        __syncthreads();
+#pragma unroll
+        for (int p = 0; p + 1 < PF; p++)
+            ring[p] = ring[p + 1];
+        if (s + PF < nsteps)
+            load_step<FMT>(ring[PF - 1], W, wsc, N, K, X, xsc, M, n0, m0, step_k(s + PF), tid);
+        if (kab == KS / QK8)
+            step_compute<FMT, EMIT, KS / QK8>(lds, buf, h, l32, wn, wm, m0, n0, M, N, nab, kk, acc, iacc, cbias, sums);
+        else
+            step_compute<FMT, EMIT, KS / QK8 / 2>(lds, buf, h, l32, wn, wm, m0, n0, M, N, nab, kk, acc, iacc, cbias,
+                                                  sums);
+    }
+
+    // store: lane holds weight rows n = 32 wn + 8 (i / 4) + 4 h + i % 4 of activation row m = 32 wm + l32
+    const int m = m0 + 32 * wm + l32;
+    if (m >= M)
+        return;
+    const float sx = PLANAR ? reinterpret_cast<const float *>(Xscale)[m] : 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; i++) {
+        const int n = n0 + 32 * wn + 8 * (i >> 2) + 4 * h + (i & 3);
+        if (n >= N)
             continue;
-        const float sx = PLANAR ? sxp[m] : 0.0f;
-#pragma unroll
-        for (int i = 0; i < 16; i++) {
-            const int n = n0 + 32 * wave + 8 * (i >> 2) + 4 * h + (i & 3);
-            if (n >= N)
-                continue;
-            if (PLANAR) {
-                if (EMIT)
-                    sums[(int64_t)m * N + n] = iacc[s][i];
-                if (!EMIT || Y != nullptr) {
-                    const float ys = (float)iacc[s][i] * sx;
-                    Y[(int64_t)m * N + n] = ys * w_scale;
-                }
-            } else if (!EMIT || Y != nullptr) {
-                Y[(int64_t)m * N + n] = acc[s][i];
+        if (PLANAR) {
+            if (EMIT)
+                sums[(int64_t)m * N + n] = iacc[i];
+            if (!EMIT || Y != nullptr) {
+                const float ys = (float)iacc[i] * sx;
+                Y[(int64_t)m * N + n] = ys * w_scale;
             }
+        } else if (!EMIT || Y != nullptr) {
+            Y[(int64_t)m * N + n] = acc[i];
         }
     }
 }
@@ -255,7 +344,7 @@ hipError_t launch_fmt(const uint8_t *W, int64_t N, int64_t K, float w_scale, con
                       int64_t M, float *Y, int32_t *sums, hipStream_t s)
 {
     const dim3 grid((unsigned)((N + TN - 1) / TN), (unsigned)((M + TM - 1) / TM));
-    hipLaunchKernelGGL((gemm_kernel<FMT, EMIT>), grid, dim3(WG), 0, s, W, (int)N, (int)K, w_scale, Xq, Xscale, (int)M,
+    hipLaunchKernelGGL((gemm_kernel<FMT, EMIT>), grid, dim3(GT), 0, s, W, (int)N, (int)K, w_scale, Xq, Xscale, (int)M,
                        Y, sums);
     return hipGetLastError();
 }
