@@ -90,7 +90,7 @@ class DecodeToken:
                 y = torch.empty(N, dtype=torch.float32, device="cuda")
                 xq = self.xq[Kx][r]
                 xs = self.xs[Kx][r] if not planar else self.xs[Kx][r:r + 1]
-                self.products.append(dict(layer=l, name=n, N=N, K=K, W=packed, y=y, xq=xq, xs=xs, w_scale=w_scale,
+                self.products.append(dict(layer=l, j=j, name=n, N=N, K=K, W=packed, y=y, xq=xq, xs=xs, w_scale=w_scale,
                                           feed=(Kx, r)))
                 descs.append(L.desc(fmt, packed, N, K, xq, xs, y, w_tensor_scale=w_scale))
                 self.weight_bytes += L.lowbit_weight_bytes(fmt, N, K)

@@ -101,7 +101,7 @@ lb_status lowbit_quantize_act(int afmt, const float *x, int64_t M, int64_t K, in
  *   afmt:   LB_ACT_Q8_0 for the ggml formats, LB_ACT_I8_ROW for planar.
  *   xq:     device int8 [K], 16-byte aligned.  xscale: binary16 [K/32] or one fp32, 4-byte aligned.
  *   y:      device fp32 [N], 4-byte aligned.
- * Limits: K <= 65536; the weight tensor must be smaller than 4 GiB.
+ * Limits: K <= 32768 and N <= 2^31 - 1; the weight tensor must be smaller than 4 GiB.
  */
 lb_status lowbit_matvec(int fmt, const void *W, int64_t N, int64_t K, float w_tensor_scale, int afmt,
                         const int8_t *xq, const void *xscale, float *y, hipStream_t s);
@@ -131,7 +131,8 @@ lb_status lowbit_block_sums(int fmt, const void *W, int64_t N, int64_t K, int af
  * Dense bf16 head matvec y[N] = sum_k bf16_to_f32(W[n][k]) * x[k], accumulated in fp32
  * (tritium "Architecture", section 3: the dense head is the largest single stream; bf16 storage).
  *   W: device uint16 bf16 bits [N][K], 16-byte aligned, K % 8 == 0; x: device fp32 [K], 16-byte aligned;
- *   y: device fp32 [N].  K <= 16384.
+ *   y: device fp32 [N].  K must be a multiple of 8 and at most 4096 (the activation vector is held in
+ *   registers); otherwise LB_ESHAPE.
  */
 lb_status dense_head_matvec(const uint16_t *W, int64_t N, int64_t K, const float *x, float *y, hipStream_t s);
 

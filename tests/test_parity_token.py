@@ -1,0 +1,70 @@
+"""GPU parity at full size, in the launch configuration bench.py times: one whole decode token (the
+batched plan over every product of every layer, plus the token's activation quantisation), checked
+against the CPU oracle on the same bytes -- every quantised activation byte, and a seeded sample of
+output rows of every product."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from bench import DecodeToken
+from gpu_util import say
+
+pytestmark = pytest.mark.gpu
+
+
+def _run_token(fmt, layer, layers, seed):
+    tok = DecodeToken(fmt, layer, layers, seed=seed, keep_blocks_layers=layers)
+    tok.quantize()
+    tok.products_launch()
+    torch.cuda.synchronize()
+    return tok
+
+
+def _check_token(tok, rows_per_product=6, seed=0):
+    g = synth.rng(seed)
+    planar = tok.fmt == synth.TERNARY_PLANAR
+    # every activation row of the token, byte for byte
+    refs = {}
+    for K, x in tok.x.items():
+        xh = x.cpu().numpy()
+        q_ref, s_ref = oracle.quantize_i8_row(xh) if planar else oracle.quantize_q8_0(xh)
+        assert np.array_equal(tok.xq[K].cpu().numpy(), q_ref), f"quantised activations (K={K}) differ"
+        assert np.array_equal(tok.xs[K].cpu().numpy(), s_ref), f"activation scales (K={K}) differ"
+        refs[K] = (q_ref, s_ref)
+    worst = 0.0
+    for j, p in enumerate(tok.products):
+        N, K = p["N"], p["K"]
+        rows = np.unique(np.concatenate([g.integers(0, N, rows_per_product), [0, N - 1]]))
+        raw = tok.blocks[(p["layer"], p["j"])]
+        raw_rows = raw[torch.from_numpy(rows).to(raw.device)].cpu().numpy()  # only the sampled rows
+        Kx, r = p["feed"]
+        q_ref, s_ref = refs[Kx]
+        y = p["y"][torch.from_numpy(rows).to(p["y"].device)].cpu().numpy()
+        n = len(rows)
+        if planar:
+            _, y_ref = oracle.matvec_planar(raw_rows, n, K, q_ref[r], s_ref[r], p["w_scale"])
+            assert np.array_equal(y, y_ref), f"planar product {j} differs"
+        else:
+            y_ref, A = oracle.matvec_q(tok.fmt, raw_rows, n, K, q_ref[r], s_ref[r])
+            ok, ratio, _ = oracle.tolerance_ok(y, y_ref, A, K // 32)
+            worst = max(worst, ratio)
+            assert ok, f"product {j} ({p['name']} layer {p['layer']}) outside tolerance (ratio {ratio})"
+    say(f"  {len(tok.products)} products checked, worst err/allowance {worst:.3g}")
+    assert len(tok.products) == 7 * tok.layers
+
+
+@pytest.mark.parametrize("fmt", [synth.Q2_0_G64, synth.Q1_0], ids=["Q2_0_g64", "Q1_0"])
+def test_qwen3_8b_token_full_size(fmt):
+    say(f"case full token fmt={fmt}")
+    tok = _run_token(fmt, synth.QWEN3_8B_LAYER, synth.QWEN3_8B_LAYERS, seed=7000 + fmt)
+    _check_token(tok, seed=7100 + fmt)
+    tok.batch.close()
+
+
+def test_bitnet_planar_token_full_size():
+    say("case full planar token")
+    tok = _run_token(synth.TERNARY_PLANAR, synth.BITNET_2B_LAYER, synth.BITNET_2B_LAYERS, seed=7300)
+    _check_token(tok, seed=7301)
+    tok.batch.close()
