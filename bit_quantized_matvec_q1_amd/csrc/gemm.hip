@@ -71,21 +71,33 @@ __device__ __forceinline__ void unpack_q2_dword(uint32_t v, uint32_t *out)
     transpose4(e[0], e[1], e[2], e[3], out);
 }
 
-// Q1_0 / planar: 32 sign bits (or plane bits) -> 8 dwords of int8 weights in order, via a byte table
-// indexed by the 0/1 (Q1_0) or pos | neg << 1 (planar) selector of each weight.
-__device__ __forceinline__ void unpack_bits_dword(uint32_t sel_lo_bits, uint32_t sel_hi_bits, bool planar,
-                                                  uint32_t *out)
+// Q1_0: one device sign dword m of a record (the sign of weight 32r + 8m + k at bit 4k + r) -> for each
+// activation block r, the 8 int8 weights 32r + 8m .. 32r + 8m + 7 as two dwords out[2r], out[2r + 1].
+// A byte table maps each 0/1 selector to -1/+1; byte t of e[s] is then the weight of bit 8t + s, i.e.
+// k = 2t + (s >> 2) of block r = s & 3, and one byte interleave per half puts k in order.
+__device__ __forceinline__ void unpack_q1_dword(uint32_t v, uint32_t *out)
 {
-    const uint32_t lut = planar ? 0x00FF0100u /* 00 -> 0, 01 -> +1, 10 -> -1, 11 -> 0 */
-                                : 0x000001FFu /* 0 -> -1, 1 -> +1 */;
+    const uint32_t lut = 0x000001FFu; // 0 -> -1, 1 -> +1
     uint32_t e[8];
 #pragma unroll
-    for (int r = 0; r < 8; r++) {
-        uint32_t s = (sel_lo_bits >> r) & 0x01010101u;
-        if (planar)
-            s |= ((sel_hi_bits >> r) & 0x01010101u) << 1;
-        e[r] = perm(0u, lut, s);
+    for (int s = 0; s < 8; s++)
+        e[s] = perm(0u, lut, (v >> s) & 0x01010101u);
+#pragma unroll
+    for (int r = 0; r < 4; r++) {
+        out[2 * r] = perm(e[r + 4], e[r], 0x05010400u);     // k = 0, 1, 2, 3
+        out[2 * r + 1] = perm(e[r + 4], e[r], 0x07030602u); // k = 4, 5, 6, 7
     }
+}
+
+// Planar: 32 plane bits -> 8 dwords of int8 weights in order, via a byte table indexed by the
+// pos | neg << 1 selector of each weight.
+__device__ __forceinline__ void unpack_planar_dword(uint32_t pos_bits, uint32_t neg_bits, uint32_t *out)
+{
+    const uint32_t lut = 0x00FF0100u; // 00 -> 0, 01 -> +1, 10 -> -1, 11 -> 0
+    uint32_t e[8];
+#pragma unroll
+    for (int r = 0; r < 8; r++)
+        e[r] = perm(0u, lut, ((pos_bits >> r) & 0x01010101u) | (((neg_bits >> r) & 0x01010101u) << 1));
     uint32_t t0[4], t1[4];
     transpose4(e[0], e[1], e[2], e[3], t0);
     transpose4(e[4], e[5], e[6], e[7], t1);
@@ -113,7 +125,7 @@ __device__ __forceinline__ void load_step(StepRegs &r, const uint8_t *__restrict
     const int kab = min(KS, K - kk) / QK8; // activation blocks in this step
     const int row = min(n0 + (tid >> 2), N - 1), p = tid & 3;
     if (FMT == LB_Q1_0) {
-        // one 128-weight record per row; thread p takes its sign dword p
+        // one 128-weight record per row; thread p takes its device sign dword p
         const int64_t idx = (int64_t)row * (K / 128) + kk / 128;
         r.wcode.x = *reinterpret_cast<const uint32_t *>(W + idx * 16 + 4 * p);
         if (p == 0)
@@ -163,10 +175,12 @@ __device__ __forceinline__ void store_step(Lds &lds, int buf, const StepRegs &r,
     const int rr = tid >> 2, p = tid & 3;
     uint32_t *wrow = lds.w[buf] + rr * WROW;
     if (FMT == LB_Q1_0) {
+        // sign dword p of the record holds 8 weights of each of the step's 4 activation blocks
         uint32_t o[8];
-        unpack_bits_dword(r.wcode.x, 0u, false, o);
-        *reinterpret_cast<uint4 *>(wrow + 8 * p) = make_uint4(o[0], o[1], o[2], o[3]);
-        *reinterpret_cast<uint4 *>(wrow + 8 * p + 4) = make_uint4(o[4], o[5], o[6], o[7]);
+        unpack_q1_dword(r.wcode.x, o);
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+            *reinterpret_cast<uint2 *>(wrow + 8 * j + 2 * p) = make_uint2(o[2 * j], o[2 * j + 1]);
         if (p == 0)
             lds.dw[buf][rr] = half_bits_to_float((uint16_t)r.wscale);
     } else {
@@ -175,7 +189,7 @@ __device__ __forceinline__ void store_step(Lds &lds, int buf, const StepRegs &r,
             uint32_t *dst = wrow + 16 * bb + 8 * hh;
             uint32_t o[8];
             if (FMT == LB_TERNARY_PLANAR) {
-                unpack_bits_dword(r.wcode.x, r.wcode.y, true, o);
+                unpack_planar_dword(r.wcode.x, r.wcode.y, o);
             } else {
                 unpack_q2_dword(r.wcode.x, o);
                 unpack_q2_dword(r.wcode.y, o + 4);

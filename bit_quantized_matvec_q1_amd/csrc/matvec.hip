@@ -15,9 +15,11 @@
 //    a dword in the order in which a shift-and-mask of a code word lays the weights out.
 //  * A row is split over L lanes; a lane owns S slices (strided by L so each wave-wide 16-byte load is
 //    contiguous) and keeps their staged activations in VGPRs across all the rows it streams.
-//  * Per code dword, one mask (and at most one shift) isolates 8 codes or 8 sign bits as nibbles, and
-//    one v_dot8_i32_i4 against the h nibbles plus one v_dot8_u32_u4 against the l nibbles accumulate
-//    sum(code * q) = 16 * sum(code * h) + sum(code * l).  The offset forms of the pages give the exact
+//  * Per code dword, one mask (Q2_0: and at most one shift) isolates 8 codes or 8 sign bits as nibbles,
+//    and one v_dot8_i32_i4 against the h nibbles plus one v_dot8_u32_u4 against the l nibbles accumulate
+//    sum(code * q) = 16 * sum(code * h) + sum(code * l).  A masked bit that stays in place has nibble
+//    value 2^r; that power of two is carried by the block scale (Q1_0, whose device records group each
+//    activation block under one mask position) or recombined once per row (planar).  The offset forms of the pages give the exact
 //    block sums: Q2_0  isum = sum(c q) - sum(q)  (code c = w + 1);  Q1_0  isum = 2 sum_{bit=1} q - sum(q);
 //    planar  acc = sum_pos q - sum_neg q.
 //  * Block scaling is one fp32 multiply-add per activation block and one per weight block (bankml
@@ -30,7 +32,8 @@ namespace lb {
 
 template <int FMT> struct F;
 // SW: weights per slice; NAB: q8_0 blocks per slice; REC: dwords of staged activation per slice
-// (SW/4 nibble words, then, for the ggml formats, d_x[NAB] (2 d_x for Q1_0) and -sum(q)[NAB])
+// (SW/4 nibble words, then, for the ggml formats, d_x[NAB] (2 d_x / 2^j for Q1_0 block j) and
+// -sum(q)[NAB])
 template <> struct F<LB_Q2_0_G64> { enum { SW = 64, NAB = 2, REC = 20 }; };
 template <> struct F<LB_Q1_0> { enum { SW = 128, NAB = 4, REC = 40 }; };
 template <> struct F<LB_TERNARY_PLANAR> { enum { SW = 64, NAB = 0, REC = 16 }; };
@@ -43,8 +46,9 @@ constexpr int CODE_BYTES = 16; // every slice is one 16-byte record
 // a-th mask extraction isolates:
 //   Q2_0  a = 2k + s   (code dword k = weights 16k..16k+15; s = 0: mask 0x33333333, s = 1: shift 2
 //                       first):  e = 16k + 2n + s
-//   Q1_0 / planar  a = 4k + r  (32-bit word k of signs / plane bits; r = the bit within each nibble):
-//                       e = 32k + 4n + r
+//   Q1_0  a = 4m + r   (device sign dword m, mask 0x11111111 << r; the device record puts the sign of
+//                       weight 32r + 8m + n at bit 4n + r of dword m):  e = 32r + 8m + n
+//   planar  a = 4k + r  (32-bit word k of plane bits; r = the bit within each nibble):  e = 32k + 4n + r
 // ------------------------------------------------------------------------------------------------
 template <int FMT>
 __device__ __forceinline__ void stage_slice(const int8_t *__restrict__ xq, const void *__restrict__ xscale, int sl,
@@ -67,7 +71,9 @@ __device__ __forceinline__ void stage_slice(const int8_t *__restrict__ xq, const
         uint32_t lo = 0, hi = 0;
 #pragma unroll
         for (int n = 0; n < 8; n++) {
-            const int e = FMT == LB_Q2_0_G64 ? 16 * (a >> 1) + 2 * n + (a & 1) : 32 * (a >> 2) + 4 * n + (a & 3);
+            const int e = FMT == LB_Q2_0_G64 ? 16 * (a >> 1) + 2 * n + (a & 1)
+                          : FMT == LB_Q1_0   ? 32 * (a & 3) + 8 * (a >> 2) + n
+                                             : 32 * (a >> 2) + 4 * n + (a & 3);
             const uint32_t v = LB_BYTE(e);
             lo |= (v & 15u) << (4 * n);
             hi |= (v >> 4) << (4 * n);
@@ -79,9 +85,11 @@ __device__ __forceinline__ void stage_slice(const int8_t *__restrict__ xq, const
         const uint16_t *xs = reinterpret_cast<const uint16_t *>(xscale);
 #pragma unroll
         for (int j = 0; j < NAB; j++) {
-            // Q1_0 keeps 2 d_x (exact): its sums are formed as 2 * S - sum(q), S = sum of q where the bit is 1
+            // Q1_0 keeps 2 d_x / 2^j (exact): its block sums are 2 S - sum(q), S = the sum of q where the
+            // bit is 1, and its products deliver 2^j S (the nibble value of mask position j)
             const float dx = half_bits_to_float(xs[NAB * sl + j]);
-            rec[SW / 4 + j] = __float_as_uint(FMT == LB_Q1_0 ? 2.0f * dx : dx);
+            const float q1f = j == 0 ? 2.0f : j == 1 ? 1.0f : j == 2 ? 0.5f : 0.25f;
+            rec[SW / 4 + j] = __float_as_uint(FMT == LB_Q1_0 ? q1f * dx : dx);
             int sq = 0;
 #pragma unroll
             for (int i = 0; i < 32; i++)
@@ -126,21 +134,22 @@ __device__ __forceinline__ void q2_isums(uint4 c, const uint32_t *A, int &i0, in
     i1 = h[1] * 16 + l[1];
 }
 
-// Q1_0: 4 sign dwords, 32 bits each (one q8_0 block each); bit r of nibble n is weight 4n + r.
-// Returns S[k] = sum of q over the weights whose bit is 1; the block sum is 2 S[k] - sum(q).
-__device__ __forceinline__ void q1_sel_sums(uint4 b, const uint32_t *A, int (&S)[4])
+// Q1_0: 4 device sign dwords; mask 0x11111111 << r of each holds 8 weights of q8_0 block r at nibble
+// value 2^r (read as -8 by the signed product when r = 3).  Returns C[r] = 2^r S_r, S_r = the sum of q
+// over the weights of block r whose bit is 1; the block sum is 2 S_r - sum(q).
+__device__ __forceinline__ void q1_group_sums(uint4 b, const uint32_t *A, int (&C)[4])
 {
     const uint32_t bw[4] = {b.x, b.y, b.z, b.w};
 #pragma unroll
-    for (int k = 0; k < 4; k++) {
+    for (int r = 0; r < 4; r++) {
         int h = 0, l = 0;
 #pragma unroll
-        for (int r = 0; r < 4; r++) {
-            const uint32_t e = (bw[k] >> r) & 0x11111111u;
-            h = sdot8(e, A[(4 * k + r) * 2 + 1], h);
-            l = udot8(e, A[(4 * k + r) * 2 + 0], l);
+        for (int m = 0; m < 4; m++) {
+            const uint32_t e = bw[m] & (0x11111111u << r);
+            h = sdot8(e, A[(4 * m + r) * 2 + 1], h);
+            l = udot8(e, A[(4 * m + r) * 2 + 0], l);
         }
-        S[k] = h * 16 + l;
+        C[r] = r < 3 ? h * 16 + l : l - h * 16;
     }
 }
 
@@ -222,38 +231,44 @@ template <int L> __device__ __forceinline__ float group_sum_f(float v)
 //
 // Loads are unconditional: a lane past the tile's last row re-reads that row and a lane past the row's
 // last slice re-reads that slice (its staged activations are zero, so it adds nothing and its result
-// is never stored).  Offsets are 32-bit from the tensor's base (the ABI keeps tensors under 4 GiB).
-// The next rows' loads are issued before the current rows are computed (ping-pong registers), and the
-// first rows' loads before the activation is staged, so the weight stream never waits on the staging.
+// is never stored).  Offsets are 32-bit byte offsets from the tensor's base (the ABI keeps tensors
+// under 4 GiB), advanced by one add per row and clamped by one min to the tile's last row, so every
+// load stays inside the tensor.  A ring of NB register buffers keeps NB - 1 rows' loads in flight
+// while a row is computed, and the first rows are requested before the activation is staged, so the
+// weight stream never waits on the staging.
 // ------------------------------------------------------------------------------------------------
-// Rows in flight per register buffer (two buffers ping-pong).
-template <int FMT> constexpr int rows_in_flight() { return 1; }
-
 template <int FMT, int S> struct RowRegs {
-    uint4 code[rows_in_flight<FMT>()][S];
-    uint32_t sc[rows_in_flight<FMT>()][S];
+    uint4 code[S];
+    uint32_t sc[S];
 };
 
-typedef unsigned v4u __attribute__((ext_vector_type(4)));
+// Register buffers in the ring (rows in flight + 1).
+constexpr int kRing = 2;
 
-// The code records are read exactly once: non-temporal loads keep the stream from displacing the
-// activations, tables and scales in the caches.
-template <int FMT, int L, int S>
-__device__ __forceinline__ void issue_rows(RowRegs<FMT, S> &r, const uint8_t *__restrict__ W,
-                                           const uint16_t *__restrict__ scales, const uint32_t (&row)[rows_in_flight<FMT>()],
-                                           int ns, int li)
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
+// Tensors are in device global memory: loads through global-address-space pointers take a scalar base
+// and a 32-bit per-lane offset (no 64-bit address arithmetic, no flat-address checks).
+typedef __attribute__((address_space(1))) const v4u gv4u;
+typedef __attribute__((address_space(1))) const uint16_t gu16;
+typedef __attribute__((address_space(1))) const uint8_t gu8;
+typedef __attribute__((address_space(1))) float gf32;
+
+// One row's S slices.  off: byte offset of the row's first record; slo[i] / sls[i]: byte offset of
+// this lane's i-th record / its scale within a row.  The code records are read exactly once:
+// non-temporal loads keep the stream from displacing the activations and scales in the caches.
+template <int FMT, int S>
+__device__ __forceinline__ void issue_row(RowRegs<FMT, S> &r, const uint8_t *__restrict__ W,
+                                          const uint8_t *__restrict__ scales, uint32_t off, const uint32_t (&slo)[S],
+                                          const uint32_t (&sls)[S])
 {
+    const uint32_t soff = off >> 3; // record idx at byte 16 idx, its binary16 scale at byte 2 idx
 #pragma unroll
-    for (int u = 0; u < rows_in_flight<FMT>(); u++)
-#pragma unroll
-        for (int i = 0; i < S; i++) {
-            const uint32_t sl = (uint32_t)min(li + i * L, ns - 1);
-            const uint32_t idx = row[u] * (uint32_t)ns + sl;
-            const v4u t = __builtin_nontemporal_load(reinterpret_cast<const v4u *>(W + idx * CODE_BYTES));
-            r.code[u][i] = make_uint4(t.x, t.y, t.z, t.w);
-            if (FMT != LB_TERNARY_PLANAR)
-                r.sc[u][i] = scales[idx]; // small, shared by neighbouring lanes: left cacheable
-        }
+    for (int i = 0; i < S; i++) {
+        const v4u t = __builtin_nontemporal_load((gv4u *)((gu8 *)W + (off + slo[i])));
+        r.code[i] = make_uint4(t.x, t.y, t.z, t.w);
+        if (FMT != LB_TERNARY_PLANAR) // small, shared by neighbouring lanes: left cacheable
+            r.sc[i] = *(gu16 *)((gu8 *)scales + (soff + sls[i]));
+    }
 }
 
 template <int FMT, int L, int S, bool EMIT>
@@ -292,14 +307,15 @@ __device__ __forceinline__ void compute_row(const uint4 (&code)[S], const uint32
                 t = fmaf(__uint_as_float(act[i][DX + 1]), (float)is[1], __uint_as_float(act[i][DX]) * (float)is[0]);
             } else {
                 // t = sum_j d_x[j] (2 S_j - sum q_j): the -sum_j d_x[j] sum q_j part is the slice constant
-                // cfold (computed once per lane), then one multiply-add by 2 d_x[j] per q8_0 block
-                int Ssel[4];
-                q1_sel_sums(code[i], act[i], Ssel);
+                // cfold (computed once per lane), then one multiply-add per q8_0 block of (2 d_x[j] / 2^j)
+                // by 2^j S_j -- the same exact product 2 d_x[j] S_j
+                int C[4];
+                q1_group_sums(code[i], act[i], C);
                 t = cfold[i];
 #pragma unroll
                 for (int j = 0; j < 4; j++) {
-                    t = fmaf(__uint_as_float(act[i][DX + j]), (float)Ssel[j], t);
-                    is[j] = 2 * Ssel[j] + (int)act[i][DX + NAB + j];
+                    t = fmaf(__uint_as_float(act[i][DX + j]), (float)C[j], t);
+                    is[j] = ((C[j] * 2) >> j) + (int)act[i][DX + NAB + j];
                 }
             }
             const float c = fmaf(half_bits_to_float((uint16_t)sc[i]), t, part);
@@ -313,7 +329,7 @@ __device__ __forceinline__ void compute_row(const uint4 (&code)[S], const uint32
         }
         part = group_sum_f<L>(part);
         if (valid && li == L - 1 && (!EMIT || y != nullptr))
-            y[row] = part;
+            *(gf32 *)((gu8 *)y + (uint32_t)row * 4u) = part;
     }
 }
 
@@ -324,27 +340,34 @@ __device__ __forceinline__ void matvec_tile(const uint8_t *__restrict__ W, int N
                                             uint32_t *__restrict__ lds)
 {
     constexpr int REC = F<FMT>::REC;
-    constexpr int GROUPS = 64 / L;              // rows per wave per iteration
-    constexpr int ROWS_IT = GROUPS * (WG / 64); // rows per workgroup per iteration
-    const int ns = K / F<FMT>::SW;              // slices per row
+    constexpr int GROUPS = 64 / L;           // rows per wave per iteration
+    constexpr int STEP = GROUPS * (WG / 64); // rows per workgroup per iteration
+    constexpr int NB = kRing;
+    const int ns = K / F<FMT>::SW; // slices per row
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int g = lane / L, li = lane % L;
-    const uint16_t *scales = reinterpret_cast<const uint16_t *>(W + (int64_t)N * ns * CODE_BYTES);
+    const uint8_t *scales = W + (int64_t)N * ns * CODE_BYTES;
     const int rbase = wave * GROUPS + g; // this lane's row within an iteration
 
-    constexpr int U = rows_in_flight<FMT>();
-    constexpr int STEP = U * ROWS_IT; // rows per workgroup per register buffer
-    auto rows_at = [&](int it, uint32_t (&rows)[U]) {
+    const uint32_t rowbytes = (uint32_t)ns * CODE_BYTES;
+    const uint32_t stepb = (uint32_t)STEP * rowbytes;
+    const uint32_t last = (uint32_t)(row0 + nrows - 1) * rowbytes; // the tile's last row
+    uint32_t slo[S], sls[S];
 #pragma unroll
-        for (int u = 0; u < U; u++)
-            rows[u] = (uint32_t)(row0 + min(it + u * ROWS_IT + rbase, nrows - 1));
-    };
+    for (int i = 0; i < S; i++) {
+        slo[i] = (uint32_t)min(li + i * L, ns - 1) * CODE_BYTES;
+        sls[i] = slo[i] >> 3;
+    }
+    // Offset of the row this lane requests next, before clamping.  Past the tile's end it may grow
+    // (or wrap) freely: min(., last) keeps every load in bounds, and such rows are never stored.
+    uint32_t onext = (uint32_t)(row0 + min(rbase, nrows - 1)) * rowbytes;
 
-    RowRegs<FMT, S> ra, rb;
-    {
-        uint32_t rows[U];
-        rows_at(0, rows);
-        issue_rows<FMT, L, S>(ra, W, scales, rows, ns, li);
+    RowRegs<FMT, S> buf[NB];
+#pragma unroll
+    for (int b = 0; b < NB - 1; b++) {
+        if (b * STEP < nrows) // uniform
+            issue_row<FMT, S>(buf[b], W, scales, min(onext, last), slo, sls);
+        onext += stepb;
     }
 
     for (int sl = threadIdx.x; sl < ns; sl += WG)
@@ -372,42 +395,33 @@ __device__ __forceinline__ void matvec_tile(const uint8_t *__restrict__ W, int N
         }
     }
     const float sx = FMT == LB_TERNARY_PLANAR ? *reinterpret_cast<const float *>(xscale) : 0.0f;
-    float cfold[S]; // Q1_0: -sum_j d_x[j] sum(q_j) of each slice (the staged words hold 2 d_x[j] and -sum(q_j))
+    float cfold[S]; // Q1_0: -sum_j d_x[j] sum(q_j) of each slice (the staged words hold 2 d_x[j] / 2^j, -sum(q_j))
 #pragma unroll
     for (int i = 0; i < S; i++) {
         float c = 0.0f;
         if (FMT == LB_Q1_0) {
 #pragma unroll
-            for (int j = 0; j < 4; j++)
-                c = fmaf(0.5f * __uint_as_float(act[i][32 + j]), (float)(int)act[i][36 + j], c);
+            for (int j = 0; j < 4; j++) {
+                const float back = j == 0 ? 0.5f : j == 1 ? 1.0f : j == 2 ? 2.0f : 4.0f; // exact
+                c = fmaf(back * __uint_as_float(act[i][32 + j]), (float)(int)act[i][36 + j], c);
+            }
         }
         cfold[i] = c;
     }
-    auto compute = [&](const RowRegs<FMT, S> &r, int it) {
-#pragma unroll
-        for (int u = 0; u < U; u++) {
-            const int rl = it + u * ROWS_IT + rbase;
-            compute_row<FMT, L, S, EMIT>(r.code[u], r.sc[u], act, cfold, ns, li, rl < nrows, row0 + rl, w_scale, sx, y,
-                                         sums);
-        }
-    };
 
-    for (int it = 0; it < nrows; it += 2 * STEP) {
-        const bool more1 = it + STEP < nrows; // uniform across the workgroup
-        if (more1) {
-            uint32_t rows[U];
-            rows_at(it + STEP, rows);
-            issue_rows<FMT, L, S>(rb, W, scales, rows, ns, li);
+    for (int it = 0; it < nrows; it += NB * STEP) {
+#pragma unroll
+        for (int b = 0; b < NB; b++) {
+            const int cur = it + b * STEP;
+            if (cur >= nrows) // uniform
+                break;
+            if (cur + (NB - 1) * STEP < nrows) // uniform
+                issue_row<FMT, S>(buf[(b + NB - 1) % NB], W, scales, min(onext, last), slo, sls);
+            onext += stepb;
+            const int rl = cur + rbase;
+            compute_row<FMT, L, S, EMIT>(buf[b].code, buf[b].sc, act, cfold, ns, li, rl < nrows, row0 + rl, w_scale,
+                                         sx, y, sums);
         }
-        compute(ra, it);
-        if (!more1)
-            break;
-        if (it + 2 * STEP < nrows) {
-            uint32_t rows[U];
-            rows_at(it + 2 * STEP, rows);
-            issue_rows<FMT, L, S>(ra, W, scales, rows, ns, li);
-        }
-        compute(rb, it + STEP);
     }
 }
 

@@ -92,6 +92,47 @@ hipError_t launch_quantize_i8_row(const float *x, int64_t M, int64_t K, int8_t *
 // ggml blocks [N][nb][2 + 16] <-> device layout [N][nb][16] code records, then [N][nb] binary16 scales.
 // Planar beats are copied unchanged.  One thread per block; byte accesses (the ggml stream has 18-byte
 // records, so nothing in it is aligned).
+// Q1_0 sign bits in the device layout.  In a ggml block, dword r (bytes 4r..4r+3) holds the signs of
+// weights 32r..32r+31, weight 32r + 8m + k at bit 8m + k.  The device record moves that bit to bit 4k + r
+// of dword m, so that masking any device dword with 0x11111111 << r isolates eight weights of q8_0
+// activation block r, one per nibble, already in place for a nibble dot product.
+__device__ __forceinline__ uint32_t spread8_nibbles(uint32_t x) // bit k of an 8-bit value -> bit 4k
+{
+    x = (x | (x << 12)) & 0x000F000Fu;
+    x = (x | (x << 6)) & 0x03030303u;
+    x = (x | (x << 3)) & 0x11111111u;
+    return x;
+}
+
+__device__ __forceinline__ uint32_t gather8_nibbles(uint32_t x) // bit 4k -> bit k (other bits zero)
+{
+    x &= 0x11111111u;
+    x = (x | (x >> 3)) & 0x03030303u;
+    x = (x | (x >> 6)) & 0x000F000Fu;
+    x = (x | (x >> 12)) & 0x000000FFu;
+    return x;
+}
+
+__device__ __forceinline__ void q1_to_device(const uint32_t (&nat)[4], uint32_t (&dev)[4])
+{
+    for (int m = 0; m < 4; m++) {
+        uint32_t v = 0;
+        for (int r = 0; r < 4; r++)
+            v |= spread8_nibbles((nat[r] >> (8 * m)) & 0xFFu) << r;
+        dev[m] = v;
+    }
+}
+
+__device__ __forceinline__ void q1_from_device(const uint32_t (&dev)[4], uint32_t (&nat)[4])
+{
+    for (int r = 0; r < 4; r++) {
+        uint32_t v = 0;
+        for (int m = 0; m < 4; m++)
+            v |= gather8_nibbles(dev[m] >> r) << (8 * m);
+        nat[r] = v;
+    }
+}
+
 __global__ __launch_bounds__(WG) void pack_kernel(int fmt, const uint8_t *__restrict__ src, int64_t nblk,
                                                   uint8_t *__restrict__ dst, int unpack)
 {
@@ -103,19 +144,32 @@ __global__ __launch_bounds__(WG) void pack_kernel(int fmt, const uint8_t *__rest
             dst[b * 16 + i] = src[b * 16 + i];
         return;
     }
-    uint8_t *codes = unpack ? nullptr : dst;
-    if (!unpack) {
-        const uint8_t *blk = src + b * 18;
-        for (int i = 0; i < 16; i++)
-            codes[b * 16 + i] = blk[2 + i];
-        dst[nblk * 16 + b * 2 + 0] = blk[0];
-        dst[nblk * 16 + b * 2 + 1] = blk[1];
+    // 16 code bytes of an 18-byte ggml block <-> one 16-byte device record (+ the binary16 scale in the
+    // scale array); Q1_0 records also permute their bits (above), Q2_0_g64 records keep them as they are
+    const uint8_t *in = unpack ? src + b * 16 : src + b * 18 + 2;
+    uint8_t *out = unpack ? dst + b * 18 + 2 : dst + b * 16;
+    uint32_t w[4], o[4];
+    for (int d = 0; d < 4; d++)
+        w[d] = (uint32_t)in[4 * d] | ((uint32_t)in[4 * d + 1] << 8) | ((uint32_t)in[4 * d + 2] << 16) |
+               ((uint32_t)in[4 * d + 3] << 24);
+    if (fmt == LB_Q1_0) {
+        if (unpack)
+            q1_from_device(w, o);
+        else
+            q1_to_device(w, o);
     } else {
-        uint8_t *blk = dst + b * 18;
-        for (int i = 0; i < 16; i++)
-            blk[2 + i] = src[b * 16 + i];
-        blk[0] = src[nblk * 16 + b * 2 + 0];
-        blk[1] = src[nblk * 16 + b * 2 + 1];
+        for (int d = 0; d < 4; d++)
+            o[d] = w[d];
+    }
+    for (int d = 0; d < 4; d++)
+        for (int i = 0; i < 4; i++)
+            out[4 * d + i] = (uint8_t)(o[d] >> (8 * i));
+    if (!unpack) {
+        dst[nblk * 16 + b * 2 + 0] = src[b * 18 + 0];
+        dst[nblk * 16 + b * 2 + 1] = src[b * 18 + 1];
+    } else {
+        dst[b * 18 + 0] = src[nblk * 16 + b * 2 + 0];
+        dst[b * 18 + 1] = src[nblk * 16 + b * 2 + 1];
     }
 }
 

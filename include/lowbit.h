@@ -73,6 +73,10 @@ int64_t lowbit_weight_bytes(int fmt, int64_t N, int64_t K);
  *   blocks: device, N rows x K/QK blocks of 18 bytes, row-major, no alignment requirement.
  *   packed: device, lowbit_weight_bytes(fmt, N, K) bytes, 16-byte aligned.  Layout: all 16-byte code
  *           records row-major ([N][K/QK][16]), then all binary16 scales row-major ([N][K/QK]).
+ *           A Q2_0_g64 record is the block's 16 code bytes as they are.  A Q1_0 record permutes the
+ *           block's 128 sign bits: the sign of weight 32r + 8m + k (r, m in 0..3, k in 0..7), at bit
+ *           8m + k of little-endian dword r in the ggml block, sits at bit 4k + r of dword m, so one
+ *           mask (0x11111111 << r) isolates eight weights of activation block r as nibbles.
  * Lossless (lowbit_unpack_weights is its inverse).  For LB_TERNARY_PLANAR the beat stream already is
  * the device layout (tritium "Architecture", section 2: the file layout is the beat stream) and pack
  * copies it unchanged.
@@ -139,7 +143,8 @@ lb_status dense_head_matvec(const uint16_t *W, int64_t N, int64_t K, const float
 /*
  * Many independent decode products in ONE launch (a token's work list).  A batch is a set-up object:
  * lowbit_batch_create validates the host-side list, and copies it with its tile table into device
- * memory it allocates once; lowbit_matvec_batched then enqueues a single kernel over every product.
+ * memory it allocates once; lowbit_matvec_batched then enqueues, on `s`, one kernel per (weight format,
+ * kernel configuration) group of the list -- one or two for a model's token -- over every product.
  * (tritium "Architecture", section 7: handing each small matvec to a pool costs more than the matvec
  * itself -- dispatch, not arithmetic, is what a token's many products must amortise.)
  */

@@ -149,8 +149,21 @@ def test_pack_round_trip(fmt):
     # the device layout is all code records, then all scales
     p = host(packed)
     nb = Wt.raw.shape[1]
-    assert np.array_equal(p[: 77 * nb * 16].reshape(77, nb, 16), Wt.raw[:, :, 2:])
+    assert np.array_equal(p[: 77 * nb * 16].reshape(77, nb, 16), device_records(fmt, Wt.raw))
     assert np.array_equal(p[77 * nb * 16:].reshape(77, nb, 2), Wt.raw[:, :, :2])
+
+
+def device_records(fmt, raw):
+    """The documented device records of ggml blocks: Q2_0_g64 code bytes as they are; Q1_0 with the
+    sign of weight 32r + 8m + k moved to bit 4k + r of little-endian dword m."""
+    codes = raw[:, :, 2:]
+    if fmt != synth.Q1_0:
+        return codes
+    bits = np.unpackbits(codes, axis=-1, bitorder="little")  # [..., 128], natural weight order
+    r, m, k = np.meshgrid(np.arange(4), np.arange(4), np.arange(8), indexing="ij")
+    dev = np.empty_like(bits)
+    dev[..., (32 * m + 4 * k + r).ravel()] = bits[..., (32 * r + 8 * m + k).ravel()]
+    return np.packbits(dev, axis=-1, bitorder="little")
 
 
 def test_launch_geometry_invariance():
