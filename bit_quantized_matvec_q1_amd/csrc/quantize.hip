@@ -4,9 +4,39 @@
 namespace lb {
 
 // q8_0 (bankml technical report, section III.2: blocks of 32 signed bytes with their own half-precision
-// scale, 127 / max|x| with round-half-to-even).  One thread per block of 32: amax is exact, the stored
-// scale is fp16_rne(amax / 127) from the correctly rounded fp32 quotient, the multiplier 127 / amax is a
-// correctly rounded fp32 quotient, and each q is round-half-even of the fp32 product (v_rndne_f32).
+// scale, 127 / max|x| with round-half-to-even): amax is exact, the stored scale is fp16_rne(amax / 127)
+// of the correctly rounded fp32 quotient, the multiplier 127 / amax a correctly rounded fp32 quotient
+// (0 when amax = 0), and each q round-half-even of the fp32 product.  Returns the scale's bits; the 32
+// bytes go to q[0..7], four per dword, little-endian.
+inline __device__ uint16_t quantize_block_q8_0(const float (&v)[32], uint32_t (&q)[8])
+{
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 32; i++)
+        amax = fmaxf(amax, fabsf(v[i]));
+    const float d = amax / 127.0f;
+    const float id = amax > 0.0f ? 127.0f / amax : 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+        uint32_t w = 0;
+#pragma unroll
+        for (int t = 0; t < 4; t++)
+            w |= (uint32_t)((int)rintf(v[4 * i + t] * id) & 0xff) << (8 * t);
+        q[i] = w;
+    }
+    return __half_as_ushort(__float2half_rn(d));
+}
+
+// Per-token int8 (tritium "Architecture", section 1): with the row's amax, s = amax / 127 and
+// q = clamp(rne(x * (127 / amax)), -128, 127); these give the multiplier and one q.
+inline __device__ float i8_row_multiplier(float amax) { return amax > 0.0f ? 127.0f / amax : 0.0f; }
+inline __device__ float i8_row_scale(float amax) { return amax / 127.0f; }
+inline __device__ int quantize_i8(float x, float id)
+{
+    return (int)fminf(fmaxf(rintf(x * id), -128.0f), 127.0f);
+}
+
+// q8_0: one thread per block of 32 (the arithmetic is quantize_block_q8_0).
 __global__ __launch_bounds__(WG) void quantize_q8_0_kernel(const float *__restrict__ x, int64_t nblocks,
                                                            int8_t *__restrict__ xq, uint16_t *__restrict__ xs)
 {
@@ -23,24 +53,8 @@ __global__ __launch_bounds__(WG) void quantize_q8_0_kernel(const float *__restri
         v[4 * i + 2] = t.z;
         v[4 * i + 3] = t.w;
     }
-    float amax = 0.0f;
-#pragma unroll
-    for (int i = 0; i < QK8; i++)
-        amax = fmaxf(amax, fabsf(v[i]));
-    const float d = amax / 127.0f;
-    const float id = amax > 0.0f ? 127.0f / amax : 0.0f;
-    xs[b] = __half_as_ushort(__float2half_rn(d));
     uint32_t packed[QK8 / 4];
-#pragma unroll
-    for (int i = 0; i < QK8 / 4; i++) {
-        uint32_t w = 0;
-#pragma unroll
-        for (int t = 0; t < 4; t++) {
-            const int q = (int)rintf(v[4 * i + t] * id);
-            w |= (uint32_t)(q & 0xff) << (8 * t);
-        }
-        packed[i] = w;
-    }
+    xs[b] = quantize_block_q8_0(v, packed);
     uint4 *dst = reinterpret_cast<uint4 *>(xq + b * QK8);
     dst[0] = make_uint4(packed[0], packed[1], packed[2], packed[3]);
     dst[1] = make_uint4(packed[4], packed[5], packed[6], packed[7]);
@@ -56,6 +70,50 @@ hipError_t launch_quantize_q8_0(const float *x, int64_t M, int64_t K, int8_t *xq
 
 // Per-token int8 (tritium "Architecture", section 1: int8 activations; one absmax scale per token).
 // One workgroup per row: amax over the row, s = amax / 127, q = clamp(rne(x * (127 / amax)), -128, 127).
+__device__ __forceinline__ float block_max(float v, float *red)
+{
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1)
+        v = fmaxf(v, __shfl_xor(v, off, 64));
+    if ((threadIdx.x & 63) == 0)
+        red[threadIdx.x >> 6] = v;
+    __syncthreads();
+    return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])); // max is exact in any order
+}
+
+// Rows whose K is a multiple of 4 and at most 4 * WG * NC: each thread holds NC float4 chunks of the row
+// in registers (all loads in flight together), so the row is read once; q leaves as packed dwords.
+template <int NC>
+__global__ __launch_bounds__(WG) void quantize_i8_row_vec_kernel(const float *__restrict__ x, int64_t K,
+                                                                 int8_t *__restrict__ xq, float *__restrict__ xs)
+{
+    __shared__ float red[WG / 64];
+    const int64_t m = blockIdx.x;
+    const float4 *xr = reinterpret_cast<const float4 *>(x + m * K);
+    const int nch = (int)(K / 4);
+    float4 v[NC];
+    float amax = 0.0f;
+#pragma unroll
+    for (int c = 0; c < NC; c++) {
+        const int i = (int)threadIdx.x + c * WG;
+        v[c] = i < nch ? xr[i] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[c].x), fabsf(v[c].y)), fmaxf(fabsf(v[c].z), fabsf(v[c].w))));
+    }
+    amax = block_max(amax, red);
+    const float id = i8_row_multiplier(amax);
+    if (threadIdx.x == 0)
+        xs[m] = i8_row_scale(amax);
+    uint32_t *qr = reinterpret_cast<uint32_t *>(xq + m * K);
+#pragma unroll
+    for (int c = 0; c < NC; c++) {
+        const int i = (int)threadIdx.x + c * WG;
+        if (i < nch)
+            qr[i] = (uint32_t)(quantize_i8(v[c].x, id) & 0xff) | (uint32_t)(quantize_i8(v[c].y, id) & 0xff) << 8 |
+                    (uint32_t)(quantize_i8(v[c].z, id) & 0xff) << 16 | (uint32_t)(quantize_i8(v[c].w, id) & 0xff) << 24;
+    }
+}
+
+// Any K: two passes over the row.
 __global__ __launch_bounds__(WG) void quantize_i8_row_kernel(const float *__restrict__ x, int64_t K,
                                                              int8_t *__restrict__ xq, float *__restrict__ xs)
 {
@@ -65,27 +123,29 @@ __global__ __launch_bounds__(WG) void quantize_i8_row_kernel(const float *__rest
     float amax = 0.0f;
     for (int64_t k = threadIdx.x; k < K; k += WG)
         amax = fmaxf(amax, fabsf(xr[k]));
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1)
-        amax = fmaxf(amax, __shfl_xor(amax, off, 64));
-    if ((threadIdx.x & 63) == 0)
-        red[threadIdx.x >> 6] = amax;
-    __syncthreads();
-    amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-    const float id = amax > 0.0f ? 127.0f / amax : 0.0f;
+    amax = block_max(amax, red);
+    const float id = i8_row_multiplier(amax);
     if (threadIdx.x == 0)
-        xs[m] = amax / 127.0f;
+        xs[m] = i8_row_scale(amax);
     int8_t *qr = xq + m * K;
-    for (int64_t k = threadIdx.x; k < K; k += WG) {
-        float v = rintf(xr[k] * id);
-        v = fminf(fmaxf(v, -128.0f), 127.0f);
-        qr[k] = (int8_t)(int)v;
-    }
+    for (int64_t k = threadIdx.x; k < K; k += WG)
+        qr[k] = (int8_t)quantize_i8(xr[k], id);
 }
 
 hipError_t launch_quantize_i8_row(const float *x, int64_t M, int64_t K, int8_t *xq, float *xs, hipStream_t s)
 {
-    hipLaunchKernelGGL(quantize_i8_row_kernel, dim3((unsigned)M), dim3(WG), 0, s, x, K, xq, xs);
+    const dim3 grid((unsigned)M), block(WG);
+    const int64_t nch = K / 4;
+    if (K % 4 == 0 && nch <= WG)
+        hipLaunchKernelGGL(quantize_i8_row_vec_kernel<1>, grid, block, 0, s, x, K, xq, xs);
+    else if (K % 4 == 0 && nch <= 2 * WG)
+        hipLaunchKernelGGL(quantize_i8_row_vec_kernel<2>, grid, block, 0, s, x, K, xq, xs);
+    else if (K % 4 == 0 && nch <= 4 * WG)
+        hipLaunchKernelGGL(quantize_i8_row_vec_kernel<4>, grid, block, 0, s, x, K, xq, xs);
+    else if (K % 4 == 0 && nch <= 8 * WG)
+        hipLaunchKernelGGL(quantize_i8_row_vec_kernel<8>, grid, block, 0, s, x, K, xq, xs);
+    else
+        hipLaunchKernelGGL(quantize_i8_row_kernel, grid, block, 0, s, x, K, xq, xs);
     return hipGetLastError();
 }
 

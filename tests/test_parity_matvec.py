@@ -203,7 +203,10 @@ def test_quantize_q8_0_bytes(M, K):
     assert np.array_equal(host(xs), d_ref)
 
 
-@pytest.mark.parametrize("M,K", [(1, 2560), (3, 6912), (2, 100)])
+# K spans each kernel variant: rows held in registers as 1, 2, 4 or 8 float4 chunks per thread (K % 4 == 0,
+# K <= 8192), and the two-pass loop (K % 4 != 0, so rows after the first are not 16-byte aligned; K > 8192)
+@pytest.mark.parametrize("M,K", [(1, 2560), (3, 6912), (2, 100), (4, 4), (2, 1028), (3, 4100), (2, 8192),
+                                 (2, 8196), (3, 30), (2, 12288)])
 def test_quantize_i8_row_bytes(M, K):
     say(f"case quantize i8_row M={M} K={K}")
     x = synth.activations(synth.rng(3100 + K), M, K)
