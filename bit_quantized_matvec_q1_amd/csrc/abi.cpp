@@ -367,7 +367,9 @@ lb_status lowbit_batch_create(const lb_matvec_desc *list, int32_t n, lb_batch **
         lb_batch::Group grp;
         grp.g.fmt = keys[gi].fmt;
         grp.g.cfg_a = keys[gi].cfg;
-        grp.g.cfg_b = -1;
+        grp.g.full = 1;
+        for (const lb::DevDesc &dd : descs[gi])
+            grp.g.full &= lb::matvec_config_full(keys[gi].fmt, keys[gi].cfg, dd.K) ? 1 : 0;
         grp.g.ntiles = (int32_t)tiles[gi].size();
         grp.g.desc = reinterpret_cast<const lb::DevDesc *>(base + off);
         e = hipMemcpy(base + off, descs[gi].data(), descs[gi].size() * sizeof(lb::DevDesc), hipMemcpyHostToDevice);

@@ -53,7 +53,8 @@ struct DevDesc {
 
 struct BatchGroup {
     int fmt;
-    int cfg_a, cfg_b;        // the kernel configuration of this launch group (cfg_b unused)
+    int cfg_a;               // the kernel configuration of this launch group
+    int full;                // every product's row has exactly L * S slices of the configuration
     int32_t ntiles;          // workgroups in the launch
     const DevDesc *desc;     // device
     const int32_t *tile_prod; // device, product index of each tile
@@ -61,6 +62,7 @@ struct BatchGroup {
 
 int matvec_config(int fmt, int64_t K);           // configuration index for a product, -1 if none
 int matvec_config_rows_per_iter(int fmt, int cfg); // rows one workgroup covers per iteration
+bool matvec_config_full(int fmt, int cfg, int64_t K); // a row of K has exactly L * S slices
 hipError_t launch_matvec_batched(const BatchGroup &g, hipStream_t s, size_t lds_bytes);
 int matvec_stage_bytes(int fmt, int64_t K); // LDS bytes of one product's staged activation
 

@@ -50,54 +50,94 @@ constexpr int CODE_BYTES = 16; // every slice is one 16-byte record
 //                       weight 32r + 8m + n at bit 4n + r of dword m):  e = 32r + 8m + n
 //   planar  a = 4k + r  (32-bit word k of plane bits; r = the bit within each nibble):  e = 32k + 4n + r
 // ------------------------------------------------------------------------------------------------
-template <int FMT>
-__device__ __forceinline__ void stage_slice(const int8_t *__restrict__ xq, const void *__restrict__ xscale, int sl,
-                                            uint32_t *__restrict__ rec)
+__device__ __forceinline__ uint32_t nibbles16(uint32_t x) // low nibbles of 4 bytes -> 16 bits, in order
 {
-    constexpr int SW = F<FMT>::SW, NAB = F<FMT>::NAB;
-    const uint4 *src = reinterpret_cast<const uint4 *>(xq + (int64_t)sl * SW);
-    uint32_t wb[SW / 4];
+    x &= 0x0F0F0F0Fu;
+    x = (x | (x >> 4)) & 0x00FF00FFu;
+    return (x | (x >> 8)) & 0x0000FFFFu;
+}
+
+// The whole activation vector, staged by all threads of the workgroup as independent items: one item
+// per nibble-word pair (the 8 activation bytes it covers, one 8/16/32-byte load, gathered with byte
+// permutes where they are strided) and one per (slice, q8_0 block) for d_x and -sum(q).  Item loads are
+// issued four at a time.
+template <int FMT>
+__device__ __forceinline__ void stage_activation(const int8_t *__restrict__ xq, const void *__restrict__ xscale, int ns,
+                                                 uint32_t *__restrict__ lds)
+{
+    constexpr int SW = F<FMT>::SW, NAB = F<FMT>::NAB, REC = F<FMT>::REC;
+    constexpr int WPS = SW / 8; // nibble-word pairs per slice
+    constexpr int UNR = 4;
+    const int nw = ns * WPS;
+    for (int base = threadIdx.x; base < nw; base += UNR * WG) {
+        uint4 v[UNR][FMT == LB_TERNARY_PLANAR ? 2 : 1];
 #pragma unroll
-    for (int i = 0; i < SW / 16; i++) {
-        const uint4 t = src[i];
-        wb[4 * i + 0] = t.x;
-        wb[4 * i + 1] = t.y;
-        wb[4 * i + 2] = t.z;
-        wb[4 * i + 3] = t.w;
-    }
-#define LB_BYTE(i) ((wb[(i) >> 2] >> (8 * ((i)&3))) & 0xffu)
-#pragma unroll
-    for (int a = 0; a < SW / 8; a++) {
-        uint32_t lo = 0, hi = 0;
-#pragma unroll
-        for (int n = 0; n < 8; n++) {
-            const int e = FMT == LB_Q2_0_G64 ? 16 * (a >> 1) + 2 * n + (a & 1)
-                          : FMT == LB_Q1_0   ? 32 * (a & 3) + 8 * (a >> 2) + n
-                                             : 32 * (a >> 2) + 4 * n + (a & 3);
-            const uint32_t v = LB_BYTE(e);
-            lo |= (v & 15u) << (4 * n);
-            hi |= (v >> 4) << (4 * n);
+        for (int q = 0; q < UNR; q++) {
+            const int it = base + q * WG;
+            if (it < nw) {
+                const int sl = it / WPS, a = it % WPS;
+                const int8_t *sb = xq + (int64_t)sl * SW;
+                if (FMT == LB_Q1_0) { // 8 consecutive bytes
+                    const uint2 t = *reinterpret_cast<const uint2 *>(sb + 32 * (a & 3) + 8 * (a >> 2));
+                    v[q][0] = make_uint4(t.x, t.y, 0u, 0u);
+                } else if (FMT == LB_Q2_0_G64) { // every other byte of 16
+                    v[q][0] = *reinterpret_cast<const uint4 *>(sb + 16 * (a >> 1));
+                } else { // every fourth byte of 32
+                    v[q][0] = *reinterpret_cast<const uint4 *>(sb + 32 * (a >> 2));
+                    v[q][FMT == LB_TERNARY_PLANAR ? 1 : 0] = *reinterpret_cast<const uint4 *>(sb + 32 * (a >> 2) + 16);
+                }
+            }
         }
-        rec[2 * a + 0] = lo;
-        rec[2 * a + 1] = hi;
+#pragma unroll
+        for (int q = 0; q < UNR; q++) {
+            const int it = base + q * WG;
+            if (it < nw) {
+                const int sl = it / WPS, a = it % WPS;
+                uint32_t u0, u1;
+                if (FMT == LB_Q1_0) {
+                    u0 = v[q][0].x;
+                    u1 = v[q][0].y;
+                } else if (FMT == LB_Q2_0_G64) {
+                    const uint32_t sel = (a & 1) ? 0x07050301u : 0x06040200u;
+                    u0 = __builtin_amdgcn_perm(v[q][0].y, v[q][0].x, sel);
+                    u1 = __builtin_amdgcn_perm(v[q][0].w, v[q][0].z, sel);
+                } else {
+                    const uint32_t r = (uint32_t)(a & 3), sel = r | ((4u + r) << 8);
+                    const uint4 lo4 = v[q][0], hi4 = v[q][FMT == LB_TERNARY_PLANAR ? 1 : 0];
+                    u0 = __builtin_amdgcn_perm(__builtin_amdgcn_perm(lo4.w, lo4.z, sel), __builtin_amdgcn_perm(lo4.y, lo4.x, sel),
+                                               0x05040100u);
+                    u1 = __builtin_amdgcn_perm(__builtin_amdgcn_perm(hi4.w, hi4.z, sel), __builtin_amdgcn_perm(hi4.y, hi4.x, sel),
+                                               0x05040100u);
+                }
+                uint32_t *rec = lds + sl * REC;
+                rec[2 * a + 0] = nibbles16(u0) | (nibbles16(u1) << 16);
+                rec[2 * a + 1] = nibbles16(u0 >> 4) | (nibbles16(u1 >> 4) << 16);
+            }
+        }
     }
     if (NAB > 0) {
-        const uint16_t *xs = reinterpret_cast<const uint16_t *>(xscale);
-#pragma unroll
-        for (int j = 0; j < NAB; j++) {
+        for (int it = threadIdx.x; it < ns * NAB; it += WG) {
+            const int sl = it / (NAB > 0 ? NAB : 1), j = it % (NAB > 0 ? NAB : 1);
+            const uint4 *src = reinterpret_cast<const uint4 *>(xq + (int64_t)sl * SW + 32 * j);
+            const uint4 b0 = src[0], b1 = src[1];
+            int sq = 0;
+            sq = __builtin_amdgcn_sdot4((int)b0.x, 0x01010101, sq, false);
+            sq = __builtin_amdgcn_sdot4((int)b0.y, 0x01010101, sq, false);
+            sq = __builtin_amdgcn_sdot4((int)b0.z, 0x01010101, sq, false);
+            sq = __builtin_amdgcn_sdot4((int)b0.w, 0x01010101, sq, false);
+            sq = __builtin_amdgcn_sdot4((int)b1.x, 0x01010101, sq, false);
+            sq = __builtin_amdgcn_sdot4((int)b1.y, 0x01010101, sq, false);
+            sq = __builtin_amdgcn_sdot4((int)b1.z, 0x01010101, sq, false);
+            sq = __builtin_amdgcn_sdot4((int)b1.w, 0x01010101, sq, false);
             // Q1_0 keeps 2 d_x / 2^j (exact): its block sums are 2 S - sum(q), S = the sum of q where the
             // bit is 1, and its products deliver 2^j S (the nibble value of mask position j)
-            const float dx = half_bits_to_float(xs[NAB * sl + j]);
+            const float dx = half_bits_to_float(reinterpret_cast<const uint16_t *>(xscale)[it]);
             const float q1f = j == 0 ? 2.0f : j == 1 ? 1.0f : j == 2 ? 0.5f : 0.25f;
+            uint32_t *rec = lds + sl * REC;
             rec[SW / 4 + j] = __float_as_uint(FMT == LB_Q1_0 ? q1f * dx : dx);
-            int sq = 0;
-#pragma unroll
-            for (int i = 0; i < 32; i++)
-                sq += (int)(int8_t)LB_BYTE(32 * j + i);
             rec[SW / 4 + NAB + j] = (uint32_t)(-sq);
         }
     }
-#undef LB_BYTE
 }
 
 __device__ __forceinline__ int sdot8(uint32_t a, uint32_t b, int c)
@@ -140,17 +180,21 @@ __device__ __forceinline__ void q2_isums(uint4 c, const uint32_t *A, int &i0, in
 __device__ __forceinline__ void q1_group_sums(uint4 b, const uint32_t *A, int (&C)[4])
 {
     const uint32_t bw[4] = {b.x, b.y, b.z, b.w};
+    // the eight accumulator chains advance together (dword by dword), so consecutive dot products are
+    // independent
+    int h[4] = {0, 0, 0, 0}, l[4] = {0, 0, 0, 0};
 #pragma unroll
-    for (int r = 0; r < 4; r++) {
-        int h = 0, l = 0;
+    for (int m = 0; m < 4; m++) {
 #pragma unroll
-        for (int m = 0; m < 4; m++) {
+        for (int r = 0; r < 4; r++) {
             const uint32_t e = bw[m] & (0x11111111u << r);
-            h = sdot8(e, A[(4 * m + r) * 2 + 1], h);
-            l = udot8(e, A[(4 * m + r) * 2 + 0], l);
+            h[r] = sdot8(e, A[(4 * m + r) * 2 + 1], h[r]);
+            l[r] = udot8(e, A[(4 * m + r) * 2 + 0], l[r]);
         }
-        C[r] = r < 3 ? h * 16 + l : l - h * 16;
     }
+#pragma unroll
+    for (int r = 0; r < 4; r++)
+        C[r] = r < 3 ? h[r] * 16 + l[r] : l[r] - h[r] * 16;
 }
 
 // Planar: plane words {pos0, pos1, neg0, neg1}.  Masking without a shift leaves bit r of a nibble in
@@ -256,22 +300,27 @@ typedef __attribute__((address_space(1))) float gf32;
 // One row's S slices.  off: byte offset of the row's first record; slo[i] / sls[i]: byte offset of
 // this lane's i-th record / its scale within a row.  The code records are read exactly once:
 // non-temporal loads keep the stream from displacing the activations and scales in the caches.
-template <int FMT, int S>
+// FULL (a row has exactly L * S slices): slice i sits a constant L * 16 * i bytes after slice 0, which
+// the loads take as an immediate offset.
+template <int FMT, int L, int S, bool FULL>
 __device__ __forceinline__ void issue_row(RowRegs<FMT, S> &r, const uint8_t *__restrict__ W,
                                           const uint8_t *__restrict__ scales, uint32_t off, const uint32_t (&slo)[S],
                                           const uint32_t (&sls)[S])
 {
     const uint32_t soff = off >> 3; // record idx at byte 16 idx, its binary16 scale at byte 2 idx
+    const gu8 *pc = (gu8 *)W + (off + slo[0]);
+    const gu8 *ps = (gu8 *)scales + (soff + sls[0]);
 #pragma unroll
     for (int i = 0; i < S; i++) {
-        const v4u t = __builtin_nontemporal_load((gv4u *)((gu8 *)W + (off + slo[i])));
+        const v4u t = __builtin_nontemporal_load(
+            (gv4u *)(FULL ? pc + i * L * CODE_BYTES : (gu8 *)W + (off + slo[i])));
         r.code[i] = make_uint4(t.x, t.y, t.z, t.w);
         if (FMT != LB_TERNARY_PLANAR) // small, shared by neighbouring lanes: left cacheable
-            r.sc[i] = *(gu16 *)((gu8 *)scales + (soff + sls[i]));
+            r.sc[i] = *(gu16 *)(FULL ? ps + i * L * 2 : (gu8 *)scales + (soff + sls[i]));
     }
 }
 
-template <int FMT, int L, int S, bool EMIT>
+template <int FMT, int L, int S, bool EMIT, bool FULL>
 __device__ __forceinline__ void compute_row(const uint4 (&code)[S], const uint32_t (&sc)[S],
                                             const uint32_t (&act)[S][F<FMT>::REC], const float (&cfold)[S], int ns, int li,
                                             bool valid, int row, float w_scale, float sx, float *__restrict__ y,
@@ -319,8 +368,8 @@ __device__ __forceinline__ void compute_row(const uint4 (&code)[S], const uint32
                 }
             }
             const float c = fmaf(half_bits_to_float((uint16_t)sc[i]), t, part);
-            part = sl < ns ? c : part;
-            if (EMIT && valid && sl < ns) {
+            part = (FULL || sl < ns) ? c : part;
+            if (EMIT && valid && (FULL || sl < ns)) {
                 int32_t *o = sums + (int64_t)row * (ns * NAB) + NAB * sl;
 #pragma unroll
                 for (int j = 0; j < NAB; j++)
@@ -333,7 +382,7 @@ __device__ __forceinline__ void compute_row(const uint4 (&code)[S], const uint32
     }
 }
 
-template <int FMT, int L, int S, bool EMIT>
+template <int FMT, int L, int S, bool EMIT, bool FULL>
 __device__ __forceinline__ void matvec_tile(const uint8_t *__restrict__ W, int N, int K, float w_scale,
                                             const int8_t *__restrict__ xq, const void *__restrict__ xscale,
                                             float *__restrict__ y, int32_t *__restrict__ sums, int row0, int nrows,
@@ -355,7 +404,8 @@ __device__ __forceinline__ void matvec_tile(const uint8_t *__restrict__ W, int N
     uint32_t slo[S], sls[S];
 #pragma unroll
     for (int i = 0; i < S; i++) {
-        slo[i] = (uint32_t)min(li + i * L, ns - 1) * CODE_BYTES;
+        // FULL: the row has exactly L * S slices (no lane past its end), so no clamp
+        slo[i] = (uint32_t)(FULL ? li + i * L : min(li + i * L, ns - 1)) * CODE_BYTES;
         sls[i] = slo[i] >> 3;
     }
     // Offset of the row this lane requests next, before clamping.  Past the tile's end it may grow
@@ -366,19 +416,18 @@ __device__ __forceinline__ void matvec_tile(const uint8_t *__restrict__ W, int N
 #pragma unroll
     for (int b = 0; b < NB - 1; b++) {
         if (b * STEP < nrows) // uniform
-            issue_row<FMT, S>(buf[b], W, scales, min(onext, last), slo, sls);
+            issue_row<FMT, L, S, FULL>(buf[b], W, scales, min(onext, last), slo, sls);
         onext += stepb;
     }
 
-    for (int sl = threadIdx.x; sl < ns; sl += WG)
-        stage_slice<FMT>(xq, xscale, sl, lds + sl * REC);
+    stage_activation<FMT>(xq, xscale, ns, lds);
     __syncthreads();
 
     uint32_t act[S][REC];
 #pragma unroll
     for (int i = 0; i < S; i++) {
         const int sl = li + i * L;
-        if (sl < ns) {
+        if (FULL || sl < ns) {
             const uint4 *p = reinterpret_cast<const uint4 *>(lds + sl * REC);
 #pragma unroll
             for (int q = 0; q < REC / 4; q++) {
@@ -416,10 +465,10 @@ __device__ __forceinline__ void matvec_tile(const uint8_t *__restrict__ W, int N
             if (cur >= nrows) // uniform
                 break;
             if (cur + (NB - 1) * STEP < nrows) // uniform
-                issue_row<FMT, S>(buf[(b + NB - 1) % NB], W, scales, min(onext, last), slo, sls);
+                issue_row<FMT, L, S, FULL>(buf[(b + NB - 1) % NB], W, scales, min(onext, last), slo, sls);
             onext += stepb;
             const int rl = cur + rbase;
-            compute_row<FMT, L, S, EMIT>(buf[b].code, buf[b].sc, act, cfold, ns, li, rl < nrows, row0 + rl, w_scale,
+            compute_row<FMT, L, S, EMIT, FULL>(buf[b].code, buf[b].sc, act, cfold, ns, li, rl < nrows, row0 + rl, w_scale,
                                          sx, y, sums);
         }
     }
@@ -484,6 +533,8 @@ int matvec_config(int fmt, int64_t K)
 
 bool matvec_supported_k(int fmt, int64_t K) { return matvec_config(fmt, K) >= 0; }
 
+bool matvec_config_full(int fmt, int cfg, int64_t K) { return (int64_t)kCfgs[cfg].L * kCfgs[cfg].S == K / sw_of(fmt); }
+
 int matvec_config_rows_per_iter(int fmt, int cfg)
 {
     (void)fmt;
@@ -500,7 +551,7 @@ __global__ __launch_bounds__(WG) void matvec_kernel(const uint8_t *__restrict__ 
     extern __shared__ uint32_t lds[];
     const int row0 = blockIdx.x * tile_rows;
     const int nrows = min(tile_rows, N - row0);
-    matvec_tile<FMT, L, S, EMIT>(W, N, K, w_scale, xq, xscale, y, sums, row0, nrows, lds);
+    matvec_tile<FMT, L, S, EMIT, false>(W, N, K, w_scale, xq, xscale, y, sums, row0, nrows, lds);
 }
 
 template <int FMT, bool EMIT>
@@ -559,7 +610,7 @@ hipError_t launch_matvec(int fmt, const uint8_t *W, int64_t N, int64_t K, float 
 // product (a uniform, scalar-cached read); every instantiation is compiled for one configuration, so
 // each gets the registers it needs and no more.
 // ------------------------------------------------------------------------------------------------
-template <int FMT, int L, int S>
+template <int FMT, int L, int S, bool FULL>
 __global__ __launch_bounds__(WG) void matvec_batched_kernel(const DevDesc *__restrict__ desc,
                                                             const int32_t *__restrict__ tile_prod)
 {
@@ -568,7 +619,7 @@ __global__ __launch_bounds__(WG) void matvec_batched_kernel(const DevDesc *__res
     const DevDesc d = desc[tile_prod[t]];
     const int row0 = (t - d.tile_begin) * d.tile_rows;
     const int nrows = min(d.tile_rows, d.N - row0);
-    matvec_tile<FMT, L, S, false>(d.W, d.N, d.K, d.w_scale, d.xq, d.xscale, d.y, nullptr, row0, nrows, lds);
+    matvec_tile<FMT, L, S, false, FULL>(d.W, d.N, d.K, d.w_scale, d.xq, d.xscale, d.y, nullptr, row0, nrows, lds);
 }
 
 template <int FMT>
@@ -577,9 +628,14 @@ static hipError_t launch_batched_fmt(const BatchGroup &g, hipStream_t stream, si
     switch (g.cfg_a) {
 #define LB_BCASE(i, l, s)                                                                                     \
     case i:                                                                                                   \
-        if constexpr (cfg_allowed(FMT, s))                                                                    \
-            hipLaunchKernelGGL((matvec_batched_kernel<FMT, l, s>), dim3(g.ntiles), dim3(WG), lds_bytes, stream,  \
-                               g.desc, g.tile_prod);                                                           \
+        if constexpr (cfg_allowed(FMT, s)) {                                                                  \
+            if (g.full)                                                                                       \
+                hipLaunchKernelGGL((matvec_batched_kernel<FMT, l, s, true>), dim3(g.ntiles), dim3(WG), lds_bytes, \
+                                   stream, g.desc, g.tile_prod);                                               \
+            else                                                                                              \
+                hipLaunchKernelGGL((matvec_batched_kernel<FMT, l, s, false>), dim3(g.ntiles), dim3(WG),          \
+                                   lds_bytes, stream, g.desc, g.tile_prod);                                    \
+        }                                                                                                     \
         break;
         LB_CFGS(LB_BCASE)
 #undef LB_BCASE
