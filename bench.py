@@ -121,6 +121,10 @@ class DecodeToken:
     def products_launch(self):
         self.batch.run()
 
+    def step(self):
+        self.quantize()
+        self.products_launch()
+
     @property
     def algorithmic_bytes(self):
         return self.weight_bytes + self.act_bytes + self.out_bytes

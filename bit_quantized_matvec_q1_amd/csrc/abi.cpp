@@ -4,7 +4,10 @@
 // falling back, so a run never measures a different kernel than the one it names).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
+#include <functional>
+#include <queue>
 #include <cstdio>
 #include <cstring>
 #include <string>
@@ -274,6 +277,73 @@ lb_status dense_head_matvec(const uint16_t *W, int64_t N, int64_t K, const float
 
 // ---- batched decode ------------------------------------------------------------------------------
 
+// Tile plan of one launch group.  Every product is cut into row tiles (whole row iterations of the
+// configuration) of about the same weight bytes, between 192 and 384 KiB (smaller tiles pay more for
+// their activation staging, larger ones leave a ragged tail: both measured slower); the size is the one
+// whose in-order dispatch onto the group's resident workgroup slots (CUs x workgroups per CU) has the
+// shortest simulated makespan, each tile costing its weight bytes plus a fixed start-up share; among
+// sizes within 0.5 % of the best, the largest -- but 256 KiB unless the simulation predicts a makespan
+// at least 5 % shorter (a group whose 256 KiB tiles leave a mostly empty last round).  Tiles are
+// emitted largest first, so the partial tiles of every product fill the tail of the launch.
+static void plan_tiles(int fmt, int cfg, std::vector<lb::DevDesc> &ds, int64_t slots, std::vector<lb::TileRef> &out)
+{
+    constexpr int64_t kStartup = 24 * 1024; // bytes-equivalent of one workgroup's staging and start-up
+    constexpr int64_t kDefault = 256 * 1024; // the best fixed size measured on the 8B-shape tokens
+    const int64_t rpi = lb::matvec_config_rows_per_iter(fmt, cfg);
+    auto rows_for = [&](int64_t tb, const lb::DevDesc &d) {
+        const int64_t rb = lowbit_weight_bytes(fmt, 1, d.K);
+        const int64_t want = std::max<int64_t>(1, (tb + rb - 1) / rb);
+        return rpi * ((want + rpi - 1) / rpi);
+    };
+    std::vector<int64_t> cand, span;
+    std::vector<int64_t> costs;
+    for (int64_t tb = 192 * 1024; tb <= 384 * 1024; tb += 16 * 1024) {
+        costs.clear();
+        for (const lb::DevDesc &d : ds) {
+            const int64_t rows = rows_for(tb, d), rb = lowbit_weight_bytes(fmt, 1, d.K);
+            for (int64_t r0 = 0; r0 < d.N; r0 += rows)
+                costs.push_back(std::min<int64_t>(rows, d.N - r0) * rb + kStartup);
+        }
+        std::sort(costs.begin(), costs.end(), std::greater<int64_t>());
+        std::priority_queue<int64_t, std::vector<int64_t>, std::greater<int64_t>> q;
+        for (int64_t i = 0; i < std::min<int64_t>(slots, (int64_t)costs.size()); i++)
+            q.push(0);
+        int64_t make = 0;
+        for (int64_t c : costs) {
+            const int64_t t = q.top() + c;
+            q.pop();
+            q.push(t);
+            make = std::max(make, t);
+        }
+        cand.push_back(tb);
+        span.push_back(make);
+    }
+    const int64_t best = *std::min_element(span.begin(), span.end());
+    int64_t tb = kDefault, at_default = 0;
+    for (size_t i = 0; i < cand.size(); i++)
+        if (cand[i] == kDefault)
+            at_default = span[i];
+    if (best * 100 < at_default * 95) // the model is coarse: leave the default unless it predicts >= 5 %
+        for (size_t i = 0; i < cand.size(); i++)
+            if (span[i] * 1000 <= best * 1005)
+                tb = cand[i];
+    struct T {
+        int64_t cost;
+        lb::TileRef ref;
+    };
+    std::vector<T> ts;
+    for (size_t p = 0; p < ds.size(); p++) {
+        const int64_t rows = rows_for(tb, ds[p]), rb = lowbit_weight_bytes(fmt, 1, ds[p].K);
+        ds[p].tile_rows = (int32_t)std::min<int64_t>(rows, INT32_MAX);
+        for (int64_t r0 = 0; r0 < ds[p].N; r0 += rows)
+            ts.push_back({std::min<int64_t>(rows, ds[p].N - r0) * rb, {(int32_t)p, (int32_t)r0}});
+    }
+    std::stable_sort(ts.begin(), ts.end(), [](const T &a, const T &b) { return a.cost > b.cost; });
+    out.clear();
+    for (const T &t : ts)
+        out.push_back(t.ref);
+}
+
 struct lb_batch {
     struct Group {
         lb::BatchGroup g;
@@ -312,7 +382,6 @@ lb_status lowbit_batch_create(const lb_matvec_desc *list, int32_t n, lb_batch **
     };
     std::vector<Key> keys;
     std::vector<std::vector<lb::DevDesc>> descs;
-    std::vector<std::vector<int32_t>> tiles;
     std::vector<size_t> lds;
     for (int32_t i = 0; i < n; i++) {
         const lb_matvec_desc &d = list[i];
@@ -325,7 +394,6 @@ lb_status lowbit_batch_create(const lb_matvec_desc *list, int32_t n, lb_batch **
         if (gi == keys.size()) {
             keys.push_back({d.fmt, cfg});
             descs.emplace_back();
-            tiles.emplace_back();
             lds.push_back(0);
         }
         lb::DevDesc dd;
@@ -337,25 +405,29 @@ lb_status lowbit_batch_create(const lb_matvec_desc *list, int32_t n, lb_batch **
         dd.K = (int32_t)d.K;
         dd.w_scale = d.w_tensor_scale;
         dd.cfg = cfg;
-        // tiles of about 256 KiB of weights (whole row iterations): enough work to amortise the activation
-        // staging, small enough that long rows still give many workgroups
-        const int rpi = lb::matvec_config_rows_per_iter(d.fmt, cfg);
-        const int64_t row_bytes = lowbit_weight_bytes(d.fmt, 1, d.K);
-        const int64_t want = std::max<int64_t>(1, (262144 + row_bytes - 1) / row_bytes);
-        dd.tile_rows = (int32_t)(rpi * ((want + rpi - 1) / rpi));
-        dd.tile_begin = (int32_t)tiles[gi].size();
-        const int64_t nt = (d.N + dd.tile_rows - 1) / dd.tile_rows;
-        for (int64_t t = 0; t < nt; t++)
-            tiles[gi].push_back((int32_t)descs[gi].size());
+        dd.tile_rows = 0; // set by the tile plan
         descs[gi].push_back(dd);
         lds[gi] = std::max(lds[gi], (size_t)lb::matvec_stage_bytes(d.fmt, d.K));
+    }
+    int device = 0, cus = 0;
+    hipGetDevice(&device);
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess || cus < 1)
+        cus = 1;
+    std::vector<std::vector<lb::TileRef>> tiles(keys.size());
+    std::vector<int> full(keys.size(), 1);
+    for (size_t gi = 0; gi < keys.size(); gi++) {
+        for (const lb::DevDesc &dd : descs[gi])
+            full[gi] &= lb::matvec_config_full(keys[gi].fmt, keys[gi].cfg, dd.K) ? 1 : 0;
+        const int64_t slots =
+            (int64_t)cus * lb::matvec_batched_blocks_per_cu(keys[gi].fmt, keys[gi].cfg, full[gi] != 0, lds[gi]);
+        plan_tiles(keys[gi].fmt, keys[gi].cfg, descs[gi], slots, tiles[gi]);
     }
     size_t bytes = 256;
     for (size_t gi = 0; gi < keys.size(); gi++)
         bytes += (descs[gi].size() * sizeof(lb::DevDesc) + 255) / 256 * 256 +
-                 (tiles[gi].size() * sizeof(int32_t) + 255) / 256 * 256;
+                 (tiles[gi].size() * sizeof(lb::TileRef) + 255) / 256 * 256;
     lb_batch *b = new lb_batch();
-    hipGetDevice(&b->device);
+    b->device = device;
     hipError_t e = hipMalloc(&b->dev, bytes);
     if (e != hipSuccess) {
         delete b;
@@ -367,17 +439,15 @@ lb_status lowbit_batch_create(const lb_matvec_desc *list, int32_t n, lb_batch **
         lb_batch::Group grp;
         grp.g.fmt = keys[gi].fmt;
         grp.g.cfg_a = keys[gi].cfg;
-        grp.g.full = 1;
-        for (const lb::DevDesc &dd : descs[gi])
-            grp.g.full &= lb::matvec_config_full(keys[gi].fmt, keys[gi].cfg, dd.K) ? 1 : 0;
+        grp.g.full = full[gi];
         grp.g.ntiles = (int32_t)tiles[gi].size();
         grp.g.desc = reinterpret_cast<const lb::DevDesc *>(base + off);
         e = hipMemcpy(base + off, descs[gi].data(), descs[gi].size() * sizeof(lb::DevDesc), hipMemcpyHostToDevice);
         off += (descs[gi].size() * sizeof(lb::DevDesc) + 255) / 256 * 256;
         if (e == hipSuccess) {
-            grp.g.tile_prod = reinterpret_cast<const int32_t *>(base + off);
-            e = hipMemcpy(base + off, tiles[gi].data(), tiles[gi].size() * sizeof(int32_t), hipMemcpyHostToDevice);
-            off += (tiles[gi].size() * sizeof(int32_t) + 255) / 256 * 256;
+            grp.g.tiles = reinterpret_cast<const lb::TileRef *>(base + off);
+            e = hipMemcpy(base + off, tiles[gi].data(), tiles[gi].size() * sizeof(lb::TileRef), hipMemcpyHostToDevice);
+            off += (tiles[gi].size() * sizeof(lb::TileRef) + 255) / 256 * 256;
         }
         if (e != hipSuccess) {
             hipFree(b->dev);

@@ -47,8 +47,11 @@ struct DevDesc {
     int32_t N, K;
     float w_scale;
     int32_t cfg;        // index into the format's configuration table
-    int32_t tile_begin; // first tile (workgroup) of this product in its launch group
     int32_t tile_rows;  // rows per tile
+};
+
+struct TileRef {        // one workgroup of a batched launch: its product and first row
+    int32_t prod, row0;
 };
 
 struct BatchGroup {
@@ -57,13 +60,14 @@ struct BatchGroup {
     int full;                // every product's row has exactly L * S slices of the configuration
     int32_t ntiles;          // workgroups in the launch
     const DevDesc *desc;     // device
-    const int32_t *tile_prod; // device, product index of each tile
+    const TileRef *tiles;    // device, one per workgroup
 };
 
 int matvec_config(int fmt, int64_t K);           // configuration index for a product, -1 if none
 int matvec_config_rows_per_iter(int fmt, int cfg); // rows one workgroup covers per iteration
 bool matvec_config_full(int fmt, int cfg, int64_t K); // a row of K has exactly L * S slices
 hipError_t launch_matvec_batched(const BatchGroup &g, hipStream_t s, size_t lds_bytes);
+int matvec_batched_blocks_per_cu(int fmt, int cfg, bool full, size_t lds_bytes); // resident workgroups per CU
 int matvec_stage_bytes(int fmt, int64_t K); // LDS bytes of one product's staged activation
 
 } // namespace lb

@@ -612,12 +612,12 @@ hipError_t launch_matvec(int fmt, const uint8_t *W, int64_t N, int64_t K, float 
 // ------------------------------------------------------------------------------------------------
 template <int FMT, int L, int S, bool FULL>
 __global__ __launch_bounds__(WG) void matvec_batched_kernel(const DevDesc *__restrict__ desc,
-                                                            const int32_t *__restrict__ tile_prod)
+                                                            const TileRef *__restrict__ tiles)
 {
     extern __shared__ uint32_t lds[];
-    const int t = blockIdx.x;
-    const DevDesc d = desc[tile_prod[t]];
-    const int row0 = (t - d.tile_begin) * d.tile_rows;
+    const TileRef tr = tiles[blockIdx.x];
+    const DevDesc d = desc[tr.prod];
+    const int row0 = tr.row0;
     const int nrows = min(d.tile_rows, d.N - row0);
     matvec_tile<FMT, L, S, false, FULL>(d.W, d.N, d.K, d.w_scale, d.xq, d.xscale, d.y, nullptr, row0, nrows, lds);
 }
@@ -631,10 +631,10 @@ static hipError_t launch_batched_fmt(const BatchGroup &g, hipStream_t stream, si
         if constexpr (cfg_allowed(FMT, s)) {                                                                  \
             if (g.full)                                                                                       \
                 hipLaunchKernelGGL((matvec_batched_kernel<FMT, l, s, true>), dim3(g.ntiles), dim3(WG), lds_bytes, \
-                                   stream, g.desc, g.tile_prod);                                               \
+                                   stream, g.desc, g.tiles);                                               \
             else                                                                                              \
                 hipLaunchKernelGGL((matvec_batched_kernel<FMT, l, s, false>), dim3(g.ntiles), dim3(WG),          \
-                                   lds_bytes, stream, g.desc, g.tile_prod);                                    \
+                                   lds_bytes, stream, g.desc, g.tiles);                                    \
         }                                                                                                     \
         break;
         LB_CFGS(LB_BCASE)
@@ -643,6 +643,40 @@ static hipError_t launch_batched_fmt(const BatchGroup &g, hipStream_t stream, si
         return hipErrorInvalidValue;
     }
     return hipGetLastError();
+}
+
+template <int FMT> static int blocks_per_cu_fmt(int cfg, bool full, size_t lds_bytes)
+{
+    int n = 0;
+    hipError_t e = hipErrorInvalidValue;
+    switch (cfg) {
+#define LB_OCASE(i, l, s)                                                                                     \
+    case i:                                                                                                   \
+        if constexpr (cfg_allowed(FMT, s))                                                                    \
+            e = full ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, matvec_batched_kernel<FMT, l, s, true>, WG, \
+                                                                    lds_bytes)                                 \
+                     : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, matvec_batched_kernel<FMT, l, s, false>,   \
+                                                                    WG, lds_bytes);                            \
+        break;
+        LB_CFGS(LB_OCASE)
+#undef LB_OCASE
+    default:
+        break;
+    }
+    return e == hipSuccess && n > 0 ? n : 1;
+}
+
+int matvec_batched_blocks_per_cu(int fmt, int cfg, bool full, size_t lds_bytes)
+{
+    switch (fmt) {
+    case LB_Q1_0:
+        return blocks_per_cu_fmt<LB_Q1_0>(cfg, full, lds_bytes);
+    case LB_Q2_0_G64:
+        return blocks_per_cu_fmt<LB_Q2_0_G64>(cfg, full, lds_bytes);
+    case LB_TERNARY_PLANAR:
+        return blocks_per_cu_fmt<LB_TERNARY_PLANAR>(cfg, full, lds_bytes);
+    }
+    return 1;
 }
 
 hipError_t launch_matvec_batched(const BatchGroup &g, hipStream_t s, size_t lds_bytes)
