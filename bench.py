@@ -40,7 +40,7 @@ def log(*a):
 class DecodeToken:
     """All products of one decode token of a layered model, batched into one launch plan."""
 
-    def __init__(self, fmt, layer_shapes, layers, seed, keep_blocks_layers=0):
+    def __init__(self, fmt, layer_shapes, layers, seed, keep_blocks_layers=0, head=None):
         import torch
 
         import bit_quantized_matvec_q1_amd.lowbit as L
@@ -108,6 +108,15 @@ class DecodeToken:
                 self.out_bytes += 4 * N
         self.batch = L.Batch(descs)
         self.afmt = L.ACT_I8_ROW if planar else L.ACT_Q8_0
+        # the dense bf16 output head of the token (its input is the final hidden state, fp32)
+        self.head, self.head_bytes = None, 0
+        if head is not None:
+            hn, hk = head
+            self.head = dict(N=hn, K=hk, W=synth.device_head_weights(hn, hk, seed + 7),
+                             x=torch.randn(hk, generator=g, device="cuda"),
+                             y=torch.empty(hn, dtype=torch.float32, device="cuda"))
+            self.head_bytes = 2 * hn * hk
+            self.weight_bytes += self.head_bytes
         torch.cuda.synchronize()
 
     def quantize(self):
@@ -121,13 +130,20 @@ class DecodeToken:
     def products_launch(self):
         self.batch.run()
 
+    def head_launch(self):
+        if self.head is not None:
+            h = self.head
+            self.L.dense_head_matvec(h["W"], h["N"], h["K"], h["x"], h["y"])
+
     def step(self):
         self.quantize()
         self.products_launch()
+        self.head_launch()
 
     @property
     def algorithmic_bytes(self):
-        return self.weight_bytes + self.act_bytes + self.out_bytes
+        """Bytes of the batched products launch (the head, if any, is a launch of its own)."""
+        return self.weight_bytes - self.head_bytes + self.act_bytes + self.out_bytes
 
 
 def time_token(tok, steps, warmup):
@@ -136,8 +152,7 @@ def time_token(tok, steps, warmup):
     import torch
 
     for _ in range(warmup):
-        tok.quantize()
-        tok.products_launch()
+        tok.step()
     torch.cuda.synchronize()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     t0 = time.perf_counter()
@@ -146,6 +161,7 @@ def time_token(tok, steps, warmup):
         a.record()
         tok.products_launch()
         b.record()
+        tok.head_launch()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     launch_ms = [a.elapsed_time(b) for a, b in ev]
@@ -195,6 +211,31 @@ def cpu_baseline(tok, budget_s=12.0):
         if t_total >= budget_s:
             break
     return t_total, wbytes, layers_done
+
+
+def head_gbs(N, K, reps=20, seed=1006):
+    """The dense bf16 head matvec alone on weights resident in HBM: (ms, GB/s of its bytes)."""
+    import torch
+
+    import bit_quantized_matvec_q1_amd.lowbit as L
+    import synth
+
+    W = synth.device_head_weights(N, K, seed)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed + 1)
+    x = torch.randn(K, generator=g, device="cuda")
+    y = torch.empty(N, dtype=torch.float32, device="cuda")
+    for _ in range(3):
+        L.dense_head_matvec(W, N, K, x, y)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        L.dense_head_matvec(W, N, K, x, y)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    return ms, (2 * N * K + 4 * K + 4 * N) / (ms * 1e-3) / 1e9
 
 
 def prefill_tops(fmt, N, K, M, reps=20, seed=1004):
@@ -347,13 +388,20 @@ def main():
             t1.batch.close()
             del t1
         elif name == "planar":
-            tp = DecodeToken(synth.TERNARY_PLANAR, synth.BITNET_2B_LAYER, synth.BITNET_2B_LAYERS, seed=1005)
+            tp = DecodeToken(synth.TERNARY_PLANAR, synth.BITNET_2B_LAYER, synth.BITNET_2B_LAYERS, seed=1005,
+                             head=synth.BITNET_HEAD)
             msp, mlp = time_token(tp, max(10, args.steps // 2), 5)
             secondary["planar_2b_token"] = {
+                "workload": "BitNet-b1.58-2B shapes, 30 layers x 7 planar products + the dense bf16 head "
+                            "128256x2560; per-token int8 activations",
                 "weight_bytes": tp.weight_bytes, "ms_per_step": round(msp, 5),
                 "gbs": round(tp.weight_bytes / (msp * 1e-3) / 1e9, 1),
-                "launch_gbs": round(tp.algorithmic_bytes / (mlp * 1e-3) / 1e9, 1),
+                "pct_hbm_peak": round(100 * tp.weight_bytes / (msp * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+                "products_launch_gbs": round(tp.algorithmic_bytes / (mlp * 1e-3) / 1e9, 1),
             }
+            hms, hg = head_gbs(*synth.BITNET_HEAD)
+            secondary["head_bf16_128256x2560"] = {"ms": round(hms, 4), "gbs": round(hg, 1),
+                                                  "pct_hbm_peak": round(100 * hg / HBM_PEAK_GBS, 2)}
             tp.batch.close()
             del tp
         elif name == "prefill":

@@ -262,6 +262,8 @@ lb_status dense_head_matvec(const uint16_t *W, int64_t N, int64_t K, const float
         return fail(LB_ESHAPE, fn, "negative size");
     if (K % 8 || K > 4096)
         return fail(LB_ESHAPE, fn, "K must be a multiple of 8 and at most 4096");
+    if (N * K * 2 >= (int64_t(1) << 32))
+        return fail(LB_ESHAPE, fn, "weight tensor of 4 GiB or more");
     if (N == 0)
         return LB_OK;
     if (!W || !x || !y)

@@ -9,6 +9,14 @@
 
 namespace lb {
 
+typedef unsigned hv4u __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(1))) const hv4u ghv4u;
+typedef __attribute__((address_space(1))) const uint8_t ghu8;
+
+// A workgroup owns a tile of rows; wave w takes rows w, w + 4, ... of it.  Loads are unconditional
+// (chunk offsets clamped to the row's last chunk, row offsets to the tile's last row -- both in bounds,
+// their results never stored or multiplied by a zero x), non-temporal (the weights are read once), and
+// issued one row ahead into a second register buffer.
 template <int S>
 __global__ __launch_bounds__(WG) void head_kernel(const uint16_t *__restrict__ W, int N, int K,
                                                   const float *__restrict__ x, float *__restrict__ y, int tile_rows)
@@ -16,9 +24,11 @@ __global__ __launch_bounds__(WG) void head_kernel(const uint16_t *__restrict__ W
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int nch = K / 8; // chunks of 8 columns per row
     float xr[S][8];
+    uint32_t co[S]; // byte offset of this lane's chunks within a row
 #pragma unroll
     for (int i = 0; i < S; i++) {
         const int ch = lane + 64 * i;
+        co[i] = (uint32_t)min(ch, nch - 1) * 16u;
         if (ch < nch) {
             const float4 a = reinterpret_cast<const float4 *>(x)[2 * ch];
             const float4 b = reinterpret_cast<const float4 *>(x)[2 * ch + 1];
@@ -30,39 +40,47 @@ __global__ __launch_bounds__(WG) void head_kernel(const uint16_t *__restrict__ W
                 xr[i][j] = 0.0f;
         }
     }
+    const bool ragged = nch != 64 * S; // some lanes' last chunk lies past the row: zero its weights too
     const int row0 = blockIdx.x * tile_rows;
     const int nrows = min(tile_rows, N - row0);
-    constexpr int U = 2;
-    for (int it = 0; it < nrows; it += U * (WG / 64)) {
-        uint4 w[U][S];
+    constexpr int STEP = WG / 64;
+    const uint32_t rowb = (uint32_t)K * 2u;
+    const uint32_t last = (uint32_t)(row0 + nrows - 1) * rowb;
+    uint32_t onext = (uint32_t)(row0 + min(wave, nrows - 1)) * rowb;
+    uint4 buf[2][S];
+    auto issue = [&](uint4 (&w)[S], uint32_t off) {
 #pragma unroll
-        for (int u = 0; u < U; u++) {
-            const int rl = it + u * (WG / 64) + wave;
-#pragma unroll
-            for (int i = 0; i < S; i++) {
-                const int ch = lane + 64 * i;
-                w[u][i] = make_uint4(0, 0, 0, 0);
-                if (rl < nrows && ch < nch)
-                    w[u][i] = reinterpret_cast<const uint4 *>(W + (int64_t)(row0 + rl) * K)[ch];
-            }
+        for (int i = 0; i < S; i++) {
+            const hv4u t = __builtin_nontemporal_load((ghv4u *)((ghu8 *)W + (off + co[i])));
+            w[i] = make_uint4(t.x, t.y, t.z, t.w);
         }
+    };
+    issue(buf[0], min(onext, last));
+    onext += STEP * rowb;
+    for (int it = 0; it < nrows; it += 2 * STEP) {
 #pragma unroll
-        for (int u = 0; u < U; u++) {
-            const int rl = it + u * (WG / 64) + wave;
+        for (int b = 0; b < 2; b++) {
+            const int cur = it + b * STEP;
+            if (cur >= nrows) // uniform
+                break;
+            if (cur + STEP < nrows) // uniform
+                issue(buf[b ^ 1], min(onext, last));
+            onext += STEP * rowb;
+            if (ragged && lane + 64 * (S - 1) >= nch)
+                buf[b][S - 1] = make_uint4(0u, 0u, 0u, 0u);
             float acc = 0.0f;
 #pragma unroll
             for (int i = 0; i < S; i++) {
-                const uint32_t v[4] = {w[u][i].x, w[u][i].y, w[u][i].z, w[u][i].w};
+                const uint32_t v[4] = {buf[b][i].x, buf[b][i].y, buf[b][i].z, buf[b][i].w};
 #pragma unroll
                 for (int j = 0; j < 4; j++) {
                     acc = fmaf(__uint_as_float(v[j] << 16), xr[i][2 * j], acc);
                     acc = fmaf(__uint_as_float(v[j] & 0xffff0000u), xr[i][2 * j + 1], acc);
                 }
             }
-#pragma unroll
-            for (int off = 32; off >= 1; off >>= 1)
-                acc += __shfl_xor(acc, off, 64);
-            if (rl < nrows && lane == 0)
+            acc = group_sum_f<64>(acc);
+            const int rl = cur + wave;
+            if (rl < nrows && lane == 63)
                 y[row0 + rl] = acc;
         }
     }

@@ -233,44 +233,6 @@ __device__ __forceinline__ int planar_total8(const PlanarAcc &a)
 }
 
 // ------------------------------------------------------------------------------------------------
-// Cross-lane sum over aligned groups of L lanes with DPP (no LDS round trip).  The total ends up in the
-// group's last lane (li == L - 1); for L <= 16 every lane of the group holds it.
-// ------------------------------------------------------------------------------------------------
-template <int L> __device__ __forceinline__ int group_sum_i(int v)
-{
-    if (L >= 2)
-        v += __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false); // quad_perm [1,0,3,2]
-    if (L >= 4)
-        v += __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false); // quad_perm [2,3,0,1]
-    if (L >= 8)
-        v += __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false); // row_half_mirror
-    if (L >= 16)
-        v += __builtin_amdgcn_update_dpp(0, v, 0x140, 0xF, 0xF, false); // row_mirror
-    if (L >= 32)
-        v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false); // row_bcast:15 into rows 1, 3
-    if (L >= 64)
-        v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false); // row_bcast:31 into rows 2, 3
-    return v;
-}
-
-template <int L> __device__ __forceinline__ float group_sum_f(float v)
-{
-    if (L >= 2)
-        v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
-    if (L >= 4)
-        v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
-    if (L >= 8)
-        v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false));
-    if (L >= 16)
-        v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false));
-    if (L >= 32)
-        v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x142, 0xA, 0xF, false));
-    if (L >= 64)
-        v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x143, 0xC, 0xF, false));
-    return v;
-}
-
-// ------------------------------------------------------------------------------------------------
 // One workgroup, one tile of rows [row0, row0 + nrows) of one product.
 //
 // Loads are unconditional: a lane past the tile's last row re-reads that row and a lane past the row's

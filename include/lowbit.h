@@ -136,7 +136,7 @@ lb_status lowbit_block_sums(int fmt, const void *W, int64_t N, int64_t K, int af
  * (tritium "Architecture", section 3: the dense head is the largest single stream; bf16 storage).
  *   W: device uint16 bf16 bits [N][K], 16-byte aligned, K % 8 == 0; x: device fp32 [K], 16-byte aligned;
  *   y: device fp32 [N].  K must be a multiple of 8 and at most 4096 (the activation vector is held in
- *   registers); otherwise LB_ESHAPE.
+ *   registers) and the weights smaller than 4 GiB; otherwise LB_ESHAPE.
  */
 lb_status dense_head_matvec(const uint16_t *W, int64_t N, int64_t K, const float *x, float *y, hipStream_t s);
 

@@ -78,6 +78,7 @@ def test_other_entry_points_validate():
     assert lib.lowbit_block_sums(L.Q2_0_G64, A16, 8, 64, L.ACT_Q8_0, A16, A16, 1, None, None) == L.LB_EINVAL
     assert lib.dense_head_matvec(A16, 8, 12, A16, A16, None) == L.LB_ESHAPE
     assert lib.dense_head_matvec(A16, 8, 8192, A16, A16, None) == L.LB_ESHAPE
+    assert lib.dense_head_matvec(A16, 1 << 20, 2048, A16, A16, None) == L.LB_ESHAPE  # 4 GiB of weights
     assert lib.dense_head_matvec(A16 + 2, 8, 64, A16, A16, None) == L.LB_EALIGN
     assert lib.lowbit_matvec_batched(None, None) == L.LB_EINVAL
     h = ctypes.c_void_p()

@@ -17,7 +17,7 @@ def gpu_head(W, N, K, x):
     return host(y)
 
 
-@pytest.mark.parametrize("N,K", [(1, 8), (77, 520), (1000, 2560), (300, 4096)])
+@pytest.mark.parametrize("N,K", [(1, 8), (3, 64), (77, 520), (65, 1032), (1000, 2560), (300, 4096)])
 def test_head_shapes(N, K):
     say(f"case head N={N} K={K}")
     W = synth.head_weights(N, K, 4000 + N)
