@@ -8,16 +8,18 @@
 //  * A workgroup owns a tile of TN = 128 weight rows x TM = 64 activation rows and walks K in steps of
 //    128 columns.  Each step is software-pipelined: the packed weight codes, activation tile and
 //    activation scales of the step three ahead are loaded into a register ring while the current step
-//    computes; at the top
-//    of a step they are written to double-buffered LDS -- the weights unpacked to int8 in natural column
-//    order (shift and mask, a 4x4 byte transpose with v_perm_b32, and a v_perm_b32 lookup from code to
-//    weight byte: Q2_0 c -> c - 1, Q1_0 bit -> +/-1, planar (pos, neg) -> pos - neg) -- and one barrier
-//    per step separates the writes from the reads.
-//  * A workgroup is 8 waves (512 threads); each wave computes one 32 x 32 tile (32 weight rows x 32
-//    activation rows): per q8_0 block (32 columns, the MFMA's K depth) one A operand (weights) and one B
-//    operand (activations) from LDS, one MFMA.  Each MFMA result is one exact int32 sum per (weight row,
-//    activation row, block).  Small per-wave state keeps about four waves per SIMD resident, so one
-//    wave's rescale arithmetic overlaps another's matrix-core and LDS latency.
+//    computes; at the top of a step they are written to double-buffered LDS -- the weights unpacked to
+//    int8 in natural column order (shift and mask, a 4x4 byte transpose with v_perm_b32, and a
+//    v_perm_b32 lookup from code to weight byte: Q2_0 c -> c - 1, Q1_0 bit -> +/-1, planar (pos, neg) ->
+//    pos - neg) -- and one barrier per step separates the writes from the reads.  Waves 0-7 load and
+//    unpack the weights, waves 8-15 load the activations.
+//  * A workgroup is 16 waves (1024 threads).  Wave w computes the 32 x 32 output tile w mod 8 (32 weight
+//    rows x 32 activation rows) over one half of every step's columns: per q8_0 block (32 columns, the
+//    MFMA's K depth) one A operand (weights) and one B operand (activations) from LDS, one MFMA.  The
+//    halves split at weight-block boundaries (a Q2_0 block, half a Q1_0 block), and the second half's
+//    partial sums join the first's through LDS at the end: four waves per SIMD, so one wave's rescale
+//    arithmetic overlaps another's matrix-core, LDS and load latency.  Each MFMA result is one exact
+//    int32 sum per (weight row, activation row, block).
 //  * The accumulator input of every MFMA is a constant register tile holding 0x4B400000 (1.5 * 2^23), so
 //    each result, read as fp32, is 1.5 * 2^23 + isum exactly; one FMA with the block's activation scale
 //    and -d_x * 1.5 * 2^23 gives round(d_x * isum) without a conversion.  The weight block scale is then
@@ -31,7 +33,8 @@ namespace lb {
 
 namespace {
 
-constexpr int GT = 512;          // threads per workgroup (8 waves)
+constexpr int GT = 1024;         // threads per workgroup (16 waves)
+constexpr int GH = GT / 2;       // threads of each role (weights / activations) and of each K half
 constexpr int TN = 128;          // weight rows per workgroup
 constexpr int TM = 64;           // activation rows per workgroup
 constexpr int KS = 128;          // columns per K-step
@@ -108,13 +111,14 @@ __device__ __forceinline__ void unpack_planar_dword(uint32_t pos_bits, uint32_t 
     }
 }
 
-// What one thread carries from global memory into a K-step: a quarter of one weight row's codes for the
-// step, 16 activation bytes, and (threads < TM) the row's four activation scales.
+// What one thread carries from global memory into a K-step, by role.  Weight threads (tid < GH): a
+// quarter of one weight row's codes for the step in a.x, a.y (Q2_0: 2 code dwords; Q1_0: 1 sign dword;
+// planar: pos dword, neg dword) and the weight block scale (binary16) in a.z where the thread stores it.
+// Activation threads: 16 activation bytes in a and, for the first TM of them, the row's four binary16
+// activation scales in b.
 struct StepRegs {
-    uint2 wcode;     // Q2_0: 2 code dwords; Q1_0: 1 sign dword (.x); planar: pos dword (.x), neg dword (.y)
-    uint32_t wscale; // the weight block scale (binary16), where this thread stores it
-    uint4 x;         // 16 activation bytes
-    uint2 dx;        // 4 binary16 activation scales
+    uint4 a;
+    uint2 b;
 };
 
 template <int FMT>
@@ -123,41 +127,44 @@ __device__ __forceinline__ void load_step(StepRegs &r, const uint8_t *__restrict
                                           int M, int n0, int m0, int kk, int tid)
 {
     const int kab = min(KS, K - kk) / QK8; // activation blocks in this step
+    if (tid >= GH) { // activation threads
+        const int t = tid - GH;
+        // activation tile: 64 rows x kab * 32 bytes; thread -> (row t / 8, 16-byte chunk t % 8)
+        const int m = min(m0 + (t >> 3), M - 1), ch = t & 7;
+        if (ch < 2 * kab)
+            r.a = *reinterpret_cast<const uint4 *>(X + (int64_t)m * K + kk + 16 * ch);
+        if (FMT != LB_TERNARY_PLANAR && t < TM) {
+            const int mm = min(m0 + t, M - 1);
+            const uint16_t *pp = xsc + (int64_t)mm * (K / QK8) + kk / QK8;
+            const uint32_t h0 = pp[0], h1 = pp[1];
+            const uint32_t h2 = kab > 2 ? pp[2] : 0u, h3 = kab > 2 ? pp[3] : 0u;
+            r.b = make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
+        }
+        return;
+    }
     const int row = min(n0 + (tid >> 2), N - 1), p = tid & 3;
     if (FMT == LB_Q1_0) {
         // one 128-weight record per row; thread p takes its device sign dword p
         const int64_t idx = (int64_t)row * (K / 128) + kk / 128;
-        r.wcode.x = *reinterpret_cast<const uint32_t *>(W + idx * 16 + 4 * p);
+        r.a.x = *reinterpret_cast<const uint32_t *>(W + idx * 16 + 4 * p);
         if (p == 0)
-            r.wscale = wsc[idx];
+            r.a.z = wsc[idx];
     } else {
         // two 64-weight records per row (one on a half step); thread p takes half p & 1 of record p >> 1
         const int bb = p >> 1, hh = p & 1;
         if (2 * bb < kab) {
             const int64_t idx = (int64_t)row * (K / 64) + kk / 64 + bb;
             if (FMT == LB_TERNARY_PLANAR) {
-                r.wcode.x = *reinterpret_cast<const uint32_t *>(W + idx * 16 + 4 * hh);     // pos
-                r.wcode.y = *reinterpret_cast<const uint32_t *>(W + idx * 16 + 8 + 4 * hh); // neg
+                r.a.x = *reinterpret_cast<const uint32_t *>(W + idx * 16 + 4 * hh);     // pos
+                r.a.y = *reinterpret_cast<const uint32_t *>(W + idx * 16 + 8 + 4 * hh); // neg
             } else {
-                r.wcode = *reinterpret_cast<const uint2 *>(W + idx * 16 + 8 * hh);
+                const uint2 c2 = *reinterpret_cast<const uint2 *>(W + idx * 16 + 8 * hh);
+                r.a.x = c2.x;
+                r.a.y = c2.y;
                 if (hh == 0)
-                    r.wscale = wsc[idx];
+                    r.a.z = wsc[idx];
             }
         }
-    }
-    // activation tile: 64 rows x kab * 32 bytes; thread -> (row tid / 8, 16-byte chunk tid % 8)
-    {
-        const int m = min(m0 + (tid >> 3), M - 1), ch = tid & 7;
-        if (ch < 2 * kab)
-            r.x = *reinterpret_cast<const uint4 *>(X + (int64_t)m * K + kk + 16 * ch);
-    }
-    if (FMT != LB_TERNARY_PLANAR && tid < TM) {
-        const int m = min(m0 + tid, M - 1);
-        const uint16_t *pp = xsc + (int64_t)m * (K / QK8) + kk / QK8;
-        uint16_t hs[4] = {0, 0, 0, 0};
-        for (int j = 0; j < kab; j++)
-            hs[j] = pp[j];
-        r.dx = make_uint2((uint32_t)hs[0] | ((uint32_t)hs[1] << 16), (uint32_t)hs[2] | ((uint32_t)hs[3] << 16));
     }
 }
 
@@ -172,52 +179,56 @@ template <int FMT>
 __device__ __forceinline__ void store_step(Lds &lds, int buf, const StepRegs &r, int K, int kk, int tid)
 {
     const int kab = min(KS, K - kk) / QK8;
+    if (tid >= GH) { // activation threads
+        const int t = tid - GH;
+        const int mr = t >> 3, ch = t & 7;
+        if (ch < 2 * kab)
+            *reinterpret_cast<uint4 *>(lds.x[buf] + mr * XROW + 4 * ch) = r.a;
+        if (FMT != LB_TERNARY_PLANAR && t < TM) {
+            lds.dx[buf][0 * TM + t] = half_bits_to_float((uint16_t)(r.b.x & 0xffffu));
+            lds.dx[buf][1 * TM + t] = half_bits_to_float((uint16_t)(r.b.x >> 16));
+            lds.dx[buf][2 * TM + t] = half_bits_to_float((uint16_t)(r.b.y & 0xffffu));
+            lds.dx[buf][3 * TM + t] = half_bits_to_float((uint16_t)(r.b.y >> 16));
+        }
+        return;
+    }
     const int rr = tid >> 2, p = tid & 3;
     uint32_t *wrow = lds.w[buf] + rr * WROW;
     if (FMT == LB_Q1_0) {
         // sign dword p of the record holds 8 weights of each of the step's 4 activation blocks
         uint32_t o[8];
-        unpack_q1_dword(r.wcode.x, o);
+        unpack_q1_dword(r.a.x, o);
 #pragma unroll
         for (int j = 0; j < 4; j++)
             *reinterpret_cast<uint2 *>(wrow + 8 * j + 2 * p) = make_uint2(o[2 * j], o[2 * j + 1]);
         if (p == 0)
-            lds.dw[buf][rr] = half_bits_to_float((uint16_t)r.wscale);
+            lds.dw[buf][rr] = half_bits_to_float((uint16_t)r.a.z);
     } else {
         const int bb = p >> 1, hh = p & 1;
         if (2 * bb < kab) {
             uint32_t *dst = wrow + 16 * bb + 8 * hh;
             uint32_t o[8];
             if (FMT == LB_TERNARY_PLANAR) {
-                unpack_planar_dword(r.wcode.x, r.wcode.y, o);
+                unpack_planar_dword(r.a.x, r.a.y, o);
             } else {
-                unpack_q2_dword(r.wcode.x, o);
-                unpack_q2_dword(r.wcode.y, o + 4);
+                unpack_q2_dword(r.a.x, o);
+                unpack_q2_dword(r.a.y, o + 4);
                 if (hh == 0)
-                    lds.dw[buf][bb * TN + rr] = half_bits_to_float((uint16_t)r.wscale);
+                    lds.dw[buf][bb * TN + rr] = half_bits_to_float((uint16_t)r.a.z);
             }
             *reinterpret_cast<uint4 *>(dst) = make_uint4(o[0], o[1], o[2], o[3]);
             *reinterpret_cast<uint4 *>(dst + 4) = make_uint4(o[4], o[5], o[6], o[7]);
         }
     }
-    {
-        const int mr = tid >> 3, ch = tid & 7;
-        if (ch < 2 * kab)
-            *reinterpret_cast<uint4 *>(lds.x[buf] + mr * XROW + 4 * ch) = r.x;
-    }
-    if (FMT != LB_TERNARY_PLANAR && tid < TM) {
-        lds.dx[buf][0 * TM + tid] = half_bits_to_float((uint16_t)(r.dx.x & 0xffffu));
-        lds.dx[buf][1 * TM + tid] = half_bits_to_float((uint16_t)(r.dx.x >> 16));
-        lds.dx[buf][2 * TM + tid] = half_bits_to_float((uint16_t)(r.dx.y & 0xffffu));
-        lds.dx[buf][3 * TM + tid] = half_bits_to_float((uint16_t)(r.dx.y >> 16));
-    }
 }
 
 // One K-step of one wave: NJ activation blocks (compile-time, so the pairing of blocks into weight
 // blocks and every register index are static).
-template <int FMT, bool EMIT, int NJ>
-__device__ __forceinline__ void step_compute(const Lds &lds, int buf, int h, int l32, int wn, int wm, int m0, int n0,
-                                             int M, int N, int nab, int kk, float (&acc)[16], v16i &iacc,
+// One wave's share of a K-step: the two q8_0 blocks jb, jb + 1 (half of the step's 128 columns), which
+// lie in one weight block (a whole Q2_0 block, half a Q1_0 block).
+template <int FMT, bool EMIT>
+__device__ __forceinline__ void step_compute(const Lds &lds, int buf, int jb, int h, int l32, int wn, int wm, int m0,
+                                             int n0, int M, int N, int nab, int kk, float (&acc)[16], v16i &iacc,
                                              const v16i &cbias, int32_t *__restrict__ sums)
 {
     constexpr bool PLANAR = FMT == LB_TERNARY_PLANAR;
@@ -226,7 +237,8 @@ __device__ __forceinline__ void step_compute(const Lds &lds, int buf, int h, int
     const uint32_t *xl = lds.x[buf] + (32 * wm + l32) * XROW + 4 * h;
     float t[16];
 #pragma unroll
-    for (int j = 0; j < NJ; j++) {
+    for (int jj = 0; jj < 2; jj++) {
+        const int j = jb + jj;
         const uint4 a4 = *reinterpret_cast<const uint4 *>(wl + 8 * j);
         const uint4 b4 = *reinterpret_cast<const uint4 *>(xl + 8 * j);
         const v4i A = {(int)a4.x, (int)a4.y, (int)a4.z, (int)a4.w};
@@ -241,7 +253,7 @@ __device__ __forceinline__ void step_compute(const Lds &lds, int buf, int h, int
 #pragma unroll
         for (int i = 0; i < 16; i++) {
             const float v = fmaf(dx, __int_as_float(D[i]), c); // round(d_x * isum)
-            t[i] = (j % JW) == 0 ? v : t[i] + v;
+            t[i] = jj == 0 ? v : t[i] + v;
         }
         if (EMIT) {
             const int m = m0 + 32 * wm + l32, kb = kk / QK8 + j;
@@ -252,22 +264,22 @@ __device__ __forceinline__ void step_compute(const Lds &lds, int buf, int h, int
                     sums[((int64_t)m * N + n) * nab + kb] = D[i] - (int)BIAS;
             }
         }
-        if ((j % JW) == JW - 1) {
-            const int b = j / JW;
+    }
+    if (!PLANAR) {
+        const int b = jb / JW;
 #pragma unroll
-            for (int g = 0; g < 4; g++) {
-                const float4 dw = *reinterpret_cast<const float4 *>(lds.dw[buf] + b * TN + 32 * wn + 8 * g + 4 * h);
-                const float dwv[4] = {dw.x, dw.y, dw.z, dw.w};
+        for (int g = 0; g < 4; g++) {
+            const float4 dw = *reinterpret_cast<const float4 *>(lds.dw[buf] + b * TN + 32 * wn + 8 * g + 4 * h);
+            const float dwv[4] = {dw.x, dw.y, dw.z, dw.w};
 #pragma unroll
-                for (int q = 0; q < 4; q++)
-                    acc[4 * g + q] = fmaf(dwv[q], t[4 * g + q], acc[4 * g + q]);
-            }
+            for (int q = 0; q < 4; q++)
+                acc[4 * g + q] = fmaf(dwv[q], t[4 * g + q], acc[4 * g + q]);
         }
     }
 }
 
 template <int FMT, bool EMIT>
-__global__ __launch_bounds__(GT, 2) void gemm_kernel(const uint8_t *__restrict__ W, int N, int K, float w_scale,
+__global__ __launch_bounds__(GT, 1) void gemm_kernel(const uint8_t *__restrict__ W, int N, int K, float w_scale,
                                                      const int8_t *__restrict__ X, const void *__restrict__ Xscale,
                                                      int M, float *__restrict__ Y, int32_t *__restrict__ sums)
 {
@@ -276,7 +288,9 @@ __global__ __launch_bounds__(GT, 2) void gemm_kernel(const uint8_t *__restrict__
     constexpr bool PLANAR = FMT == LB_TERNARY_PLANAR;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int h = lane >> 5, l32 = lane & 31;
-    const int wn = wave & 3, wm = wave >> 2; // this wave's 32 x 32 tile inside the 128 x 64 workgroup tile
+    // this wave's 32 x 32 tile inside the 128 x 64 workgroup tile, and its half of each step's columns
+    const int ti = wave & 7, kh = wave >> 3;
+    const int wn = ti & 3, wm = ti >> 2;
     const int n0 = blockIdx.x * TN, m0 = blockIdx.y * TM;
     const int nrec = FMT == LB_Q1_0 ? K / 128 : K / 64; // 16-byte records per weight row
     const int nab = K / QK8;                             // activation blocks per row
@@ -305,7 +319,7 @@ __global__ __launch_bounds__(GT, 2) void gemm_kernel(const uint8_t *__restrict__
     auto step_k = [&](int s) { return ((s + rot) % nsteps) * KS; };
 
     // register ring: the loads of step s + PF are issued while step s computes
-    constexpr int PF = 2;
+    constexpr int PF = 3;
     StepRegs ring[PF];
 #pragma unroll
     for (int p = 0; p < PF; p++)
@@ -323,11 +337,31 @@ __global__ __launch_bounds__(GT, 2) void gemm_kernel(const uint8_t *__restrict__
             ring[p] = ring[p + 1];
         if (s + PF < nsteps)
             load_step<FMT>(ring[PF - 1], W, wsc, N, K, X, xsc, M, n0, m0, step_k(s + PF), tid);
-        if (kab == KS / QK8)
-            step_compute<FMT, EMIT, KS / QK8>(lds, buf, h, l32, wn, wm, m0, n0, M, N, nab, kk, acc, iacc, cbias, sums);
+        // a full step: each K half takes two blocks; a half step (the K tail of Q2_0 / planar): the first
+        // half takes both (uniform per wave)
+        if (kab == KS / QK8 || kh == 0)
+            step_compute<FMT, EMIT>(lds, buf, kab == KS / QK8 ? 2 * kh : 0, h, l32, wn, wm, m0, n0, M, N, nab, kk, acc,
+                                    iacc, cbias, sums);
+    }
+
+    // the second K half hands its partial sums to the first through LDS (the weight buffers are free now)
+    __syncthreads();
+    uint32_t *red = lds.w[0];
+    if (kh == 1) {
+#pragma unroll
+        for (int i = 0; i < 16; i++)
+            red[(ti * 16 + i) * 64 + lane] = PLANAR ? (uint32_t)iacc[i] : __float_as_uint(acc[i]);
+    }
+    __syncthreads();
+    if (kh == 1)
+        return;
+#pragma unroll
+    for (int i = 0; i < 16; i++) {
+        const uint32_t o = red[(ti * 16 + i) * 64 + lane];
+        if (PLANAR)
+            iacc[i] += (int)o;
         else
-            step_compute<FMT, EMIT, KS / QK8 / 2>(lds, buf, h, l32, wn, wm, m0, n0, M, N, nab, kk, acc, iacc, cbias,
-                                                  sums);
+            acc[i] += __uint_as_float(o);
     }
 
     // store: lane holds weight rows n = 32 wn + 8 (i / 4) + 4 h + i % 4 of activation row m = 32 wm + l32
