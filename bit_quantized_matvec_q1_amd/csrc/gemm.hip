@@ -11,8 +11,8 @@
 //    computes; at the top of a step they are written to double-buffered LDS -- the weights unpacked to
 //    int8 in natural column order (shift and mask, a 4x4 byte transpose with v_perm_b32, and a
 //    v_perm_b32 lookup from code to weight byte: Q2_0 c -> c - 1, Q1_0 bit -> +/-1, planar (pos, neg) ->
-//    pos - neg) -- and one barrier per step separates the writes from the reads.  Waves 0-7 load and
-//    unpack the weights, waves 8-15 load the activations.
+//    pos - neg) -- and one barrier per step separates the writes from the reads.  Every thread loads and
+//    unpacks an equal share of the weight tile and copies an equal share of the activation tile.
 //  * A workgroup is 16 waves (1024 threads).  Wave w computes the 32 x 32 output tile w mod 8 (32 weight
 //    rows x 32 activation rows) over one half of every step's columns: per q8_0 block (32 columns, the
 //    MFMA's K depth) one A operand (weights) and one B operand (activations) from LDS, one MFMA.  The
@@ -34,7 +34,6 @@ namespace lb {
 namespace {
 
 constexpr int GT = 1024;         // threads per workgroup (16 waves)
-constexpr int GH = GT / 2;       // threads of each role (weights / activations) and of each K half
 constexpr int TN = 128;          // weight rows per workgroup
 constexpr int TM = 64;           // activation rows per workgroup
 constexpr int KS = 128;          // columns per K-step
@@ -74,51 +73,15 @@ __device__ __forceinline__ void unpack_q2_dword(uint32_t v, uint32_t *out)
     transpose4(e[0], e[1], e[2], e[3], out);
 }
 
-// Q1_0: one device sign dword m of a record (the sign of weight 32r + 8m + k at bit 4k + r) -> for each
-// activation block r, the 8 int8 weights 32r + 8m .. 32r + 8m + 7 as two dwords out[2r], out[2r + 1].
-// A byte table maps each 0/1 selector to -1/+1; byte t of e[s] is then the weight of bit 8t + s, i.e.
-// k = 2t + (s >> 2) of block r = s & 3, and one byte interleave per half puts k in order.
-__device__ __forceinline__ void unpack_q1_dword(uint32_t v, uint32_t *out)
-{
-    const uint32_t lut = 0x000001FFu; // 0 -> -1, 1 -> +1
-    uint32_t e[8];
-#pragma unroll
-    for (int s = 0; s < 8; s++)
-        e[s] = perm(0u, lut, (v >> s) & 0x01010101u);
-#pragma unroll
-    for (int r = 0; r < 4; r++) {
-        out[2 * r] = perm(e[r + 4], e[r], 0x05010400u);     // k = 0, 1, 2, 3
-        out[2 * r + 1] = perm(e[r + 4], e[r], 0x07030602u); // k = 4, 5, 6, 7
-    }
-}
-
-// Planar: 32 plane bits -> 8 dwords of int8 weights in order, via a byte table indexed by the
-// pos | neg << 1 selector of each weight.
-__device__ __forceinline__ void unpack_planar_dword(uint32_t pos_bits, uint32_t neg_bits, uint32_t *out)
-{
-    const uint32_t lut = 0x00FF0100u; // 00 -> 0, 01 -> +1, 10 -> -1, 11 -> 0
-    uint32_t e[8];
-#pragma unroll
-    for (int r = 0; r < 8; r++)
-        e[r] = perm(0u, lut, ((pos_bits >> r) & 0x01010101u) | (((neg_bits >> r) & 0x01010101u) << 1));
-    uint32_t t0[4], t1[4];
-    transpose4(e[0], e[1], e[2], e[3], t0);
-    transpose4(e[4], e[5], e[6], e[7], t1);
-#pragma unroll
-    for (int t = 0; t < 4; t++) {
-        out[2 * t] = t0[t];
-        out[2 * t + 1] = t1[t];
-    }
-}
-
-// What one thread carries from global memory into a K-step, by role.  Weight threads (tid < GH): a
-// quarter of one weight row's codes for the step in a.x, a.y (Q2_0: 2 code dwords; Q1_0: 1 sign dword;
-// planar: pos dword, neg dword) and the weight block scale (binary16) in a.z where the thread stores it.
-// Activation threads: 16 activation bytes in a and, for the first TM of them, the row's four binary16
-// activation scales in b.
+// What one thread carries from global memory into a K-step.  Every thread takes one share of the weight
+// tile -- Q2_0: one code dword (16 weights); Q1_0: one sign dword, of which it builds two of the four
+// activation blocks; planar: one (pos, neg) dword pair, of which it builds half -- in a.x (planar neg in
+// a.y, the weight block scale's binary16 in a.z where the thread stores it), 8 activation bytes in b,
+// and, for the first TM threads, the four binary16 activation scales of one activation row in c.
 struct StepRegs {
     uint4 a;
     uint2 b;
+    uint2 c;
 };
 
 template <int FMT>
@@ -126,45 +89,39 @@ __device__ __forceinline__ void load_step(StepRegs &r, const uint8_t *__restrict
                                           int N, int K, const int8_t *__restrict__ X, const uint16_t *__restrict__ xsc,
                                           int M, int n0, int m0, int kk, int tid)
 {
+    // Every load is unconditional, its index clamped into the tensor: on a half step (the K tail) the
+    // shares past the row's end re-read its last block and are not stored.  The registers are filled
+    // straight from memory, so nothing waits on them until the step is stored.
     const int kab = min(KS, K - kk) / QK8; // activation blocks in this step
-    if (tid >= GH) { // activation threads
-        const int t = tid - GH;
-        // activation tile: 64 rows x kab * 32 bytes; thread -> (row t / 8, 16-byte chunk t % 8)
-        const int m = min(m0 + (t >> 3), M - 1), ch = t & 7;
-        if (ch < 2 * kab)
-            r.a = *reinterpret_cast<const uint4 *>(X + (int64_t)m * K + kk + 16 * ch);
-        if (FMT != LB_TERNARY_PLANAR && t < TM) {
-            const int mm = min(m0 + t, M - 1);
-            const uint16_t *pp = xsc + (int64_t)mm * (K / QK8) + kk / QK8;
-            const uint32_t h0 = pp[0], h1 = pp[1];
-            const uint32_t h2 = kab > 2 ? pp[2] : 0u, h3 = kab > 2 ? pp[3] : 0u;
-            r.b = make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
-        }
-        return;
+    // activation tile: 64 rows x kab * 32 bytes; thread -> (row tid / 16, 8-byte chunk tid % 16)
+    {
+        const int m = min(m0 + (tid >> 4), M - 1), ch = min(tid & 15, 4 * kab - 1);
+        r.b = *reinterpret_cast<const uint2 *>(X + (int64_t)m * K + kk + 8 * ch);
     }
-    const int row = min(n0 + (tid >> 2), N - 1), p = tid & 3;
+    if (FMT != LB_TERNARY_PLANAR && tid < TM) { // one activation row's four block scales
+        const int mm = min(m0 + (tid & (TM - 1)), M - 1);
+        const uint32_t *pp = reinterpret_cast<const uint32_t *>(xsc + (int64_t)mm * (K / QK8) + kk / QK8);
+        r.c.x = pp[0];                 // blocks 0, 1 (4-byte aligned: K / 32 and kk / 32 are even)
+        r.c.y = pp[kab > 2 ? 1 : 0];   // blocks 2, 3 (unused on a half step)
+    }
+    const int row = min(n0 + (tid >> 3), N - 1), p = tid & 7;
     if (FMT == LB_Q1_0) {
-        // one 128-weight record per row; thread p takes its device sign dword p
+        // one 128-weight record per row and step; thread p takes sign dword p / 2
         const int64_t idx = (int64_t)row * (K / 128) + kk / 128;
-        r.a.x = *reinterpret_cast<const uint32_t *>(W + idx * 16 + 4 * p);
-        if (p == 0)
-            r.a.z = wsc[idx];
+        r.a.x = *reinterpret_cast<const uint32_t *>(W + idx * 16 + 4 * (p >> 1));
+        r.a.z = wsc[idx];
+    } else if (FMT == LB_Q2_0_G64) {
+        // two 64-weight records per row (one on a half step); thread p takes dword p % 4 of record p / 4
+        const int bb = min(p >> 2, kab / 2 - 1), d = p & 3;
+        const int64_t idx = (int64_t)row * (K / 64) + kk / 64 + bb;
+        r.a.x = *reinterpret_cast<const uint32_t *>(W + idx * 16 + 4 * d);
+        r.a.z = wsc[idx];
     } else {
-        // two 64-weight records per row (one on a half step); thread p takes half p & 1 of record p >> 1
-        const int bb = p >> 1, hh = p & 1;
-        if (2 * bb < kab) {
-            const int64_t idx = (int64_t)row * (K / 64) + kk / 64 + bb;
-            if (FMT == LB_TERNARY_PLANAR) {
-                r.a.x = *reinterpret_cast<const uint32_t *>(W + idx * 16 + 4 * hh);     // pos
-                r.a.y = *reinterpret_cast<const uint32_t *>(W + idx * 16 + 8 + 4 * hh); // neg
-            } else {
-                const uint2 c2 = *reinterpret_cast<const uint2 *>(W + idx * 16 + 8 * hh);
-                r.a.x = c2.x;
-                r.a.y = c2.y;
-                if (hh == 0)
-                    r.a.z = wsc[idx];
-            }
-        }
+        // two 64-column beats per row; thread p takes the (pos, neg) dword pair (p / 2) % 2 of beat p / 4
+        const int bb = min(p >> 2, kab / 2 - 1), hh = (p >> 1) & 1;
+        const int64_t idx = (int64_t)row * (K / 64) + kk / 64 + bb;
+        r.a.x = *reinterpret_cast<const uint32_t *>(W + idx * 16 + 4 * hh);     // pos
+        r.a.y = *reinterpret_cast<const uint32_t *>(W + idx * 16 + 8 + 4 * hh); // neg
     }
 }
 
@@ -179,51 +136,64 @@ template <int FMT>
 __device__ __forceinline__ void store_step(Lds &lds, int buf, const StepRegs &r, int K, int kk, int tid)
 {
     const int kab = min(KS, K - kk) / QK8;
-    if (tid >= GH) { // activation threads
-        const int t = tid - GH;
-        const int mr = t >> 3, ch = t & 7;
-        if (ch < 2 * kab)
-            *reinterpret_cast<uint4 *>(lds.x[buf] + mr * XROW + 4 * ch) = r.a;
-        if (FMT != LB_TERNARY_PLANAR && t < TM) {
-            lds.dx[buf][0 * TM + t] = half_bits_to_float((uint16_t)(r.b.x & 0xffffu));
-            lds.dx[buf][1 * TM + t] = half_bits_to_float((uint16_t)(r.b.x >> 16));
-            lds.dx[buf][2 * TM + t] = half_bits_to_float((uint16_t)(r.b.y & 0xffffu));
-            lds.dx[buf][3 * TM + t] = half_bits_to_float((uint16_t)(r.b.y >> 16));
-        }
-        return;
+    {
+        const int mr = tid >> 4, ch = tid & 15;
+        if (ch < 4 * kab)
+            *reinterpret_cast<uint2 *>(lds.x[buf] + mr * XROW + 2 * ch) = r.b;
     }
-    const int rr = tid >> 2, p = tid & 3;
+    if (FMT != LB_TERNARY_PLANAR && tid < TM) {
+        // (on a half step the values of blocks 2 and 3 are not read)
+        lds.dx[buf][0 * TM + tid] = half_bits_to_float((uint16_t)(r.c.x & 0xffffu));
+        lds.dx[buf][1 * TM + tid] = half_bits_to_float((uint16_t)(r.c.x >> 16));
+        lds.dx[buf][2 * TM + tid] = half_bits_to_float((uint16_t)(r.c.y & 0xffffu));
+        lds.dx[buf][3 * TM + tid] = half_bits_to_float((uint16_t)(r.c.y >> 16));
+    }
+    const int rr = tid >> 3, p = tid & 7;
     uint32_t *wrow = lds.w[buf] + rr * WROW;
     if (FMT == LB_Q1_0) {
-        // sign dword p of the record holds 8 weights of each of the step's 4 activation blocks
-        uint32_t o[8];
-        unpack_q1_dword(r.a.x, o);
+        // sign dword m holds 8 weights of each activation block; this thread builds blocks 2 hb, 2 hb + 1
+        const int m = p >> 1, hb = p & 1;
+        const uint32_t v = r.a.x, lut = 0x000001FFu; // 0 -> -1, 1 -> +1
 #pragma unroll
-        for (int j = 0; j < 4; j++)
-            *reinterpret_cast<uint2 *>(wrow + 8 * j + 2 * p) = make_uint2(o[2 * j], o[2 * j + 1]);
+        for (int q = 0; q < 2; q++) {
+            const int j = 2 * hb + q;
+            const uint32_t e0 = __builtin_amdgcn_perm(0u, lut, (v >> j) & 0x01010101u);       // k = 0, 2, 4, 6
+            const uint32_t e1 = __builtin_amdgcn_perm(0u, lut, (v >> (j + 4)) & 0x01010101u); // k = 1, 3, 5, 7
+            *reinterpret_cast<uint2 *>(wrow + 8 * j + 2 * m) =
+                make_uint2(__builtin_amdgcn_perm(e1, e0, 0x05010400u), __builtin_amdgcn_perm(e1, e0, 0x07030602u));
+        }
         if (p == 0)
             lds.dw[buf][rr] = half_bits_to_float((uint16_t)r.a.z);
-    } else {
-        const int bb = p >> 1, hh = p & 1;
+    } else if (FMT == LB_Q2_0_G64) {
+        const int bb = p >> 2, d = p & 3;
         if (2 * bb < kab) {
-            uint32_t *dst = wrow + 16 * bb + 8 * hh;
-            uint32_t o[8];
-            if (FMT == LB_TERNARY_PLANAR) {
-                unpack_planar_dword(r.a.x, r.a.y, o);
-            } else {
-                unpack_q2_dword(r.a.x, o);
-                unpack_q2_dword(r.a.y, o + 4);
-                if (hh == 0)
-                    lds.dw[buf][bb * TN + rr] = half_bits_to_float((uint16_t)r.a.z);
+            uint32_t o[4];
+            unpack_q2_dword(r.a.x, o);
+            *reinterpret_cast<uint4 *>(wrow + 16 * bb + 4 * d) = make_uint4(o[0], o[1], o[2], o[3]);
+            if (d == 0)
+                lds.dw[buf][bb * TN + rr] = half_bits_to_float((uint16_t)r.a.z);
+        }
+    } else {
+        const int bb = p >> 2, hh = (p >> 1) & 1, sub = p & 1;
+        if (2 * bb < kab) {
+            // bits 4 sub .. 4 sub + 3 of each byte: weights 8 t + 4 sub + s of the dword pair's 32
+            const uint32_t lut = 0x00FF0100u; // (pos, neg): 00 -> 0, 01 -> +1, 10 -> -1, 11 -> 0
+            uint32_t e[4];
+#pragma unroll
+            for (int s = 0; s < 4; s++) {
+                const int rb = 4 * sub + s;
+                e[s] = __builtin_amdgcn_perm(0u, lut, ((r.a.x >> rb) & 0x01010101u) | (((r.a.y >> rb) & 0x01010101u) << 1));
             }
-            *reinterpret_cast<uint4 *>(dst) = make_uint4(o[0], o[1], o[2], o[3]);
-            *reinterpret_cast<uint4 *>(dst + 4) = make_uint4(o[4], o[5], o[6], o[7]);
+            uint32_t t[4];
+            transpose4(e[0], e[1], e[2], e[3], t);
+            uint32_t *dst = wrow + 16 * bb + 8 * hh;
+#pragma unroll
+            for (int q = 0; q < 4; q++)
+                dst[2 * q + sub] = t[q];
         }
     }
 }
 
-// One K-step of one wave: NJ activation blocks (compile-time, so the pairing of blocks into weight
-// blocks and every register index are static).
 // One wave's share of a K-step: the two q8_0 blocks jb, jb + 1 (half of the step's 128 columns), which
 // lie in one weight block (a whole Q2_0 block, half a Q1_0 block).
 template <int FMT, bool EMIT>
@@ -318,25 +288,29 @@ __global__ __launch_bounds__(GT, 1) void gemm_kernel(const uint8_t *__restrict__
     const int rot = blockIdx.x % nsteps;
     auto step_k = [&](int s) { return ((s + rot) % nsteps) * KS; };
 
-    // register ring: the loads of step s + PF are issued while step s computes
+    // register ring: the loads of step s + PF are issued into the slot step s frees; the step loop is
+    // unrolled by the ring length so every slot is a fixed set of registers and the compiler can wait
+    // for exactly the oldest step's loads
     constexpr int PF = 3;
     StepRegs ring[PF];
 #pragma unroll
     for (int p = 0; p < PF; p++)
-        if (p < nsteps)
-            load_step<FMT>(ring[p], W, wsc, N, K, X, xsc, M, n0, m0, step_k(p), tid);
+        load_step<FMT>(ring[p], W, wsc, N, K, X, xsc, M, n0, m0, step_k(min(p, nsteps - 1)), tid);
 
-    int buf = 0;
-    for (int s = 0; s < nsteps; s++, buf ^= 1) {
+    for (int s0 = 0; s0 < nsteps; s0 += PF)
+#pragma unroll
+    for (int q = 0; q < PF; q++) {
+        const int s = s0 + q;
+        if (s >= nsteps) // uniform
+            break;
+        const int buf = s & 1;
         const int kk = step_k(s);
         const int kab = min(KS, K - kk) / QK8;
-        store_step<FMT>(lds, buf, ring[0], K, kk, tid);
+        store_step<FMT>(lds, buf, ring[q], K, kk, tid);
         __syncthreads();
-#pragma unroll
-        for (int p = 0; p + 1 < PF; p++)
-            ring[p] = ring[p + 1];
-        if (s + PF < nsteps)
-            load_step<FMT>(ring[PF - 1], W, wsc, N, K, X, xsc, M, n0, m0, step_k(s + PF), tid);
+        // unconditional (the last steps re-load the final step, unused): a load under a branch would make
+        // the compiler wait for every outstanding load at the next store instead of only this slot's
+        load_step<FMT>(ring[q], W, wsc, N, K, X, xsc, M, n0, m0, step_k(min(s + PF, nsteps - 1)), tid);
         // a full step: each K half takes two blocks; a half step (the K tail of Q2_0 / planar): the first
         // half takes both (uniform per wave)
         if (kab == KS / QK8 || kh == 0)
