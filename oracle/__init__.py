@@ -4,7 +4,7 @@ Only ``tests/``, ``__graft_entry__.smoke()`` and ``bench.py``'s ``cpu_baseline``
 package.  It wraps ``lowbit_oracle.c`` (plain scalar C, single-threaded, built with gcc
 ``-O2 -ffp-contract=off``) through ctypes and shares nothing with the HIP library.
 
-Parity unpinned: ggml's exact fp32 operation order for the Q1_0/Q2_0_g64 outputs and the absolute
+Parity unpinned: ggml's exact fp32 operation order for the Q1_0/Q2_0_g64/Q8_0 outputs and the absolute
 Q1_0 sign polarity relative to ggml (bit 1 is read as +1 here); everything else is pinned by
 ``tests/test_oracle_*.py``.
 """
@@ -20,7 +20,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "lowbit_oracle.c")
 _LIB = os.path.join(_HERE, "liblowbit_oracle.so")
 
-Q1_0, Q2_0_G64, TERNARY_PLANAR = 1, 2, 3
+Q1_0, Q2_0_G64, TERNARY_PLANAR, Q8_0 = 1, 2, 3, 4
 QK8 = 32
 
 CFLAGS = ["-O2", "-std=c99", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared", "-Wall"]

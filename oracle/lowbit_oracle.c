@@ -11,7 +11,8 @@
  *   [TR]  "bankml: verified low-bit inference on commodity CPUs -- a technical report"
  *         (bankml docs/TECHNICAL.md), sections III.2, III.3, III.5, III.8.
  *   [ARCH] tritium "Architecture" page, sections 1, 2, 4.1, 5, 8.
- *   [BH]  bankml BUILD_HISTORY.md, checklist "P2 -- own the kernels".
+ *   [BH]  bankml BUILD_HISTORY.md, checklist "P2 -- own the kernels", and the 0.3.9 entry (ggml's q8_0
+ *         quantizer and vec_dot_q8_0_q8_0 for the KV cache; "Q8_0 weights" among what remains).
  *
  * What it computes, and in which precision:
  *   - block decode to one small integer per weight (the tritsim approach: one i8 per weight, [ARCH] s.5);
@@ -20,7 +21,8 @@
  *   - exact integer per-block sums (int64 arithmetic, checked to fit int32), computed three ways
  *     (multiply, select, offset) that must agree ([TR] III.8; [BH]);
  *   - the ggml-format outputs y = sum_b d_w[b] * sum_{j in b} d_x[j] * isum[j] in fp64 (every term is
- *     exact in fp64; only the additions round);
+ *     exact in fp64; only the additions round) -- Q1_0, Q2_0_g64, and Q8_0 weights against q8_0
+ *     activations (vec_dot_q8_0_q8_0 of [BH] 0.3.9: one block of 32 on each side, one scale each);
  *   - the planar output ((float)acc * s_x) * s_w in fp32 with two roundings ([ARCH] s.5 names the
  *     twice-multiplied order);
  *   - the dense bf16 head y = sum_k bf16(W) * x in fp64 (every product exact).
@@ -37,8 +39,9 @@
 #define QK2 64  /* weights per Q2_0_g64 block ([TR] III.5) */
 #define QKP 64  /* columns per planar beat  ([ARCH] s.2) */
 #define QK8 32  /* activations per q8_0 block ([TR] III.2) */
+#define QKW8 32 /* weights per Q8_0 weight block: the q8_0 block of [TR] III.2 applied to weights ([BH] 0.3.9) */
 
-enum { FMT_Q1_0 = 1, FMT_Q2_0_G64 = 2, FMT_PLANAR = 3 };
+enum { FMT_Q1_0 = 1, FMT_Q2_0_G64 = 2, FMT_PLANAR = 3, FMT_Q8_0 = 4 };
 
 /* ------------------------------------------------------------------------------------------------
  * binary16 and bfloat16 conversions ([TR] III.2: the scale is "a 16-bit IEEE 754 half-precision" value)
@@ -117,13 +120,17 @@ static uint64_t le64(const uint8_t *p)
 
 int64_t lbo_block_weights(int fmt)
 {
-    return fmt == FMT_Q1_0 ? QK1 : fmt == FMT_Q2_0_G64 ? QK2 : fmt == FMT_PLANAR ? QKP : 0;
+    return fmt == FMT_Q1_0 ? QK1 : fmt == FMT_Q2_0_G64 ? QK2 : fmt == FMT_PLANAR ? QKP : fmt == FMT_Q8_0 ? QKW8 : 0;
 }
 
+/* Q8_0: a binary16 scale and 32 signed bytes, 34 bytes per 32 weights (8.5 bits per weight) */
 int64_t lbo_block_bytes(int fmt)
 {
-    return fmt == FMT_Q1_0 ? 2 + QK1 / 8 : fmt == FMT_Q2_0_G64 ? 2 + QK2 / 4 : fmt == FMT_PLANAR ? 16 : 0;
+    return fmt == FMT_Q1_0 ? 2 + QK1 / 8 : fmt == FMT_Q2_0_G64 ? 2 + QK2 / 4 : fmt == FMT_PLANAR ? 16
+         : fmt == FMT_Q8_0 ? 2 + QKW8 : 0;
 }
+
+static int is_ggml(int fmt) { return fmt == FMT_Q1_0 || fmt == FMT_Q2_0_G64 || fmt == FMT_Q8_0; }
 
 int64_t lbo_weight_bytes(int fmt, int64_t N, int64_t K)
 {
@@ -145,6 +152,16 @@ static int q1_weight(const uint8_t *blk, int i) { return ((blk[2 + (i >> 3)] >> 
  * lowest bits first; the weight is (c - 1) * d, c - 1 in {-1, 0, +1, +2}. */
 static int q2_code(const uint8_t *blk, int i) { return (blk[2 + (i >> 2)] >> (2 * (i & 3))) & 3; }
 
+/* Q8_0 ([TR] III.2, the q8_0 block: a half-precision scale, then 32 signed bytes): weight i is d * (int8)
+ * byte i of the block's payload. */
+static int q8_weight(const uint8_t *blk, int i) { return (int)(int8_t)blk[2 + i]; }
+
+/* The integer value of weight i of a ggml-format block. */
+static int ggml_weight(int fmt, const uint8_t *blk, int i)
+{
+    return fmt == FMT_Q1_0 ? q1_weight(blk, i) : fmt == FMT_Q2_0_G64 ? q2_code(blk, i) - 1 : q8_weight(blk, i);
+}
+
 /* planar ([ARCH] s.2): beat = {u64 pos, u64 neg}; column c is bit c of each plane; weight = pos - neg
  * (a column with both bits set reads 0 -- the pages leave that pattern undefined). */
 static int planar_weight(const uint8_t *beat, int c)
@@ -165,8 +182,7 @@ int lbo_decode(int fmt, const uint8_t *raw, int64_t N, int64_t K, int8_t *w, flo
         for (int64_t b = 0; b < nb; b++) {
             const uint8_t *blk = raw + (r * nb + b) * bb;
             for (int i = 0; i < qk; i++) {
-                int v = fmt == FMT_Q1_0 ? q1_weight(blk, i) : fmt == FMT_Q2_0_G64 ? q2_code(blk, i) - 1
-                                                                                  : planar_weight(blk, i);
+                int v = fmt == FMT_PLANAR ? planar_weight(blk, i) : ggml_weight(fmt, blk, i);
                 w[r * K + b * qk + i] = (int8_t)v;
             }
             if (d && fmt != FMT_PLANAR)
@@ -201,7 +217,9 @@ int lbo_encode(int fmt, const int8_t *w, const uint16_t *dh, int64_t N, int64_t 
             blk[0] = (uint8_t)(dh[r * nb + b] & 0xff);
             blk[1] = (uint8_t)(dh[r * nb + b] >> 8);
             for (int i = 0; i < qk; i++) {
-                if (fmt == FMT_Q1_0) {
+                if (fmt == FMT_Q8_0) {
+                    blk[2 + i] = (uint8_t)wb[i]; /* two's complement byte */
+                } else if (fmt == FMT_Q1_0) {
                     if (wb[i] != 1 && wb[i] != -1)
                         return -1;
                     if (wb[i] == 1)
@@ -287,7 +305,7 @@ int lbo_block_sums_multiply(int fmt, const uint8_t *raw, int64_t N, int64_t K, c
                             const int64_t *rows, int64_t nrows, int32_t *isum)
 {
     int64_t qk = lbo_block_weights(fmt), bb = lbo_block_bytes(fmt);
-    if ((fmt != FMT_Q1_0 && fmt != FMT_Q2_0_G64) || K % qk)
+    if (!is_ggml(fmt) || K % qk)
         return -1;
     int64_t nb = K / qk;
     for (int64_t t = 0; t < nrows; t++) {
@@ -299,7 +317,7 @@ int lbo_block_sums_multiply(int fmt, const uint8_t *raw, int64_t N, int64_t K, c
             for (int i = 0; i < QK8; i++) {
                 int64_t k = j * QK8 + i;
                 const uint8_t *blk = raw + (r * nb + k / qk) * bb;
-                int wv = fmt == FMT_Q1_0 ? q1_weight(blk, (int)(k % qk)) : q2_code(blk, (int)(k % qk)) - 1;
+                int wv = ggml_weight(fmt, blk, (int)(k % qk));
                 acc += (int64_t)wv * (int64_t)q[k];
             }
             if (acc > INT32_MAX || acc < INT32_MIN)
@@ -310,12 +328,14 @@ int lbo_block_sums_multiply(int fmt, const uint8_t *raw, int64_t N, int64_t K, c
     return 0;
 }
 
-/* select form: add the activation where the weight is +1, subtract it where -1, skip 0, add twice for +2. */
+/* select form: add the activation where the weight is +1, subtract it where -1, skip 0, add twice for +2.
+ * Q8_0 (a weight is any signed byte): the sign-and-add form of [TR] III.8 -- add |w| copies of the
+ * activation carrying the weight's sign (the activation negated where w < 0, skipped where w = 0). */
 int lbo_block_sums_select(int fmt, const uint8_t *raw, int64_t N, int64_t K, const int8_t *q,
                           const int64_t *rows, int64_t nrows, int32_t *isum)
 {
     int64_t qk = lbo_block_weights(fmt), bb = lbo_block_bytes(fmt);
-    if ((fmt != FMT_Q1_0 && fmt != FMT_Q2_0_G64) || K % qk)
+    if (!is_ggml(fmt) || K % qk)
         return -1;
     int64_t nb = K / qk;
     for (int64_t t = 0; t < nrows; t++) {
@@ -328,7 +348,13 @@ int lbo_block_sums_select(int fmt, const uint8_t *raw, int64_t N, int64_t K, con
                 int64_t k = j * QK8 + i;
                 const uint8_t *blk = raw + (r * nb + k / qk) * bb;
                 int i_in = (int)(k % qk);
-                if (fmt == FMT_Q1_0) {
+                if (fmt == FMT_Q8_0) {
+                    int wv = (int)(int8_t)blk[2 + i_in];
+                    int mag = wv < 0 ? -wv : wv;
+                    int64_t signed_q = wv < 0 ? -(int64_t)q[k] : wv > 0 ? (int64_t)q[k] : 0;
+                    for (int c = 0; c < mag; c++)
+                        plus += signed_q;
+                } else if (fmt == FMT_Q1_0) {
                     if ((blk[2 + (i_in >> 3)] >> (i_in & 7)) & 1)
                         plus += q[k];
                     else
@@ -352,12 +378,14 @@ int lbo_block_sums_select(int fmt, const uint8_t *raw, int64_t N, int64_t K, con
     return 0;
 }
 
-/* offset form: Q2_0 sum c*q - sum q (stored code c = w + 1); Q1_0 2 * sum_{bit=1} q - sum q. */
+/* offset form: Q2_0 sum c*q - sum q (stored code c = w + 1); Q1_0 2 * sum_{bit=1} q - sum q; Q8_0 the
+ * same offset idea on a byte, sum (w + 128) * q - 128 * sum q (the unsigned code u = w + 128 of [TR] III.8's
+ * offset form). */
 int lbo_block_sums_offset(int fmt, const uint8_t *raw, int64_t N, int64_t K, const int8_t *q,
                           const int64_t *rows, int64_t nrows, int32_t *isum)
 {
     int64_t qk = lbo_block_weights(fmt), bb = lbo_block_bytes(fmt);
-    if ((fmt != FMT_Q1_0 && fmt != FMT_Q2_0_G64) || K % qk)
+    if (!is_ggml(fmt) || K % qk)
         return -1;
     int64_t nb = K / qk;
     for (int64_t t = 0; t < nrows; t++) {
@@ -373,10 +401,12 @@ int lbo_block_sums_offset(int fmt, const uint8_t *raw, int64_t N, int64_t K, con
                 sq += q[k];
                 if (fmt == FMT_Q1_0)
                     sel += ((blk[2 + (i_in >> 3)] >> (i_in & 7)) & 1) * (int64_t)q[k];
-                else
+                else if (fmt == FMT_Q2_0_G64)
                     sel += ((blk[2 + (i_in >> 2)] >> (2 * (i_in & 3))) & 3) * (int64_t)q[k];
+                else
+                    sel += ((int64_t)(int8_t)blk[2 + i_in] + 128) * (int64_t)q[k];
             }
-            int64_t acc = fmt == FMT_Q1_0 ? 2 * sel - sq : sel - sq;
+            int64_t acc = fmt == FMT_Q1_0 ? 2 * sel - sq : fmt == FMT_Q2_0_G64 ? sel - sq : sel - 128 * sq;
             if (acc > INT32_MAX || acc < INT32_MIN)
                 return -2;
             isum[t * (K / QK8) + j] = (int32_t)acc;
@@ -398,7 +428,7 @@ int lbo_matvec_q(int fmt, const uint8_t *raw, int64_t N, int64_t K, const int8_t
                  const int64_t *rows, int64_t nrows, double *y, double *A)
 {
     int64_t qk = lbo_block_weights(fmt), bb = lbo_block_bytes(fmt);
-    if ((fmt != FMT_Q1_0 && fmt != FMT_Q2_0_G64) || K % qk)
+    if (!is_ggml(fmt) || K % qk)
         return -1;
     int64_t nb = K / qk, per = qk / QK8;
     int32_t isum_blk[QK1 / QK8];
@@ -413,7 +443,7 @@ int lbo_matvec_q(int fmt, const uint8_t *raw, int64_t N, int64_t K, const int8_t
                 int64_t s = 0;
                 for (int i = 0; i < QK8; i++) {
                     int wi = (int)(jj * QK8 + i);
-                    int wv = fmt == FMT_Q1_0 ? q1_weight(blk, wi) : q2_code(blk, wi) - 1;
+                    int wv = ggml_weight(fmt, blk, wi);
                     s += (int64_t)wv * q[b * qk + wi];
                 }
                 isum_blk[jj] = (int32_t)s;
@@ -421,7 +451,8 @@ int lbo_matvec_q(int fmt, const uint8_t *raw, int64_t N, int64_t K, const int8_t
             double dw = (double)lbo_half_to_float(le16(blk));
             for (int64_t jj = 0; jj < per; jj++) {
                 double dx = (double)lbo_half_to_float(dxh[b * per + jj]);
-                double term = dw * dx * (double)isum_blk[jj]; /* exact: 11 + 11 + 14 significant bits */
+                /* exact: 11 + 11 + at most 20 significant bits (|isum| <= 32 * 128 * 128 for Q8_0) */
+                double term = dw * dx * (double)isum_blk[jj];
                 acc += term;
                 mag += fabs(term);
             }

@@ -14,11 +14,16 @@ Formats (byte layouts as the pages define them):
   i//4, bits 2*(i%4)); code c stands for weight c-1.
 * planar ternary ``.trit v1`` beat -- tritium "Architecture", section 2 "The one design commitment: bit
   planes": 16 bytes per 64 consecutive columns of one row, ``{u64 pos, u64 neg}``, column c at bit c.
+* ggml ``Q8_0`` weights -- the q8_0 block of the bankml report, section III.2 (a binary16 scale, then 32
+  signed bytes), used for weights as the build history's 0.3.9 entry and its "Q8_0 weights" item do:
+  34-byte blocks of 32 weights.
 
 Workload shapes and value distributions follow the five workloads this library is measured on: block
 scales fp16(|N(0,1)|*0.02), ternary codes -1/0/+1 at 31/38/31 % (the split the bankml report observed
 in Ternary-Bonsai-8B), 1-bit signs Bernoulli(0.5), activations fp32 N(0,1), head weights N(0,0.02)
-rounded to bfloat16.  Random numbers come from numpy's PCG64 stream seeded per input.
+rounded to bfloat16.  Q8_0 weights (no workload on the pages fixes their values) take signed bytes
+rint(36 * N(0,1)) clipped to [-127, 127] -- about 3.5 standard deviations to the byte's end, as a block
+scaled to its largest value would hold -- with scales fp16(|N(0,1)| * 0.02 / 36).  Random numbers come from numpy's PCG64 stream seeded per input.
 """
 from __future__ import annotations
 
@@ -27,14 +32,15 @@ import numpy as np
 Q1_0 = 1
 Q2_0_G64 = 2
 TERNARY_PLANAR = 3
+Q8_0 = 4
 
 QK1 = 128  # weights per Q1_0 block
 QK2 = 64  # weights per Q2_0_g64 block
 QKP = 64  # columns per planar beat
-QK8 = 32  # activations per q8_0 block
+QK8 = 32  # activations per q8_0 block (and weights per Q8_0 weight block)
 
-BLOCK_BYTES = {Q1_0: 18, Q2_0_G64: 18, TERNARY_PLANAR: 16}
-BLOCK_WEIGHTS = {Q1_0: QK1, Q2_0_G64: QK2, TERNARY_PLANAR: QKP}
+BLOCK_BYTES = {Q1_0: 18, Q2_0_G64: 18, TERNARY_PLANAR: 16, Q8_0: 34}
+BLOCK_WEIGHTS = {Q1_0: QK1, Q2_0_G64: QK2, TERNARY_PLANAR: QKP, Q8_0: QK8}
 
 # ternary weight distribution of the ggml file the pages measured: P(-1), P(0), P(+1), P(+2)
 TERNARY_P = (0.31, 0.38, 0.31, 0.0)
@@ -57,6 +63,16 @@ def ternary_weights(g: np.random.Generator, N: int, K: int, p=TERNARY_P) -> np.n
 def sign_weights(g: np.random.Generator, N: int, K: int) -> np.ndarray:
     """Dense int8 matrix of weights in {-1, +1}, each sign a fair coin."""
     return np.where(g.integers(0, 2, size=(N, K), dtype=np.int8) == 1, 1, -1).astype(np.int8)
+
+
+def byte_weights(g: np.random.Generator, N: int, K: int) -> np.ndarray:
+    """Dense int8 matrix of signed-byte weights: rint(36 * N(0,1)) clipped to [-127, 127]."""
+    return np.clip(np.rint(g.standard_normal((N, K)) * 36.0), -127, 127).astype(np.int8)
+
+
+def q8_scales(g: np.random.Generator, n: int) -> np.ndarray:
+    """fp16(|z| * 0.02 / 36): Q8_0 block scales that give the byte weights a spread of about 0.02."""
+    return (np.abs(g.standard_normal(n)) * (0.02 / 36.0)).astype(np.float16)
 
 
 def _bits_lsb_first(bits: np.ndarray) -> np.ndarray:
@@ -90,6 +106,18 @@ def lay_out_q2_0(w: np.ndarray, d: np.ndarray) -> np.ndarray:
     return out
 
 
+def lay_out_q8_0(w: np.ndarray, d: np.ndarray) -> np.ndarray:
+    """ggml Q8_0 bytes for signed-byte weights ``w`` [N][K] and fp16 scales ``d`` [N][K/32]: per block the
+    little-endian binary16 scale, then the 32 weights as two's-complement bytes.  Returns uint8 [N][K/32][34]."""
+    N, K = w.shape
+    nb = K // QK8
+    assert K % QK8 == 0 and d.shape == (N, nb)
+    out = np.empty((N, nb, 34), dtype=np.uint8)
+    out[:, :, 0:2] = d.astype("<f2").view(np.uint8).reshape(N, nb, 2)
+    out[:, :, 2:34] = w.reshape(N, nb, QK8).view(np.uint8)
+    return out
+
+
 def lay_out_planar(w: np.ndarray) -> np.ndarray:
     """Planar beats for ternary ``w`` [N][K] in {-1,0,+1}: per 64 columns 8 bytes of the "+1" plane
     then 8 bytes of the "-1" plane, column c at bit c (little-endian u64).  Returns uint8 [N][K/64][16]."""
@@ -120,7 +148,7 @@ class Weights:
 
     def __init__(self, fmt, N, K, raw, w, d=None, s_w=None):
         self.fmt, self.N, self.K = fmt, N, K
-        self.raw = raw  # uint8, ggml blocks [N][K/QK][18] or planar beats [N][K/64][16]
+        self.raw = raw  # uint8, ggml blocks [N][K/QK][18 or 34] or planar beats [N][K/64][16]
         self.w = w  # int8 [N][K], the drawn weight values (before scaling)
         self.d = d  # fp16 [N][K/QK] block scales (ggml formats)
         self.s_w = s_w  # fp32 per-tensor scale (planar)
@@ -140,6 +168,10 @@ def make_weights(fmt: int, N: int, K: int, seed: int, p=TERNARY_P) -> Weights:
         w = ternary_weights(g, N, K, p)
         d = fp16_scales(g, N * (K // QK2)).reshape(N, K // QK2)
         return Weights(fmt, N, K, lay_out_q2_0(w, d), w, d=d)
+    if fmt == Q8_0:
+        w = byte_weights(g, N, K)
+        d = q8_scales(g, N * (K // QK8)).reshape(N, K // QK8)
+        return Weights(fmt, N, K, lay_out_q8_0(w, d), w, d=d)
     if fmt == TERNARY_PLANAR:
         p3 = np.asarray(p[:3], dtype=np.float64)
         w = ternary_weights(g, N, K, tuple(p3 / p3.sum()) + (0.0,))
@@ -187,7 +219,7 @@ PREFILL_SHAPES = ((4096, 4096), (12288, 4096))
 
 
 def format_bytes(fmt: int, N: int, K: int) -> int:
-    """Bytes of a packed weight tensor in its on-disk format (18 B per ggml block, 16 B per beat)."""
+    """Bytes of a packed weight tensor in its on-disk format (18 or 34 B per ggml block, 16 B per beat)."""
     return N * (K // BLOCK_WEIGHTS[fmt]) * BLOCK_BYTES[fmt]
 
 
@@ -197,13 +229,20 @@ def format_bytes(fmt: int, N: int, K: int) -> int:
 # tests use the host generators above; the bench uses these.
 
 def device_ggml_blocks(fmt: int, N: int, K: int, seed: int, device="cuda"):
-    """ggml Q1_0 / Q2_0_g64 blocks [N][K/QK][18] (uint8) drawn on the device."""
+    """ggml Q1_0 / Q2_0_g64 blocks [N][K/QK][18] or Q8_0 blocks [N][K/32][34] (uint8) drawn on the device."""
     import torch
 
     g = torch.Generator(device=device)
     g.manual_seed(seed)
     qk = BLOCK_WEIGHTS[fmt]
     nb = K // qk
+    if fmt == Q8_0:
+        d = (torch.randn((N, nb), generator=g, device=device).abs() * (0.02 / 36.0)).to(torch.float16)
+        out = torch.empty((N, nb, 34), dtype=torch.uint8, device=device)
+        out[:, :, 0:2] = d.view(torch.uint8).view(N, nb, 2)
+        w = (torch.randn((N, nb, 32), generator=g, device=device) * 36.0).round().clamp(-127, 127).to(torch.int8)
+        out[:, :, 2:34] = w.view(torch.uint8)
+        return out
     d = (torch.randn((N, nb), generator=g, device=device).abs() * 0.02).to(torch.float16)
     out = torch.empty((N, nb, 18), dtype=torch.uint8, device=device)
     out[:, :, 0:2] = d.view(torch.uint8).view(N, nb, 2)

@@ -70,7 +70,7 @@ def _golden_blocks():
 @pytest.mark.parametrize("case", _golden_blocks(), ids=lambda c: c[0] + c[1][:4].hex())
 def test_decode_hand_decoded_blocks(case):
     name, raw, d, first, rest = case
-    fmt = {"q1": oracle.Q1_0, "q2": oracle.Q2_0_G64, "planar": oracle.TERNARY_PLANAR}[name]
+    fmt = {"q1": oracle.Q1_0, "q2": oracle.Q2_0_G64, "planar": oracle.TERNARY_PLANAR, "q8": oracle.Q8_0}[name]
     K = oracle.block_weights(fmt)
     w, dd = oracle.decode(fmt, np.frombuffer(raw, dtype=np.uint8), 1, K)
     assert list(w[0, :16]) == first
@@ -103,6 +103,17 @@ def test_block_sizes_and_bits_per_weight():
     assert oracle.weight_bytes(oracle.Q1_0, 4, 100) == -1  # K not a whole number of blocks
 
 
+def test_q8_0_block_size_against_the_cache_fraction():
+    """A q8_0 block is a binary16 scale and 32 bytes: 34 bytes where f16 takes 64, the "53 %" the pages give
+    for the q8_0 KV cache, and 8.5 bits per weight."""
+    p = _page_sizes()
+    assert oracle.block_weights(oracle.Q8_0) == 32 and oracle.block_bytes(oracle.Q8_0) == 34
+    assert round(100 * oracle.block_bytes(oracle.Q8_0) / (2 * oracle.block_weights(oracle.Q8_0))) == p[
+        "q8_0_cache_percent_of_f16"]
+    assert oracle.weight_bytes(oracle.Q8_0, 4096, 4096) == 4096 * 4096 * 17 // 16
+    assert oracle.weight_bytes(oracle.Q8_0, 4, 48) == -1
+
+
 def test_qwen3_8b_shapes_reproduce_the_pages_counts():
     p = _page_sizes()
     layer = sum(N * K for _, N, K in synth.QWEN3_8B_LAYER)
@@ -126,14 +137,14 @@ def test_bitnet_shapes_reproduce_the_pages_counts():
 
 
 def test_generator_format_bytes_agree_with_oracle():
-    for fmt in (oracle.Q1_0, oracle.Q2_0_G64, oracle.TERNARY_PLANAR):
+    for fmt in (oracle.Q1_0, oracle.Q2_0_G64, oracle.TERNARY_PLANAR, oracle.Q8_0):
         for N, K in ((3, 128), (1024, 4096), (7, 12288)):
             assert synth.format_bytes(fmt, N, K) == oracle.weight_bytes(fmt, N, K)
 
 
 # --- decode / encode against the generator's drawn values ----------------------------------------------
 
-@pytest.mark.parametrize("fmt", [oracle.Q1_0, oracle.Q2_0_G64, oracle.TERNARY_PLANAR])
+@pytest.mark.parametrize("fmt", [oracle.Q1_0, oracle.Q2_0_G64, oracle.TERNARY_PLANAR, oracle.Q8_0])
 def test_decode_recovers_drawn_weights(fmt):
     Wt = synth.make_weights(fmt, 9, 384, seed=11)
     w, d = oracle.decode(fmt, Wt.raw, 9, 384)
@@ -142,12 +153,14 @@ def test_decode_recovers_drawn_weights(fmt):
         assert np.array_equal(d, Wt.d.astype(np.float32))
 
 
-@pytest.mark.parametrize("fmt", [oracle.Q1_0, oracle.Q2_0_G64, oracle.TERNARY_PLANAR])
+@pytest.mark.parametrize("fmt", [oracle.Q1_0, oracle.Q2_0_G64, oracle.TERNARY_PLANAR, oracle.Q8_0])
 def test_encode_decode_round_trip(fmt):
     g = np.random.default_rng(3)
     N, K = 5, 640
     if fmt == oracle.Q1_0:
         w = np.where(g.integers(0, 2, (N, K)) == 1, 1, -1).astype(np.int8)
+    elif fmt == oracle.Q8_0:
+        w = g.integers(-128, 128, (N, K)).astype(np.int8)  # every byte, -128 included
     elif fmt == oracle.Q2_0_G64:
         w = g.integers(-1, 3, (N, K)).astype(np.int8)  # includes code 3 (+2)
     else:
@@ -160,7 +173,8 @@ def test_encode_decode_round_trip(fmt):
     if dh is not None:
         assert np.array_equal(d2, dh.view(np.float16).astype(np.float32))
         # the oracle's encoder lays bytes out exactly as the generator does
-        gen = (synth.lay_out_q1_0 if fmt == oracle.Q1_0 else synth.lay_out_q2_0)(w, dh.view(np.float16))
+        lay = {oracle.Q1_0: synth.lay_out_q1_0, oracle.Q2_0_G64: synth.lay_out_q2_0, oracle.Q8_0: synth.lay_out_q8_0}
+        gen = lay[fmt](w, dh.view(np.float16))
         assert np.array_equal(raw, gen.ravel())
     else:
         assert np.array_equal(raw, synth.lay_out_planar(w).ravel())

@@ -10,7 +10,7 @@ import torch
 import oracle
 import synth
 
-Q_FMTS = [oracle.Q1_0, oracle.Q2_0_G64]
+Q_FMTS = [oracle.Q1_0, oracle.Q2_0_G64, oracle.Q8_0]
 
 
 def _blocks_np(w, q):
@@ -45,6 +45,31 @@ def test_q2_code_map_special_cases():
         raw = oracle.encode(oracle.Q2_0_G64, w, np.full((1, 2), 0x3C00, np.uint16), 1, K)
         s = oracle.block_sums(oracle.Q2_0_G64, raw, 1, K, q)
         assert np.array_equal(s[0].astype(np.int64), mult * sq)
+
+
+def test_q8_special_cases():
+    """Q8_0 weights: a constant byte c gives c * sum q per block; the byte extremes -128 and +127 against
+    activations -128 give 32 * 16384 and -32 * 16256 per block (no wrap anywhere); a one-hot activation
+    reads one column of the dequantised weights."""
+    K = 256
+    q = np.random.default_rng(10).integers(-128, 128, K).astype(np.int8)
+    sq = q.reshape(-1, 32).astype(np.int64).sum(axis=1)
+    dh = np.full((1, K // 32), 0x3C00, np.uint16)
+    for c in (-128, -1, 0, 1, 7, 127):
+        raw = oracle.encode(oracle.Q8_0, np.full((1, K), c, np.int8), dh, 1, K)
+        for form in ("multiply", "select", "offset"):
+            assert np.array_equal(oracle.block_sums(oracle.Q8_0, raw, 1, K, q, form=form)[0].astype(np.int64),
+                                  c * sq), (c, form)
+    qm = np.full(K, -128, np.int8)
+    for c, per in ((-128, 32 * 16384), (127, -32 * 16256)):
+        raw = oracle.encode(oracle.Q8_0, np.full((1, K), c, np.int8), dh, 1, K)
+        assert np.all(oracle.block_sums(oracle.Q8_0, raw, 1, K, qm) == per)
+    Wt = synth.make_weights(oracle.Q8_0, 8, K, seed=52)
+    k = 101
+    q1 = np.zeros(K, np.int8)
+    q1[k] = 1
+    y, _ = oracle.matvec_q(oracle.Q8_0, Wt.raw, 8, K, q1, np.full(K // 32, 0x3C00, np.uint16))
+    assert np.array_equal(y, Wt.w[:, k].astype(np.float64) * Wt.d[:, k // 32].astype(np.float64))
 
 
 def test_q1_special_cases():
