@@ -295,8 +295,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle leg (profiling runs)")
-    ap.add_argument("--secondary", default="q1,planar,prefill",
-                    help="comma list of extra workloads: q1, planar, prefill, none")
+    ap.add_argument("--secondary", default="q1,planar,q8,prefill",
+                    help="comma list of extra workloads: q1, planar, q8, prefill, none")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU: this library has no multi-GPU path (asked for --gpus {args.gpus}). "
@@ -404,6 +404,19 @@ def main():
                                                   "pct_hbm_peak": round(100 * hg / HBM_PEAK_GBS, 2)}
             tp.batch.close()
             del tp
+        elif name == "q8":
+            t8 = DecodeToken(synth.Q8_0, synth.QWEN3_8B_LAYER, synth.QWEN3_8B_LAYERS, seed=1007)
+            ms8, ml8 = time_token(t8, max(10, args.steps // 5), 3)
+            secondary["q8_0_8b_token"] = {
+                "workload": "Q8_0 weights x q8_0 activations (vec_dot_q8_0_q8_0), Qwen3-8B shapes, 36 layers x 7 "
+                            "products, batch 1",
+                "weight_bytes": t8.weight_bytes, "ms_per_step": round(ms8, 5),
+                "gbs": round(t8.weight_bytes / (ms8 * 1e-3) / 1e9, 1),
+                "launch_gbs": round(t8.algorithmic_bytes / (ml8 * 1e-3) / 1e9, 1),
+                "pct_hbm_peak": round(100 * t8.weight_bytes / (ms8 * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+            }
+            t8.batch.close()
+            del t8
         elif name == "prefill":
             pre = {}
             for fmt, fname in ((synth.Q2_0_G64, "q2_0_g64"), (synth.Q1_0, "q1_0")):

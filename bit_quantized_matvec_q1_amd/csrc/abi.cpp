@@ -33,9 +33,9 @@ lb_status hip_fail(const char *fn, hipError_t e)
 
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
-bool is_wfmt(int f) { return f == LB_Q1_0 || f == LB_Q2_0_G64 || f == LB_TERNARY_PLANAR; }
-int64_t block_weights(int f) { return f == LB_Q1_0 ? 128 : 64; }
-int64_t block_bytes(int f) { return f == LB_TERNARY_PLANAR ? 16 : 18; }
+bool is_wfmt(int f) { return f == LB_Q1_0 || f == LB_Q2_0_G64 || f == LB_TERNARY_PLANAR || f == LB_Q8_0; }
+int64_t block_weights(int f) { return f == LB_Q1_0 ? 128 : f == LB_Q8_0 ? 32 : 64; }
+int64_t block_bytes(int f) { return f == LB_TERNARY_PLANAR ? 16 : f == LB_Q8_0 ? 34 : 18; }
 int paired_afmt(int f) { return f == LB_TERNARY_PLANAR ? LB_ACT_I8_ROW : LB_ACT_Q8_0; }
 
 constexpr int kMaxDevices = 64;
@@ -74,13 +74,15 @@ lb_status check_product(const char *fn, int fmt, const void *W, int64_t N, int64
         return fail(LB_EINVAL, fn, "unknown weight or activation format");
     if (afmt != paired_afmt(fmt))
         return fail(LB_EINVAL, fn, "activation format does not match the weight format "
-                                   "(Q1_0/Q2_0_g64 take LB_ACT_Q8_0, planar takes LB_ACT_I8_ROW)");
+                                   "(Q1_0/Q2_0_g64/Q8_0 take LB_ACT_Q8_0, planar takes LB_ACT_I8_ROW)");
     if (N < 0 || K < 0)
         return fail(LB_ESHAPE, fn, "negative size");
     if (K % block_weights(fmt))
-        return fail(LB_ESHAPE, fn, "K is not a multiple of the weight block (128 for Q1_0, 64 otherwise)");
+        return fail(LB_ESHAPE, fn, "K is not a multiple of the weight block (128 for Q1_0, 32 for Q8_0, 64 otherwise)");
     if (K > 32768 || N > INT32_MAX)
         return fail(LB_ESHAPE, fn, "K above 32768 or N above 2^31-1");
+    if (fmt == LB_Q8_0 && K > 16384) // a row is at most one wave of lanes with 8 blocks each
+        return fail(LB_ESHAPE, fn, "K above 16384 for Q8_0");
     if (N * (K / block_weights(fmt)) * block_bytes(fmt) >= (int64_t(1) << 32))
         return fail(LB_ESHAPE, fn, "weight tensor of 4 GiB or more");
     if (N == 0)

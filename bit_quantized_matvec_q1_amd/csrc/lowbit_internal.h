@@ -15,7 +15,7 @@ constexpr int WG = 256;   // threads per workgroup for the streaming kernels (4 
 // Weights per 16-byte code record ("slice"): one Q2_0_g64 block, one Q1_0 block's sign bits, one
 // planar beat.  The device layout of the ggml formats is [N][K/QK][16 B] code records followed by
 // [N][K/QK] binary16 scales.
-constexpr int slice_weights(int fmt) { return fmt == LB_Q1_0 ? 128 : 64; }
+constexpr int slice_weights(int fmt) { return fmt == LB_Q1_0 ? 128 : fmt == LB_Q8_0 ? 32 : 64; }
 
 inline __device__ float half_bits_to_float(uint16_t h) { return __half2float(__ushort_as_half(h)); }
 
@@ -105,5 +105,14 @@ bool matvec_config_full(int fmt, int cfg, int64_t K); // a row of K has exactly 
 hipError_t launch_matvec_batched(const BatchGroup &g, hipStream_t s, size_t lds_bytes);
 int matvec_batched_blocks_per_cu(int fmt, int cfg, bool full, size_t lds_bytes); // resident workgroups per CU
 int matvec_stage_bytes(int fmt, int64_t K); // LDS bytes of one product's staged activation
+
+// Q8_0 weights x q8_0 activations (q8.hip): configurations in their own index space
+int q8_config(int64_t K);
+int q8_rows_per_iter(int cfg);
+size_t q8_stage_bytes(int64_t K);
+hipError_t launch_q8(const uint8_t *W, int64_t N, int64_t K, const int8_t *xq, const uint16_t *xs, float *y,
+                     int32_t *sums, hipStream_t s);
+hipError_t launch_q8_batched(const BatchGroup &g, size_t lds, hipStream_t s);
+int q8_blocks_per_cu(int cfg, size_t lds);
 
 } // namespace lb

@@ -488,6 +488,8 @@ static int pick_cfg(int fmt, int64_t ns)
 
 int matvec_config(int fmt, int64_t K)
 {
+    if (fmt == LB_Q8_0)
+        return q8_config(K);
     if (K <= 0 || K % sw_of(fmt))
         return -1;
     return pick_cfg(fmt, K / sw_of(fmt));
@@ -495,15 +497,26 @@ int matvec_config(int fmt, int64_t K)
 
 bool matvec_supported_k(int fmt, int64_t K) { return matvec_config(fmt, K) >= 0; }
 
-bool matvec_config_full(int fmt, int cfg, int64_t K) { return (int64_t)kCfgs[cfg].L * kCfgs[cfg].S == K / sw_of(fmt); }
+bool matvec_config_full(int fmt, int cfg, int64_t K)
+{
+    if (fmt == LB_Q8_0)
+        return true; // one kernel per configuration; idle lanes are clamped inside it
+    return (int64_t)kCfgs[cfg].L * kCfgs[cfg].S == K / sw_of(fmt);
+}
 
 int matvec_config_rows_per_iter(int fmt, int cfg)
 {
-    (void)fmt;
+    if (fmt == LB_Q8_0)
+        return q8_rows_per_iter(cfg);
     return (64 / kCfgs[cfg].L) * (WG / 64);
 }
 
-int matvec_stage_bytes(int fmt, int64_t K) { return (int)((K / sw_of(fmt)) * rec_of(fmt) * 4); }
+int matvec_stage_bytes(int fmt, int64_t K)
+{
+    if (fmt == LB_Q8_0)
+        return (int)q8_stage_bytes(K);
+    return (int)((K / sw_of(fmt)) * rec_of(fmt) * 4);
+}
 
 template <int FMT, int L, int S, bool EMIT>
 __global__ __launch_bounds__(WG) void matvec_kernel(const uint8_t *__restrict__ W, int N, int K, float w_scale,
@@ -540,6 +553,8 @@ static hipError_t launch_single(int cfg, const uint8_t *W, int N, int K, float w
 hipError_t launch_matvec(int fmt, const uint8_t *W, int64_t N, int64_t K, float w_scale, const int8_t *xq,
                          const void *xscale, float *y, int32_t *sums, hipStream_t s)
 {
+    if (fmt == LB_Q8_0)
+        return launch_q8(W, N, K, xq, static_cast<const uint16_t *>(xscale), y, sums, s);
     const int cfg = matvec_config(fmt, K);
     if (cfg < 0)
         return hipErrorInvalidValue;
@@ -637,6 +652,8 @@ int matvec_batched_blocks_per_cu(int fmt, int cfg, bool full, size_t lds_bytes)
         return blocks_per_cu_fmt<LB_Q2_0_G64>(cfg, full, lds_bytes);
     case LB_TERNARY_PLANAR:
         return blocks_per_cu_fmt<LB_TERNARY_PLANAR>(cfg, full, lds_bytes);
+    case LB_Q8_0:
+        return q8_blocks_per_cu(cfg, lds_bytes);
     }
     return 1;
 }
@@ -650,6 +667,8 @@ hipError_t launch_matvec_batched(const BatchGroup &g, hipStream_t s, size_t lds_
         return launch_batched_fmt<LB_Q2_0_G64>(g, s, lds_bytes);
     case LB_TERNARY_PLANAR:
         return launch_batched_fmt<LB_TERNARY_PLANAR>(g, s, lds_bytes);
+    case LB_Q8_0:
+        return launch_q8_batched(g, lds_bytes, s);
     }
     return hipErrorInvalidValue;
 }

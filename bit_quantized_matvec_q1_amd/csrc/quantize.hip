@@ -204,6 +204,21 @@ __global__ __launch_bounds__(WG) void pack_kernel(int fmt, const uint8_t *__rest
             dst[b * 16 + i] = src[b * 16 + i];
         return;
     }
+    if (fmt == LB_Q8_0) {
+        // 34-byte block (binary16 scale, 32 weight bytes) <-> a 32-byte record + the scale in the scale array
+        if (!unpack) {
+            for (int i = 0; i < 32; i++)
+                dst[b * 32 + i] = src[b * 34 + 2 + i];
+            dst[nblk * 32 + b * 2 + 0] = src[b * 34 + 0];
+            dst[nblk * 32 + b * 2 + 1] = src[b * 34 + 1];
+        } else {
+            for (int i = 0; i < 32; i++)
+                dst[b * 34 + 2 + i] = src[b * 32 + i];
+            dst[b * 34 + 0] = src[nblk * 32 + b * 2 + 0];
+            dst[b * 34 + 1] = src[nblk * 32 + b * 2 + 1];
+        }
+        return;
+    }
     // 16 code bytes of an 18-byte ggml block <-> one 16-byte device record (+ the binary16 scale in the
     // scale array); Q1_0 records also permute their bits (above), Q2_0_g64 records keep them as they are
     const uint8_t *in = unpack ? src + b * 16 : src + b * 18 + 2;
@@ -236,7 +251,7 @@ __global__ __launch_bounds__(WG) void pack_kernel(int fmt, const uint8_t *__rest
 hipError_t launch_pack(int fmt, const uint8_t *blocks, int64_t N, int64_t K, uint8_t *packed, bool unpack,
                        hipStream_t s)
 {
-    const int64_t nblk = N * (K / (fmt == LB_Q1_0 ? 128 : 64));
+    const int64_t nblk = N * (K / (fmt == LB_Q1_0 ? 128 : fmt == LB_Q8_0 ? 32 : 64));
     const int64_t grid = (nblk + WG - 1) / WG;
     if (unpack)
         hipLaunchKernelGGL(pack_kernel, dim3((unsigned)grid), dim3(WG), 0, s, fmt, (const uint8_t *)packed, nblk,

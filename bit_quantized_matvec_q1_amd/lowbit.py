@@ -12,7 +12,7 @@ import os
 
 import torch
 
-Q1_0, Q2_0_G64, TERNARY_PLANAR = 1, 2, 3
+Q1_0, Q2_0_G64, TERNARY_PLANAR, Q8_0 = 1, 2, 3, 4
 ACT_Q8_0, ACT_I8_ROW = 1, 2
 LB_OK, LB_EINVAL, LB_ESHAPE, LB_EALIGN, LB_EUNSUPPORTED, LB_EDEVICE = range(6)
 

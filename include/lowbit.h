@@ -12,6 +12,11 @@
  *   LB_TERNARY_PLANAR the planar ternary beat: 16 bytes per 64 consecutive columns of one row,
  *                     {u64 pos, u64 neg}, column c at bit c; weight = pos_c - neg_c, times one fp32
  *                     per-tensor scale.  (tritium "Architecture", section 2 "bit planes".)
+ *   LB_Q8_0           ggml Q8_0 weights: 34-byte blocks of 32 weights, binary16 scale d then 32 signed
+ *                     bytes; weight = d * byte.  The q8_0 block of the bankml technical report, section
+ *                     III.2, used for weights ("Q8_0 weights" and vec_dot_q8_0_q8_0 for the KV cache in
+ *                     the bankml build history's 0.3.9 entry).  Decode (lowbit_matvec, the batch and
+ *                     lowbit_block_sums with M = 1) only; lowbit_gemm returns LB_EUNSUPPORTED.
  *
  * Activation formats:
  *   LB_ACT_Q8_0       ggml q8_0: int8 xq[M][K] plus binary16 scales xscale[M][K/32]; one block of 32
@@ -43,15 +48,15 @@
 extern "C" {
 #endif
 
-typedef enum { LB_Q1_0 = 1, LB_Q2_0_G64 = 2, LB_TERNARY_PLANAR = 3 } lb_wfmt;
+typedef enum { LB_Q1_0 = 1, LB_Q2_0_G64 = 2, LB_TERNARY_PLANAR = 3, LB_Q8_0 = 4 } lb_wfmt;
 typedef enum { LB_ACT_Q8_0 = 1, LB_ACT_I8_ROW = 2 } lb_afmt;
 
 typedef enum {
     LB_OK = 0,
     LB_EINVAL = 1,       /* null pointer, unknown enum, or a weight/activation format pairing that is not defined */
-    LB_ESHAPE = 2,       /* negative size, K not a multiple of the weight block (128, 64, 64), or over a limit */
+    LB_ESHAPE = 2,       /* negative size, K not a multiple of the weight block (128, 64, 64, 32), or over a limit */
     LB_EALIGN = 3,       /* a pointer is not aligned as its argument requires */
-    LB_EUNSUPPORTED = 4, /* the current device is not gfx950 */
+    LB_EUNSUPPORTED = 4, /* the current device is not gfx950, or the entry point has no kernel for the format */
     LB_EDEVICE = 5       /* a HIP call failed; lowbit_last_error() holds the runtime's message */
 } lb_status;
 
@@ -62,17 +67,19 @@ const char *lowbit_status_str(lb_status st);
 const char *lowbit_last_error(void);
 
 /*
- * Bytes of the device layout of an N x K weight tensor in format `fmt`: 18 per ggml block (128 or 64
- * weights), 16 per planar beat -- the same count as the on-disk format (1.125, 2.25 and 2 bits per
- * weight; bankml technical report sections III.2 and III.5).  Returns -1 for a bad format or shape.
+ * Bytes of the device layout of an N x K weight tensor in format `fmt`: 18 per Q1_0 / Q2_0_g64 block (128
+ * or 64 weights), 34 per Q8_0 block (32 weights), 16 per planar beat -- the same count as the on-disk
+ * format (1.125, 2.25, 8.5 and 2 bits per weight; bankml technical report sections III.2 and III.5).
+ * Returns -1 for a bad format or shape.
  */
 int64_t lowbit_weight_bytes(int fmt, int64_t N, int64_t K);
 
 /*
  * One-time conversion of a ggml block stream into the device layout the kernels read.
- *   blocks: device, N rows x K/QK blocks of 18 bytes, row-major, no alignment requirement.
+ *   blocks: device, N rows x K/QK blocks of 18 bytes (34 for Q8_0), row-major, no alignment requirement.
  *   packed: device, lowbit_weight_bytes(fmt, N, K) bytes, 16-byte aligned.  Layout: all 16-byte code
- *           records row-major ([N][K/QK][16]), then all binary16 scales row-major ([N][K/QK]).
+ *           records row-major ([N][K/QK][16]; Q8_0: 32-byte records of the block's weight bytes,
+ *           [N][K/32][32]), then all binary16 scales row-major ([N][K/QK]).
  *           A Q2_0_g64 record is the block's 16 code bytes as they are.  A Q1_0 record permutes the
  *           block's 128 sign bits: the sign of weight 32r + 8m + k (r, m in 0..3, k in 0..7), at bit
  *           8m + k of little-endian dword r in the ggml block, sits at bit 4k + r of dword m, so one
@@ -105,7 +112,7 @@ lb_status lowbit_quantize_act(int afmt, const float *x, int64_t M, int64_t K, in
  *   afmt:   LB_ACT_Q8_0 for the ggml formats, LB_ACT_I8_ROW for planar.
  *   xq:     device int8 [K], 16-byte aligned.  xscale: binary16 [K/32] or one fp32, 4-byte aligned.
  *   y:      device fp32 [N], 4-byte aligned.
- * Limits: K <= 32768 and N <= 2^31 - 1; the weight tensor must be smaller than 4 GiB.
+ * Limits: K <= 32768 (16384 for LB_Q8_0) and N <= 2^31 - 1; the weight tensor must be smaller than 4 GiB.
  */
 lb_status lowbit_matvec(int fmt, const void *W, int64_t N, int64_t K, float w_tensor_scale, int afmt,
                         const int8_t *xq, const void *xscale, float *y, hipStream_t s);

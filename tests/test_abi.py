@@ -38,6 +38,8 @@ def test_weight_bytes():
     assert L.lowbit_weight_bytes(L.Q1_0, 4096, 4096) == 2_359_296
     assert L.lowbit_weight_bytes(L.Q2_0_G64, 4096, 4096) == 4_718_592
     assert L.lowbit_weight_bytes(L.TERNARY_PLANAR, 6912, 2560) == 4_423_680
+    assert L.lowbit_weight_bytes(L.Q8_0, 4096, 4096) == 17_825_792  # 34 bytes per 32 weights
+    assert L.lowbit_weight_bytes(L.Q8_0, 4, 48) == -1
     assert L.lowbit_weight_bytes(L.Q1_0, 4, 64) == -1
     assert L.lowbit_weight_bytes(7, 4, 64) == -1
     assert L.lowbit_weight_bytes(L.Q2_0_G64, -1, 64) == -1
@@ -56,6 +58,8 @@ def test_matvec_validation_codes():
     assert mv(K=96) == L.LB_ESHAPE  # not a multiple of 64
     assert mv(fmt=L.Q1_0, K=192) == L.LB_ESHAPE  # not a multiple of 128
     assert mv(K=32768 + 64) == L.LB_ESHAPE
+    assert mv(fmt=L.Q8_0, K=16384 + 32) == L.LB_ESHAPE  # Q8_0 rows are at most 16384 weights
+    assert mv(fmt=L.Q8_0, K=48) == L.LB_ESHAPE  # not a multiple of 32
     assert mv(W=None) == L.LB_EINVAL
     assert mv(y=None) == L.LB_EINVAL
     assert mv(W=A16 + 8) == L.LB_EALIGN

@@ -45,7 +45,7 @@ def _product(fmt, N, K, seed):
     return Wt, packed_weights(Wt), q, xs
 
 
-@pytest.mark.parametrize("fmt", [synth.Q1_0, synth.Q2_0_G64, synth.TERNARY_PLANAR])
+@pytest.mark.parametrize("fmt", [synth.Q1_0, synth.Q2_0_G64, synth.TERNARY_PLANAR, synth.Q8_0])
 def test_batched_matches_single_and_oracle(fmt):
     shapes = [(300, 1024), (1024, 4096), (129, 12288), (1, 128), (517, 2560)]
     if fmt != synth.Q1_0:

@@ -1,4 +1,4 @@
-"""GPU parity of the decode products (Q1_0, Q2_0_g64, planar) and the activation quantisers against the
+"""GPU parity of the decode products (Q1_0, Q2_0_g64, planar, Q8_0) and the activation quantisers against the
 CPU oracle, through the C ABI: per-block integer sums bit-exact, fp32 outputs within 1e-5 relative
 (with the cancellation floor), planar outputs and quantised bytes bit-exact."""
 import numpy as np
@@ -12,9 +12,10 @@ from gpu_util import act_for, assert_close, dev, gpu_matvec, gpu_sums, host, pac
 
 pytestmark = pytest.mark.gpu
 
-Q_FMTS = [synth.Q1_0, synth.Q2_0_G64]
+Q_FMTS = [synth.Q1_0, synth.Q2_0_G64, synth.Q8_0]
 ALL_FMTS = Q_FMTS + [synth.TERNARY_PLANAR]
-NAMES = {synth.Q1_0: "Q1_0", synth.Q2_0_G64: "Q2_0_g64", synth.TERNARY_PLANAR: "planar"}
+NAMES = {synth.Q1_0: "Q1_0", synth.Q2_0_G64: "Q2_0_g64", synth.TERNARY_PLANAR: "planar", synth.Q8_0: "Q8_0"}
+QK = {synth.Q1_0: 128, synth.Q2_0_G64: 64, synth.Q8_0: 32}
 
 
 def check_product(fmt, N, K, seed, p=synth.TERNARY_P, q_override=None, rows=None):
@@ -49,13 +50,14 @@ def test_matvec_shapes(fmt, N, K):
 @pytest.mark.parametrize("fmt", ALL_FMTS, ids=NAMES.get)
 def test_matvec_odd_block_counts(fmt):
     # ragged tails: odd numbers of blocks per row, and row counts that leave partial tiles
-    for K in ((128 * 3, 128 * 5, 128 * 9) if fmt == synth.Q1_0 else (64 * 3, 64 * 7, 64 * 33)):
+    qk = QK.get(fmt, 64)
+    for K in (qk * 3, qk * 5, qk * 9) if fmt == synth.Q1_0 else (qk * 3, qk * 7, qk * 33):
         check_product(fmt, 129, K, seed=2000 + K)
 
 
 @pytest.mark.parametrize("fmt", ALL_FMTS, ids=NAMES.get)
 def test_matvec_largest_k(fmt):
-    check_product(fmt, 20, 32768, seed=2100)
+    check_product(fmt, 20, 16384 if fmt == synth.Q8_0 else 32768, seed=2100)
 
 
 def test_q2_code3_and_minus_128():
@@ -77,6 +79,8 @@ def test_minus_128_against_all_minus_one(fmt):
     w = np.full((N, K), -1, np.int8)
     if fmt == synth.Q1_0:
         raw = synth.lay_out_q1_0(w, np.full((N, K // 128), 1.0, np.float16))
+    elif fmt == synth.Q8_0:
+        raw = synth.lay_out_q8_0(w, np.full((N, K // 32), 1.0, np.float16))
     elif fmt == synth.Q2_0_G64:
         raw = synth.lay_out_q2_0(w, np.full((N, K // 64), 1.0, np.float16))
     else:
@@ -94,15 +98,32 @@ def test_minus_128_against_all_minus_one(fmt):
     assert np.all(y == 128.0 * K)
 
 
+def test_q8_byte_extremes():
+    """Q8_0 bytes -128 and +127 against activations -128: 32 * 16384 and -32 * 16256 per block, and with
+    unit scales the row totals 2^24 and -16256 * 1024 exactly (no wrap in any 8- or 16-bit step)."""
+    N, K = 40, 1024
+    q = np.full(K, -128, np.int8)
+    ones = np.full(K // 32, 0x3C00, np.uint16)
+    for c, per in ((-128, 32 * 16384), (127, -32 * 16256)):
+        say(f"case q8 extremes c={c}")
+        w = np.full((N, K), c, np.int8)
+        Wt = synth.Weights(synth.Q8_0, N, K, synth.lay_out_q8_0(w, np.full((N, K // 32), 1.0, np.float16)), w)
+        packed = packed_weights(Wt)
+        assert np.all(gpu_sums(synth.Q8_0, packed, N, K, q[None, :], ones[None, :])[0] == per)
+        assert np.all(gpu_matvec(synth.Q8_0, packed, N, K, q, ones) == float(per * (K // 32)))
+
+
 @pytest.mark.parametrize("fmt", Q_FMTS, ids=NAMES.get)
 def test_unit_scales_bit_exact(fmt):
     """With every binary16 scale 1.0 each term is an integer below 2^24: y must equal the oracle exactly."""
     N, K = 300, 4096
     say(f"case unit-scales {NAMES[fmt]}")
     Wt = synth.make_weights(fmt, N, K, seed=2300)
-    qk = 128 if fmt == synth.Q1_0 else 64
-    raw = oracle.encode(fmt, Wt.w, np.full((N, K // qk), 0x3C00, np.uint16), N, K)
-    Wu = synth.Weights(fmt, N, K, raw.reshape(N, K // qk, 18), Wt.w)
+    qk = QK[fmt]
+    # Q8_0 bytes are brought down to [-15, 15] so that every partial sum of a row stays below 2^24
+    w = (Wt.w // 8).astype(np.int8) if fmt == synth.Q8_0 else Wt.w
+    raw = oracle.encode(fmt, w, np.full((N, K // qk), 0x3C00, np.uint16), N, K)
+    Wu = synth.Weights(fmt, N, K, raw.reshape(N, K // qk, synth.BLOCK_BYTES[fmt]), w)
     q, _, _ = act_for(fmt, K, 2301)
     ones = np.full(K // 32, 0x3C00, np.uint16)
     y = gpu_matvec(fmt, packed_weights(Wu), N, K, q, ones)
@@ -146,16 +167,17 @@ def test_pack_round_trip(fmt):
     back = torch.empty(Wt.raw.size, dtype=torch.uint8, device="cuda")
     L.lowbit_unpack_weights(fmt, packed, 77, 1024, back)
     assert np.array_equal(host(back), Wt.raw.reshape(-1))
-    # the device layout is all code records, then all scales
+    # the device layout is all code records (32 bytes for Q8_0, 16 otherwise), then all scales
     p = host(packed)
     nb = Wt.raw.shape[1]
-    assert np.array_equal(p[: 77 * nb * 16].reshape(77, nb, 16), device_records(fmt, Wt.raw))
-    assert np.array_equal(p[77 * nb * 16:].reshape(77, nb, 2), Wt.raw[:, :, :2])
+    rb = synth.BLOCK_BYTES[fmt] - 2
+    assert np.array_equal(p[: 77 * nb * rb].reshape(77, nb, rb), device_records(fmt, Wt.raw))
+    assert np.array_equal(p[77 * nb * rb:].reshape(77, nb, 2), Wt.raw[:, :, :2])
 
 
 def device_records(fmt, raw):
-    """The documented device records of ggml blocks: Q2_0_g64 code bytes as they are; Q1_0 with the
-    sign of weight 32r + 8m + k moved to bit 4k + r of little-endian dword m."""
+    """The documented device records of ggml blocks: Q2_0_g64 code bytes and Q8_0 weight bytes as they are;
+    Q1_0 with the sign of weight 32r + 8m + k moved to bit 4k + r of little-endian dword m."""
     codes = raw[:, :, 2:]
     if fmt != synth.Q1_0:
         return codes
