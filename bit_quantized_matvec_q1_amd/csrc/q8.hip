@@ -25,12 +25,15 @@ typedef __attribute__((address_space(1))) const uint8_t gu8;
 typedef __attribute__((address_space(1))) const uint16_t gu16;
 
 constexpr int QB = 32; // bytes per Q8_0 record (and weights per block)
+constexpr int UB = 16; // bytes per unit: half a record, one 16-byte beat
 
-// Configurations (L lanes per row, S blocks per lane).
+// Configurations (L lanes per row, S units per lane).  The unit of work is half a block (16 weights):
+// lane li takes units li, li + L, ..., so one wave-wide load is 64 consecutive beats, and L is even, so
+// the two halves of a block sit in lanes li and li ^ 1 of the same row.
 #define LB_Q8_CFGS(X)                                                                                         \
-    X(0, 8, 1) X(1, 8, 2) X(2, 8, 3) X(3, 8, 4) X(4, 8, 6) X(5, 8, 8) X(6, 16, 1) X(7, 16, 2) X(8, 16, 3)      \
-    X(9, 16, 4) X(10, 16, 6) X(11, 16, 8) X(12, 32, 1) X(13, 32, 2) X(14, 32, 3) X(15, 32, 4) X(16, 32, 6)    \
-    X(17, 32, 8) X(18, 64, 1) X(19, 64, 2) X(20, 64, 3) X(21, 64, 4) X(22, 64, 6) X(23, 64, 8)
+    X(0, 8, 1) X(1, 8, 2) X(2, 8, 4) X(3, 8, 6) X(4, 8, 8) X(5, 16, 1) X(6, 16, 2) X(7, 16, 4) X(8, 16, 6)      \
+    X(9, 16, 8) X(10, 32, 2) X(11, 32, 3) X(12, 32, 4) X(13, 32, 6) X(14, 32, 8) X(15, 64, 2) X(16, 64, 3)    \
+    X(17, 64, 4) X(18, 64, 5) X(19, 64, 6) X(20, 64, 8) X(21, 64, 10) X(22, 64, 12) X(23, 64, 16)
 
 struct CfgLS {
     int L, S;
@@ -41,24 +44,21 @@ constexpr CfgLS kQ8Cfgs[] = {LB_Q8_CFGS(LB_Q8_ENTRY)};
 constexpr int kQ8NumCfgs = sizeof(kQ8Cfgs) / sizeof(kQ8Cfgs[0]);
 
 template <int S> struct Q8Row {
-    uint4 lo[S], hi[S]; // the block's weight bytes 0..15 and 16..31
-    uint32_t sc[S];     // its binary16 scale
+    uint4 w[S];     // the unit's 16 weight bytes
+    uint32_t sc[S]; // its block's binary16 scale
 };
 
 template <int L, int S>
 __device__ __forceinline__ void q8_issue(Q8Row<S> &r, const uint8_t *__restrict__ W, const uint8_t *__restrict__ scales,
-                                         uint32_t off, const uint32_t (&bo)[S])
+                                         uint32_t off, const uint32_t (&uo)[S])
 {
-    // off: byte offset of the row's first record; bo[i]: byte offset of this lane's i-th record in a row
+    // off: byte offset of the row's first record; uo[i]: byte offset of this lane's i-th unit in a row
     const uint32_t soff = off >> 4; // record index at byte 32 idx, its scale at byte 2 idx
 #pragma unroll
     for (int i = 0; i < S; i++) {
-        const gu8 *p = (gu8 *)W + (off + bo[i]);
-        const v4u a = __builtin_nontemporal_load((gv4u *)p);
-        const v4u b = __builtin_nontemporal_load((gv4u *)(p + 16));
-        r.lo[i] = make_uint4(a.x, a.y, a.z, a.w);
-        r.hi[i] = make_uint4(b.x, b.y, b.z, b.w);
-        r.sc[i] = *(gu16 *)((gu8 *)scales + (soff + (bo[i] >> 4)));
+        const v4u a = __builtin_nontemporal_load((gv4u *)((gu8 *)W + (off + uo[i])));
+        r.w[i] = make_uint4(a.x, a.y, a.z, a.w);
+        r.sc[i] = *(gu16 *)((gu8 *)scales + (soff + ((uo[i] >> 5) << 1)));
     }
 }
 
@@ -77,7 +77,7 @@ __device__ __forceinline__ void q8_tile(const uint8_t *__restrict__ W, int N, in
 {
     constexpr int GROUPS = 64 / L;
     constexpr int STEP = GROUPS * (WG / 64);
-    const int nb = K / QB;
+    const int nb = K / QB, nu = K / UB;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int g = lane / L, li = lane % L;
     const uint8_t *scales = W + (size_t)N * nb * QB;
@@ -85,35 +85,33 @@ __device__ __forceinline__ void q8_tile(const uint8_t *__restrict__ W, int N, in
     const uint32_t rowbytes = (uint32_t)nb * QB;
     const uint32_t stepb = (uint32_t)STEP * rowbytes;
     const uint32_t last = (uint32_t)(row0 + nrows - 1) * rowbytes;
-    uint32_t bo[S];
+    uint32_t uo[S];
 #pragma unroll
     for (int i = 0; i < S; i++)
-        bo[i] = (uint32_t)min(li + i * L, nb - 1) * QB; // a lane past the row's end re-reads its last block
+        uo[i] = (uint32_t)min(li + i * L, nu - 1) * UB; // a lane past the row's end re-reads its last unit
     uint32_t onext = (uint32_t)(row0 + min(rbase, nrows - 1)) * rowbytes;
 
     Q8Row<S> buf[2];
-    q8_issue<L, S>(buf[0], W, scales, min(onext, last), bo);
+    q8_issue<L, S>(buf[0], W, scales, min(onext, last), uo);
     onext += stepb;
 
     // stage the activation bytes and the scales (as floats) once for the workgroup
     uint4 *xl = reinterpret_cast<uint4 *>(lds);
     float *dl = reinterpret_cast<float *>(lds + K / 4);
-    for (int i = threadIdx.x; i < K / 16; i += WG)
+    for (int i = threadIdx.x; i < nu; i += WG)
         xl[i] = reinterpret_cast<const uint4 *>(xq)[i];
     for (int i = threadIdx.x; i < nb; i += WG)
         dl[i] = half_bits_to_float(xs[i]);
     __syncthreads();
 
-    uint4 xlo[S], xhi[S];
+    uint4 xu[S];
     float dx[S];
 #pragma unroll
     for (int i = 0; i < S; i++) {
-        const int b = li + i * L;
-        const bool in = b < nb;
-        const int bb = in ? b : 0;
-        xlo[i] = in ? xl[2 * bb] : make_uint4(0u, 0u, 0u, 0u);
-        xhi[i] = in ? xl[2 * bb + 1] : make_uint4(0u, 0u, 0u, 0u);
-        dx[i] = in ? dl[bb] : 0.0f;
+        const int u = li + i * L;
+        const bool in = u < nu;
+        xu[i] = in ? xl[u] : make_uint4(0u, 0u, 0u, 0u);
+        dx[i] = in ? dl[u >> 1] : 0.0f;
     }
 
     for (int it = 0; it < nrows; it += 2 * STEP) {
@@ -123,20 +121,25 @@ __device__ __forceinline__ void q8_tile(const uint8_t *__restrict__ W, int N, in
             if (cur >= nrows) // uniform
                 break;
             if (cur + STEP < nrows) // uniform
-                q8_issue<L, S>(buf[p ^ 1], W, scales, min(onext, last), bo);
+                q8_issue<L, S>(buf[p ^ 1], W, scales, min(onext, last), uo);
             onext += stepb;
             const int rl = cur + rbase;
             const bool valid = rl < nrows;
             float part = 0.0f;
 #pragma unroll
             for (int i = 0; i < S; i++) {
-                const int isum = dot16(buf[p].hi[i], xhi[i], dot16(buf[p].lo[i], xlo[i], 0));
-                // bankml report, section III.3: one multiply-add per q8_0 block, then one per weight block
-                // (here the same block): t = d_x * isum, then part += d_w * t
-                const float t = dx[i] * (float)isum;
+                const int ih = dot16(buf[p].w[i], xu[i], 0); // half a block's sum
+                // bankml report, section III.3: a multiply-add by d_x, then one by the block's weight scale;
+                // the two halves of a block are scaled separately and meet in the row sum
+                const float t = dx[i] * (float)ih;
                 part = fmaf(half_bits_to_float((uint16_t)buf[p].sc[i]), t, part);
-                if (EMIT && valid && li + i * L < nb)
-                    sums[(size_t)(row0 + rl) * nb + li + i * L] = isum;
+                if (EMIT) {
+                    // the block's exact sum: this half plus its neighbour lane's (li ^ 1)
+                    const int isum = ih + __builtin_amdgcn_update_dpp(0, ih, 0xB1, 0xF, 0xF, false);
+                    const int u = li + i * L;
+                    if (valid && (li & 1) == 0 && u < nu)
+                        sums[(size_t)(row0 + rl) * nb + (u >> 1)] = isum;
+                }
             }
             part = group_sum_f<L>(part);
             if (valid && li == L - 1 && (!EMIT || y != nullptr))
@@ -167,13 +170,13 @@ __global__ __launch_bounds__(WG) void q8_batched_kernel(const DevDesc *__restric
 
 } // namespace
 
-// Choice: the fewest idle lane slots; then S nearest 4 (a light register load with enough blocks per lane
+// Choice: the fewest idle lane slots; then S nearest 4 (a light register load with enough units per lane
 // to amortise the row's reduction); then more lanes per row.
 int q8_config(int64_t K)
 {
     if (K <= 0 || K % QB)
         return -1;
-    const int64_t nb = K / QB;
+    const int64_t nb = K / UB; // units per row
     int best = -1;
     int64_t bw = 0;
     int bd = 0;
