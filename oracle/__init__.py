@@ -60,6 +60,7 @@ def lib():
             "lbo_matvec_q": (I, [I, P, I64, I64, P, P, P, I64, P, P]),
             "lbo_matvec_planar": (I, [P, I64, I64, P, ctypes.c_float, ctypes.c_float, P, I64, P, P]),
             "lbo_head_matvec": (I, [P, I64, I64, P, P, I64, P, P]),
+            "lbo_head_matvec_i8": (I, [P, P, I64, I64, P, P, I64, P, P]),
         }
         for name, (res, args) in sig.items():
             f = getattr(_lib, name)
@@ -211,6 +212,18 @@ def head_matvec(W, N, K, x, rows=None):
     y = np.empty(n, dtype=np.float64)
     A = np.empty(n, dtype=np.float64)
     _check(lib().lbo_head_matvec(_p(W), N, K, _p(x), _p(r), n, _p(y), _p(A)), "head_matvec")
+    return y, A
+
+
+def head_matvec_i8(W, s_w, N, K, x, rows=None):
+    """W int8 [N][K], s_w float32 [N] (one scale per row), x float32 [K] -> (y float64, A float64) [nrows]"""
+    W = _c(W, np.int8)
+    s_w = _c(s_w, np.float32).ravel()
+    x = _c(x, np.float32).ravel()
+    r, n = _rows(rows, N)
+    y = np.empty(n, dtype=np.float64)
+    A = np.empty(n, dtype=np.float64)
+    _check(lib().lbo_head_matvec_i8(_p(W), _p(s_w), N, K, _p(x), _p(r), n, _p(y), _p(A)), "head_matvec_i8")
     return y, A
 
 

@@ -25,7 +25,8 @@
  *     activations (vec_dot_q8_0_q8_0 of [BH] 0.3.9: one block of 32 on each side, one scale each);
  *   - the planar output ((float)acc * s_x) * s_w in fp32 with two roundings ([ARCH] s.5 names the
  *     twice-multiplied order);
- *   - the dense bf16 head y = sum_k bf16(W) * x in fp64 (every product exact).
+ *   - the dense bf16 head y = sum_k bf16(W) * x in fp64 (every product exact), and the int8 head
+ *     y = s_w[r] * sum_k W * x with one fp32 scale per row, also in fp64.
  *
  * Parity pins live in tests/test_oracle_*.py.  Parity unpinned: ggml's exact fp32 operation order (only
  * recoverable from a compiled binary) and the absolute Q1_0 sign polarity relative to ggml; this oracle
@@ -520,6 +521,32 @@ int lbo_head_matvec(const uint16_t *W, int64_t N, int64_t K, const float *x, con
         y[t] = acc;
         if (A)
             A[t] = mag;
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------------------------------
+ * int8 dense head ([ARCH] s.10 open questions: the f32 head's "obvious move" is int8; the reading taken
+ * here: int8 weights W[N][K] with one fp32 scale per row, s_w[r], against the head's fp32 input x):
+ *   y[r] = s_w[r] * sum_k W[r][k] * x[k]  in fp64 (each product of an 8-bit integer and a 24-bit
+ *   significand is exact), A[r] = |s_w[r]| * sum_k |W[r][k] * x[k]|.
+ * ---------------------------------------------------------------------------------------------- */
+int lbo_head_matvec_i8(const int8_t *W, const float *s_w, int64_t N, int64_t K, const float *x, const int64_t *rows,
+                       int64_t nrows, double *y, double *A)
+{
+    for (int64_t t = 0; t < nrows; t++) {
+        int64_t r = row_of(rows, t);
+        if (r < 0 || r >= N)
+            return -1;
+        double acc = 0.0, mag = 0.0;
+        for (int64_t k = 0; k < K; k++) {
+            double p = (double)W[r * K + k] * (double)x[k];
+            acc += p;
+            mag += fabs(p);
+        }
+        y[t] = (double)s_w[r] * acc;
+        if (A)
+            A[t] = fabs((double)s_w[r]) * mag;
     }
     return 0;
 }

@@ -186,6 +186,15 @@ def head_weights(N: int, K: int, seed: int) -> np.ndarray:
     return bf16_bits((g.standard_normal((N, K)) * 0.02).astype(np.float32))
 
 
+def head_weights_i8(N: int, K: int, seed: int):
+    """int8 head: signed bytes rint(36 * N(0,1)) clipped to [-127, 127] [N][K] and one fp32 scale per row,
+    |N(0,1)| * 0.02 / 36 (so the weights spread like the bf16 head's N(0, 0.02))."""
+    g = rng(seed)
+    W = byte_weights(g, N, K)
+    s = (np.abs(g.standard_normal(N)) * (0.02 / 36.0)).astype(np.float32)
+    return W, s
+
+
 # --- the measured workloads' shapes -------------------------------------------------------------
 
 # Qwen3-8B-like projections (rows x K) of one transformer block, in file order.
@@ -272,6 +281,17 @@ def device_planar_beats(N: int, K: int, seed: int, device="cuda"):
     out[:, :, 0:8] = (pos[:, :, 0] << shifts).sum(dim=-1, dtype=torch.uint8)
     out[:, :, 8:16] = (neg[:, :, 0] << shifts).sum(dim=-1, dtype=torch.uint8)
     return out
+
+
+def device_head_weights_i8(N: int, K: int, seed: int, device="cuda"):
+    """int8 head weights [N][K] and fp32 row scales [N] with the recipe of head_weights_i8, on the device."""
+    import torch
+
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    W = (torch.randn((N, K), generator=g, device=device) * 36.0).round().clamp(-127, 127).to(torch.int8)
+    s = torch.randn(N, generator=g, device=device).abs() * (0.02 / 36.0)
+    return W, s
 
 
 def device_head_weights(N: int, K: int, seed: int, device="cuda"):

@@ -203,6 +203,48 @@ def test_head_against_numpy_fp64():
     assert np.allclose(A, np.abs(Wf * x.astype(np.float64)).sum(axis=1), rtol=1e-12)
 
 
+def test_head_i8_against_numpy_and_rationals():
+    """int8 head: fp64 numpy (exact products) on a full-width sample, exact rationals on a tiny case, and a
+    per-row scale of 1 with integer x gives the integer dot product exactly."""
+    N, K = 40, 2560
+    W, s = synth.head_weights_i8(N, K, seed=73)
+    x = synth.activations(np.random.default_rng(74), 1, K)[0]
+    y, A = oracle.head_matvec_i8(W, s, N, K, x)
+    dots = W.astype(np.float64) @ x.astype(np.float64)
+    assert np.all(np.abs(y - s.astype(np.float64) * dots) <= 2 * K * 2.0 ** -53 * A)
+    mags = np.abs(W.astype(np.float64) * x.astype(np.float64)).sum(axis=1)
+    assert np.allclose(A, np.abs(s.astype(np.float64)) * mags, rtol=1e-12)
+    Wt, st = W[:3, :16], s[:3]
+    xt = x[:16]
+    y3, _ = oracle.head_matvec_i8(Wt, st, 3, 16, xt)
+    for r in range(3):
+        exact = Fraction(float(st[r])) * sum(Fraction(int(Wt[r, k])) * Fraction(float(xt[k])) for k in range(16))
+        assert abs(Fraction(y3[r]) - exact) <= Fraction(16 * 2.0 ** -52) * abs(exact) + Fraction(2.0 ** -1074)
+    xi = np.random.default_rng(75).integers(-50, 50, K).astype(np.float32)
+    yi, _ = oracle.head_matvec_i8(W, np.ones(N, np.float32), N, K, xi)
+    assert np.array_equal(yi, (W.astype(np.int64) @ xi.astype(np.int64)).astype(np.float64))
+
+
+def test_int8_head_speedup_the_pages_quote():
+    """An int8 head (N*K bytes plus one fp32 scale per row) in place of the f32 one shrinks the tied-head
+    2B token by the ~2.2x the pages give, with the ternary body that makes the f32 head 2.5:1."""
+    import os
+    p = {}
+    with open(os.path.join(os.path.dirname(__file__), "golden", "page_sizes.txt")) as f:
+        for line in f:
+            if line.strip() and not line.startswith("#"):
+                name, value, _ = [t.strip() for t in line.split("|")]
+                p[name] = float(value)
+    N, K = synth.BITNET_HEAD
+    body = p["bitnet_gqa_ternary_body_bytes"]
+    # the body the 2.5:1 figure implies: 4 x 2560^2 with k/v at 640 rows, 2 x 6912 x 2560, 2560 x 6912, 30 layers
+    gqa = sum(oracle.weight_bytes(oracle.TERNARY_PLANAR, n, k) for n, k in
+              ((2560, 2560), (640, 2560), (640, 2560), (2560, 2560), (6912, 2560), (6912, 2560), (2560, 6912))) * 30
+    assert gqa == body and round(p["head_f32_bytes"] / body, 1) == 2.5
+    int8_head = N * K + 4 * N
+    assert round((p["head_f32_bytes"] + body) / (int8_head + body), 1) == p["head_int8_token_speedup"]
+
+
 def test_gemm_rows_are_matvecs():
     N, K, M = 16, 512, 5
     Wt = synth.make_weights(oracle.Q1_0, N, K, seed=81)
