@@ -238,6 +238,29 @@ def head_gbs(N, K, reps=20, seed=1006):
     return ms, (2 * N * K + 4 * K + 4 * N) / (ms * 1e-3) / 1e9
 
 
+def head_i8_gbs(N, K, reps=20, seed=1008):
+    """The int8 head with one fp32 scale per row: (ms per launch, GB/s of its N*K + 4N weight bytes)."""
+    import torch
+
+    import bit_quantized_matvec_q1_amd.lowbit as L
+    import synth
+
+    W, s = synth.device_head_weights_i8(N, K, seed)
+    x = torch.randn(K, device="cuda")
+    y = torch.empty(N, dtype=torch.float32, device="cuda")
+    for _ in range(3):
+        L.dense_head_matvec_i8(W, s, N, K, x, y)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        L.dense_head_matvec_i8(W, s, N, K, x, y)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    return ms, (N * K + 4 * N) / (ms * 1e-3) / 1e9
+
+
 def prefill_tops(fmt, N, K, M, reps=20, seed=1004):
     """Time the prefill product (M activation rows x N weight rows x K) on inputs resident in HBM."""
     import torch
@@ -402,6 +425,10 @@ def main():
             hms, hg = head_gbs(*synth.BITNET_HEAD)
             secondary["head_bf16_128256x2560"] = {"ms": round(hms, 4), "gbs": round(hg, 1),
                                                   "pct_hbm_peak": round(100 * hg / HBM_PEAK_GBS, 2)}
+            ims, ig = head_i8_gbs(*synth.BITNET_HEAD)
+            secondary["head_int8_128256x2560"] = {"ms": round(ims, 4), "gbs": round(ig, 1),
+                                                  "pct_hbm_peak": round(100 * ig / HBM_PEAK_GBS, 2),
+                                                  "speedup_vs_bf16_head": round(hms / ims, 3)}
             tp.batch.close()
             del tp
         elif name == "q8":

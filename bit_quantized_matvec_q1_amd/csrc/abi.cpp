@@ -279,6 +279,29 @@ lb_status dense_head_matvec(const uint16_t *W, int64_t N, int64_t K, const float
     return e == hipSuccess ? LB_OK : hip_fail(fn, e);
 }
 
+lb_status dense_head_matvec_i8(const int8_t *W, const float *row_scale, int64_t N, int64_t K, const float *x, float *y,
+                               hipStream_t s)
+{
+    const char *fn = "dense_head_matvec_i8";
+    if (N < 0 || K < 0 || N > INT32_MAX)
+        return fail(LB_ESHAPE, fn, "negative size");
+    if (K % 16 || K > 8192)
+        return fail(LB_ESHAPE, fn, "K must be a multiple of 16 and at most 8192");
+    if (N * K >= (int64_t(1) << 32))
+        return fail(LB_ESHAPE, fn, "weight tensor of 4 GiB or more");
+    if (N == 0)
+        return LB_OK;
+    if (!W || !row_scale || !x || !y)
+        return fail(LB_EINVAL, fn, "null pointer");
+    if (!aligned(W, 16) || !aligned(x, 16) || !aligned(y, 4) || !aligned(row_scale, 4))
+        return fail(LB_EALIGN, fn, "W and x need 16-byte alignment, row_scale and y 4-byte alignment");
+    lb_status st = check_device(fn);
+    if (st != LB_OK)
+        return st;
+    hipError_t e = K == 0 ? lb::launch_fill_zero(y, N, s) : lb::launch_head_i8(W, row_scale, N, K, x, y, s);
+    return e == hipSuccess ? LB_OK : hip_fail(fn, e);
+}
+
 // ---- batched decode ------------------------------------------------------------------------------
 
 // Tile plan of one launch group.  Every product is cut into row tiles (whole row iterations of the

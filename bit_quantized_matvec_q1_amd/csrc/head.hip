@@ -86,6 +86,99 @@ __global__ __launch_bounds__(WG) void head_kernel(const uint16_t *__restrict__ W
     }
 }
 
+// int8 head: y[n] = s_w[n] * sum_k W[n][k] * x[k] (tritium "Architecture", section 10: int8 as the obvious
+// move for the head; one fp32 scale per row).  Half the bytes of the bf16 head: the same streaming
+// structure with 16-byte loads of 16 weights, each widened to fp32 exactly (a signed byte) and
+// multiply-added against x held in VGPRs; the row's scale multiplies the finished sum.
+template <int S>
+__global__ __launch_bounds__(WG) void head_i8_kernel(const int8_t *__restrict__ W, const float *__restrict__ sw, int N,
+                                                     int K, const float *__restrict__ x, float *__restrict__ y,
+                                                     int tile_rows)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int nch = K / 16; // chunks of 16 columns per row
+    float xr[S][16];
+    uint32_t co[S]; // byte offset of this lane's chunks within a row
+#pragma unroll
+    for (int i = 0; i < S; i++) {
+        const int ch = lane + 64 * i;
+        co[i] = (uint32_t)min(ch, nch - 1) * 16u;
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+            const float4 a = ch < nch ? reinterpret_cast<const float4 *>(x)[4 * ch + q] : make_float4(0.f, 0.f, 0.f, 0.f);
+            xr[i][4 * q + 0] = a.x, xr[i][4 * q + 1] = a.y, xr[i][4 * q + 2] = a.z, xr[i][4 * q + 3] = a.w;
+        }
+    }
+    const int row0 = blockIdx.x * tile_rows;
+    const int nrows = min(tile_rows, N - row0);
+    constexpr int STEP = WG / 64;
+    const uint32_t rowb = (uint32_t)K;
+    const uint32_t last = (uint32_t)(row0 + nrows - 1) * rowb;
+    uint32_t onext = (uint32_t)(row0 + min(wave, nrows - 1)) * rowb;
+    // a ring of NB register buffers: NB - 1 rows' loads in flight while a row is computed (deeper rings
+    // measured no faster: at two VALU operations per weight byte the kernel is bound by issue, not latency)
+    constexpr int NB = 2;
+    uint4 buf[NB][S];
+    auto issue = [&](uint4 (&w)[S], uint32_t off) {
+#pragma unroll
+        for (int i = 0; i < S; i++) {
+            const hv4u t = __builtin_nontemporal_load((ghv4u *)((ghu8 *)W + (off + co[i])));
+            w[i] = make_uint4(t.x, t.y, t.z, t.w);
+        }
+    };
+#pragma unroll
+    for (int b = 0; b < NB - 1; b++) {
+        if (b * STEP < nrows) // uniform
+            issue(buf[b], min(onext, last));
+        onext += STEP * rowb;
+    }
+    for (int it = 0; it < nrows; it += NB * STEP) {
+#pragma unroll
+        for (int b = 0; b < NB; b++) {
+            const int cur = it + b * STEP;
+            if (cur >= nrows) // uniform
+                break;
+            if (cur + (NB - 1) * STEP < nrows) // uniform
+                issue(buf[(b + NB - 1) % NB], min(onext, last));
+            onext += STEP * rowb;
+            // a lane's chunk past the row's end re-read the last chunk; its x is zero, so it adds nothing
+            float acc = 0.0f;
+#pragma unroll
+            for (int i = 0; i < S; i++) {
+                const uint32_t v[4] = {buf[b][i].x, buf[b][i].y, buf[b][i].z, buf[b][i].w};
+#pragma unroll
+                for (int j = 0; j < 4; j++)
+#pragma unroll
+                    for (int t = 0; t < 4; t++)
+                        acc = fmaf((float)(int)(int8_t)(v[j] >> (8 * t)), xr[i][4 * j + t], acc);
+            }
+            acc = group_sum_f<64>(acc);
+            const int rl = cur + wave;
+            if (rl < nrows && lane == 63)
+                y[row0 + rl] = sw[row0 + rl] * acc;
+        }
+    }
+}
+
+hipError_t launch_head_i8(const int8_t *W, const float *sw, int64_t N, int64_t K, const float *x, float *y, hipStream_t s)
+{
+    const int nch = (int)(K / 16);
+    const int S = (nch + 63) / 64;
+    const int tile = 64; // rows per workgroup
+    const int grid = (int)((N + tile - 1) / tile);
+    switch (S) {
+#define LB_HEAD_I8(n)                                                                                         \
+    case n:                                                                                                   \
+        hipLaunchKernelGGL(head_i8_kernel<n>, dim3(grid), dim3(WG), 0, s, W, sw, (int)N, (int)K, x, y, tile); \
+        break;
+        LB_HEAD_I8(1) LB_HEAD_I8(2) LB_HEAD_I8(3) LB_HEAD_I8(4) LB_HEAD_I8(5) LB_HEAD_I8(6) LB_HEAD_I8(7) LB_HEAD_I8(8)
+#undef LB_HEAD_I8
+    default:
+        return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
 hipError_t launch_head(const uint16_t *W, int64_t N, int64_t K, const float *x, float *y, hipStream_t s)
 {
     const int nch = (int)(K / 8);

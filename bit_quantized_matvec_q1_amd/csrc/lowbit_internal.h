@@ -73,6 +73,8 @@ hipError_t launch_gemm(int fmt, const uint8_t *W, int64_t N, int64_t K, float w_
                        const void *Xscale, int64_t M, float *Y, int32_t *sums, hipStream_t s);
 
 hipError_t launch_head(const uint16_t *W, int64_t N, int64_t K, const float *x, float *y, hipStream_t s);
+hipError_t launch_head_i8(const int8_t *W, const float *sw, int64_t N, int64_t K, const float *x, float *y,
+                          hipStream_t s);
 
 // batched decode: a device table of products, grouped by kernel configuration
 struct DevDesc {

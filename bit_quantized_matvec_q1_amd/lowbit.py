@@ -37,6 +37,7 @@ SIGNATURES = {
     "lowbit_gemm": (_I, [_I, _P, _I64, _I64, _F, _I, _P, _P, _I64, _P, _P]),
     "lowbit_block_sums": (_I, [_I, _P, _I64, _I64, _I, _P, _P, _I64, _P, _P]),
     "dense_head_matvec": (_I, [_P, _I64, _I64, _P, _P, _P]),
+    "dense_head_matvec_i8": (_I, [_P, _P, _I64, _I64, _P, _P, _P]),
     "lowbit_batch_create": (_I, [_P, ctypes.c_int32, _P]),
     "lowbit_matvec_batched": (_I, [_P, _P]),
     "lowbit_batch_destroy": (None, [_P]),
@@ -125,6 +126,11 @@ def lowbit_block_sums(fmt, W, N, K, afmt, Xq, Xscale, M, sums, stream=None):
 
 def dense_head_matvec(W, N, K, x, y, stream=None):
     _check(lib.dense_head_matvec(_ptr(W), N, K, _ptr(x), _ptr(y), _stream(stream, y)), "dense_head_matvec")
+
+
+def dense_head_matvec_i8(W, row_scale, N, K, x, y, stream=None):
+    _check(lib.dense_head_matvec_i8(_ptr(W), _ptr(row_scale), N, K, _ptr(x), _ptr(y), _stream(stream, y)),
+           "dense_head_matvec_i8")
 
 
 class Batch:

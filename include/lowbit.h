@@ -148,6 +148,17 @@ lb_status lowbit_block_sums(int fmt, const void *W, int64_t N, int64_t K, int af
 lb_status dense_head_matvec(const uint16_t *W, int64_t N, int64_t K, const float *x, float *y, hipStream_t s);
 
 /*
+ * int8 dense head matvec y[n] = row_scale[n] * sum_k W[n][k] * x[k], accumulated in fp32 (tritium
+ * "Architecture", section 10: int8 is the obvious move for the head, at half the bf16 head's bytes; the
+ * reading taken: symmetric int8 weights with one fp32 scale per row).
+ *   W: device int8 [N][K], 16-byte aligned; row_scale: device fp32 [N], 4-byte aligned; x: device fp32 [K],
+ *   16-byte aligned; y: device fp32 [N], 4-byte aligned.  K must be a multiple of 16 and at most 8192
+ *   (the activation vector is held in registers) and the weights smaller than 4 GiB; otherwise LB_ESHAPE.
+ */
+lb_status dense_head_matvec_i8(const int8_t *W, const float *row_scale, int64_t N, int64_t K, const float *x, float *y,
+                               hipStream_t s);
+
+/*
  * Many independent decode products in ONE launch (a token's work list).  A batch is a set-up object:
  * lowbit_batch_create validates the host-side list, and copies it with its tile table into device
  * memory it allocates once; lowbit_matvec_batched then enqueues, on `s`, one kernel per (weight format,

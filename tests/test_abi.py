@@ -84,6 +84,12 @@ def test_other_entry_points_validate():
     assert lib.dense_head_matvec(A16, 8, 8192, A16, A16, None) == L.LB_ESHAPE
     assert lib.dense_head_matvec(A16, 1 << 20, 2048, A16, A16, None) == L.LB_ESHAPE  # 4 GiB of weights
     assert lib.dense_head_matvec(A16 + 2, 8, 64, A16, A16, None) == L.LB_EALIGN
+    assert lib.dense_head_matvec_i8(A16, A16, 8, 24, A16, A16, None) == L.LB_ESHAPE  # K % 16
+    assert lib.dense_head_matvec_i8(A16, A16, 8, 8192 + 16, A16, A16, None) == L.LB_ESHAPE
+    assert lib.dense_head_matvec_i8(A16, A16, 1 << 20, 4096, A16, A16, None) == L.LB_ESHAPE  # 4 GiB of weights
+    assert lib.dense_head_matvec_i8(A16 + 8, A16, 8, 64, A16, A16, None) == L.LB_EALIGN
+    assert lib.dense_head_matvec_i8(A16, None, 8, 64, A16, A16, None) == L.LB_EINVAL
+    assert lib.dense_head_matvec_i8(None, None, 0, 64, None, None, None) == L.LB_OK
     assert lib.lowbit_matvec_batched(None, None) == L.LB_EINVAL
     h = ctypes.c_void_p()
     assert lib.lowbit_batch_create(None, 0, ctypes.byref(h)) == L.LB_EINVAL

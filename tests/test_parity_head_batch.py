@@ -1,4 +1,4 @@
-"""GPU parity of the dense bf16 head and of the batched decode launch against the CPU oracle."""
+"""GPU parity of the dense bf16 and int8 heads and of the batched decode launch against the CPU oracle."""
 import numpy as np
 import pytest
 import torch
@@ -37,6 +37,40 @@ def test_head_full_size_sampled():
     rows = np.unique(np.concatenate([synth.rng(4102).integers(0, N, 2000), [0, N - 1]]))
     y_ref, A = oracle.head_matvec(W, N, K, x, rows=rows)
     assert_close(y[rows], y_ref, A, K, "head full size (sampled rows)")
+
+
+def gpu_head_i8(W, s, N, K, x):
+    y = torch.empty(max(N, 1), dtype=torch.float32, device="cuda")
+    L.dense_head_matvec_i8(dev(W), dev(s), N, K, dev(x), y)
+    return host(y)[:N]
+
+
+@pytest.mark.parametrize("N,K", [(1, 16), (3, 64), (77, 528), (65, 1040), (1000, 2560), (300, 4096), (17, 8192),
+                                 (129, 6912)])
+def test_head_i8_shapes(N, K):
+    say(f"case head int8 N={N} K={K}")
+    W, s = synth.head_weights_i8(N, K, 4200 + N)
+    x = synth.activations(synth.rng(4201 + K), 1, K)[0]
+    y = gpu_head_i8(W, s, N, K, x)
+    y_ref, A = oracle.head_matvec_i8(W, s, N, K, x)
+    assert_close(y, y_ref, A, K, f"head int8 {N}x{K}")
+
+
+def test_head_i8_full_size_sampled_and_extremes():
+    """The 128256 x 2560 head in int8 (oracle on a seeded sample of rows); bytes -128 and +127 with a unit
+    scale against integer activations give the integer dot products exactly."""
+    N, K = synth.BITNET_HEAD
+    say(f"case head int8 full {N}x{K}")
+    W, s = synth.head_weights_i8(N, K, 4300)
+    x = synth.activations(synth.rng(4301), 1, K)[0]
+    y = gpu_head_i8(W, s, N, K, x)
+    rows = np.unique(np.concatenate([synth.rng(4302).integers(0, N, 2000), [0, N - 1]]))
+    y_ref, A = oracle.head_matvec_i8(W, s, N, K, x, rows=rows)
+    assert_close(y[rows], y_ref, A, K, "head int8 full size (sampled rows)")
+    Wx = np.where(synth.rng(4303).integers(0, 2, (64, 1024)) == 1, 127, -128).astype(np.int8)
+    xi = synth.rng(4304).integers(-64, 64, 1024).astype(np.float32)
+    yi = gpu_head_i8(Wx, np.ones(64, np.float32), 64, 1024, xi)
+    assert np.array_equal(yi.astype(np.float64), (Wx.astype(np.int64) @ xi.astype(np.int64)).astype(np.float64))
 
 
 def _product(fmt, N, K, seed):
