@@ -146,6 +146,69 @@ class DecodeToken:
         return self.weight_bytes - self.head_bytes + self.act_bytes + self.out_bytes
 
 
+FEEDS = {"attn_q": 0, "attn_k": 0, "attn_v": 0, "attn_output": 1, "ffn_gate": 2, "ffn_up": 2, "ffn_down": 3}
+
+
+class LayeredGraph:
+    """A token in dependency order: per layer, the q/k/v products, then o, then gate/up, then down, each phase
+    one batched launch after the quantisation of its own input row (288 launches for 36 layers), captured
+    once as a HIP graph and replayed."""
+
+    def __init__(self, tok):
+        import torch
+
+        L = tok.L
+        self.tok, self.phases = tok, []
+        for l in range(tok.layers):
+            for f in range(4):
+                prods = [p for p in tok.products if p["layer"] == l and FEEDS[p["name"]] == f]
+                if not prods:
+                    continue
+                K, r = prods[0]["feed"]
+                descs = [L.desc(tok.fmt, p["W"], p["N"], p["K"], p["xq"], p["xs"], p["y"], w_tensor_scale=p["w_scale"])
+                         for p in prods]
+                self.phases.append((K, r, L.Batch(descs)))
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            self.eager()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        self.graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.graph):
+            self.eager()
+        torch.cuda.synchronize()
+
+    def eager(self):
+        t, L = self.tok, self.tok.L
+        for K, r, b in self.phases:
+            L.lowbit_quantize_act(t.afmt, t.x[K][r:r + 1], 1, K, t.xq[K][r:r + 1], t.xs[K][r:r + 1])
+            b.run()
+
+    def launches(self):
+        return 2 * len(self.phases)
+
+    def close(self):
+        for _, _, b in self.phases:
+            b.close()
+
+
+def time_graph(lg, steps, warmup):
+    """ms per replay of the layered token graph, by HIP events on the replay stream."""
+    import torch
+
+    for _ in range(warmup):
+        lg.graph.replay()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        lg.graph.replay()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / steps
+
+
 def time_token(tok, steps, warmup):
     """Time `steps` whole steps (quantise + batched products) and, inside them, the batched launch alone
     with HIP events on the stream the kernels run on (torch's current stream)."""
@@ -318,8 +381,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle leg (profiling runs)")
-    ap.add_argument("--secondary", default="q1,planar,q8,prefill",
-                    help="comma list of extra workloads: q1, planar, q8, prefill, none")
+    ap.add_argument("--secondary", default="layered,q1,planar,q8,prefill",
+                    help="comma list of extra workloads: layered, q1, planar, q8, prefill, none")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU: this library has no multi-GPU path (asked for --gpus {args.gpus}). "
@@ -393,11 +456,23 @@ def main():
             "sample": f"first {layers} of 36 layers (all 7 products each, q8_0 quantise included), the same "
                       f"bytes as the GPU run: {wb} weight bytes in {t_cpu:.2f} s on one host thread",
         }
+    secondary = {}
+    if "layered" in args.secondary.split(","):
+        # the same token in dependency order (per layer q/k/v, o, gate/up, down), replayed as one HIP graph
+        lg = LayeredGraph(tok)
+        msg = time_graph(lg, args.steps, args.warmup)
+        secondary["q2_0_8b_token_layered_graph"] = {
+            "workload": "the headline token in dependency order: per layer q/k/v, o, gate/up, down, each phase a "
+                        "q8_0 quantise of its input plus one batched launch, captured as one HIP graph",
+            "launches": lg.launches(), "ms_per_token": round(msg, 5),
+            "gbs": round(tok.weight_bytes / (msg * 1e-3) / 1e9, 1),
+            "pct_hbm_peak": round(100 * tok.weight_bytes / (msg * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+        }
+        lg.close()
     tok.batch.close()
     del tok
     torch.cuda.empty_cache()
 
-    secondary = {}
     for name in [s for s in args.secondary.split(",") if s and s != "none"]:
         if name == "q1":
             t1 = DecodeToken(synth.Q1_0, synth.QWEN3_8B_LAYER, synth.QWEN3_8B_LAYERS, seed=1002)

@@ -8,7 +8,7 @@ import torch
 
 import oracle
 import synth
-from bench import DecodeToken
+from bench import DecodeToken, LayeredGraph
 from gpu_util import say
 
 pytestmark = pytest.mark.gpu
@@ -55,7 +55,7 @@ def _check_token(tok, rows_per_product=6, seed=0):
     assert len(tok.products) == 7 * tok.layers
 
 
-@pytest.mark.parametrize("fmt", [synth.Q2_0_G64, synth.Q1_0], ids=["Q2_0_g64", "Q1_0"])
+@pytest.mark.parametrize("fmt", [synth.Q2_0_G64, synth.Q1_0, synth.Q8_0], ids=["Q2_0_g64", "Q1_0", "Q8_0"])
 def test_qwen3_8b_token_full_size(fmt):
     say(f"case full token fmt={fmt}")
     tok = _run_token(fmt, synth.QWEN3_8B_LAYER, synth.QWEN3_8B_LAYERS, seed=7000 + fmt)
@@ -67,4 +67,31 @@ def test_bitnet_planar_token_full_size():
     say("case full planar token")
     tok = _run_token(synth.TERNARY_PLANAR, synth.BITNET_2B_LAYER, synth.BITNET_2B_LAYERS, seed=7300)
     _check_token(tok, seed=7301)
+    tok.batch.close()
+
+
+@pytest.mark.parametrize("fmt", [synth.Q2_0_G64, synth.TERNARY_PLANAR], ids=["Q2_0_g64", "planar"])
+def test_layered_graph_replays_match_eager_and_oracle(fmt):
+    """The dependency-ordered token captured as one HIP graph: every replay (with eager work and a clobber of
+    every output between replays) gives the eager outputs bit for bit, and those match the oracle."""
+    layer = synth.QWEN3_8B_LAYER if fmt != synth.TERNARY_PLANAR else synth.BITNET_2B_LAYER
+    say(f"case layered graph fmt={fmt}")
+    tok = DecodeToken(fmt, layer, 3, seed=7400 + fmt, keep_blocks_layers=3)
+    lg = LayeredGraph(tok)
+    lg.eager()
+    torch.cuda.synchronize()
+    ref = [p["y"].clone() for p in tok.products]
+    _check_token(tok, seed=7401)
+    for rep in range(3):
+        for p in tok.products:
+            p["y"].fill_(float("nan"))
+        tok.xqbuf.zero_()
+        torch.cuda.synchronize()
+        lg.graph.replay()
+        torch.cuda.synchronize()
+        for p, y0 in zip(tok.products, ref):
+            assert torch.equal(p["y"], y0), f"replay {rep}: {p['name']} layer {p['layer']} differs from eager"
+        tok.step()  # eager work between replays
+        torch.cuda.synchronize()
+    lg.close()
     tok.batch.close()
