@@ -20,7 +20,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "lowbit_oracle.c")
 _LIB = os.path.join(_HERE, "liblowbit_oracle.so")
 
-Q1_0, Q2_0_G64, TERNARY_PLANAR, Q8_0 = 1, 2, 3, 4
+Q1_0, Q2_0_G64, TERNARY_PLANAR, Q8_0, TERNARY_B3 = 1, 2, 3, 4, 5
 QK8 = 32
 
 CFLAGS = ["-O2", "-std=c99", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared", "-Wall"]
@@ -61,6 +61,9 @@ def lib():
             "lbo_matvec_planar": (I, [P, I64, I64, P, ctypes.c_float, ctypes.c_float, P, I64, P, P]),
             "lbo_head_matvec": (I, [P, I64, I64, P, P, I64, P, P]),
             "lbo_head_matvec_i8": (I, [P, P, I64, I64, P, P, I64, P, P]),
+            "lbo_b3_decode": (I, [P, I64, I64, P]),
+            "lbo_b3_encode": (I, [P, I64, I64, P]),
+            "lbo_matvec_b3": (I, [P, I64, I64, P, ctypes.c_float, ctypes.c_float, P, I64, P, P]),
         }
         for name, (res, args) in sig.items():
             f = getattr(_lib, name)
@@ -201,6 +204,33 @@ def matvec_planar(raw, N, K, q, s_x, s_w, rows=None):
     y = np.empty(n, dtype=np.float32)
     _check(lib().lbo_matvec_planar(_p(raw), N, K, _p(q), float(s_x), float(s_w), _p(r), n, _p(acc), _p(y)),
            "matvec_planar")
+    return acc, y
+
+
+def b3_decode(raw, N, K):
+    """base-3 beats -> w int8 [N][K] in {-1, 0, +1}"""
+    raw = _c(raw, np.uint8)
+    w = np.empty((N, K), dtype=np.int8)
+    _check(lib().lbo_b3_decode(_p(raw), N, K, _p(w)), "b3_decode")
+    return w
+
+
+def b3_encode(w, N, K):
+    """w int8 [N][K] in {-1, 0, +1} -> base-3 beat bytes"""
+    w = _c(w, np.int8)
+    raw = np.empty(weight_bytes(TERNARY_B3, N, K), dtype=np.uint8)
+    _check(lib().lbo_b3_encode(_p(w), N, K, _p(raw)), "b3_encode")
+    return raw
+
+
+def matvec_b3(raw, N, K, q, s_x, s_w, rows=None):
+    """-> (acc int32 [nrows], y float32 [nrows]) with y = ((float)acc * s_x) * s_w"""
+    raw = _c(raw, np.uint8)
+    q = _c(q, np.int8).ravel()
+    r, n = _rows(rows, N)
+    acc = np.empty(n, dtype=np.int32)
+    y = np.empty(n, dtype=np.float32)
+    _check(lib().lbo_matvec_b3(_p(raw), N, K, _p(q), float(s_x), float(s_w), _p(r), n, _p(acc), _p(y)), "matvec_b3")
     return acc, y
 
 

@@ -25,6 +25,7 @@
  *     activations (vec_dot_q8_0_q8_0 of [BH] 0.3.9: one block of 32 on each side, one scale each);
  *   - the planar output ((float)acc * s_x) * s_w in fp32 with two roundings ([ARCH] s.5 names the
  *     twice-multiplied order);
+ *   - base-3 ternary beats (five trits per byte) with the planar format's output rule, bit-exact;
  *   - the dense bf16 head y = sum_k bf16(W) * x in fp64 (every product exact), and the int8 head
  *     y = s_w[r] * sum_k W * x with one fp32 scale per row, also in fp64.
  *
@@ -41,8 +42,9 @@
 #define QKP 64  /* columns per planar beat  ([ARCH] s.2) */
 #define QK8 32  /* activations per q8_0 block ([TR] III.2) */
 #define QKW8 32 /* weights per Q8_0 weight block: the q8_0 block of [TR] III.2 applied to weights ([BH] 0.3.9) */
+#define QKB3 80 /* columns per base-3 beat: 16 bytes of five trits each ([TR] III.8: 3^5 = 243 <= 256) */
 
-enum { FMT_Q1_0 = 1, FMT_Q2_0_G64 = 2, FMT_PLANAR = 3, FMT_Q8_0 = 4 };
+enum { FMT_Q1_0 = 1, FMT_Q2_0_G64 = 2, FMT_PLANAR = 3, FMT_Q8_0 = 4, FMT_B3 = 5 };
 
 /* ------------------------------------------------------------------------------------------------
  * binary16 and bfloat16 conversions ([TR] III.2: the scale is "a 16-bit IEEE 754 half-precision" value)
@@ -121,22 +123,29 @@ static uint64_t le64(const uint8_t *p)
 
 int64_t lbo_block_weights(int fmt)
 {
-    return fmt == FMT_Q1_0 ? QK1 : fmt == FMT_Q2_0_G64 ? QK2 : fmt == FMT_PLANAR ? QKP : fmt == FMT_Q8_0 ? QKW8 : 0;
+    return fmt == FMT_Q1_0 ? QK1 : fmt == FMT_Q2_0_G64 ? QK2 : fmt == FMT_PLANAR ? QKP : fmt == FMT_Q8_0 ? QKW8
+         : fmt == FMT_B3 ? QKB3 : 0;
 }
 
 /* Q8_0: a binary16 scale and 32 signed bytes, 34 bytes per 32 weights (8.5 bits per weight) */
 int64_t lbo_block_bytes(int fmt)
 {
     return fmt == FMT_Q1_0 ? 2 + QK1 / 8 : fmt == FMT_Q2_0_G64 ? 2 + QK2 / 4 : fmt == FMT_PLANAR ? 16
-         : fmt == FMT_Q8_0 ? 2 + QKW8 : 0;
+         : fmt == FMT_Q8_0 ? 2 + QKW8 : fmt == FMT_B3 ? QKB3 / 5 : 0;
 }
 
 static int is_ggml(int fmt) { return fmt == FMT_Q1_0 || fmt == FMT_Q2_0_G64 || fmt == FMT_Q8_0; }
 
+/* Base-3 beats: a row of K columns (K a multiple of 64, as planar rows) takes ceil(K / 80) beats, the
+ * columns past K coded as weight 0; every other format takes whole blocks. */
 int64_t lbo_weight_bytes(int fmt, int64_t N, int64_t K)
 {
     int64_t qk = lbo_block_weights(fmt);
-    if (qk == 0 || N < 0 || K < 0 || K % qk)
+    if (qk == 0 || N < 0 || K < 0)
+        return -1;
+    if (fmt == FMT_B3)
+        return K % 64 ? -1 : N * ((K + QKB3 - 1) / QKB3) * 16;
+    if (K % qk)
         return -1;
     return N * (K / qk) * lbo_block_bytes(fmt);
 }
@@ -176,7 +185,7 @@ static int planar_weight(const uint8_t *beat, int c)
 int lbo_decode(int fmt, const uint8_t *raw, int64_t N, int64_t K, int8_t *w, float *d)
 {
     int64_t qk = lbo_block_weights(fmt), bb = lbo_block_bytes(fmt);
-    if (qk == 0 || K % qk)
+    if (qk == 0 || K % qk || fmt == FMT_B3) /* base-3 beats: lbo_b3_decode */
         return -1;
     int64_t nb = K / qk;
     for (int64_t r = 0; r < N; r++)
@@ -196,7 +205,7 @@ int lbo_decode(int fmt, const uint8_t *raw, int64_t N, int64_t K, int8_t *w, flo
 int lbo_encode(int fmt, const int8_t *w, const uint16_t *dh, int64_t N, int64_t K, uint8_t *raw)
 {
     int64_t qk = lbo_block_weights(fmt), bb = lbo_block_bytes(fmt);
-    if (qk == 0 || K % qk)
+    if (qk == 0 || K % qk || fmt == FMT_B3) /* base-3 beats: lbo_b3_encode */
         return -1;
     int64_t nb = K / qk;
     for (int64_t r = 0; r < N; r++)
@@ -547,6 +556,86 @@ int lbo_head_matvec_i8(const int8_t *W, const float *s_w, int64_t N, int64_t K, 
         y[t] = (double)s_w[r] * acc;
         if (A)
             A[t] = fabs((double)s_w[r]) * mag;
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------------------------------
+ * Base-3 ternary beats ([TR] III.8 "Information": 3^5 = 243 <= 256, so five trits fit in one byte,
+ * 1.6 bits per trit; [ARCH] s.10: base-3 packing at 1.6 b/w as the next step for the ternary body,
+ * whose planar layout this format replaces).  The readings taken: byte j of a 16-byte beat holds columns
+ * 5j .. 5j + 4 of the beat's 80 as the base-3 integer sum_t (w + 1) * 3^t, lowest digit first (as the
+ * 2-bit codes are "lowest bits first"); a row of K columns takes ceil(K / 80) beats, columns past K coded
+ * 0; one fp32 per-tensor scale and per-token int8 activations, as the planar format it replaces:
+ *   acc[r] = sum_k w[r][k] * q[k]  (exact integer),   y[r] = ((float)acc[r] * s_x) * s_w.
+ * ---------------------------------------------------------------------------------------------- */
+
+/* weight of column c of a row's beat stream: digit c % 5 of byte c / 5, by repeated division */
+static int b3_weight(const uint8_t *row, int64_t c)
+{
+    int v = row[c / 5];
+    for (int t = 0; t < (int)(c % 5); t++)
+        v /= 3;
+    return v % 3 - 1;
+}
+
+int lbo_b3_decode(const uint8_t *raw, int64_t N, int64_t K, int8_t *w)
+{
+    if (K % 64)
+        return -1;
+    int64_t rb = (K + QKB3 - 1) / QKB3 * 16;
+    for (int64_t r = 0; r < N; r++)
+        for (int64_t c = 0; c < K; c++) {
+            int v = raw[r * rb + c / 5];
+            if (v > 242)
+                return -2; /* not a base-3 byte */
+            w[r * K + c] = (int8_t)b3_weight(raw + r * rb, c);
+        }
+    return 0;
+}
+
+int lbo_b3_encode(const int8_t *w, int64_t N, int64_t K, uint8_t *raw)
+{
+    if (K % 64)
+        return -1;
+    int64_t nbt = (K + QKB3 - 1) / QKB3, rb = nbt * 16;
+    for (int64_t r = 0; r < N; r++)
+        for (int64_t j = 0; j < rb; j++) {
+            int v = 0;
+            for (int t = 4; t >= 0; t--) {
+                int64_t c = 5 * j + t;
+                int wv = c < K ? w[r * K + c] : 0;
+                if (wv < -1 || wv > 1)
+                    return -1;
+                v = 3 * v + (wv + 1);
+            }
+            raw[r * rb + j] = (uint8_t)v;
+        }
+    return 0;
+}
+
+int lbo_matvec_b3(const uint8_t *raw, int64_t N, int64_t K, const int8_t *q, float s_x, float s_w,
+                  const int64_t *rows, int64_t nrows, int32_t *acc_out, float *y)
+{
+    if (K % 64)
+        return -1;
+    int64_t rb = (K + QKB3 - 1) / QKB3 * 16;
+    for (int64_t t = 0; t < nrows; t++) {
+        int64_t r = row_of(rows, t);
+        if (r < 0 || r >= N)
+            return -1;
+        int64_t acc = 0;
+        for (int64_t c = 0; c < K; c++)
+            acc += (int64_t)b3_weight(raw + r * rb, c) * q[c];
+        if (acc > INT32_MAX || acc < INT32_MIN)
+            return -2;
+        if (acc_out)
+            acc_out[t] = (int32_t)acc;
+        if (y) {
+            float a = (float)acc; /* exact: |acc| < 2^24 */
+            float ys = a * s_x;
+            y[t] = ys * s_w;
+        }
     }
     return 0;
 }

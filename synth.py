@@ -14,6 +14,10 @@ Formats (byte layouts as the pages define them):
   i//4, bits 2*(i%4)); code c stands for weight c-1.
 * planar ternary ``.trit v1`` beat -- tritium "Architecture", section 2 "The one design commitment: bit
   planes": 16 bytes per 64 consecutive columns of one row, ``{u64 pos, u64 neg}``, column c at bit c.
+* base-3 ternary beats -- the bankml report, section III.8 "Information" (five trits fit in one byte,
+  3^5 = 243 <= 256) and tritium "Architecture", section 10 (base-3 packing at 1.6 b/w for the ternary
+  body): 16 bytes per 80 consecutive columns of one row, byte j holding columns 5j..5j+4 as the base-3
+  integer sum_t (w + 1) * 3^t, lowest digit first; a row takes ceil(K/80) beats, columns past K coded 0.
 * ggml ``Q8_0`` weights -- the q8_0 block of the bankml report, section III.2 (a binary16 scale, then 32
   signed bytes), used for weights as the build history's 0.3.9 entry and its "Q8_0 weights" item do:
   34-byte blocks of 32 weights.
@@ -33,10 +37,12 @@ Q1_0 = 1
 Q2_0_G64 = 2
 TERNARY_PLANAR = 3
 Q8_0 = 4
+TERNARY_B3 = 5
 
 QK1 = 128  # weights per Q1_0 block
 QK2 = 64  # weights per Q2_0_g64 block
 QKP = 64  # columns per planar beat
+QKB3 = 80  # columns per base-3 beat (16 bytes of five trits)
 QK8 = 32  # activations per q8_0 block (and weights per Q8_0 weight block)
 
 BLOCK_BYTES = {Q1_0: 18, Q2_0_G64: 18, TERNARY_PLANAR: 16, Q8_0: 34}
@@ -118,6 +124,18 @@ def lay_out_q8_0(w: np.ndarray, d: np.ndarray) -> np.ndarray:
     return out
 
 
+def lay_out_b3(w: np.ndarray) -> np.ndarray:
+    """Base-3 beats for ternary ``w`` [N][K] in {-1,0,+1}: columns padded with 0 to a whole number of 80-column
+    beats, then byte j of a row = sum_t (w[5j+t] + 1) * 3^t.  Returns uint8 [N][ceil(K/80)][16]."""
+    N, K = w.shape
+    nbt = -(-K // QKB3)
+    c = np.ones((N, nbt * QKB3), dtype=np.int64)  # code 1 = weight 0 for the padding columns
+    c[:, :K] = w.astype(np.int64) + 1
+    digits = c.reshape(N, nbt * 16, 5)
+    v = digits[..., 0] + 3 * digits[..., 1] + 9 * digits[..., 2] + 27 * digits[..., 3] + 81 * digits[..., 4]
+    return v.astype(np.uint8).reshape(N, nbt, 16)
+
+
 def lay_out_planar(w: np.ndarray) -> np.ndarray:
     """Planar beats for ternary ``w`` [N][K] in {-1,0,+1}: per 64 columns 8 bytes of the "+1" plane
     then 8 bytes of the "-1" plane, column c at bit c (little-endian u64).  Returns uint8 [N][K/64][16]."""
@@ -172,6 +190,11 @@ def make_weights(fmt: int, N: int, K: int, seed: int, p=TERNARY_P) -> Weights:
         w = byte_weights(g, N, K)
         d = q8_scales(g, N * (K // QK8)).reshape(N, K // QK8)
         return Weights(fmt, N, K, lay_out_q8_0(w, d), w, d=d)
+    if fmt == TERNARY_B3:
+        p3 = np.asarray(p[:3], dtype=np.float64)
+        w = ternary_weights(g, N, K, tuple(p3 / p3.sum()) + (0.0,))
+        s_w = np.float32(abs(g.standard_normal()) * 0.02)
+        return Weights(fmt, N, K, lay_out_b3(w), w, s_w=s_w)
     if fmt == TERNARY_PLANAR:
         p3 = np.asarray(p[:3], dtype=np.float64)
         w = ternary_weights(g, N, K, tuple(p3 / p3.sum()) + (0.0,))
@@ -229,6 +252,8 @@ PREFILL_SHAPES = ((4096, 4096), (12288, 4096))
 
 def format_bytes(fmt: int, N: int, K: int) -> int:
     """Bytes of a packed weight tensor in its on-disk format (18 or 34 B per ggml block, 16 B per beat)."""
+    if fmt == TERNARY_B3:
+        return N * (-(-K // QKB3)) * 16
     return N * (K // BLOCK_WEIGHTS[fmt]) * BLOCK_BYTES[fmt]
 
 
@@ -281,6 +306,22 @@ def device_planar_beats(N: int, K: int, seed: int, device="cuda"):
     out[:, :, 0:8] = (pos[:, :, 0] << shifts).sum(dim=-1, dtype=torch.uint8)
     out[:, :, 8:16] = (neg[:, :, 0] << shifts).sum(dim=-1, dtype=torch.uint8)
     return out
+
+
+def device_b3_beats(N: int, K: int, seed: int, device="cuda"):
+    """Base-3 beats [N][ceil(K/80)][16] (uint8) with weights -1/0/+1 at 31/38/31 %, drawn on the device."""
+    import torch
+
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    nbt = -(-K // QKB3)
+    u = torch.rand((N, nbt * QKB3), generator=g, device=device)
+    lo, hi = TERNARY_P[0], TERNARY_P[0] + TERNARY_P[1]
+    c = (u >= lo).to(torch.int32) + (u >= hi).to(torch.int32)  # code 0, 1, 2 = weight -1, 0, +1
+    c[:, K:] = 1
+    d = c.view(N, nbt * 16, 5)
+    v = d[..., 0] + 3 * d[..., 1] + 9 * d[..., 2] + 27 * d[..., 3] + 81 * d[..., 4]
+    return v.to(torch.uint8).view(N, nbt, 16)
 
 
 def device_head_weights_i8(N: int, K: int, seed: int, device="cuda"):
