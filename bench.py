@@ -47,7 +47,7 @@ class DecodeToken:
         import synth
 
         self.fmt, self.layers, self.L = fmt, layers, L
-        planar = fmt == synth.TERNARY_PLANAR
+        planar = fmt in (synth.TERNARY_PLANAR, synth.TERNARY_B3)  # per-token activations, per-tensor scale
         # distinct activation vectors per layer: attention input (q, k, v), o input, ffn input (gate, up),
         # down input -- grouped by K so each group is quantised by one launch
         names = [n for n, _, _ in layer_shapes]
@@ -85,9 +85,14 @@ class DecodeToken:
         for l in range(layers):
             for j, (n, N, K) in enumerate(layer_shapes):
                 s = seed + 1000 * (l + 1) + j
-                if planar:
+                if fmt == synth.TERNARY_PLANAR:
                     raw = synth.device_planar_beats(N, K, s)
                     packed = raw.reshape(-1)
+                    w_scale = float(abs(torch.randn((), generator=g, device="cuda").item()) * 0.02)
+                elif fmt == synth.TERNARY_B3:
+                    raw = synth.device_b3_beats(N, K, s)
+                    packed = torch.empty(L.lowbit_weight_bytes(fmt, N, K), dtype=torch.uint8, device="cuda")
+                    L.lowbit_pack_weights(fmt, raw.reshape(-1), N, K, packed)
                     w_scale = float(abs(torch.randn((), generator=g, device="cuda").item()) * 0.02)
                 else:
                     raw = synth.device_ggml_blocks(fmt, N, K, s)
@@ -381,8 +386,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle leg (profiling runs)")
-    ap.add_argument("--secondary", default="layered,q1,planar,q8,prefill",
-                    help="comma list of extra workloads: layered, q1, planar, q8, prefill, none")
+    ap.add_argument("--secondary", default="layered,q1,planar,b3,q8,prefill",
+                    help="comma list of extra workloads: layered, q1, planar, b3, q8, prefill, none")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU: this library has no multi-GPU path (asked for --gpus {args.gpus}). "
@@ -495,6 +500,7 @@ def main():
                 "weight_bytes": tp.weight_bytes, "ms_per_step": round(msp, 5),
                 "gbs": round(tp.weight_bytes / (msp * 1e-3) / 1e9, 1),
                 "pct_hbm_peak": round(100 * tp.weight_bytes / (msp * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+                "products_launch_ms": round(mlp, 5),
                 "products_launch_gbs": round(tp.algorithmic_bytes / (mlp * 1e-3) / 1e9, 1),
             }
             hms, hg = head_gbs(*synth.BITNET_HEAD)
@@ -506,6 +512,21 @@ def main():
                                                   "speedup_vs_bf16_head": round(hms / ims, 3)}
             tp.batch.close()
             del tp
+        elif name == "b3":
+            tb = DecodeToken(synth.TERNARY_B3, synth.BITNET_2B_LAYER, synth.BITNET_2B_LAYERS, seed=1009,
+                             head=synth.BITNET_HEAD)
+            msb, mlb = time_token(tb, max(10, args.steps // 2), 5)
+            secondary["base3_2b_token"] = {
+                "workload": "the BitNet-b1.58-2B token with base-3 ternary beats (five trits per byte, 1.6 b/w) "
+                            "in place of planar beats, 30 layers x 7 products + the dense bf16 head",
+                "weight_bytes": tb.weight_bytes, "ms_per_step": round(msb, 5),
+                "gbs": round(tb.weight_bytes / (msb * 1e-3) / 1e9, 1),
+                "pct_hbm_peak": round(100 * tb.weight_bytes / (msb * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+                "products_launch_ms": round(mlb, 5),
+                "products_launch_gbs": round(tb.algorithmic_bytes / (mlb * 1e-3) / 1e9, 1),
+            }
+            tb.batch.close()
+            del tb
         elif name == "q8":
             t8 = DecodeToken(synth.Q8_0, synth.QWEN3_8B_LAYER, synth.QWEN3_8B_LAYERS, seed=1007)
             ms8, ml8 = time_token(t8, max(10, args.steps // 5), 3)

@@ -33,10 +33,21 @@ lb_status hip_fail(const char *fn, hipError_t e)
 
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
-bool is_wfmt(int f) { return f == LB_Q1_0 || f == LB_Q2_0_G64 || f == LB_TERNARY_PLANAR || f == LB_Q8_0; }
+bool is_wfmt(int f)
+{
+    return f == LB_Q1_0 || f == LB_Q2_0_G64 || f == LB_TERNARY_PLANAR || f == LB_Q8_0 || f == LB_TERNARY_B3;
+}
+// K must be a multiple of this (base-3 rows are whole planar widths; their beats hold 80 columns)
 int64_t block_weights(int f) { return f == LB_Q1_0 ? 128 : f == LB_Q8_0 ? 32 : 64; }
 int64_t block_bytes(int f) { return f == LB_TERNARY_PLANAR ? 16 : f == LB_Q8_0 ? 34 : 18; }
-int paired_afmt(int f) { return f == LB_TERNARY_PLANAR ? LB_ACT_I8_ROW : LB_ACT_Q8_0; }
+int paired_afmt(int f) { return f == LB_TERNARY_PLANAR || f == LB_TERNARY_B3 ? LB_ACT_I8_ROW : LB_ACT_Q8_0; }
+// bytes of an N x K tensor (K a multiple of block_weights)
+int64_t tensor_bytes(int f, int64_t N, int64_t K)
+{
+    if (f == LB_TERNARY_B3)
+        return N * ((K + 79) / 80) * 16;
+    return N * (K / block_weights(f)) * block_bytes(f);
+}
 
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_dev_state[kMaxDevices]; // 0 unknown, 1 gfx950, 2 other
@@ -79,11 +90,13 @@ lb_status check_product(const char *fn, int fmt, const void *W, int64_t N, int64
         return fail(LB_ESHAPE, fn, "negative size");
     if (K % block_weights(fmt))
         return fail(LB_ESHAPE, fn, "K is not a multiple of the weight block (128 for Q1_0, 32 for Q8_0, 64 otherwise)");
+    if (fmt == LB_TERNARY_B3 && K > 10240) // a row is at most 64 lanes of two beats
+        return fail(LB_ESHAPE, fn, "K above 10240 for base-3 beats");
     if (K > 32768 || N > INT32_MAX)
         return fail(LB_ESHAPE, fn, "K above 32768 or N above 2^31-1");
     if (fmt == LB_Q8_0 && K > 16384) // a row is at most one wave of lanes with 8 blocks each
         return fail(LB_ESHAPE, fn, "K above 16384 for Q8_0");
-    if (N * (K / block_weights(fmt)) * block_bytes(fmt) >= (int64_t(1) << 32))
+    if (tensor_bytes(fmt, N, K) >= (int64_t(1) << 32))
         return fail(LB_ESHAPE, fn, "weight tensor of 4 GiB or more");
     if (N == 0)
         return LB_OK;
@@ -123,7 +136,7 @@ int64_t lowbit_weight_bytes(int fmt, int64_t N, int64_t K)
 {
     if (!is_wfmt(fmt) || N < 0 || K < 0 || K % block_weights(fmt))
         return -1;
-    return N * (K / block_weights(fmt)) * block_bytes(fmt);
+    return tensor_bytes(fmt, N, K);
 }
 
 static lb_status pack_common(const char *fn, int fmt, const void *src, int64_t N, int64_t K, void *dst,

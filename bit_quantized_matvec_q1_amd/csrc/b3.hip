@@ -1,0 +1,298 @@
+// Batch-1 decode product of base-3 ternary beats (five trits per byte) with per-token int8 activations.
+//
+// Arithmetic (bankml technical report, section III.8 "Information" and "Operation": five trits fit in a
+// byte, 3^5 = 243 <= 256, and the ternary product is an exact signed sum; tritium "Architecture",
+// sections 1, 2, 5 and 10: the planar body's select-accumulate, its output rule y = ((float)acc * s_x) * s_w,
+// and base-3 packing at 1.6 bits per weight as the open question this kernel measures): with the stored code
+// c = w + 1 of each trit, acc = sum c q - sum q, exactly.
+//
+// Decode on CDNA4.  The device layout (lowbit_pack_weights) keeps the beat stream but stores each base-3
+// byte v as the 8-bit fraction b = ceil(256 v / 243): then the leading m base-3 digits of v are
+// F_m = floor(3^m b / 256), digit 5 - m is F_m - 3 F_(m-1), and for the five columns j0 .. j0 + 4 of a byte
+//     sum_t c_t q_(j0+t) = sum_(m=1..5) F_m * Q_m,   Q_m = q_(j0+5-m) - 3 q_(j0+4-m) (m <= 4),   Q_5 = q_j0,
+// so the activation (not the weights) carries the base-3 structure, rearranged once per workgroup.  Per
+// pair of bytes held in the 16-bit halves of a register (one byte permute per pair), each m costs one
+// multiply by 3, one byte permute (the two fields' high bytes are the floors) and one v_dot2_i32_i16
+// against a staged pair of Q_m: 15 operations per 10 weights, against 4 for the 2-bit planar beat.
+//
+// Work split as in the other decode kernels: a row over L lanes, S beats per lane (strided by L so a
+// wave-wide 16-byte load is contiguous), the staged activation pairs held in registers for every row a
+// lane streams, the next row's loads in flight, a DPP tree per row; rows never split across workgroups.
+#include "lowbit_internal.h"
+
+namespace lb {
+namespace {
+
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(1))) const v4u gv4u;
+typedef __attribute__((address_space(1))) const uint8_t gu8;
+typedef short v2s __attribute__((ext_vector_type(2)));
+
+constexpr int BCOLS = 80; // columns per beat
+constexpr int REC = 40;   // staged dwords per beat: 4 dwords x {even, odd bytes} x 5 values of m
+
+#define LB_B3_CFGS(X) X(0, 16, 1) X(1, 16, 2) X(2, 32, 1) X(3, 32, 2) X(4, 32, 3) X(5, 64, 1) X(6, 64, 2)
+
+struct CfgLS {
+    int L, S;
+};
+#define LB_B3_ENTRY(i, l, s) {l, s},
+constexpr CfgLS kB3Cfgs[] = {LB_B3_CFGS(LB_B3_ENTRY)};
+#undef LB_B3_ENTRY
+constexpr int kB3NumCfgs = sizeof(kB3Cfgs) / sizeof(kB3Cfgs[0]);
+
+__device__ __forceinline__ int dot2(uint32_t a, uint32_t b, int c)
+{
+    return __builtin_amdgcn_sdot2(__builtin_bit_cast(v2s, a), __builtin_bit_cast(v2s, b), c, false);
+}
+
+// sum over the 4 bytes of one record dword: pairs (bytes 0, 2) and (bytes 1, 3), m = 1..5
+__device__ __forceinline__ int b3_dword(uint32_t d, const uint32_t *A, int acc)
+{
+#pragma unroll
+    for (int h = 0; h < 2; h++) {
+        // bytes h and h + 2 of d into the low bytes of the two 16-bit halves
+        uint32_t y = __builtin_amdgcn_perm(0u, d, h ? 0x0C030C01u : 0x0C020C00u);
+#pragma unroll
+        for (int m = 0; m < 5; m++) {
+            y = y * 3u; // 3^(m+1) b per half: below 2^16, so the halves never carry into each other
+            const uint32_t f = __builtin_amdgcn_perm(0u, y, 0x0C030C01u); // floor(3^(m+1) b / 256) per half
+            acc = dot2(f, A[h * 5 + m], acc);
+        }
+    }
+    return acc;
+}
+
+// Stage the activation once per workgroup: per beat, per record dword, per byte pair, the five Q_m pairs
+// (columns past K read q = 0), and the row's sum of q.
+__device__ __forceinline__ void b3_stage(const int8_t *__restrict__ xq, int K, int nbt, uint32_t *__restrict__ lds,
+                                         int *__restrict__ sumq)
+{
+    for (int it = threadIdx.x; it < nbt * 8; it += WG) {
+        const int bt = it >> 3, d = (it >> 1) & 3, h = it & 1;
+        uint32_t *rec = lds + bt * REC + d * 10 + h * 5;
+#pragma unroll
+        for (int m = 1; m <= 5; m++) {
+            uint32_t pair = 0;
+#pragma unroll
+            for (int f = 0; f < 2; f++) {
+                const int byte = bt * 16 + 4 * d + h + 2 * f; // byte index within the row
+                const int j0 = 5 * byte;
+                auto qa = [&](int c) { return c < K ? (int)xq[c] : 0; };
+                const int Q = m == 5 ? qa(j0) : qa(j0 + 5 - m) - 3 * qa(j0 + 4 - m);
+                pair |= ((uint32_t)Q & 0xffffu) << (16 * f);
+            }
+            rec[m - 1] = pair;
+        }
+    }
+    // sum of q over the row (one wave)
+    if (threadIdx.x < 64) {
+        int s = 0;
+        for (int c = threadIdx.x; c < K; c += 64)
+            s += xq[c];
+        s = group_sum_i<64>(s);
+        if (threadIdx.x == 63)
+            *sumq = s;
+    }
+}
+
+template <int S> struct B3Row {
+    uint4 code[S];
+};
+
+template <int L, int S, bool EMIT>
+__device__ __forceinline__ void b3_tile(const uint8_t *__restrict__ W, int K, float w_scale, const int8_t *__restrict__ xq,
+                                        float sx, float *__restrict__ y, int32_t *__restrict__ sums, int row0, int nrows,
+                                        uint32_t *__restrict__ lds)
+{
+    constexpr int GROUPS = 64 / L;
+    constexpr int STEP = GROUPS * (WG / 64);
+    const int nbt = (K + BCOLS - 1) / BCOLS;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int g = lane / L, li = lane % L;
+    const int rbase = wave * GROUPS + g;
+    const uint32_t rowbytes = (uint32_t)nbt * 16u;
+    const uint32_t stepb = (uint32_t)STEP * rowbytes;
+    const uint32_t last = (uint32_t)(row0 + nrows - 1) * rowbytes;
+    uint32_t bo[S];
+#pragma unroll
+    for (int i = 0; i < S; i++)
+        bo[i] = (uint32_t)min(li + i * L, nbt - 1) * 16u; // a lane past the row's end re-reads its last beat
+    uint32_t onext = (uint32_t)(row0 + min(rbase, nrows - 1)) * rowbytes;
+
+    auto issue = [&](B3Row<S> &r, uint32_t off) {
+#pragma unroll
+        for (int i = 0; i < S; i++) {
+            const v4u t = __builtin_nontemporal_load((gv4u *)((gu8 *)W + (off + bo[i])));
+            r.code[i] = make_uint4(t.x, t.y, t.z, t.w);
+        }
+    };
+    B3Row<S> buf[2];
+    issue(buf[0], min(onext, last));
+    onext += stepb;
+
+    int *sumq = reinterpret_cast<int *>(lds + nbt * REC);
+    b3_stage(xq, K, nbt, lds, sumq);
+    __syncthreads();
+
+    uint32_t act[S][REC];
+#pragma unroll
+    for (int i = 0; i < S; i++) {
+        const int bt = li + i * L;
+        const uint4 *p = reinterpret_cast<const uint4 *>(lds + min(bt, nbt - 1) * REC);
+#pragma unroll
+        for (int q = 0; q < REC / 4; q++) {
+            const uint4 t = p[q];
+            const bool in = bt < nbt; // a lane past the row's end multiplies by zero
+            act[i][4 * q + 0] = in ? t.x : 0u;
+            act[i][4 * q + 1] = in ? t.y : 0u;
+            act[i][4 * q + 2] = in ? t.z : 0u;
+            act[i][4 * q + 3] = in ? t.w : 0u;
+        }
+    }
+    const int sq = *sumq;
+
+    for (int it = 0; it < nrows; it += 2 * STEP) {
+#pragma unroll
+        for (int p = 0; p < 2; p++) {
+            const int cur = it + p * STEP;
+            if (cur >= nrows) // uniform
+                break;
+            if (cur + STEP < nrows) // uniform
+                issue(buf[p ^ 1], min(onext, last));
+            onext += stepb;
+            int acc = 0;
+#pragma unroll
+            for (int i = 0; i < S; i++) {
+                acc = b3_dword(buf[p].code[i].x, act[i] + 0, acc);
+                acc = b3_dword(buf[p].code[i].y, act[i] + 10, acc);
+                acc = b3_dword(buf[p].code[i].z, act[i] + 20, acc);
+                acc = b3_dword(buf[p].code[i].w, act[i] + 30, acc);
+            }
+            acc = group_sum_i<L>(acc);
+            const int rl = cur + rbase;
+            if (rl < nrows && li == L - 1) {
+                const int a = acc - sq; // sum (w + 1) q - sum q
+                if (EMIT)
+                    sums[row0 + rl] = a;
+                // tritium "Architecture", section 5: activation scale, then weight scale, in fp32
+                const float ys = (float)a * sx;
+                if (!EMIT || y != nullptr)
+                    y[row0 + rl] = ys * w_scale;
+            }
+        }
+    }
+}
+
+template <int L, int S, bool EMIT>
+__global__ __launch_bounds__(WG) void b3_kernel(const uint8_t *__restrict__ W, int N, int K, float w_scale,
+                                                 const int8_t *__restrict__ xq, const float *__restrict__ xs,
+                                                 float *__restrict__ y, int32_t *__restrict__ sums, int tile_rows)
+{
+    extern __shared__ uint4 lds4[];
+    const int row0 = blockIdx.x * tile_rows;
+    b3_tile<L, S, EMIT>(W, K, w_scale, xq, xs[0], y, sums, row0, min(tile_rows, N - row0),
+                        reinterpret_cast<uint32_t *>(lds4));
+}
+
+template <int L, int S>
+__global__ __launch_bounds__(WG) void b3_batched_kernel(const DevDesc *__restrict__ desc, const TileRef *__restrict__ tiles)
+{
+    extern __shared__ uint4 lds4[];
+    const TileRef tr = tiles[blockIdx.x];
+    const DevDesc d = desc[tr.prod];
+    b3_tile<L, S, false>(d.W, d.K, d.w_scale, d.xq, *static_cast<const float *>(d.xscale), d.y, nullptr, tr.row0,
+                         min(d.tile_rows, d.N - tr.row0), reinterpret_cast<uint32_t *>(lds4));
+}
+
+} // namespace
+
+// Choice: the fewest idle lane slots among the configurations whose staged activation fits 120 registers
+// per lane; then fewer lanes per row.
+int b3_config(int64_t K)
+{
+    if (K <= 0 || K % 64)
+        return -1;
+    const int64_t nbt = (K + BCOLS - 1) / BCOLS;
+    int best = -1;
+    int64_t bw = 0;
+    for (int c = 0; c < kB3NumCfgs; c++) {
+        const int64_t slots = (int64_t)kB3Cfgs[c].L * kB3Cfgs[c].S;
+        if (slots < nbt)
+            continue;
+        const int64_t waste = slots - nbt;
+        if (best < 0 || waste < bw || (waste == bw && kB3Cfgs[c].L < kB3Cfgs[best].L)) {
+            best = c;
+            bw = waste;
+        }
+    }
+    return best;
+}
+
+int b3_rows_per_iter(int cfg) { return (64 / kB3Cfgs[cfg].L) * (WG / 64); }
+size_t b3_stage_bytes(int64_t K) { return (size_t)((K + BCOLS - 1) / BCOLS) * REC * 4 + 16; }
+
+hipError_t launch_b3(const uint8_t *W, int64_t N, int64_t K, float w_scale, const int8_t *xq, const float *xs, float *y,
+                     int32_t *sums, hipStream_t stream)
+{
+    const int cfg = b3_config(K);
+    if (cfg < 0)
+        return hipErrorInvalidValue;
+    const int rpi = b3_rows_per_iter(cfg);
+    int64_t tile = (N + 1023) / 1024;
+    tile = (tile + rpi - 1) / rpi * rpi;
+    tile = tile < rpi ? rpi : tile > 32 * rpi ? 32 * rpi : tile;
+    const int ntiles = (int)((N + tile - 1) / tile);
+    const size_t lds = b3_stage_bytes(K);
+    const int n = (int)N, k = (int)K, t = (int)tile;
+    switch (cfg) {
+#define LB_B3_CASE(i, l, s)                                                                                   \
+    case i:                                                                                                   \
+        if (sums)                                                                                             \
+            hipLaunchKernelGGL((b3_kernel<l, s, true>), dim3(ntiles), dim3(WG), lds, stream, W, n, k, w_scale,  \
+                               xq, xs, y, sums, t);                                                           \
+        else                                                                                                  \
+            hipLaunchKernelGGL((b3_kernel<l, s, false>), dim3(ntiles), dim3(WG), lds, stream, W, n, k, w_scale, \
+                               xq, xs, y, sums, t);                                                           \
+        break;
+        LB_B3_CFGS(LB_B3_CASE)
+#undef LB_B3_CASE
+    default:
+        return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_b3_batched(const BatchGroup &g, size_t lds, hipStream_t stream)
+{
+    switch (g.cfg_a) {
+#define LB_B3_BCASE(i, l, s)                                                                                  \
+    case i:                                                                                                   \
+        hipLaunchKernelGGL((b3_batched_kernel<l, s>), dim3(g.ntiles), dim3(WG), lds, stream, g.desc, g.tiles);  \
+        break;
+        LB_B3_CFGS(LB_B3_BCASE)
+#undef LB_B3_BCASE
+    default:
+        return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+int b3_blocks_per_cu(int cfg, size_t lds)
+{
+    int nb = 0;
+    hipError_t e = hipErrorInvalidValue;
+    switch (cfg) {
+#define LB_B3_OCASE(i, l, s)                                                                                  \
+    case i:                                                                                                   \
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, b3_batched_kernel<l, s>, WG, lds);             \
+        break;
+        LB_B3_CFGS(LB_B3_OCASE)
+#undef LB_B3_OCASE
+    default:
+        break;
+    }
+    return e == hipSuccess && nb > 0 ? nb : 1;
+}
+
+} // namespace lb

@@ -388,6 +388,7 @@ hipError_t launch_gemm(int fmt, const uint8_t *W, int64_t N, int64_t K, float w_
         return emit ? launch_fmt<LB_TERNARY_PLANAR, true>(W, N, K, w_scale, Xq, Xscale, M, Y, sums, s)
                     : launch_fmt<LB_TERNARY_PLANAR, false>(W, N, K, w_scale, Xq, Xscale, M, Y, sums, s);
     case LB_Q8_0:
+    case LB_TERNARY_B3:
         return hipErrorNotSupported; // decode only
     }
     return hipErrorInvalidValue;

@@ -490,6 +490,8 @@ int matvec_config(int fmt, int64_t K)
 {
     if (fmt == LB_Q8_0)
         return q8_config(K);
+    if (fmt == LB_TERNARY_B3)
+        return b3_config(K);
     if (K <= 0 || K % sw_of(fmt))
         return -1;
     return pick_cfg(fmt, K / sw_of(fmt));
@@ -499,7 +501,7 @@ bool matvec_supported_k(int fmt, int64_t K) { return matvec_config(fmt, K) >= 0;
 
 bool matvec_config_full(int fmt, int cfg, int64_t K)
 {
-    if (fmt == LB_Q8_0)
+    if (fmt == LB_Q8_0 || fmt == LB_TERNARY_B3)
         return true; // one kernel per configuration; idle lanes are clamped inside it
     return (int64_t)kCfgs[cfg].L * kCfgs[cfg].S == K / sw_of(fmt);
 }
@@ -508,6 +510,8 @@ int matvec_config_rows_per_iter(int fmt, int cfg)
 {
     if (fmt == LB_Q8_0)
         return q8_rows_per_iter(cfg);
+    if (fmt == LB_TERNARY_B3)
+        return b3_rows_per_iter(cfg);
     return (64 / kCfgs[cfg].L) * (WG / 64);
 }
 
@@ -515,6 +519,8 @@ int matvec_stage_bytes(int fmt, int64_t K)
 {
     if (fmt == LB_Q8_0)
         return (int)q8_stage_bytes(K);
+    if (fmt == LB_TERNARY_B3)
+        return (int)b3_stage_bytes(K);
     return (int)((K / sw_of(fmt)) * rec_of(fmt) * 4);
 }
 
@@ -555,6 +561,8 @@ hipError_t launch_matvec(int fmt, const uint8_t *W, int64_t N, int64_t K, float 
 {
     if (fmt == LB_Q8_0)
         return launch_q8(W, N, K, xq, static_cast<const uint16_t *>(xscale), y, sums, s);
+    if (fmt == LB_TERNARY_B3)
+        return launch_b3(W, N, K, w_scale, xq, static_cast<const float *>(xscale), y, sums, s);
     const int cfg = matvec_config(fmt, K);
     if (cfg < 0)
         return hipErrorInvalidValue;
@@ -654,6 +662,8 @@ int matvec_batched_blocks_per_cu(int fmt, int cfg, bool full, size_t lds_bytes)
         return blocks_per_cu_fmt<LB_TERNARY_PLANAR>(cfg, full, lds_bytes);
     case LB_Q8_0:
         return q8_blocks_per_cu(cfg, lds_bytes);
+    case LB_TERNARY_B3:
+        return b3_blocks_per_cu(cfg, lds_bytes);
     }
     return 1;
 }
@@ -669,6 +679,8 @@ hipError_t launch_matvec_batched(const BatchGroup &g, hipStream_t s, size_t lds_
         return launch_batched_fmt<LB_TERNARY_PLANAR>(g, s, lds_bytes);
     case LB_Q8_0:
         return launch_q8_batched(g, lds_bytes, s);
+    case LB_TERNARY_B3:
+        return launch_b3_batched(g, lds_bytes, s);
     }
     return hipErrorInvalidValue;
 }

@@ -204,6 +204,14 @@ __global__ __launch_bounds__(WG) void pack_kernel(int fmt, const uint8_t *__rest
             dst[b * 16 + i] = src[b * 16 + i];
         return;
     }
+    if (fmt == LB_TERNARY_B3) {
+        // base-3 byte v <-> the 8-bit fraction b = ceil(256 v / 243) the decode kernel reads (v = 243 b >> 8)
+        for (int i = 0; i < 16; i++) {
+            const uint32_t v = src[b * 16 + i];
+            dst[b * 16 + i] = (uint8_t)(unpack ? (243u * v) >> 8 : (256u * v + 242u) / 243u);
+        }
+        return;
+    }
     if (fmt == LB_Q8_0) {
         // 34-byte block (binary16 scale, 32 weight bytes) <-> a 32-byte record + the scale in the scale array
         if (!unpack) {
@@ -251,7 +259,8 @@ __global__ __launch_bounds__(WG) void pack_kernel(int fmt, const uint8_t *__rest
 hipError_t launch_pack(int fmt, const uint8_t *blocks, int64_t N, int64_t K, uint8_t *packed, bool unpack,
                        hipStream_t s)
 {
-    const int64_t nblk = N * (K / (fmt == LB_Q1_0 ? 128 : fmt == LB_Q8_0 ? 32 : 64));
+    const int64_t nblk = fmt == LB_TERNARY_B3 ? N * ((K + 79) / 80) // beats of 16 bytes
+                                              : N * (K / (fmt == LB_Q1_0 ? 128 : fmt == LB_Q8_0 ? 32 : 64));
     const int64_t grid = (nblk + WG - 1) / WG;
     if (unpack)
         hipLaunchKernelGGL(pack_kernel, dim3((unsigned)grid), dim3(WG), 0, s, fmt, (const uint8_t *)packed, nblk,

@@ -12,7 +12,7 @@ import os
 
 import torch
 
-Q1_0, Q2_0_G64, TERNARY_PLANAR, Q8_0 = 1, 2, 3, 4
+Q1_0, Q2_0_G64, TERNARY_PLANAR, Q8_0, TERNARY_B3 = 1, 2, 3, 4, 5
 ACT_Q8_0, ACT_I8_ROW = 1, 2
 LB_OK, LB_EINVAL, LB_ESHAPE, LB_EALIGN, LB_EUNSUPPORTED, LB_EDEVICE = range(6)
 
@@ -161,5 +161,5 @@ class Batch:
 
 def desc(fmt, W, N, K, xq, xscale, y, w_tensor_scale=1.0, afmt=None) -> lb_matvec_desc:
     if afmt is None:
-        afmt = ACT_I8_ROW if fmt == TERNARY_PLANAR else ACT_Q8_0
+        afmt = ACT_I8_ROW if fmt in (TERNARY_PLANAR, TERNARY_B3) else ACT_Q8_0
     return lb_matvec_desc(fmt, afmt, N, K, _ptr(W), float(w_tensor_scale), _ptr(xq), _ptr(xscale), _ptr(y))

@@ -17,6 +17,13 @@
  *                     III.2, used for weights ("Q8_0 weights" and vec_dot_q8_0_q8_0 for the KV cache in
  *                     the bankml build history's 0.3.9 entry).  Decode (lowbit_matvec, the batch and
  *                     lowbit_block_sums with M = 1) only; lowbit_gemm returns LB_EUNSUPPORTED.
+ *   LB_TERNARY_B3     base-3 ternary beats: 16 bytes per 80 consecutive columns of one row, byte j holding
+ *                     columns 5j..5j+4 as the integer sum_t (w + 1) * 3^t, lowest digit first (0..242);
+ *                     a row of K columns (K % 64 == 0) takes ceil(K/80) beats, the columns past K coded 0.
+ *                     Weight = w times one fp32 per-tensor scale, with per-token int8 activations and the
+ *                     planar output rule.  Five trits per byte (bankml technical report, section III.8
+ *                     "Information"); base-3 packing of the planar body at 1.6 bits per weight (tritium
+ *                     "Architecture", section 10).  Decode only; bytes above 242 are not base-3 bytes.
  *
  * Activation formats:
  *   LB_ACT_Q8_0       ggml q8_0: int8 xq[M][K] plus binary16 scales xscale[M][K/32]; one block of 32
@@ -48,13 +55,13 @@
 extern "C" {
 #endif
 
-typedef enum { LB_Q1_0 = 1, LB_Q2_0_G64 = 2, LB_TERNARY_PLANAR = 3, LB_Q8_0 = 4 } lb_wfmt;
+typedef enum { LB_Q1_0 = 1, LB_Q2_0_G64 = 2, LB_TERNARY_PLANAR = 3, LB_Q8_0 = 4, LB_TERNARY_B3 = 5 } lb_wfmt;
 typedef enum { LB_ACT_Q8_0 = 1, LB_ACT_I8_ROW = 2 } lb_afmt;
 
 typedef enum {
     LB_OK = 0,
     LB_EINVAL = 1,       /* null pointer, unknown enum, or a weight/activation format pairing that is not defined */
-    LB_ESHAPE = 2,       /* negative size, K not a multiple of the weight block (128, 64, 64, 32), or over a limit */
+    LB_ESHAPE = 2,       /* negative size, K not a multiple of the weight block (128, 64, 64, 32, 64), or over a limit */
     LB_EALIGN = 3,       /* a pointer is not aligned as its argument requires */
     LB_EUNSUPPORTED = 4, /* the current device is not gfx950, or the entry point has no kernel for the format */
     LB_EDEVICE = 5       /* a HIP call failed; lowbit_last_error() holds the runtime's message */
@@ -68,8 +75,9 @@ const char *lowbit_last_error(void);
 
 /*
  * Bytes of the device layout of an N x K weight tensor in format `fmt`: 18 per Q1_0 / Q2_0_g64 block (128
- * or 64 weights), 34 per Q8_0 block (32 weights), 16 per planar beat -- the same count as the on-disk
- * format (1.125, 2.25, 8.5 and 2 bits per weight; bankml technical report sections III.2 and III.5).
+ * or 64 weights), 34 per Q8_0 block (32 weights), 16 per planar beat (64 columns) or base-3 beat (80
+ * columns, ceil(K/80) per row) -- the same count as the on-disk format (1.125, 2.25, 8.5, 2 and 1.6 bits
+ * per weight; bankml technical report sections III.2, III.5 and III.8).
  * Returns -1 for a bad format or shape.
  */
 int64_t lowbit_weight_bytes(int fmt, int64_t N, int64_t K);
@@ -86,7 +94,8 @@ int64_t lowbit_weight_bytes(int fmt, int64_t N, int64_t K);
  *           mask (0x11111111 << r) isolates eight weights of activation block r as nibbles.
  * Lossless (lowbit_unpack_weights is its inverse).  For LB_TERNARY_PLANAR the beat stream already is
  * the device layout (tritium "Architecture", section 2: the file layout is the beat stream) and pack
- * copies it unchanged.
+ * copies it unchanged.  For LB_TERNARY_B3 pack keeps the beat stream and writes each base-3 byte v as
+ * b = ceil(256 v / 243), whose leading m base-3 digits are floor(3^m b / 256) (unpack: v = 243 b >> 8).
  */
 lb_status lowbit_pack_weights(int fmt, const void *blocks, int64_t N, int64_t K, void *packed, hipStream_t s);
 lb_status lowbit_unpack_weights(int fmt, const void *packed, int64_t N, int64_t K, void *blocks, hipStream_t s);
@@ -108,11 +117,12 @@ lb_status lowbit_quantize_act(int afmt, const float *x, int64_t M, int64_t K, in
  * activations, exact integer sums per activation block, scaled per block in fp32
  * (bankml technical report, sections III.2, III.5 and III.8; tritium "Architecture", sections 1-2).
  *   W:      device layout of the N x K tensor (lowbit_pack_weights; planar beats as they are), 16-byte aligned.
- *   w_tensor_scale: planar per-tensor scale s_w (y = ((float)acc * s_x) * s_w); ignored otherwise.
- *   afmt:   LB_ACT_Q8_0 for the ggml formats, LB_ACT_I8_ROW for planar.
+ *   w_tensor_scale: planar and base-3 per-tensor scale s_w (y = ((float)acc * s_x) * s_w); ignored otherwise.
+ *   afmt:   LB_ACT_Q8_0 for the ggml formats, LB_ACT_I8_ROW for planar and base-3 beats.
  *   xq:     device int8 [K], 16-byte aligned.  xscale: binary16 [K/32] or one fp32, 4-byte aligned.
  *   y:      device fp32 [N], 4-byte aligned.
- * Limits: K <= 32768 (16384 for LB_Q8_0) and N <= 2^31 - 1; the weight tensor must be smaller than 4 GiB.
+ * Limits: K <= 32768 (16384 for LB_Q8_0, 10240 for LB_TERNARY_B3) and N <= 2^31 - 1; the weight tensor must
+ * be smaller than 4 GiB.
  */
 lb_status lowbit_matvec(int fmt, const void *W, int64_t N, int64_t K, float w_tensor_scale, int afmt,
                         const int8_t *xq, const void *xscale, float *y, hipStream_t s);

@@ -35,7 +35,7 @@ def act_for(fmt: int, K: int, seed: int, x: np.ndarray | None = None):
     """Oracle-quantised activation for one token: (q int8 [K], scale array, host x)."""
     if x is None:
         x = synth.activations(synth.rng(seed), 1, K)
-    if fmt == synth.TERNARY_PLANAR:
+    if fmt in (synth.TERNARY_PLANAR, synth.TERNARY_B3):
         q, s = oracle.quantize_i8_row(x)
         return q[0], s, x
     q, dh = oracle.quantize_q8_0(x)
@@ -44,14 +44,15 @@ def act_for(fmt: int, K: int, seed: int, x: np.ndarray | None = None):
 
 def gpu_matvec(fmt, packed, N, K, q, xs, w_scale=1.0):
     y = torch.empty(max(N, 1), dtype=torch.float32, device="cuda")
-    afmt = L.ACT_I8_ROW if fmt == synth.TERNARY_PLANAR else L.ACT_Q8_0
+    afmt = L.ACT_I8_ROW if fmt in (synth.TERNARY_PLANAR, synth.TERNARY_B3) else L.ACT_Q8_0
     L.lowbit_matvec(fmt, packed, N, K, w_scale, afmt, dev(q), dev(xs), y)
     return host(y)[:N]
 
 
 def gpu_sums(fmt, packed, N, K, Q, XS, M=1):
-    afmt = L.ACT_I8_ROW if fmt == synth.TERNARY_PLANAR else L.ACT_Q8_0
-    shape = (M, N) if fmt == synth.TERNARY_PLANAR else (M, N, K // 32)
+    row_sums = fmt in (synth.TERNARY_PLANAR, synth.TERNARY_B3)
+    afmt = L.ACT_I8_ROW if row_sums else L.ACT_Q8_0
+    shape = (M, N) if row_sums else (M, N, K // 32)
     sums = torch.empty(shape, dtype=torch.int32, device="cuda")
     L.lowbit_block_sums(fmt, packed, N, K, afmt, dev(Q), dev(XS), M, sums)
     return host(sums)

@@ -40,6 +40,9 @@ def test_weight_bytes():
     assert L.lowbit_weight_bytes(L.TERNARY_PLANAR, 6912, 2560) == 4_423_680
     assert L.lowbit_weight_bytes(L.Q8_0, 4096, 4096) == 17_825_792  # 34 bytes per 32 weights
     assert L.lowbit_weight_bytes(L.Q8_0, 4, 48) == -1
+    assert L.lowbit_weight_bytes(L.TERNARY_B3, 2560, 6912) == 2560 * 87 * 16  # ceil(6912 / 80) beats per row
+    assert L.lowbit_weight_bytes(L.TERNARY_B3, 2560, 2560) == 2560 * 512  # 1.6 bits per weight
+    assert L.lowbit_weight_bytes(L.TERNARY_B3, 4, 80) == -1  # rows are whole planar widths
     assert L.lowbit_weight_bytes(L.Q1_0, 4, 64) == -1
     assert L.lowbit_weight_bytes(7, 4, 64) == -1
     assert L.lowbit_weight_bytes(L.Q2_0_G64, -1, 64) == -1
@@ -60,6 +63,8 @@ def test_matvec_validation_codes():
     assert mv(K=32768 + 64) == L.LB_ESHAPE
     assert mv(fmt=L.Q8_0, K=16384 + 32) == L.LB_ESHAPE  # Q8_0 rows are at most 16384 weights
     assert mv(fmt=L.Q8_0, K=48) == L.LB_ESHAPE  # not a multiple of 32
+    assert mv(fmt=L.TERNARY_B3, afmt=L.ACT_I8_ROW, K=10240 + 64) == L.LB_ESHAPE  # base-3 rows <= 10240
+    assert mv(fmt=L.TERNARY_B3, afmt=L.ACT_Q8_0) == L.LB_EINVAL  # base-3 takes per-token activations
     assert mv(W=None) == L.LB_EINVAL
     assert mv(y=None) == L.LB_EINVAL
     assert mv(W=A16 + 8) == L.LB_EALIGN

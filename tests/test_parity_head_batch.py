@@ -79,9 +79,9 @@ def _product(fmt, N, K, seed):
     return Wt, packed_weights(Wt), q, xs
 
 
-@pytest.mark.parametrize("fmt", [synth.Q1_0, synth.Q2_0_G64, synth.TERNARY_PLANAR, synth.Q8_0])
+@pytest.mark.parametrize("fmt", [synth.Q1_0, synth.Q2_0_G64, synth.TERNARY_PLANAR, synth.Q8_0, synth.TERNARY_B3])
 def test_batched_matches_single_and_oracle(fmt):
-    shapes = [(300, 1024), (1024, 4096), (129, 12288), (1, 128), (517, 2560)]
+    shapes = [(300, 1024), (1024, 4096), (129, 12288 if fmt != synth.TERNARY_B3 else 10240), (1, 128), (517, 2560)]
     if fmt != synth.Q1_0:
         shapes.append((70, 6912 // 64 * 64))
     say(f"case batched fmt={fmt} shapes={shapes}")
@@ -100,8 +100,9 @@ def test_batched_matches_single_and_oracle(fmt):
         yb = host(y)
         ys_single = gpu_matvec(fmt, packed, N, K, q, xs, w_scale=Wt.s_w if Wt.s_w is not None else 1.0)
         assert np.array_equal(yb, ys_single), f"batched != single for {N}x{K}"
-        if fmt == synth.TERNARY_PLANAR:
-            _, y_ref = oracle.matvec_planar(Wt.raw, N, K, q, xs[0], Wt.s_w)
+        if fmt in (synth.TERNARY_PLANAR, synth.TERNARY_B3):
+            mv = oracle.matvec_planar if fmt == synth.TERNARY_PLANAR else oracle.matvec_b3
+            _, y_ref = mv(Wt.raw, N, K, q, xs[0], Wt.s_w)
             assert np.array_equal(yb, y_ref)
         else:
             y_ref, A = oracle.matvec_q(fmt, Wt.raw, N, K, q, xs)

@@ -13,8 +13,11 @@ from gpu_util import act_for, assert_close, dev, gpu_matvec, gpu_sums, host, pac
 pytestmark = pytest.mark.gpu
 
 Q_FMTS = [synth.Q1_0, synth.Q2_0_G64, synth.Q8_0]
-ALL_FMTS = Q_FMTS + [synth.TERNARY_PLANAR]
-NAMES = {synth.Q1_0: "Q1_0", synth.Q2_0_G64: "Q2_0_g64", synth.TERNARY_PLANAR: "planar", synth.Q8_0: "Q8_0"}
+ALL_FMTS = Q_FMTS + [synth.TERNARY_PLANAR, synth.TERNARY_B3]
+ROW_FMTS = (synth.TERNARY_PLANAR, synth.TERNARY_B3)  # per-token activations, per-tensor scale, row sums
+NAMES = {synth.Q1_0: "Q1_0", synth.Q2_0_G64: "Q2_0_g64", synth.TERNARY_PLANAR: "planar", synth.Q8_0: "Q8_0",
+         synth.TERNARY_B3: "base3"}
+MAX_K = {synth.Q8_0: 16384, synth.TERNARY_B3: 10240}
 QK = {synth.Q1_0: 128, synth.Q2_0_G64: 64, synth.Q8_0: 32}
 
 
@@ -26,12 +29,13 @@ def check_product(fmt, N, K, seed, p=synth.TERNARY_P, q_override=None, rows=None
         q = q_override(q)
     packed = packed_weights(Wt)
     y = gpu_matvec(fmt, packed, N, K, q, xs, w_scale=Wt.s_w if Wt.s_w is not None else 1.0)
-    sums = gpu_sums(fmt, packed, N, K, q[None, :], xs[None, :] if fmt != synth.TERNARY_PLANAR else xs)[0]
+    sums = gpu_sums(fmt, packed, N, K, q[None, :], xs[None, :] if fmt not in ROW_FMTS else xs)[0]
     r = np.arange(N) if rows is None else np.asarray(rows)
-    if fmt == synth.TERNARY_PLANAR:
-        acc, y_ref = oracle.matvec_planar(Wt.raw, N, K, q, xs[0], Wt.s_w, rows=r)
-        assert np.array_equal(sums[r], acc), "planar row sums differ"
-        assert np.array_equal(y[r], y_ref), "planar outputs differ"
+    if fmt in ROW_FMTS:
+        mv = oracle.matvec_planar if fmt == synth.TERNARY_PLANAR else oracle.matvec_b3
+        acc, y_ref = mv(Wt.raw, N, K, q, xs[0], Wt.s_w, rows=r)
+        assert np.array_equal(sums[r], acc), "row sums differ"
+        assert np.array_equal(y[r], y_ref), "outputs differ"
     else:
         ref_sums = oracle.block_sums(fmt, Wt.raw, N, K, q, rows=r)
         assert np.array_equal(sums[r], ref_sums), "per-block integer sums differ"
@@ -44,6 +48,8 @@ def check_product(fmt, N, K, seed, p=synth.TERNARY_P, q_override=None, rows=None
 @pytest.mark.parametrize("N,K", [(1, 128), (37, 384), (300, 640), (1000, 1024), (517, 2560), (130, 4096),
                                  (70, 6912), (33, 12288)])
 def test_matvec_shapes(fmt, N, K):
+    if K > MAX_K.get(fmt, 32768):
+        pytest.skip(f"{NAMES[fmt]} rows are limited to K <= {MAX_K[fmt]}")
     check_product(fmt, N, K, seed=1000 + N + K)
 
 
@@ -57,7 +63,7 @@ def test_matvec_odd_block_counts(fmt):
 
 @pytest.mark.parametrize("fmt", ALL_FMTS, ids=NAMES.get)
 def test_matvec_largest_k(fmt):
-    check_product(fmt, 20, 16384 if fmt == synth.Q8_0 else 32768, seed=2100)
+    check_product(fmt, 20, MAX_K.get(fmt, 32768), seed=2100)
 
 
 def test_q2_code3_and_minus_128():
@@ -83,15 +89,17 @@ def test_minus_128_against_all_minus_one(fmt):
         raw = synth.lay_out_q8_0(w, np.full((N, K // 32), 1.0, np.float16))
     elif fmt == synth.Q2_0_G64:
         raw = synth.lay_out_q2_0(w, np.full((N, K // 64), 1.0, np.float16))
+    elif fmt == synth.TERNARY_B3:
+        raw = synth.lay_out_b3(w)
     else:
         raw = synth.lay_out_planar(w)
     Wt = synth.Weights(fmt, N, K, raw, w, s_w=np.float32(1.0))
     q = np.full(K, -128, np.int8)
-    xs = np.array([1.0], np.float32) if fmt == synth.TERNARY_PLANAR else np.full(K // 32, 0x3C00, np.uint16)
+    xs = np.array([1.0], np.float32) if fmt in ROW_FMTS else np.full(K // 32, 0x3C00, np.uint16)
     packed = packed_weights(Wt)
-    sums = gpu_sums(fmt, packed, N, K, q[None, :], xs[None, :] if fmt != synth.TERNARY_PLANAR else xs)[0]
+    sums = gpu_sums(fmt, packed, N, K, q[None, :], xs[None, :] if fmt not in ROW_FMTS else xs)[0]
     y = gpu_matvec(fmt, packed, N, K, q, xs)
-    if fmt == synth.TERNARY_PLANAR:
+    if fmt in ROW_FMTS:
         assert np.all(sums == 128 * K)
     else:
         assert np.all(sums == 4096)
@@ -157,6 +165,18 @@ def test_empty_and_k0():
     assert np.all(host(y) == 7.0)
     L.lowbit_matvec(synth.Q2_0_G64, W, 5, 0, 1.0, L.ACT_Q8_0, q, xs, y)  # K = 0: empty sums
     assert np.all(host(y) == 0.0)
+
+
+def test_b3_pack_round_trip():
+    """Base-3 beats: pack writes ceil(256 v / 243) per byte and unpack restores every byte exactly."""
+    say("case pack base3")
+    Wt = synth.make_weights(synth.TERNARY_B3, 77, 2560, 2510)
+    packed = packed_weights(Wt)
+    v = Wt.raw.reshape(-1).astype(np.int64)
+    assert np.array_equal(host(packed).astype(np.int64), -(-256 * v // 243))
+    back = torch.empty(Wt.raw.size, dtype=torch.uint8, device="cuda")
+    L.lowbit_unpack_weights(synth.TERNARY_B3, packed, 77, 2560, back)
+    assert np.array_equal(host(back), Wt.raw.reshape(-1))
 
 
 @pytest.mark.parametrize("fmt", Q_FMTS, ids=NAMES.get)

@@ -24,7 +24,7 @@ def _run_token(fmt, layer, layers, seed):
 
 def _check_token(tok, rows_per_product=6, seed=0):
     g = synth.rng(seed)
-    planar = tok.fmt == synth.TERNARY_PLANAR
+    planar = tok.fmt in (synth.TERNARY_PLANAR, synth.TERNARY_B3)
     # every activation row of the token, byte for byte
     refs = {}
     for K, x in tok.x.items():
@@ -44,7 +44,8 @@ def _check_token(tok, rows_per_product=6, seed=0):
         y = p["y"][torch.from_numpy(rows).to(p["y"].device)].cpu().numpy()
         n = len(rows)
         if planar:
-            _, y_ref = oracle.matvec_planar(raw_rows, n, K, q_ref[r], s_ref[r], p["w_scale"])
+            mv = oracle.matvec_planar if tok.fmt == synth.TERNARY_PLANAR else oracle.matvec_b3
+            _, y_ref = mv(raw_rows, n, K, q_ref[r], s_ref[r], p["w_scale"])
             assert np.array_equal(y, y_ref), f"planar product {j} differs"
         else:
             y_ref, A = oracle.matvec_q(tok.fmt, raw_rows, n, K, q_ref[r], s_ref[r])
@@ -63,9 +64,10 @@ def test_qwen3_8b_token_full_size(fmt):
     tok.batch.close()
 
 
-def test_bitnet_planar_token_full_size():
-    say("case full planar token")
-    tok = _run_token(synth.TERNARY_PLANAR, synth.BITNET_2B_LAYER, synth.BITNET_2B_LAYERS, seed=7300)
+@pytest.mark.parametrize("fmt", [synth.TERNARY_PLANAR, synth.TERNARY_B3], ids=["planar", "base3"])
+def test_bitnet_token_full_size(fmt):
+    say(f"case full 2B token fmt={fmt}")
+    tok = _run_token(fmt, synth.BITNET_2B_LAYER, synth.BITNET_2B_LAYERS, seed=7300 + fmt)
     _check_token(tok, seed=7301)
     tok.batch.close()
 
