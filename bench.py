@@ -329,6 +329,38 @@ def head_i8_gbs(N, K, reps=20, seed=1008):
     return ms, (N * K + 4 * N) / (ms * 1e-3) / 1e9
 
 
+def popcount_gbs(reps=20, seed=1010):
+    """The bit-serial popcount kernel over one BitNet-2B layer's seven planar products: (ms per layer, GB/s)."""
+    import torch
+
+    import bit_quantized_matvec_q1_amd.lowbit as L
+    import synth
+
+    prods = []
+    for j, (_, N, K) in enumerate(synth.BITNET_2B_LAYER):
+        W = synth.device_planar_beats(N, K, seed + j).reshape(-1)
+        xq = torch.randint(-128, 128, (K,), dtype=torch.int8, device="cuda")
+        xs = torch.ones(1, dtype=torch.float32, device="cuda")
+        prods.append((W, N, K, xq, xs, torch.empty(N, dtype=torch.float32, device="cuda")))
+    nbytes = sum(W.numel() for W, *_ in prods)
+
+    def layer():
+        for W, N, K, xq, xs, y in prods:
+            L.lowbit_matvec_popcount(W, N, K, 1.0, xq, xs, y)
+
+    for _ in range(3):
+        layer()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        layer()
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    return ms, nbytes / (ms * 1e-3) / 1e9
+
+
 def prefill_tops(fmt, N, K, M, reps=20, seed=1004):
     """Time the prefill product (M activation rows x N weight rows x K) on inputs resident in HBM."""
     import torch
@@ -510,6 +542,11 @@ def main():
             secondary["head_int8_128256x2560"] = {"ms": round(ims, 4), "gbs": round(ig, 1),
                                                   "pct_hbm_peak": round(100 * ig / HBM_PEAK_GBS, 2),
                                                   "speedup_vs_bf16_head": round(hms / ims, 3)}
+            pms, pg = popcount_gbs()
+            secondary["planar_popcount_2b_layer"] = {
+                "workload": "the bit-serial popcount kernel (the third implementation of the planar product) over "
+                            "one BitNet-2B layer's seven products, one launch each",
+                "ms": round(pms, 4), "gbs": round(pg, 1)}
             tp.batch.close()
             del tp
         elif name == "b3":

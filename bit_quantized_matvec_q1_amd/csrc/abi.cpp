@@ -292,6 +292,32 @@ lb_status dense_head_matvec(const uint16_t *W, int64_t N, int64_t K, const float
     return e == hipSuccess ? LB_OK : hip_fail(fn, e);
 }
 
+lb_status lowbit_matvec_popcount(const void *W, int64_t N, int64_t K, float w_tensor_scale, const int8_t *xq,
+                                 const float *xscale, float *y, int32_t *row_sums, hipStream_t s)
+{
+    const char *fn = "lowbit_matvec_popcount";
+    lb_status st = check_product(fn, LB_TERNARY_PLANAR, W, N, K, LB_ACT_I8_ROW, xq, xscale,
+                                 y ? (const void *)y : (const void *)row_sums);
+    if (st != LB_OK || N == 0)
+        return st;
+    if (K > 8192)
+        return fail(LB_ESHAPE, fn, "K above 8192 (the activation planes are held in registers)");
+    if (row_sums && !aligned(row_sums, 4))
+        return fail(LB_EALIGN, fn, "row_sums needs 4-byte alignment");
+    st = check_device(fn);
+    if (st != LB_OK)
+        return st;
+    hipError_t e;
+    if (K == 0) {
+        e = y ? lb::launch_fill_zero(y, N, s) : hipSuccess;
+        if (e == hipSuccess && row_sums)
+            e = lb::launch_fill_zero_i32(row_sums, N, s);
+    } else {
+        e = lb::launch_popcount(static_cast<const uint8_t *>(W), N, K, w_tensor_scale, xq, xscale, y, row_sums, s);
+    }
+    return e == hipSuccess ? LB_OK : hip_fail(fn, e);
+}
+
 lb_status dense_head_matvec_i8(const int8_t *W, const float *row_scale, int64_t N, int64_t K, const float *x, float *y,
                                hipStream_t s)
 {

@@ -117,6 +117,10 @@ hipError_t launch_q8(const uint8_t *W, int64_t N, int64_t K, const int8_t *xq, c
 hipError_t launch_q8_batched(const BatchGroup &g, size_t lds, hipStream_t s);
 int q8_blocks_per_cu(int cfg, size_t lds);
 
+// the planar product by bit-serial popcounts (popcount.hip): a third implementation for differential tests
+hipError_t launch_popcount(const uint8_t *W, int64_t N, int64_t K, float w_scale, const int8_t *xq, const float *xs,
+                           float *y, int32_t *sums, hipStream_t s);
+
 // base-3 ternary beats x per-token int8 activations (b3.hip)
 int b3_config(int64_t K);
 int b3_rows_per_iter(int cfg);

@@ -38,6 +38,7 @@ SIGNATURES = {
     "lowbit_block_sums": (_I, [_I, _P, _I64, _I64, _I, _P, _P, _I64, _P, _P]),
     "dense_head_matvec": (_I, [_P, _I64, _I64, _P, _P, _P]),
     "dense_head_matvec_i8": (_I, [_P, _P, _I64, _I64, _P, _P, _P]),
+    "lowbit_matvec_popcount": (_I, [_P, _I64, _I64, ctypes.c_float, _P, _P, _P, _P, _P]),
     "lowbit_batch_create": (_I, [_P, ctypes.c_int32, _P]),
     "lowbit_matvec_batched": (_I, [_P, _P]),
     "lowbit_batch_destroy": (None, [_P]),
@@ -126,6 +127,11 @@ def lowbit_block_sums(fmt, W, N, K, afmt, Xq, Xscale, M, sums, stream=None):
 
 def dense_head_matvec(W, N, K, x, y, stream=None):
     _check(lib.dense_head_matvec(_ptr(W), N, K, _ptr(x), _ptr(y), _stream(stream, y)), "dense_head_matvec")
+
+
+def lowbit_matvec_popcount(W, N, K, w_tensor_scale, xq, xscale, y, row_sums=None, stream=None):
+    _check(lib.lowbit_matvec_popcount(_ptr(W), N, K, float(w_tensor_scale), _ptr(xq), _ptr(xscale), _ptr(y),
+                                      _ptr(row_sums), _stream(stream, xq)), "lowbit_matvec_popcount")
 
 
 def dense_head_matvec_i8(W, row_scale, N, K, x, y, stream=None):

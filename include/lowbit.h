@@ -158,6 +158,18 @@ lb_status lowbit_block_sums(int fmt, const void *W, int64_t N, int64_t K, int af
 lb_status dense_head_matvec(const uint16_t *W, int64_t N, int64_t K, const float *x, float *y, hipStream_t s);
 
 /*
+ * The planar product computed by bit-serial popcounts: with q = sum_p t_p bit_p(q) (t_p = 2^p, t_7 = -128),
+ * acc = sum_p t_p (popcount(pos & Q_p) - popcount(neg & Q_p)) over the activation bit planes Q_p (tritium
+ * "Architecture", section 4.3 "About popcount": the formulation kept as a third independent implementation
+ * for differential tests; section 5: the implementations must agree).  Same arguments and output rule as
+ * lowbit_matvec for LB_TERNARY_PLANAR with LB_ACT_I8_ROW activations, plus row_sums (device int32 [N],
+ * 4-byte aligned, may be NULL): the exact integer acc per row.  y may be NULL when row_sums is not.
+ * Results are bit-identical to lowbit_matvec / lowbit_block_sums.  K <= 8192; otherwise LB_ESHAPE.
+ */
+lb_status lowbit_matvec_popcount(const void *W, int64_t N, int64_t K, float w_tensor_scale, const int8_t *xq,
+                                 const float *xscale, float *y, int32_t *row_sums, hipStream_t s);
+
+/*
  * int8 dense head matvec y[n] = row_scale[n] * sum_k W[n][k] * x[k], accumulated in fp32 (tritium
  * "Architecture", section 10: int8 is the obvious move for the head, at half the bf16 head's bytes; the
  * reading taken: symmetric int8 weights with one fp32 scale per row).

@@ -89,6 +89,10 @@ def test_other_entry_points_validate():
     assert lib.dense_head_matvec(A16, 8, 8192, A16, A16, None) == L.LB_ESHAPE
     assert lib.dense_head_matvec(A16, 1 << 20, 2048, A16, A16, None) == L.LB_ESHAPE  # 4 GiB of weights
     assert lib.dense_head_matvec(A16 + 2, 8, 64, A16, A16, None) == L.LB_EALIGN
+    assert lib.lowbit_matvec_popcount(A16, 8, 8192 + 64, 1.0, A16, A16, A16, None, None) == L.LB_ESHAPE
+    assert lib.lowbit_matvec_popcount(A16, 8, 96, 1.0, A16, A16, A16, None, None) == L.LB_ESHAPE  # K % 64
+    assert lib.lowbit_matvec_popcount(A16, 8, 128, 1.0, A16, A16, None, None, None) == L.LB_EINVAL  # no output
+    assert lib.lowbit_matvec_popcount(A16, 8, 128, 1.0, A16, A16, None, A16 + 2, None) == L.LB_EALIGN
     assert lib.dense_head_matvec_i8(A16, A16, 8, 24, A16, A16, None) == L.LB_ESHAPE  # K % 16
     assert lib.dense_head_matvec_i8(A16, A16, 8, 8192 + 16, A16, A16, None) == L.LB_ESHAPE
     assert lib.dense_head_matvec_i8(A16, A16, 1 << 20, 4096, A16, A16, None) == L.LB_ESHAPE  # 4 GiB of weights

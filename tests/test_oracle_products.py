@@ -183,6 +183,22 @@ def test_planar_against_numpy():
     assert np.array_equal(y, ref_y.astype(np.float32))
 
 
+def test_planar_bit_serial_identity():
+    """The bit-serial form the popcount kernel computes (two's-complement activation planes, sign plane weighing
+    -128) gives the oracle's planar sums exactly, every activation byte included."""
+    N, K = 16, 2560
+    Wt = synth.make_weights(oracle.TERNARY_PLANAR, N, K, seed=63)
+    q = np.random.default_rng(64).integers(-128, 128, K).astype(np.int8)
+    q[:4] = [-128, 127, -1, 0]
+    acc, _ = oracle.matvec_planar(Wt.raw, N, K, q, 1.0, 1.0)
+    bits = np.unpackbits(q.view(np.uint8)[:, None], axis=1, bitorder="little")  # [K][8], plane p = bit p
+    weight = np.array([1, 2, 4, 8, 16, 32, 64, -128], np.int64)
+    pos, neg = (Wt.w == 1), (Wt.w == -1)
+    serial = sum(weight[p] * ((pos & bits[:, p].astype(bool)).sum(axis=1) - (neg & bits[:, p].astype(bool)).sum(axis=1))
+                 for p in range(8))
+    assert np.array_equal(serial, acc.astype(np.int64))
+
+
 def test_planar_both_planes_set_reads_zero():
     raw = np.zeros(16, np.uint8)
     raw[0] = 0xFF  # columns 0..7 in the +1 plane

@@ -167,6 +167,31 @@ def test_empty_and_k0():
     assert np.all(host(y) == 0.0)
 
 
+@pytest.mark.parametrize("N,K", [(1, 64), (37, 384), (300, 640), (517, 2560), (70, 6912), (9, 8192)])
+def test_popcount_agrees_with_select_accumulate_and_oracle(N, K):
+    """Three implementations of the planar product (tritium "Architecture", section 5): the bit-serial popcount
+    kernel, the select-accumulate kernel and the oracle give the same row sums and the same fp32 outputs, bit
+    for bit, with the activation extremes included."""
+    fmt = synth.TERNARY_PLANAR
+    say(f"case popcount N={N} K={K}")
+    Wt = synth.make_weights(fmt, N, K, 2700 + K)
+    q, xs, _ = act_for(fmt, K, 2701 + K)
+    q = q.copy()
+    q[::13] = -128
+    q[5::17] = 127
+    packed = packed_weights(Wt)
+    y = torch.empty(N, dtype=torch.float32, device="cuda")
+    sums = torch.empty(N, dtype=torch.int32, device="cuda")
+    L.lowbit_matvec_popcount(packed, N, K, float(Wt.s_w), dev(q), dev(xs), y, sums)
+    acc, y_ref = oracle.matvec_planar(Wt.raw, N, K, q, xs[0], Wt.s_w)
+    assert np.array_equal(host(sums), acc)
+    assert np.array_equal(host(y), y_ref)
+    assert np.array_equal(host(y), gpu_matvec(fmt, packed, N, K, q, xs, w_scale=Wt.s_w))
+    y_only = torch.empty(N, dtype=torch.float32, device="cuda")
+    L.lowbit_matvec_popcount(packed, N, K, float(Wt.s_w), dev(q), dev(xs), y_only)
+    assert np.array_equal(host(y_only), y_ref)
+
+
 def test_b3_pack_round_trip():
     """Base-3 beats: pack writes ceil(256 v / 243) per byte and unpack restores every byte exactly."""
     say("case pack base3")
