@@ -6,25 +6,37 @@ namespace lb {
 // q8_0 (bankml technical report, section III.2: blocks of 32 signed bytes with their own half-precision
 // scale, 127 / max|x| with round-half-to-even): amax is exact, the stored scale is fp16_rne(amax / 127)
 // of the correctly rounded fp32 quotient, the multiplier 127 / amax a correctly rounded fp32 quotient
-// (0 when amax = 0), and each q round-half-even of the fp32 product.  Returns the scale's bits; the 32
-// bytes go to q[0..7], four per dword, little-endian.
-inline __device__ uint16_t quantize_block_q8_0(const float (&v)[32], uint32_t (&q)[8])
+// (0 when amax = 0), and each q round-half-even of the fp32 product.
+//
+// Eight lanes per block, one float4 each, so a wave reads 1 KiB of consecutive activations and writes
+// 256 consecutive bytes of q; the block's amax is the maximum over its eight lanes (exact in any order).
+// Workgroups hold whole blocks (WG is a multiple of 8), so a block's lanes are all in range or all out.
+__global__ __launch_bounds__(WG) void quantize_q8_0_kernel(const float *__restrict__ x, int64_t nblocks,
+                                                           int8_t *__restrict__ xq, uint16_t *__restrict__ xs)
 {
-    float amax = 0.0f;
+    const int64_t c = (int64_t)blockIdx.x * WG + threadIdx.x; // float4 chunk: block c / 8, values 4 (c % 8) ..
+    const bool in = (c >> 3) < nblocks;
+    const float4 v = in ? reinterpret_cast<const float4 *>(x)[c] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    float amax = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
 #pragma unroll
-    for (int i = 0; i < 32; i++)
-        amax = fmaxf(amax, fabsf(v[i]));
-    const float d = amax / 127.0f;
+    for (int o = 1; o < 8; o <<= 1)
+        amax = fmaxf(amax, __shfl_xor(amax, o, 8));
+    if (!in)
+        return;
     const float id = amax > 0.0f ? 127.0f / amax : 0.0f;
-#pragma unroll
-    for (int i = 0; i < 8; i++) {
-        uint32_t w = 0;
-#pragma unroll
-        for (int t = 0; t < 4; t++)
-            w |= (uint32_t)((int)rintf(v[4 * i + t] * id) & 0xff) << (8 * t);
-        q[i] = w;
-    }
-    return __half_as_ushort(__float2half_rn(d));
+    const uint32_t w = (uint32_t)((int)rintf(v.x * id) & 0xff) | (uint32_t)((int)rintf(v.y * id) & 0xff) << 8 |
+                       (uint32_t)((int)rintf(v.z * id) & 0xff) << 16 | (uint32_t)((int)rintf(v.w * id) & 0xff) << 24;
+    reinterpret_cast<uint32_t *>(xq)[c] = w;
+    if ((c & 7) == 0)
+        xs[c >> 3] = __half_as_ushort(__float2half_rn(amax / 127.0f));
+}
+
+hipError_t launch_quantize_q8_0(const float *x, int64_t M, int64_t K, int8_t *xq, uint16_t *xs, hipStream_t s)
+{
+    const int64_t nblocks = M * (K / QK8);
+    const int64_t grid = (nblocks * 8 + WG - 1) / WG;
+    hipLaunchKernelGGL(quantize_q8_0_kernel, dim3((unsigned)grid), dim3(WG), 0, s, x, nblocks, xq, xs);
+    return hipGetLastError();
 }
 
 // Per-token int8 (tritium "Architecture", section 1): with the row's amax, s = amax / 127 and
@@ -34,38 +46,6 @@ inline __device__ float i8_row_scale(float amax) { return amax / 127.0f; }
 inline __device__ int quantize_i8(float x, float id)
 {
     return (int)fminf(fmaxf(rintf(x * id), -128.0f), 127.0f);
-}
-
-// q8_0: one thread per block of 32 (the arithmetic is quantize_block_q8_0).
-__global__ __launch_bounds__(WG) void quantize_q8_0_kernel(const float *__restrict__ x, int64_t nblocks,
-                                                           int8_t *__restrict__ xq, uint16_t *__restrict__ xs)
-{
-    const int64_t b = (int64_t)blockIdx.x * WG + threadIdx.x;
-    if (b >= nblocks)
-        return;
-    const float4 *src = reinterpret_cast<const float4 *>(x + b * QK8);
-    float v[QK8];
-#pragma unroll
-    for (int i = 0; i < QK8 / 4; i++) {
-        float4 t = src[i];
-        v[4 * i + 0] = t.x;
-        v[4 * i + 1] = t.y;
-        v[4 * i + 2] = t.z;
-        v[4 * i + 3] = t.w;
-    }
-    uint32_t packed[QK8 / 4];
-    xs[b] = quantize_block_q8_0(v, packed);
-    uint4 *dst = reinterpret_cast<uint4 *>(xq + b * QK8);
-    dst[0] = make_uint4(packed[0], packed[1], packed[2], packed[3]);
-    dst[1] = make_uint4(packed[4], packed[5], packed[6], packed[7]);
-}
-
-hipError_t launch_quantize_q8_0(const float *x, int64_t M, int64_t K, int8_t *xq, uint16_t *xs, hipStream_t s)
-{
-    const int64_t nblocks = M * (K / QK8);
-    const int64_t grid = (nblocks + WG - 1) / WG;
-    hipLaunchKernelGGL(quantize_q8_0_kernel, dim3((unsigned)grid), dim3(WG), 0, s, x, nblocks, xq, xs);
-    return hipGetLastError();
 }
 
 // Per-token int8 (tritium "Architecture", section 1: int8 activations; one absmax scale per token).

@@ -254,7 +254,7 @@ def test_launch_geometry_invariance():
 
 # --- quantisers -----------------------------------------------------------------------------------
 
-@pytest.mark.parametrize("M,K", [(1, 32), (1, 4096), (7, 12288), (512, 4096)])
+@pytest.mark.parametrize("M,K", [(1, 32), (3, 96), (2, 4128), (1, 4096), (7, 12288), (512, 4096)])
 def test_quantize_q8_0_bytes(M, K):
     say(f"case quantize q8_0 M={M} K={K}")
     g = synth.rng(3000 + M + K)
