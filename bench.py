@@ -214,24 +214,34 @@ def time_graph(lg, steps, warmup):
     return a.elapsed_time(b) / steps
 
 
+def warm_steps(tok, ms=100.0):
+    """Warm-up steps worth about `ms` of GPU time (at 6 TB/s): a freshly generated token's first ~15 ms of
+    steps run up to 15 % slower than the steady state, so a fixed small count is not enough."""
+    return max(20, int(ms * 1e-3 / (tok.weight_bytes / 6e12)))
+
+
 def time_token(tok, steps, warmup):
-    """Time `steps` whole steps (quantise + batched products) and, inside them, the batched launch alone
-    with HIP events on the stream the kernels run on (torch's current stream)."""
+    """Time `steps` whole steps (quantise + batched products [+ head]) with nothing else in the stream, then
+    `steps` batched launches alone, each bracketed by HIP events on the stream the kernels run on (torch's
+    current stream).  The events sit in a pass of their own: an event recorded between two kernels of a
+    step holds the stream for a few microseconds, which would be counted in the step time."""
     import torch
 
     for _ in range(warmup):
         tok.step()
     torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     t0 = time.perf_counter()
+    for _ in range(steps):
+        tok.step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     for a, b in ev:
-        tok.quantize()
         a.record()
         tok.products_launch()
         b.record()
-        tok.head_launch()
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
     launch_ms = [a.elapsed_time(b) for a, b in ev]
     return wall / steps * 1e3, sum(launch_ms) / len(launch_ms)
 
@@ -281,7 +291,22 @@ def cpu_baseline(tok, budget_s=12.0):
     return t_total, wbytes, layers_done
 
 
-def head_gbs(N, K, reps=20, seed=1006):
+def warm_up(fn, ms=100.0):
+    """Call fn (at least 3 times) until about `ms` of wall time has passed, synchronising every 8 calls so
+    the wall time is GPU time: short kernels on a GPU that was idle run slow for their first ~15 ms."""
+    import torch
+
+    torch.cuda.synchronize()
+    t0, n = time.perf_counter(), 0
+    while n < 3 or (time.perf_counter() - t0) * 1e3 < ms:
+        fn()
+        n += 1
+        if n % 8 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+
+
+def head_gbs(N, K, reps=100, seed=1006):
     """The dense bf16 head matvec alone on weights resident in HBM: (ms, GB/s of its bytes)."""
     import torch
 
@@ -293,9 +318,7 @@ def head_gbs(N, K, reps=20, seed=1006):
     g.manual_seed(seed + 1)
     x = torch.randn(K, generator=g, device="cuda")
     y = torch.empty(N, dtype=torch.float32, device="cuda")
-    for _ in range(3):
-        L.dense_head_matvec(W, N, K, x, y)
-    torch.cuda.synchronize()
+    warm_up(lambda: L.dense_head_matvec(W, N, K, x, y))
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(reps):
@@ -306,7 +329,7 @@ def head_gbs(N, K, reps=20, seed=1006):
     return ms, (2 * N * K + 4 * K + 4 * N) / (ms * 1e-3) / 1e9
 
 
-def head_i8_gbs(N, K, reps=20, seed=1008):
+def head_i8_gbs(N, K, reps=100, seed=1008):
     """The int8 head with one fp32 scale per row: (ms per launch, GB/s of its N*K + 4N weight bytes)."""
     import torch
 
@@ -316,9 +339,7 @@ def head_i8_gbs(N, K, reps=20, seed=1008):
     W, s = synth.device_head_weights_i8(N, K, seed)
     x = torch.randn(K, device="cuda")
     y = torch.empty(N, dtype=torch.float32, device="cuda")
-    for _ in range(3):
-        L.dense_head_matvec_i8(W, s, N, K, x, y)
-    torch.cuda.synchronize()
+    warm_up(lambda: L.dense_head_matvec_i8(W, s, N, K, x, y))
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a.record()
     for _ in range(reps):
@@ -329,7 +350,7 @@ def head_i8_gbs(N, K, reps=20, seed=1008):
     return ms, (N * K + 4 * N) / (ms * 1e-3) / 1e9
 
 
-def popcount_gbs(reps=20, seed=1010):
+def popcount_gbs(reps=100, seed=1010):
     """The bit-serial popcount kernel over one BitNet-2B layer's seven planar products: (ms per layer, GB/s)."""
     import torch
 
@@ -348,9 +369,7 @@ def popcount_gbs(reps=20, seed=1010):
         for W, N, K, xq, xs, y in prods:
             L.lowbit_matvec_popcount(W, N, K, 1.0, xq, xs, y)
 
-    for _ in range(3):
-        layer()
-    torch.cuda.synchronize()
+    warm_up(layer)
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a.record()
     for _ in range(reps):
@@ -361,7 +380,7 @@ def popcount_gbs(reps=20, seed=1010):
     return ms, nbytes / (ms * 1e-3) / 1e9
 
 
-def prefill_tops(fmt, N, K, M, reps=20, seed=1004):
+def prefill_tops(fmt, N, K, M, reps=100, seed=1004):
     """Time the prefill product (M activation rows x N weight rows x K) on inputs resident in HBM."""
     import torch
 
@@ -378,9 +397,7 @@ def prefill_tops(fmt, N, K, M, reps=20, seed=1004):
     Xs = torch.empty((M, K // 32), dtype=torch.uint16, device="cuda")
     L.lowbit_quantize_act(L.ACT_Q8_0, X, M, K, Xq, Xs)
     Y = torch.empty((M, N), dtype=torch.float32, device="cuda")
-    for _ in range(3):
-        L.lowbit_gemm(fmt, W, N, K, 1.0, L.ACT_Q8_0, Xq, Xs, M, Y)
-    torch.cuda.synchronize()
+    warm_up(lambda: L.lowbit_gemm(fmt, W, N, K, 1.0, L.ACT_Q8_0, Xq, Xs, M, Y))
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(reps):
@@ -415,8 +432,8 @@ def copy_probe_gbs(nbytes=1 << 31, reps=5):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle leg (profiling runs)")
     ap.add_argument("--secondary", default="layered,q1,planar,b3,q8,prefill",
                     help="comma list of extra workloads: layered, q1, planar, b3, q8, prefill, none")
@@ -513,7 +530,7 @@ def main():
     for name in [s for s in args.secondary.split(",") if s and s != "none"]:
         if name == "q1":
             t1 = DecodeToken(synth.Q1_0, synth.QWEN3_8B_LAYER, synth.QWEN3_8B_LAYERS, seed=1002)
-            ms1, ml1 = time_token(t1, max(10, args.steps // 2), 5)
+            ms1, ml1 = time_token(t1, max(50, args.steps // 2), warm_steps(t1))
             secondary["q1_0_8b_token"] = {
                 "weight_bytes": t1.weight_bytes, "ms_per_step": round(ms1, 5),
                 "gbs": round(t1.weight_bytes / (ms1 * 1e-3) / 1e9, 1),
@@ -525,7 +542,7 @@ def main():
         elif name == "planar":
             tp = DecodeToken(synth.TERNARY_PLANAR, synth.BITNET_2B_LAYER, synth.BITNET_2B_LAYERS, seed=1005,
                              head=synth.BITNET_HEAD)
-            msp, mlp = time_token(tp, max(10, args.steps // 2), 5)
+            msp, mlp = time_token(tp, max(50, args.steps // 2), warm_steps(tp))
             secondary["planar_2b_token"] = {
                 "workload": "BitNet-b1.58-2B shapes, 30 layers x 7 planar products + the dense bf16 head "
                             "128256x2560; per-token int8 activations",
@@ -552,7 +569,7 @@ def main():
         elif name == "b3":
             tb = DecodeToken(synth.TERNARY_B3, synth.BITNET_2B_LAYER, synth.BITNET_2B_LAYERS, seed=1009,
                              head=synth.BITNET_HEAD)
-            msb, mlb = time_token(tb, max(10, args.steps // 2), 5)
+            msb, mlb = time_token(tb, max(50, args.steps // 2), warm_steps(tb))
             secondary["base3_2b_token"] = {
                 "workload": "the BitNet-b1.58-2B token with base-3 ternary beats (five trits per byte, 1.6 b/w) "
                             "in place of planar beats, 30 layers x 7 products + the dense bf16 head",
@@ -566,7 +583,7 @@ def main():
             del tb
         elif name == "q8":
             t8 = DecodeToken(synth.Q8_0, synth.QWEN3_8B_LAYER, synth.QWEN3_8B_LAYERS, seed=1007)
-            ms8, ml8 = time_token(t8, max(10, args.steps // 5), 3)
+            ms8, ml8 = time_token(t8, max(20, args.steps // 5), warm_steps(t8))
             secondary["q8_0_8b_token"] = {
                 "workload": "Q8_0 weights x q8_0 activations (vec_dot_q8_0_q8_0), Qwen3-8B shapes, 36 layers x 7 "
                             "products, batch 1",
