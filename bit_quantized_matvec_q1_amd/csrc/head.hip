@@ -89,19 +89,24 @@ __global__ __launch_bounds__(WG) void head_kernel(const uint16_t *__restrict__ W
 // int8 head: y[n] = s_w[n] * sum_k W[n][k] * x[k] (tritium "Architecture", section 10: int8 as the obvious
 // move for the head; one fp32 scale per row).  Half the bytes of the bf16 head: the same streaming
 // structure with 16-byte loads of 16 weights, each widened to fp32 exactly (a signed byte) and
-// multiply-added against x held in VGPRs; the row's scale multiplies the finished sum.
-template <int S>
+// multiply-added against x held in VGPRs; the row's scale multiplies the finished sum.  A row takes L
+// lanes (64 / L rows per wave) and each lane S chunks, L chosen so that L * S covers the row's chunks with
+// the fewest idle lane slots (K = 2560: 160 chunks = 32 lanes x 5).
+template <int L, int S>
 __global__ __launch_bounds__(WG) void head_i8_kernel(const int8_t *__restrict__ W, const float *__restrict__ sw, int N,
                                                      int K, const float *__restrict__ x, float *__restrict__ y,
                                                      int tile_rows)
 {
+    constexpr int G = 64 / L;            // rows per wave
+    constexpr int STEP = G * (WG / 64);  // rows per workgroup iteration
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int g = lane / L, li = lane % L;
     const int nch = K / 16; // chunks of 16 columns per row
     float xr[S][16];
     uint32_t co[S]; // byte offset of this lane's chunks within a row
 #pragma unroll
     for (int i = 0; i < S; i++) {
-        const int ch = lane + 64 * i;
+        const int ch = li + L * i;
         co[i] = (uint32_t)min(ch, nch - 1) * 16u;
 #pragma unroll
         for (int q = 0; q < 4; q++) {
@@ -111,12 +116,12 @@ __global__ __launch_bounds__(WG) void head_i8_kernel(const int8_t *__restrict__ 
     }
     const int row0 = blockIdx.x * tile_rows;
     const int nrows = min(tile_rows, N - row0);
-    constexpr int STEP = WG / 64;
+    const int rbase = wave * G + g; // this lane's row within an iteration
     const uint32_t rowb = (uint32_t)K;
     const uint32_t last = (uint32_t)(row0 + nrows - 1) * rowb;
-    uint32_t onext = (uint32_t)(row0 + min(wave, nrows - 1)) * rowb;
+    uint32_t onext = (uint32_t)(row0 + min(rbase, nrows - 1)) * rowb;
     // a ring of NB register buffers: NB - 1 rows' loads in flight while a row is computed (deeper rings
-    // measured no faster: at two VALU operations per weight byte the kernel is bound by issue, not latency)
+    // measured no faster)
     constexpr int NB = 2;
     uint4 buf[NB][S];
     auto issue = [&](uint4 (&w)[S], uint32_t off) {
@@ -141,7 +146,8 @@ __global__ __launch_bounds__(WG) void head_i8_kernel(const int8_t *__restrict__ 
             if (cur + (NB - 1) * STEP < nrows) // uniform
                 issue(buf[(b + NB - 1) % NB], min(onext, last));
             onext += STEP * rowb;
-            // a lane's chunk past the row's end re-read the last chunk; its x is zero, so it adds nothing
+            // a lane's chunk past the row's end re-read the last chunk; its x is zero, so it adds nothing;
+            // a lane past the tile's last row re-read that row, and its sum is not stored
             float acc = 0.0f;
 #pragma unroll
             for (int i = 0; i < S; i++) {
@@ -152,9 +158,9 @@ __global__ __launch_bounds__(WG) void head_i8_kernel(const int8_t *__restrict__ 
                     for (int t = 0; t < 4; t++)
                         acc = fmaf((float)(int)(int8_t)(v[j] >> (8 * t)), xr[i][4 * j + t], acc);
             }
-            acc = group_sum_f<64>(acc);
-            const int rl = cur + wave;
-            if (rl < nrows && lane == 63)
+            acc = group_sum_f<L>(acc);
+            const int rl = cur + rbase;
+            if (rl < nrows && li == L - 1)
                 y[row0 + rl] = sw[row0 + rl] * acc;
         }
     }
@@ -163,15 +169,23 @@ __global__ __launch_bounds__(WG) void head_i8_kernel(const int8_t *__restrict__ 
 hipError_t launch_head_i8(const int8_t *W, const float *sw, int64_t N, int64_t K, const float *x, float *y, hipStream_t s)
 {
     const int nch = (int)(K / 16);
-    const int S = (nch + 63) / 64;
+    // lanes per row: the fewest idle lane slots (L * S - nch) with S <= 8, then the most lanes
+    int L = 64, S = (nch + 63) / 64;
+    for (int l : {32, 16}) {
+        const int sl = (nch + l - 1) / l;
+        if (sl <= 8 && l * sl - nch < L * S - nch) {
+            L = l;
+            S = sl;
+        }
+    }
     const int tile = 64; // rows per workgroup
     const int grid = (int)((N + tile - 1) / tile);
-    switch (S) {
-#define LB_HEAD_I8(n)                                                                                         \
-    case n:                                                                                                   \
-        hipLaunchKernelGGL(head_i8_kernel<n>, dim3(grid), dim3(WG), 0, s, W, sw, (int)N, (int)K, x, y, tile); \
-        break;
-        LB_HEAD_I8(1) LB_HEAD_I8(2) LB_HEAD_I8(3) LB_HEAD_I8(4) LB_HEAD_I8(5) LB_HEAD_I8(6) LB_HEAD_I8(7) LB_HEAD_I8(8)
+    const int n = (int)N, k = (int)K;
+    switch (L * 16 + S) {
+#define LB_HEAD_I8(l, sv)                                                                                         case l * 16 + sv:                                                                                                 hipLaunchKernelGGL((head_i8_kernel<l, sv>), dim3(grid), dim3(WG), 0, s, W, sw, n, k, x, y, tile);             break;
+#define LB_HEAD_I8_L(l)                                                                                           LB_HEAD_I8(l, 1) LB_HEAD_I8(l, 2) LB_HEAD_I8(l, 3) LB_HEAD_I8(l, 4) LB_HEAD_I8(l, 5) LB_HEAD_I8(l, 6)           LB_HEAD_I8(l, 7) LB_HEAD_I8(l, 8)
+        LB_HEAD_I8_L(16) LB_HEAD_I8_L(32) LB_HEAD_I8_L(64)
+#undef LB_HEAD_I8_L
 #undef LB_HEAD_I8
     default:
         return hipErrorInvalidValue;
