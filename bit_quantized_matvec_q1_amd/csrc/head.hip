@@ -7,6 +7,8 @@
 // contiguous) and closed with a cross-lane tree.
 #include "lowbit_internal.h"
 
+#include <atomic>
+
 namespace lb {
 
 typedef unsigned hv4u __attribute__((ext_vector_type(4)));
@@ -102,27 +104,19 @@ __global__ __launch_bounds__(WG) void head_i8_kernel(const int8_t *__restrict__ 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int g = lane / L, li = lane % L;
     const int nch = K / 16; // chunks of 16 columns per row
-    float xr[S][16];
-    uint32_t co[S]; // byte offset of this lane's chunks within a row
+    uint32_t co[S];         // byte offset of this lane's chunks within a row
 #pragma unroll
-    for (int i = 0; i < S; i++) {
-        const int ch = li + L * i;
-        co[i] = (uint32_t)min(ch, nch - 1) * 16u;
-#pragma unroll
-        for (int q = 0; q < 4; q++) {
-            const float4 a = ch < nch ? reinterpret_cast<const float4 *>(x)[4 * ch + q] : make_float4(0.f, 0.f, 0.f, 0.f);
-            xr[i][4 * q + 0] = a.x, xr[i][4 * q + 1] = a.y, xr[i][4 * q + 2] = a.z, xr[i][4 * q + 3] = a.w;
-        }
-    }
+    for (int i = 0; i < S; i++)
+        co[i] = (uint32_t)min(li + L * i, nch - 1) * 16u;
     const int row0 = blockIdx.x * tile_rows;
     const int nrows = min(tile_rows, N - row0);
     const int rbase = wave * G + g; // this lane's row within an iteration
     const uint32_t rowb = (uint32_t)K;
     const uint32_t last = (uint32_t)(row0 + nrows - 1) * rowb;
     uint32_t onext = (uint32_t)(row0 + min(rbase, nrows - 1)) * rowb;
-    // a ring of NB register buffers: NB - 1 rows' loads in flight while a row is computed (deeper rings
-    // measured no faster)
-    constexpr int NB = 2;
+    // a ring of NB register buffers: NB - 1 rows' loads in flight while a row is computed (3 measured
+    // fastest: 2 leaves HBM idle, 4 costs occupancy)
+    constexpr int NB = 3;
     uint4 buf[NB][S];
     auto issue = [&](uint4 (&w)[S], uint32_t off) {
 #pragma unroll
@@ -136,6 +130,17 @@ __global__ __launch_bounds__(WG) void head_i8_kernel(const int8_t *__restrict__ 
         if (b * STEP < nrows) // uniform
             issue(buf[b], min(onext, last));
         onext += STEP * rowb;
+    }
+    // x into registers while the first rows stream in (columns past K read zero)
+    float xr[S][16];
+#pragma unroll
+    for (int i = 0; i < S; i++) {
+        const int ch = li + L * i;
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+            const float4 a = ch < nch ? reinterpret_cast<const float4 *>(x)[4 * ch + q] : make_float4(0.f, 0.f, 0.f, 0.f);
+            xr[i][4 * q + 0] = a.x, xr[i][4 * q + 1] = a.y, xr[i][4 * q + 2] = a.z, xr[i][4 * q + 3] = a.w;
+        }
     }
     for (int it = 0; it < nrows; it += NB * STEP) {
 #pragma unroll
@@ -166,6 +171,41 @@ __global__ __launch_bounds__(WG) void head_i8_kernel(const int8_t *__restrict__ 
     }
 }
 
+// Resident workgroups of one int8-head configuration on the current device, cached per device.
+template <int L, int S> static int head_i8_slots()
+{
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return 256;
+    int v = cache[dev].load(std::memory_order_relaxed);
+    if (v == 0) {
+        int cus = 0, nb = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+            cus = 1;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, head_i8_kernel<L, S>, WG, 0) != hipSuccess || nb < 1)
+            nb = 1;
+        v = cus * nb;
+        cache[dev].store(v, std::memory_order_relaxed);
+    }
+    return v;
+}
+
+template <int L, int S>
+static hipError_t launch_head_i8_cfg(const int8_t *W, const float *sw, int N, int K, const float *x, float *y,
+                                     hipStream_t s)
+{
+    // one workgroup per resident slot, each streaming one contiguous range of rows with x loaded once:
+    // no second, partly filled round of workgroups, and x is read from L2 once per slot
+    constexpr int STEP = (64 / L) * (WG / 64);
+    const int slots = head_i8_slots<L, S>();
+    int tile = (N + slots - 1) / slots;
+    tile = (tile + STEP - 1) / STEP * STEP;
+    const int grid = (N + tile - 1) / tile;
+    hipLaunchKernelGGL((head_i8_kernel<L, S>), dim3(grid), dim3(WG), 0, s, W, sw, N, K, x, y, tile);
+    return hipGetLastError();
+}
+
 hipError_t launch_head_i8(const int8_t *W, const float *sw, int64_t N, int64_t K, const float *x, float *y, hipStream_t s)
 {
     const int nch = (int)(K / 16);
@@ -178,19 +218,20 @@ hipError_t launch_head_i8(const int8_t *W, const float *sw, int64_t N, int64_t K
             S = sl;
         }
     }
-    const int tile = 64; // rows per workgroup
-    const int grid = (int)((N + tile - 1) / tile);
     const int n = (int)N, k = (int)K;
     switch (L * 16 + S) {
-#define LB_HEAD_I8(l, sv)                                                                                         case l * 16 + sv:                                                                                                 hipLaunchKernelGGL((head_i8_kernel<l, sv>), dim3(grid), dim3(WG), 0, s, W, sw, n, k, x, y, tile);             break;
-#define LB_HEAD_I8_L(l)                                                                                           LB_HEAD_I8(l, 1) LB_HEAD_I8(l, 2) LB_HEAD_I8(l, 3) LB_HEAD_I8(l, 4) LB_HEAD_I8(l, 5) LB_HEAD_I8(l, 6)           LB_HEAD_I8(l, 7) LB_HEAD_I8(l, 8)
+#define LB_HEAD_I8(l, sv)                                                                                     \
+    case l * 16 + sv:                                                                                         \
+        return launch_head_i8_cfg<l, sv>(W, sw, n, k, x, y, s);
+#define LB_HEAD_I8_L(l)                                                                                       \
+    LB_HEAD_I8(l, 1) LB_HEAD_I8(l, 2) LB_HEAD_I8(l, 3) LB_HEAD_I8(l, 4) LB_HEAD_I8(l, 5) LB_HEAD_I8(l, 6)       \
+    LB_HEAD_I8(l, 7) LB_HEAD_I8(l, 8)
         LB_HEAD_I8_L(16) LB_HEAD_I8_L(32) LB_HEAD_I8_L(64)
 #undef LB_HEAD_I8_L
 #undef LB_HEAD_I8
     default:
         return hipErrorInvalidValue;
     }
-    return hipGetLastError();
 }
 
 hipError_t launch_head(const uint16_t *W, int64_t N, int64_t K, const float *x, float *y, hipStream_t s)
