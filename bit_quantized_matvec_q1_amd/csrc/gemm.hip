@@ -5,26 +5,26 @@
 // tile loads each weight block once and applies it to several activation columns).
 //
 // Mapping to CDNA4:
-//  * A workgroup owns a tile of TN = 128 weight rows x TM = 64 activation rows and walks K in steps of
+//  * A workgroup owns a tile of TN = 64 weight rows x TM = 128 activation rows and walks K in steps of
 //    128 columns.  Each step is software-pipelined: the packed weight codes, activation tile and
-//    activation scales of the step three ahead are loaded into a register ring while the current step
+//    activation scales of the step two ahead are loaded into a register ring while the current step
 //    computes; at the top of a step they are written to double-buffered LDS -- the weights unpacked to
 //    int8 in natural column order (shift and mask, a 4x4 byte transpose with v_perm_b32, and a
 //    v_perm_b32 lookup from code to weight byte: Q2_0 c -> c - 1, Q1_0 bit -> +/-1, planar (pos, neg) ->
 //    pos - neg) -- and one barrier per step separates the writes from the reads.  Every thread loads and
 //    unpacks an equal share of the weight tile and copies an equal share of the activation tile.
-//  * A workgroup is 16 waves (1024 threads).  Wave w computes the 32 x 32 output tile w mod 8 (32 weight
-//    rows x 32 activation rows) over one half of every step's columns: per q8_0 block (32 columns, the
-//    MFMA's K depth) one A operand (weights) and one B operand (activations) from LDS, one MFMA.  The
-//    halves split at weight-block boundaries (a Q2_0 block, half a Q1_0 block), and the second half's
-//    partial sums join the first's through LDS at the end: four waves per SIMD, so one wave's rescale
-//    arithmetic overlaps another's matrix-core, LDS and load latency.  Each MFMA result is one exact
-//    int32 sum per (weight row, activation row, block).
-//  * The accumulator input of every MFMA is a constant register tile holding 0x4B400000 (1.5 * 2^23), so
-//    each result, read as fp32, is 1.5 * 2^23 + isum exactly; one FMA with the block's activation scale
-//    and -d_x * 1.5 * 2^23 gives round(d_x * isum) without a conversion.  The weight block scale is then
-//    applied with one more FMA (bankml technical report, section III.3: one multiply-add per q8_0 block,
-//    then one per weight block).
+//  * A workgroup is 8 waves (512 threads), two per SIMD, and two workgroups fit a CU.  Wave w computes
+//    the 32 x 32 output tile (weight rows 32 (w mod 2), activation rows 32 (w / 2)) over every step's
+//    four q8_0 blocks (32 columns each, the MFMA's K depth): per block one A operand (weights) and one B
+//    operand (activations) from LDS, one MFMA, one exact int32 sum per (weight row, activation row,
+//    block).  The weight unpack is shared by the 128 activation rows of the tile and the activation copy
+//    by its 64 weight rows, so per MFMA the per-step work stays small next to the rescale below.
+//  * Q2_0: the accumulator input of every MFMA is a constant register tile holding 0x4B400000 (1.5 * 2^23),
+//    so each result, read as fp32, is 1.5 * 2^23 + isum exactly; one FMA with the block's activation
+//    scale and -d_x * 1.5 * 2^23 gives round(d_x * isum) without a conversion.  Q1_0: a zero accumulator,
+//    each exact int32 result converted and multiply-added into the weight block's sum (fewer registers,
+//    which keeps two workgroups per CU).  The weight block scale is then applied with one more FMA (bankml
+//    technical report, section III.3: one multiply-add per q8_0 block, then one per weight block).
 //  * Planar weights have no block scales: the MFMA accumulates int32 over the whole row and the two
 //    per-row / per-tensor scales are applied once at the end.
 #include "lowbit_internal.h"
@@ -33,9 +33,9 @@ namespace lb {
 
 namespace {
 
-constexpr int GT = 1024;         // threads per workgroup (16 waves)
-constexpr int TN = 128;          // weight rows per workgroup
-constexpr int TM = 64;           // activation rows per workgroup
+constexpr int GT = 512;          // threads per workgroup (8 waves)
+constexpr int TN = 64;           // weight rows per workgroup
+constexpr int TM = 128;          // activation rows per workgroup
 constexpr int KS = 128;          // columns per K-step
 constexpr int WROW = KS / 4 + 4; // LDS dwords per unpacked weight row (padded against bank conflicts)
 constexpr int XROW = KS / 4 + 4; // LDS dwords per activation row
@@ -44,6 +44,7 @@ constexpr float BIASF = 12582912.0f;
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ uint32_t perm(uint32_t s0, uint32_t s1, uint32_t sel)
 {
@@ -76,11 +77,12 @@ __device__ __forceinline__ void unpack_q2_dword(uint32_t v, uint32_t *out)
 // What one thread carries from global memory into a K-step.  Every thread takes one share of the weight
 // tile -- Q2_0: one code dword (16 weights); Q1_0: one sign dword, of which it builds two of the four
 // activation blocks; planar: one (pos, neg) dword pair, of which it builds half -- in a.x (planar neg in
-// a.y, the weight block scale's binary16 in a.z where the thread stores it), 8 activation bytes in b,
-// and, for the first TM threads, the four binary16 activation scales of one activation row in c.
+// a.y, the weight block scale's binary16 in a.z where the thread stores it), 32 activation bytes (one
+// q8_0 block of one activation row) in b0, b1, and, for the first TM threads, the four binary16
+// activation scales of one activation row in c.
 struct StepRegs {
     uint4 a;
-    uint2 b;
+    v4u b0, b1; // native vectors: copied as registers, never through memory
     uint2 c;
 };
 
@@ -93,10 +95,12 @@ __device__ __forceinline__ void load_step(StepRegs &r, const uint8_t *__restrict
     // shares past the row's end re-read its last block and are not stored.  The registers are filled
     // straight from memory, so nothing waits on them until the step is stored.
     const int kab = min(KS, K - kk) / QK8; // activation blocks in this step
-    // activation tile: 64 rows x kab * 32 bytes; thread -> (row tid / 16, 8-byte chunk tid % 16)
+    // activation tile: 128 rows x kab blocks of 32 bytes; thread -> (row tid / 4, block tid % 4)
     {
-        const int m = min(m0 + (tid >> 4), M - 1), ch = min(tid & 15, 4 * kab - 1);
-        r.b = *reinterpret_cast<const uint2 *>(X + (int64_t)m * K + kk + 8 * ch);
+        const int m = min(m0 + (tid >> 2), M - 1), ch = min(tid & 3, kab - 1);
+        const v4u *px = reinterpret_cast<const v4u *>(X + (int64_t)m * K + kk + 32 * ch);
+        r.b0 = px[0];
+        r.b1 = px[1];
     }
     if (FMT != LB_TERNARY_PLANAR && tid < TM) { // one activation row's four block scales
         const int mm = min(m0 + (tid & (TM - 1)), M - 1);
@@ -137,9 +141,12 @@ __device__ __forceinline__ void store_step(Lds &lds, int buf, const StepRegs &r,
 {
     const int kab = min(KS, K - kk) / QK8;
     {
-        const int mr = tid >> 4, ch = tid & 15;
-        if (ch < 4 * kab)
-            *reinterpret_cast<uint2 *>(lds.x[buf] + mr * XROW + 2 * ch) = r.b;
+        const int mr = tid >> 2, ch = tid & 3;
+        if (ch < kab) {
+            v4u *dst = reinterpret_cast<v4u *>(lds.x[buf] + mr * XROW + 8 * ch);
+            dst[0] = r.b0;
+            dst[1] = r.b1;
+        }
     }
     if (FMT != LB_TERNARY_PLANAR && tid < TM) {
         // (on a half step the values of blocks 2 and 3 are not read)
@@ -194,21 +201,23 @@ __device__ __forceinline__ void store_step(Lds &lds, int buf, const StepRegs &r,
     }
 }
 
-// One wave's share of a K-step: the two q8_0 blocks jb, jb + 1 (half of the step's 128 columns), which
-// lie in one weight block (a whole Q2_0 block, half a Q1_0 block).
+// One wave's share of a K-step: its 32 x 32 output tile over the step's kab q8_0 blocks (4, or 2 on the
+// half step that ends a Q2_0 / planar row of an odd number of weight blocks).
 template <int FMT, bool EMIT>
-__device__ __forceinline__ void step_compute(const Lds &lds, int buf, int jb, int h, int l32, int wn, int wm, int m0,
+__device__ __forceinline__ void step_compute(const Lds &lds, int buf, int kab, int h, int l32, int wn, int wm, int m0,
                                              int n0, int M, int N, int nab, int kk, float (&acc)[16], v16i &iacc,
                                              const v16i &cbias, int32_t *__restrict__ sums)
 {
     constexpr bool PLANAR = FMT == LB_TERNARY_PLANAR;
-    constexpr int JW = FMT == LB_Q1_0 ? 4 : 2; // activation blocks per weight block
+    constexpr bool BIASED = FMT == LB_Q2_0_G64; // accumulator preset to the bias (else zero)
+    constexpr int JW = FMT == LB_Q1_0 ? 4 : 2;  // activation blocks per weight block
     const uint32_t *wl = lds.w[buf] + (32 * wn + l32) * WROW + 4 * h;
     const uint32_t *xl = lds.x[buf] + (32 * wm + l32) * XROW + 4 * h;
     float t[16];
 #pragma unroll
-    for (int jj = 0; jj < 2; jj++) {
-        const int j = jb + jj;
+    for (int j = 0; j < KS / QK8; j++) {
+        if (j >= kab) // uniform
+            break;
         const uint4 a4 = *reinterpret_cast<const uint4 *>(wl + 8 * j);
         const uint4 b4 = *reinterpret_cast<const uint4 *>(xl + 8 * j);
         const v4i A = {(int)a4.x, (int)a4.y, (int)a4.z, (int)a4.w};
@@ -219,11 +228,17 @@ __device__ __forceinline__ void step_compute(const Lds &lds, int buf, int jb, in
         }
         const v16i D = __builtin_amdgcn_mfma_i32_32x32x32_i8(A, B, cbias, 0, 0, 0);
         const float dx = lds.dx[buf][j * TM + 32 * wm + l32];
-        const float c = -dx * BIASF; // exact: an 11-bit significand times 3 * 2^22
+        if (BIASED) {
+            const float c = -dx * BIASF; // exact: an 11-bit significand times 3 * 2^22
 #pragma unroll
-        for (int i = 0; i < 16; i++) {
-            const float v = fmaf(dx, __int_as_float(D[i]), c); // round(d_x * isum)
-            t[i] = jj == 0 ? v : t[i] + v;
+            for (int i = 0; i < 16; i++) {
+                const float v = fmaf(dx, __int_as_float(D[i]), c); // round(d_x * isum)
+                t[i] = j % JW == 0 ? v : t[i] + v;
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 16; i++) // (float)isum is exact: |isum| < 2^24
+                t[i] = j % JW == 0 ? dx * (float)D[i] : fmaf(dx, (float)D[i], t[i]);
         }
         if (EMIT) {
             const int m = m0 + 32 * wm + l32, kb = kk / QK8 + j;
@@ -231,46 +246,56 @@ __device__ __forceinline__ void step_compute(const Lds &lds, int buf, int jb, in
             for (int i = 0; i < 16; i++) {
                 const int n = n0 + 32 * wn + 8 * (i >> 2) + 4 * h + (i & 3);
                 if (m < M && n < N)
-                    sums[((int64_t)m * N + n) * nab + kb] = D[i] - (int)BIAS;
+                    sums[((int64_t)m * N + n) * nab + kb] = BIASED ? D[i] - (int)BIAS : D[i];
             }
         }
-    }
-    if (!PLANAR) {
-        const int b = jb / JW;
+        if (j % JW == JW - 1) { // the weight block is complete
+            const int b = j / JW;
 #pragma unroll
-        for (int g = 0; g < 4; g++) {
-            const float4 dw = *reinterpret_cast<const float4 *>(lds.dw[buf] + b * TN + 32 * wn + 8 * g + 4 * h);
-            const float dwv[4] = {dw.x, dw.y, dw.z, dw.w};
+            for (int g = 0; g < 4; g++) {
+                const float4 dw = *reinterpret_cast<const float4 *>(lds.dw[buf] + b * TN + 32 * wn + 8 * g + 4 * h);
+                const float dwv[4] = {dw.x, dw.y, dw.z, dw.w};
 #pragma unroll
-            for (int q = 0; q < 4; q++)
-                acc[4 * g + q] = fmaf(dwv[q], t[4 * g + q], acc[4 * g + q]);
+                for (int q = 0; q < 4; q++)
+                    acc[4 * g + q] = fmaf(dwv[q], t[4 * g + q], acc[4 * g + q]);
+            }
         }
     }
 }
 
 template <int FMT, bool EMIT>
-__global__ __launch_bounds__(GT, 1) void gemm_kernel(const uint8_t *__restrict__ W, int N, int K, float w_scale,
+__global__ __launch_bounds__(GT, 2) void gemm_kernel(const uint8_t *__restrict__ W, int N, int K, float w_scale,
                                                      const int8_t *__restrict__ X, const void *__restrict__ Xscale,
-                                                     int M, float *__restrict__ Y, int32_t *__restrict__ sums)
+                                                     int M, float *__restrict__ Y, int32_t *__restrict__ sums, int ntn)
 {
     __shared__ Lds lds;
 
     constexpr bool PLANAR = FMT == LB_TERNARY_PLANAR;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int h = lane >> 5, l32 = lane & 31;
-    // this wave's 32 x 32 tile inside the 128 x 64 workgroup tile, and its half of each step's columns
-    const int ti = wave & 7, kh = wave >> 3;
-    const int wn = ti & 3, wm = ti >> 2;
-    const int n0 = blockIdx.x * TN, m0 = blockIdx.y * TM;
+    // this wave's 32 x 32 output tile inside the 64 x 128 workgroup tile
+    const int wn = wave & 1, wm = wave >> 1;
+    const int bn = blockIdx.x % ntn, bm = blockIdx.x / ntn; // weight tiles vary fastest
+    const int n0 = bn * TN, m0 = bm * TM;
     const int nrec = FMT == LB_Q1_0 ? K / 128 : K / 64; // 16-byte records per weight row
     const int nab = K / QK8;                             // activation blocks per row
     const uint16_t *wsc = reinterpret_cast<const uint16_t *>(W + (int64_t)N * nrec * 16);
     const uint16_t *xsc = reinterpret_cast<const uint16_t *>(Xscale);
 
+    // Q2_0: 16 registers of the bias, each made opaque to the compiler: a tile it knows to be uniform it
+    // rebuilds before every MFMA (16 moves each) instead of keeping it live.  Q1_0: a zero accumulator
+    // (its results are converted instead: the bias registers would push it past 128 VGPRs, and so to one
+    // workgroup per CU)
     v16i cbias;
 #pragma unroll
-    for (int i = 0; i < 16; i++)
-        cbias[i] = (int)BIAS;
+    for (int i = 0; i < 16; i++) {
+        int b = (int)BIAS;
+        if (FMT == LB_Q2_0_G64)
+            asm volatile("; opaque bias %0" : "+v"(b));
+        else
+            b = 0;
+        cbias[i] = b;
+    }
     float acc[16];
     v16i iacc;
 #pragma unroll
@@ -285,13 +310,13 @@ __global__ __launch_bounds__(GT, 1) void gemm_kernel(const uint8_t *__restrict__
     // cache channels.  Integer block sums do not depend on the order; only the fp32 accumulation order
     // of the weight blocks does.
     const int nsteps = (K + KS - 1) / KS;
-    const int rot = blockIdx.x % nsteps;
+    const int rot = bn % nsteps;
     auto step_k = [&](int s) { return ((s + rot) % nsteps) * KS; };
 
     // register ring: the loads of step s + PF are issued into the slot step s frees; the step loop is
     // unrolled by the ring length so every slot is a fixed set of registers and the compiler can wait
     // for exactly the oldest step's loads
-    constexpr int PF = 3;
+    constexpr int PF = 2; // (3 measured slower: its registers cost the second workgroup per CU)
     StepRegs ring[PF];
 #pragma unroll
     for (int p = 0; p < PF; p++)
@@ -311,31 +336,7 @@ __global__ __launch_bounds__(GT, 1) void gemm_kernel(const uint8_t *__restrict__
         // unconditional (the last steps re-load the final step, unused): a load under a branch would make
         // the compiler wait for every outstanding load at the next store instead of only this slot's
         load_step<FMT>(ring[q], W, wsc, N, K, X, xsc, M, n0, m0, step_k(min(s + PF, nsteps - 1)), tid);
-        // a full step: each K half takes two blocks; a half step (the K tail of Q2_0 / planar): the first
-        // half takes both (uniform per wave)
-        if (kab == KS / QK8 || kh == 0)
-            step_compute<FMT, EMIT>(lds, buf, kab == KS / QK8 ? 2 * kh : 0, h, l32, wn, wm, m0, n0, M, N, nab, kk, acc,
-                                    iacc, cbias, sums);
-    }
-
-    // the second K half hands its partial sums to the first through LDS (the weight buffers are free now)
-    __syncthreads();
-    uint32_t *red = lds.w[0];
-    if (kh == 1) {
-#pragma unroll
-        for (int i = 0; i < 16; i++)
-            red[(ti * 16 + i) * 64 + lane] = PLANAR ? (uint32_t)iacc[i] : __float_as_uint(acc[i]);
-    }
-    __syncthreads();
-    if (kh == 1)
-        return;
-#pragma unroll
-    for (int i = 0; i < 16; i++) {
-        const uint32_t o = red[(ti * 16 + i) * 64 + lane];
-        if (PLANAR)
-            iacc[i] += (int)o;
-        else
-            acc[i] += __uint_as_float(o);
+        step_compute<FMT, EMIT>(lds, buf, kab, h, l32, wn, wm, m0, n0, M, N, nab, kk, acc, iacc, cbias, sums);
     }
 
     // store: lane holds weight rows n = 32 wn + 8 (i / 4) + 4 h + i % 4 of activation row m = 32 wm + l32
@@ -365,9 +366,11 @@ template <int FMT, bool EMIT>
 hipError_t launch_fmt(const uint8_t *W, int64_t N, int64_t K, float w_scale, const int8_t *Xq, const void *Xscale,
                       int64_t M, float *Y, int32_t *sums, hipStream_t s)
 {
-    const dim3 grid((unsigned)((N + TN - 1) / TN), (unsigned)((M + TM - 1) / TM));
-    hipLaunchKernelGGL((gemm_kernel<FMT, EMIT>), grid, dim3(GT), 0, s, W, (int)N, (int)K, w_scale, Xq, Xscale, (int)M,
-                       Y, sums);
+    const int64_t ntn = (N + TN - 1) / TN, ntm = (M + TM - 1) / TM;
+    if (ntn * ntm > INT32_MAX)
+        return hipErrorInvalidValue;
+    hipLaunchKernelGGL((gemm_kernel<FMT, EMIT>), dim3((unsigned)(ntn * ntm)), dim3(GT), 0, s, W, (int)N, (int)K,
+                       w_scale, Xq, Xscale, (int)M, Y, sums, (int)ntn);
     return hipGetLastError();
 }
 
