@@ -155,23 +155,27 @@ FEEDS = {"attn_q": 0, "attn_k": 0, "attn_v": 0, "attn_output": 1, "ffn_gate": 2,
 
 
 class LayeredGraph:
-    """A token in dependency order: per layer, the q/k/v products, then o, then gate/up, then down, each phase
-    one batched launch after the quantisation of its own input row (288 launches for 36 layers), captured
-    once as a HIP graph and replayed."""
+    """A token in dependency order: per layer, the q/k/v products, then o, then gate/up, then down, captured
+    once as a HIP graph and replayed.  Each phase is one batched launch after the quantisation of its own
+    input row (288 launches for 36 layers), or, fused (ggml formats), one batched launch that quantises its
+    fp32 input itself (144 launches)."""
 
-    def __init__(self, tok):
+    def __init__(self, tok, fused=False):
         import torch
 
         L = tok.L
-        self.tok, self.phases = tok, []
+        self.tok, self.phases, self.fused = tok, [], fused
         for l in range(tok.layers):
             for f in range(4):
                 prods = [p for p in tok.products if p["layer"] == l and FEEDS[p["name"]] == f]
                 if not prods:
                     continue
                 K, r = prods[0]["feed"]
-                descs = [L.desc(tok.fmt, p["W"], p["N"], p["K"], p["xq"], p["xs"], p["y"], w_tensor_scale=p["w_scale"])
-                         for p in prods]
+                if fused:
+                    descs = [L.desc(tok.fmt, p["W"], p["N"], p["K"], None, None, p["y"], x=tok.x[K][r]) for p in prods]
+                else:
+                    descs = [L.desc(tok.fmt, p["W"], p["N"], p["K"], p["xq"], p["xs"], p["y"],
+                                    w_tensor_scale=p["w_scale"]) for p in prods]
                 self.phases.append((K, r, L.Batch(descs)))
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
@@ -187,11 +191,12 @@ class LayeredGraph:
     def eager(self):
         t, L = self.tok, self.tok.L
         for K, r, b in self.phases:
-            L.lowbit_quantize_act(t.afmt, t.x[K][r:r + 1], 1, K, t.xq[K][r:r + 1], t.xs[K][r:r + 1])
+            if not self.fused:
+                L.lowbit_quantize_act(t.afmt, t.x[K][r:r + 1], 1, K, t.xq[K][r:r + 1], t.xs[K][r:r + 1])
             b.run()
 
     def launches(self):
-        return 2 * len(self.phases)
+        return (1 if self.fused else 2) * len(self.phases)
 
     def close(self):
         for _, _, b in self.phases:
@@ -513,16 +518,20 @@ def main():
     secondary = {}
     if "layered" in args.secondary.split(","):
         # the same token in dependency order (per layer q/k/v, o, gate/up, down), replayed as one HIP graph
-        lg = LayeredGraph(tok)
-        msg = time_graph(lg, args.steps, args.warmup)
-        secondary["q2_0_8b_token_layered_graph"] = {
-            "workload": "the headline token in dependency order: per layer q/k/v, o, gate/up, down, each phase a "
-                        "q8_0 quantise of its input plus one batched launch, captured as one HIP graph",
-            "launches": lg.launches(), "ms_per_token": round(msg, 5),
-            "gbs": round(tok.weight_bytes / (msg * 1e-3) / 1e9, 1),
-            "pct_hbm_peak": round(100 * tok.weight_bytes / (msg * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
-        }
-        lg.close()
+        for fused, key, what in ((True, "q2_0_8b_token_layered_graph",
+                                  "each phase one batched launch that quantises its fp32 input to q8_0 itself"),
+                                 (False, "q2_0_8b_token_layered_graph_separate_quantise",
+                                  "each phase a q8_0 quantise launch plus one batched launch")):
+            lg = LayeredGraph(tok, fused=fused)
+            msg = time_graph(lg, args.steps, args.warmup)
+            secondary[key] = {
+                "workload": "the headline token in dependency order: per layer q/k/v, o, gate/up, down, " + what +
+                            ", captured as one HIP graph",
+                "launches": lg.launches(), "ms_per_token": round(msg, 5),
+                "gbs": round(tok.weight_bytes / (msg * 1e-3) / 1e9, 1),
+                "pct_hbm_peak": round(100 * tok.weight_bytes / (msg * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+            }
+            lg.close()
     tok.batch.close()
     del tok
     torch.cuda.empty_cache()

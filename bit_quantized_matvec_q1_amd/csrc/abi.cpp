@@ -344,13 +344,15 @@ lb_status dense_head_matvec_i8(const int8_t *W, const float *row_scale, int64_t 
 // ---- batched decode ------------------------------------------------------------------------------
 
 // Tile plan of one launch group.  Every product is cut into row tiles (whole row iterations of the
-// configuration) of about the same weight bytes, between 192 and 384 KiB (smaller tiles pay more for
-// their activation staging, larger ones leave a ragged tail: both measured slower); the size is the one
-// whose in-order dispatch onto the group's resident workgroup slots (CUs x workgroups per CU) has the
-// shortest simulated makespan, each tile costing its weight bytes plus a fixed start-up share; among
-// sizes within 0.5 % of the best, the largest -- but 256 KiB unless the simulation predicts a makespan
-// at least 5 % shorter (a group whose 256 KiB tiles leave a mostly empty last round).  Tiles are
-// emitted largest first, so the partial tiles of every product fill the tail of the launch.
+// configuration) of about the same weight bytes, between 16 and 384 KiB; the size is the one whose
+// in-order dispatch onto the group's resident workgroup slots (CUs x workgroups per CU) has the shortest
+// simulated makespan, each tile costing its weight bytes plus a fixed start-up share; among sizes within
+// 0.5 % of the best, the largest -- but 256 KiB unless the simulation predicts a makespan at least 5 %
+// shorter.  A whole token's products (gigabytes) keep 256 KiB tiles (smaller tiles pay more for their
+// activation staging, larger ones leave a ragged tail: both measured slower); a small batch -- one
+// dependency phase of a token, a few tens of MB -- gets tiles small enough to occupy every CU instead of
+// a few dozen workgroups.  Tiles are emitted largest first, so the partial tiles of every product fill
+// the tail of the launch.
 static void plan_tiles(int fmt, int cfg, std::vector<lb::DevDesc> &ds, int64_t slots, std::vector<lb::TileRef> &out)
 {
     constexpr int64_t kStartup = 24 * 1024; // bytes-equivalent of one workgroup's staging and start-up
@@ -363,7 +365,11 @@ static void plan_tiles(int fmt, int cfg, std::vector<lb::DevDesc> &ds, int64_t s
     };
     std::vector<int64_t> cand, span;
     std::vector<int64_t> costs;
-    for (int64_t tb = 192 * 1024; tb <= 384 * 1024; tb += 16 * 1024) {
+    std::vector<int64_t> sizes = {16 * 1024, 24 * 1024, 32 * 1024, 48 * 1024, 64 * 1024, 96 * 1024, 128 * 1024,
+                                  160 * 1024};
+    for (int64_t tb = 192 * 1024; tb <= 384 * 1024; tb += 16 * 1024)
+        sizes.push_back(tb);
+    for (int64_t tb : sizes) {
         costs.clear();
         for (const lb::DevDesc &d : ds) {
             const int64_t rows = rows_for(tb, d), rb = lowbit_weight_bytes(fmt, 1, d.K);
@@ -430,7 +436,20 @@ lb_status lowbit_batch_create(const lb_matvec_desc *list, int32_t n, lb_batch **
         return fail(LB_EINVAL, fn, "empty or null work list");
     for (int32_t i = 0; i < n; i++) {
         const lb_matvec_desc &d = list[i];
-        lb_status st = check_product(fn, d.fmt, d.W, d.N, d.K, d.afmt, d.xq, d.xscale, d.y);
+        lb_status st;
+        if (d.afmt == LB_ACT_F32_Q8_0) {
+            // fp32 activations quantised in the product's own launch
+            if (is_wfmt(d.fmt) && d.fmt != LB_Q1_0 && d.fmt != LB_Q2_0_G64)
+                return fail(LB_EUNSUPPORTED, fn, "LB_ACT_F32_Q8_0 is for Q1_0 and Q2_0_g64 weights only");
+            if (d.N > 0 && !d.x)
+                return fail(LB_EINVAL, fn, "null x for LB_ACT_F32_Q8_0");
+            if (d.N > 0 && !aligned(d.x, 16))
+                return fail(LB_EALIGN, fn, "x needs 16-byte alignment");
+            // x stands in for xq and xscale in the shared checks
+            st = check_product(fn, d.fmt, d.W, d.N, d.K, LB_ACT_Q8_0, d.x, d.x, d.y);
+        } else {
+            st = check_product(fn, d.fmt, d.W, d.N, d.K, d.afmt, d.xq, d.xscale, d.y);
+        }
         if (st != LB_OK)
             return st;
         if (d.K == 0 && d.N > 0)
@@ -444,7 +463,7 @@ lb_status lowbit_batch_create(const lb_matvec_desc *list, int32_t n, lb_batch **
 
     // one launch group per (weight format, kernel configuration) present, products in list order
     struct Key {
-        int fmt, cfg;
+        int fmt, cfg, qin;
     };
     std::vector<Key> keys;
     std::vector<std::vector<lb::DevDesc>> descs;
@@ -454,11 +473,12 @@ lb_status lowbit_batch_create(const lb_matvec_desc *list, int32_t n, lb_batch **
         if (d.N == 0)
             continue;
         const int cfg = lb::matvec_config(d.fmt, d.K);
+        const int qin = d.afmt == LB_ACT_F32_Q8_0 ? 1 : 0;
         size_t gi = 0;
-        while (gi < keys.size() && !(keys[gi].fmt == d.fmt && keys[gi].cfg == cfg))
+        while (gi < keys.size() && !(keys[gi].fmt == d.fmt && keys[gi].cfg == cfg && keys[gi].qin == qin))
             gi++;
         if (gi == keys.size()) {
-            keys.push_back({d.fmt, cfg});
+            keys.push_back({d.fmt, cfg, qin});
             descs.emplace_back();
             lds.push_back(0);
         }
@@ -472,8 +492,10 @@ lb_status lowbit_batch_create(const lb_matvec_desc *list, int32_t n, lb_batch **
         dd.w_scale = d.w_tensor_scale;
         dd.cfg = cfg;
         dd.tile_rows = 0; // set by the tile plan
+        dd.x = qin ? d.x : nullptr;
         descs[gi].push_back(dd);
-        lds[gi] = std::max(lds[gi], (size_t)lb::matvec_stage_bytes(d.fmt, d.K));
+        lds[gi] = std::max(lds[gi], (size_t)lb::matvec_stage_bytes(d.fmt, d.K) +
+                                        (qin ? (size_t)lb::q8_0_lds_bytes(d.K) : 0));
     }
     int device = 0, cus = 0;
     hipGetDevice(&device);
@@ -485,7 +507,8 @@ lb_status lowbit_batch_create(const lb_matvec_desc *list, int32_t n, lb_batch **
         for (const lb::DevDesc &dd : descs[gi])
             full[gi] &= lb::matvec_config_full(keys[gi].fmt, keys[gi].cfg, dd.K) ? 1 : 0;
         const int64_t slots =
-            (int64_t)cus * lb::matvec_batched_blocks_per_cu(keys[gi].fmt, keys[gi].cfg, full[gi] != 0, lds[gi]);
+            (int64_t)cus * lb::matvec_batched_blocks_per_cu(keys[gi].fmt, keys[gi].cfg, full[gi] != 0,
+                                                            keys[gi].qin != 0, lds[gi]);
         plan_tiles(keys[gi].fmt, keys[gi].cfg, descs[gi], slots, tiles[gi]);
     }
     size_t bytes = 256;
@@ -506,6 +529,7 @@ lb_status lowbit_batch_create(const lb_matvec_desc *list, int32_t n, lb_batch **
         grp.g.fmt = keys[gi].fmt;
         grp.g.cfg_a = keys[gi].cfg;
         grp.g.full = full[gi];
+        grp.g.qin = keys[gi].qin;
         grp.g.ntiles = (int32_t)tiles[gi].size();
         grp.g.desc = reinterpret_cast<const lb::DevDesc *>(base + off);
         e = hipMemcpy(base + off, descs[gi].data(), descs[gi].size() * sizeof(lb::DevDesc), hipMemcpyHostToDevice);

@@ -21,6 +21,28 @@ inline __device__ float half_bits_to_float(uint16_t h) { return __half2float(__u
 
 // --- cross-lane sum over aligned groups of L lanes with DPP (no LDS round trip).  The total ends up in
 // the group's last lane (li == L - 1); for L <= 16 every lane of the group holds it.
+// q8_0 (bankml technical report, section III.2: blocks of 32 signed bytes with their own half-precision
+// scale, 127 / max|x| with round-half-to-even), as computed by eight lanes per block, one float4 each:
+// the block's amax is the maximum over the eight lanes (exact in any order), the multiplier 127 / amax a
+// correctly rounded fp32 quotient (0 when amax = 0), each q round-half-even of the fp32 product, and the
+// stored scale fp16_rne(amax / 127) of the correctly rounded fp32 quotient.  Every quantiser of the
+// library goes through these two functions, so they all give the same bytes.
+inline __device__ float q8_0_block_amax8(float4 v)
+{
+    float amax = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+#pragma unroll
+    for (int o = 1; o < 8; o <<= 1)
+        amax = fmaxf(amax, __shfl_xor(amax, o, 8));
+    return amax;
+}
+inline __device__ uint32_t q8_0_pack4(float4 v, float amax)
+{
+    const float id = amax > 0.0f ? 127.0f / amax : 0.0f;
+    return (uint32_t)((int)rintf(v.x * id) & 0xff) | (uint32_t)((int)rintf(v.y * id) & 0xff) << 8 |
+           (uint32_t)((int)rintf(v.z * id) & 0xff) << 16 | (uint32_t)((int)rintf(v.w * id) & 0xff) << 24;
+}
+inline __device__ uint16_t q8_0_scale_bits(float amax) { return __half_as_ushort(__float2half_rn(amax / 127.0f)); }
+
 template <int L> inline __device__ int group_sum_i(int v)
 {
     if (L >= 2)
@@ -86,6 +108,7 @@ struct DevDesc {
     float w_scale;
     int32_t cfg;        // index into the format's configuration table
     int32_t tile_rows;  // rows per tile
+    const float *x;     // fp32 activations quantised in the launch (LB_ACT_F32_Q8_0), else null
 };
 
 struct TileRef {        // one workgroup of a batched launch: its product and first row
@@ -96,6 +119,7 @@ struct BatchGroup {
     int fmt;
     int cfg_a;               // the kernel configuration of this launch group
     int full;                // every product's row has exactly L * S slices of the configuration
+    int qin;                 // the products' activations are fp32, quantised to q8_0 in the launch
     int32_t ntiles;          // workgroups in the launch
     const DevDesc *desc;     // device
     const TileRef *tiles;    // device, one per workgroup
@@ -105,7 +129,9 @@ int matvec_config(int fmt, int64_t K);           // configuration index for a pr
 int matvec_config_rows_per_iter(int fmt, int cfg); // rows one workgroup covers per iteration
 bool matvec_config_full(int fmt, int cfg, int64_t K); // a row of K has exactly L * S slices
 hipError_t launch_matvec_batched(const BatchGroup &g, hipStream_t s, size_t lds_bytes);
-int matvec_batched_blocks_per_cu(int fmt, int cfg, bool full, size_t lds_bytes); // resident workgroups per CU
+int matvec_batched_blocks_per_cu(int fmt, int cfg, bool full, bool qin, size_t lds_bytes); // resident per CU
+// LDS bytes of one row of K activations quantised to q8_0 in a launch (int8 [K], then binary16 [K/32])
+inline int64_t q8_0_lds_bytes(int64_t K) { return (K + K / 16 + 15) / 16 * 16; }
 int matvec_stage_bytes(int fmt, int64_t K); // LDS bytes of one product's staged activation
 
 // Q8_0 weights x q8_0 activations (q8.hip): configurations in their own index space

@@ -344,11 +344,11 @@ __device__ __forceinline__ void compute_row(const uint4 (&code)[S], const uint32
     }
 }
 
-template <int FMT, int L, int S, bool EMIT, bool FULL>
+template <int FMT, int L, int S, bool EMIT, bool FULL, bool QIN = false>
 __device__ __forceinline__ void matvec_tile(const uint8_t *__restrict__ W, int N, int K, float w_scale,
                                             const int8_t *__restrict__ xq, const void *__restrict__ xscale,
                                             float *__restrict__ y, int32_t *__restrict__ sums, int row0, int nrows,
-                                            uint32_t *__restrict__ lds)
+                                            uint32_t *__restrict__ lds, const float *__restrict__ x = nullptr)
 {
     constexpr int REC = F<FMT>::REC;
     constexpr int GROUPS = 64 / L;           // rows per wave per iteration
@@ -382,7 +382,38 @@ __device__ __forceinline__ void matvec_tile(const uint8_t *__restrict__ W, int N
         onext += stepb;
     }
 
-    stage_activation<FMT>(xq, xscale, ns, lds);
+    if (QIN) {
+        // fp32 activations (LB_ACT_F32_Q8_0): quantised to q8_0 into LDS past the staged records with the
+        // arithmetic of the quantise kernel, then staged from there like quantised ones
+        int8_t *qb = reinterpret_cast<int8_t *>(lds + ns * REC);
+        uint16_t *qs = reinterpret_cast<uint16_t *>(qb + K);
+        // K / 4 float4 chunks, eight per block, four chunks per thread in flight at once; WG is a
+        // multiple of 8, so a block's eight lanes are all in range or all out
+        constexpr int QU = 4;
+        const int nc = K / 4;
+        for (int c0 = threadIdx.x; c0 < nc; c0 += QU * WG) {
+            float4 v[QU];
+#pragma unroll
+            for (int u = 0; u < QU; u++) {
+                const int c = c0 + u * WG;
+                v[u] = c < nc ? reinterpret_cast<const float4 *>(x)[c] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+            }
+#pragma unroll
+            for (int u = 0; u < QU; u++) {
+                const int c = c0 + u * WG;
+                const float amax = q8_0_block_amax8(v[u]);
+                if (c < nc) {
+                    reinterpret_cast<uint32_t *>(qb)[c] = q8_0_pack4(v[u], amax);
+                    if ((c & 7) == 0)
+                        qs[c >> 3] = q8_0_scale_bits(amax);
+                }
+            }
+        }
+        __syncthreads();
+        stage_activation<FMT>(qb, qs, ns, lds);
+    } else {
+        stage_activation<FMT>(xq, xscale, ns, lds);
+    }
     __syncthreads();
 
     uint32_t act[S][REC];
@@ -595,7 +626,7 @@ hipError_t launch_matvec(int fmt, const uint8_t *W, int64_t N, int64_t K, float 
 // product (a uniform, scalar-cached read); every instantiation is compiled for one configuration, so
 // each gets the registers it needs and no more.
 // ------------------------------------------------------------------------------------------------
-template <int FMT, int L, int S, bool FULL>
+template <int FMT, int L, int S, bool FULL, bool QIN>
 __global__ __launch_bounds__(WG) void matvec_batched_kernel(const DevDesc *__restrict__ desc,
                                                             const TileRef *__restrict__ tiles)
 {
@@ -604,8 +635,12 @@ __global__ __launch_bounds__(WG) void matvec_batched_kernel(const DevDesc *__res
     const DevDesc d = desc[tr.prod];
     const int row0 = tr.row0;
     const int nrows = min(d.tile_rows, d.N - row0);
-    matvec_tile<FMT, L, S, false, FULL>(d.W, d.N, d.K, d.w_scale, d.xq, d.xscale, d.y, nullptr, row0, nrows, lds);
+    matvec_tile<FMT, L, S, false, FULL, QIN>(d.W, d.N, d.K, d.w_scale, d.xq, d.xscale, d.y, nullptr, row0, nrows, lds,
+                                             d.x);
 }
+
+// fp32 activations quantised in the launch: the ggml formats (q8_0 activations) only
+constexpr bool qin_allowed(int fmt) { return fmt == LB_Q1_0 || fmt == LB_Q2_0_G64; }
 
 template <int FMT>
 static hipError_t launch_batched_fmt(const BatchGroup &g, hipStream_t stream, size_t lds_bytes)
@@ -614,12 +649,24 @@ static hipError_t launch_batched_fmt(const BatchGroup &g, hipStream_t stream, si
 #define LB_BCASE(i, l, s)                                                                                     \
     case i:                                                                                                   \
         if constexpr (cfg_allowed(FMT, s)) {                                                                  \
-            if (g.full)                                                                                       \
-                hipLaunchKernelGGL((matvec_batched_kernel<FMT, l, s, true>), dim3(g.ntiles), dim3(WG), lds_bytes, \
-                                   stream, g.desc, g.tiles);                                               \
-            else                                                                                              \
-                hipLaunchKernelGGL((matvec_batched_kernel<FMT, l, s, false>), dim3(g.ntiles), dim3(WG),          \
-                                   lds_bytes, stream, g.desc, g.tiles);                                    \
+            if (g.qin) {                                                                                      \
+                if constexpr (qin_allowed(FMT)) {                                                             \
+                    if (g.full)                                                                               \
+                        hipLaunchKernelGGL((matvec_batched_kernel<FMT, l, s, true, true>), dim3(g.ntiles),    \
+                                           dim3(WG), lds_bytes, stream, g.desc, g.tiles);                     \
+                    else                                                                                      \
+                        hipLaunchKernelGGL((matvec_batched_kernel<FMT, l, s, false, true>), dim3(g.ntiles),   \
+                                           dim3(WG), lds_bytes, stream, g.desc, g.tiles);                     \
+                } else {                                                                                      \
+                    return hipErrorInvalidValue;                                                              \
+                }                                                                                             \
+            } else if (g.full) {                                                                              \
+                hipLaunchKernelGGL((matvec_batched_kernel<FMT, l, s, true, false>), dim3(g.ntiles), dim3(WG),    \
+                                   lds_bytes, stream, g.desc, g.tiles);                                       \
+            } else {                                                                                          \
+                hipLaunchKernelGGL((matvec_batched_kernel<FMT, l, s, false, false>), dim3(g.ntiles), dim3(WG),   \
+                                   lds_bytes, stream, g.desc, g.tiles);                                       \
+            }                                                                                                 \
         }                                                                                                     \
         break;
         LB_CFGS(LB_BCASE)
@@ -630,18 +677,27 @@ static hipError_t launch_batched_fmt(const BatchGroup &g, hipStream_t stream, si
     return hipGetLastError();
 }
 
-template <int FMT> static int blocks_per_cu_fmt(int cfg, bool full, size_t lds_bytes)
+template <int FMT> static int blocks_per_cu_fmt(int cfg, bool full, bool qin, size_t lds_bytes)
 {
     int n = 0;
     hipError_t e = hipErrorInvalidValue;
     switch (cfg) {
 #define LB_OCASE(i, l, s)                                                                                     \
     case i:                                                                                                   \
-        if constexpr (cfg_allowed(FMT, s))                                                                    \
-            e = full ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, matvec_batched_kernel<FMT, l, s, true>, WG, \
-                                                                    lds_bytes)                                 \
-                     : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, matvec_batched_kernel<FMT, l, s, false>,   \
-                                                                    WG, lds_bytes);                            \
+        if constexpr (cfg_allowed(FMT, s)) {                                                                  \
+            if (qin) {                                                                                        \
+                if constexpr (qin_allowed(FMT))                                                               \
+                    e = full ? hipOccupancyMaxActiveBlocksPerMultiprocessor(                                  \
+                                   &n, matvec_batched_kernel<FMT, l, s, true, true>, WG, lds_bytes)           \
+                             : hipOccupancyMaxActiveBlocksPerMultiprocessor(                                  \
+                                   &n, matvec_batched_kernel<FMT, l, s, false, true>, WG, lds_bytes);         \
+            } else {                                                                                          \
+                e = full ? hipOccupancyMaxActiveBlocksPerMultiprocessor(                                      \
+                               &n, matvec_batched_kernel<FMT, l, s, true, false>, WG, lds_bytes)              \
+                         : hipOccupancyMaxActiveBlocksPerMultiprocessor(                                      \
+                               &n, matvec_batched_kernel<FMT, l, s, false, false>, WG, lds_bytes);            \
+            }                                                                                                 \
+        }                                                                                                     \
         break;
         LB_CFGS(LB_OCASE)
 #undef LB_OCASE
@@ -651,15 +707,15 @@ template <int FMT> static int blocks_per_cu_fmt(int cfg, bool full, size_t lds_b
     return e == hipSuccess && n > 0 ? n : 1;
 }
 
-int matvec_batched_blocks_per_cu(int fmt, int cfg, bool full, size_t lds_bytes)
+int matvec_batched_blocks_per_cu(int fmt, int cfg, bool full, bool qin, size_t lds_bytes)
 {
     switch (fmt) {
     case LB_Q1_0:
-        return blocks_per_cu_fmt<LB_Q1_0>(cfg, full, lds_bytes);
+        return blocks_per_cu_fmt<LB_Q1_0>(cfg, full, qin, lds_bytes);
     case LB_Q2_0_G64:
-        return blocks_per_cu_fmt<LB_Q2_0_G64>(cfg, full, lds_bytes);
+        return blocks_per_cu_fmt<LB_Q2_0_G64>(cfg, full, qin, lds_bytes);
     case LB_TERNARY_PLANAR:
-        return blocks_per_cu_fmt<LB_TERNARY_PLANAR>(cfg, full, lds_bytes);
+        return blocks_per_cu_fmt<LB_TERNARY_PLANAR>(cfg, full, false, lds_bytes);
     case LB_Q8_0:
         return q8_blocks_per_cu(cfg, lds_bytes);
     case LB_TERNARY_B3:

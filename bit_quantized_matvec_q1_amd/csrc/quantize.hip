@@ -17,18 +17,12 @@ __global__ __launch_bounds__(WG) void quantize_q8_0_kernel(const float *__restri
     const int64_t c = (int64_t)blockIdx.x * WG + threadIdx.x; // float4 chunk: block c / 8, values 4 (c % 8) ..
     const bool in = (c >> 3) < nblocks;
     const float4 v = in ? reinterpret_cast<const float4 *>(x)[c] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-    float amax = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
-#pragma unroll
-    for (int o = 1; o < 8; o <<= 1)
-        amax = fmaxf(amax, __shfl_xor(amax, o, 8));
+    const float amax = q8_0_block_amax8(v);
     if (!in)
         return;
-    const float id = amax > 0.0f ? 127.0f / amax : 0.0f;
-    const uint32_t w = (uint32_t)((int)rintf(v.x * id) & 0xff) | (uint32_t)((int)rintf(v.y * id) & 0xff) << 8 |
-                       (uint32_t)((int)rintf(v.z * id) & 0xff) << 16 | (uint32_t)((int)rintf(v.w * id) & 0xff) << 24;
-    reinterpret_cast<uint32_t *>(xq)[c] = w;
+    reinterpret_cast<uint32_t *>(xq)[c] = q8_0_pack4(v, amax);
     if ((c & 7) == 0)
-        xs[c >> 3] = __half_as_ushort(__float2half_rn(amax / 127.0f));
+        xs[c >> 3] = q8_0_scale_bits(amax);
 }
 
 hipError_t launch_quantize_q8_0(const float *x, int64_t M, int64_t K, int8_t *xq, uint16_t *xs, hipStream_t s)

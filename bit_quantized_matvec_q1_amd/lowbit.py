@@ -13,7 +13,7 @@ import os
 import torch
 
 Q1_0, Q2_0_G64, TERNARY_PLANAR, Q8_0, TERNARY_B3 = 1, 2, 3, 4, 5
-ACT_Q8_0, ACT_I8_ROW = 1, 2
+ACT_Q8_0, ACT_I8_ROW, ACT_F32_Q8_0 = 1, 2, 3
 LB_OK, LB_EINVAL, LB_ESHAPE, LB_EALIGN, LB_EUNSUPPORTED, LB_EDEVICE = range(6)
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblowbit.so")
@@ -66,6 +66,7 @@ class lb_matvec_desc(ctypes.Structure):
         ("xq", ctypes.c_void_p),
         ("xscale", ctypes.c_void_p),
         ("y", ctypes.c_void_p),
+        ("x", ctypes.c_void_p),
     ]
 
 
@@ -165,7 +166,9 @@ class Batch:
             pass
 
 
-def desc(fmt, W, N, K, xq, xscale, y, w_tensor_scale=1.0, afmt=None) -> lb_matvec_desc:
+def desc(fmt, W, N, K, xq, xscale, y, w_tensor_scale=1.0, afmt=None, x=None) -> lb_matvec_desc:
+    """One work-list entry.  With x (fp32 activations) and afmt ACT_F32_Q8_0 the product quantises x to
+    q8_0 in its own launch; xq and xscale are then ignored (pass None)."""
     if afmt is None:
-        afmt = ACT_I8_ROW if fmt in (TERNARY_PLANAR, TERNARY_B3) else ACT_Q8_0
-    return lb_matvec_desc(fmt, afmt, N, K, _ptr(W), float(w_tensor_scale), _ptr(xq), _ptr(xscale), _ptr(y))
+        afmt = ACT_F32_Q8_0 if x is not None else ACT_I8_ROW if fmt in (TERNARY_PLANAR, TERNARY_B3) else ACT_Q8_0
+    return lb_matvec_desc(fmt, afmt, N, K, _ptr(W), float(w_tensor_scale), _ptr(xq), _ptr(xscale), _ptr(y), _ptr(x))

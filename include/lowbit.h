@@ -31,6 +31,10 @@
  *                     two ggml weight formats.
  *   LB_ACT_I8_ROW     int8 xq[M][K] plus one fp32 scale per row (per token), xscale[M] (tritium
  *                     "Architecture", section 1: activations are int8).  Used with the planar format.
+ *   LB_ACT_F32_Q8_0   fp32 x[K], quantised to q8_0 inside the product's own launch, with exactly the
+ *                     arithmetic of lowbit_quantize_act(LB_ACT_Q8_0) (so the results are bit-identical
+ *                     to quantising first).  Batched decode of LB_Q1_0 and LB_Q2_0_G64 only: a product
+ *                     that depends on the previous one's output then costs one launch instead of two.
  *
  * Conventions for every entry point:
  *   - Tensor pointers are DEVICE pointers unless stated otherwise; the caller owns every buffer.  No
@@ -56,7 +60,7 @@ extern "C" {
 #endif
 
 typedef enum { LB_Q1_0 = 1, LB_Q2_0_G64 = 2, LB_TERNARY_PLANAR = 3, LB_Q8_0 = 4, LB_TERNARY_B3 = 5 } lb_wfmt;
-typedef enum { LB_ACT_Q8_0 = 1, LB_ACT_I8_ROW = 2 } lb_afmt;
+typedef enum { LB_ACT_Q8_0 = 1, LB_ACT_I8_ROW = 2, LB_ACT_F32_Q8_0 = 3 } lb_afmt;
 
 typedef enum {
     LB_OK = 0,
@@ -194,15 +198,18 @@ typedef struct {
     int64_t N, K;         /* rows, columns */
     const void *W;        /* device layout, 16-byte aligned */
     float w_tensor_scale; /* planar only */
-    const int8_t *xq;     /* device int8 [K] */
-    const void *xscale;   /* device binary16 [K/32] or fp32 [1] */
+    const int8_t *xq;     /* device int8 [K] (ignored for LB_ACT_F32_Q8_0) */
+    const void *xscale;   /* device binary16 [K/32] or fp32 [1] (ignored for LB_ACT_F32_Q8_0) */
     float *y;             /* device fp32 [N] */
+    const float *x;       /* LB_ACT_F32_Q8_0 only: device fp32 [K], 16-byte aligned; else ignored */
 } lb_matvec_desc;
 
 typedef struct lb_batch lb_batch;
 
 /* list: HOST array of n descriptors (n >= 1).  On success *out owns device memory until destroyed.
- * The buffers the descriptors point to must stay valid while the batch is used. */
+ * The buffers the descriptors point to must stay valid while the batch is used.  A descriptor with
+ * afmt LB_ACT_F32_Q8_0 takes its activations from x and needs fmt LB_Q1_0 or LB_Q2_0_G64 (else
+ * LB_EUNSUPPORTED); null x is LB_EINVAL, x not 16-byte aligned LB_EALIGN. */
 lb_status lowbit_batch_create(const lb_matvec_desc *list, int32_t n, lb_batch **out);
 lb_status lowbit_matvec_batched(const lb_batch *b, hipStream_t s);
 void lowbit_batch_destroy(lb_batch *b);

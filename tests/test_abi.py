@@ -105,6 +105,17 @@ def test_other_entry_points_validate():
     bad = (L.lb_matvec_desc * 1)(L.lb_matvec_desc(L.Q2_0_G64, L.ACT_Q8_0, 8, 100, A16, 1.0, A16, A16, A16))
     assert lib.lowbit_batch_create(ctypes.cast(bad, ctypes.c_void_p), 1, ctypes.byref(h)) == L.LB_ESHAPE
 
+    # fp32 activations quantised in the launch: Q1_0 / Q2_0_g64 only, x required and 16-byte aligned
+    def fused(fmt, x, K=128):
+        d = (L.lb_matvec_desc * 1)(L.lb_matvec_desc(fmt, L.ACT_F32_Q8_0, 8, K, A16, 1.0, None, None, A16, x))
+        return lib.lowbit_batch_create(ctypes.cast(d, ctypes.c_void_p), 1, ctypes.byref(h))
+
+    assert fused(L.TERNARY_PLANAR, A16) == L.LB_EUNSUPPORTED
+    assert fused(L.Q8_0, A16) == L.LB_EUNSUPPORTED
+    assert fused(L.Q2_0_G64, None) == L.LB_EINVAL
+    assert fused(L.Q2_0_G64, A16 + 4) == L.LB_EALIGN
+    assert fused(L.Q1_0, A16, K=192) == L.LB_ESHAPE  # K % 128
+
 
 def _has_device():
     import torch

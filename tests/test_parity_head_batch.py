@@ -130,3 +130,47 @@ def test_batched_mixed_formats():
         ref = gpu_matvec(fmt, packed, N, K, q, xs, w_scale=Wt.s_w if Wt.s_w is not None else 1.0)
         assert np.array_equal(host(y), ref)
     b.close()
+
+
+@pytest.mark.parametrize("fmt", [synth.Q1_0, synth.Q2_0_G64])
+def test_batched_fp32_activations_quantised_in_launch(fmt):
+    """LB_ACT_F32_Q8_0: each product quantises its fp32 input inside its own launch.  Outputs are
+    bit-identical to quantising first (lowbit_quantize_act) and running the same batch, and within the
+    tolerance of the oracle on the oracle's q8_0 of the same x; two products share one x, as q/k/v do."""
+    shapes = [(300, 1024), (1024, 4096), (129, 12288), (1, 128), (517, 2560), (64, 4096)]
+    say(f"case batched fp32 activations fmt={fmt} shapes={shapes}")
+    fused, quantised, keep = [], [], []
+    x_shared = None
+    for i, (N, K) in enumerate(shapes):
+        Wt = synth.make_weights(fmt, N, K, 5800 + 10 * i)
+        packed = packed_weights(Wt)
+        if i == len(shapes) - 1:
+            x, xd = x_shared  # the last product reads the 4096-column input of the second one
+        else:
+            x = synth.activations(synth.rng(5801 + 10 * i), 1, K)[0]
+            x[:32] = 0.0  # an all-zero block
+            xd = dev(x)
+            if K == 4096:
+                x_shared = (x, xd)
+        xq = torch.empty(K, dtype=torch.int8, device="cuda")
+        xs = torch.empty(K // 32, dtype=torch.uint16, device="cuda")
+        L.lowbit_quantize_act(L.ACT_Q8_0, xd, 1, K, xq, xs)
+        yf = torch.full((N,), float("nan"), dtype=torch.float32, device="cuda")
+        yq = torch.full((N,), float("nan"), dtype=torch.float32, device="cuda")
+        fused.append(L.desc(fmt, packed, N, K, None, None, yf, x=xd))
+        quantised.append(L.desc(fmt, packed, N, K, xq, xs, yq))
+        keep.append((N, K, Wt, packed, x, xd, xq, xs, yf, yq))
+    bf, bq = L.Batch(fused), L.Batch(quantised)
+    for _ in range(2):  # a second launch of the same plans gives the same bits
+        bf.run()
+        bq.run()
+        torch.cuda.synchronize()
+        for N, K, Wt, packed, x, xd, xq, xs, yf, yq in keep:
+            assert np.array_equal(host(yf), host(yq)), f"in-launch quantisation differs for {N}x{K}"
+    for N, K, Wt, packed, x, xd, xq, xs, yf, yq in keep:
+        q_ref, d_ref = oracle.quantize_q8_0(x[None, :])
+        assert np.array_equal(host(xq), q_ref[0]) and np.array_equal(host(xs), d_ref[0])
+        y_ref, A = oracle.matvec_q(fmt, Wt.raw, N, K, q_ref[0], d_ref[0])
+        assert_close(host(yf), y_ref, A, K // 32, f"fp32-activation batch {N}x{K}")
+    bf.close()
+    bq.close()

@@ -97,3 +97,33 @@ def test_layered_graph_replays_match_eager_and_oracle(fmt):
         torch.cuda.synchronize()
     lg.close()
     tok.batch.close()
+
+
+def test_layered_graph_fused_quantisation_matches_separate():
+    """The dependency-ordered token with every phase quantising its own fp32 input inside its batched launch
+    (LB_ACT_F32_Q8_0: half the launches): every replay gives the outputs of the separate-quantise graph bit
+    for bit, with the int8 activation buffers clobbered (the fused path does not read them)."""
+    fmt = synth.Q2_0_G64
+    say("case layered graph fused quantisation")
+    tok = DecodeToken(fmt, synth.QWEN3_8B_LAYER, 3, seed=7500, keep_blocks_layers=0)
+    sep = LayeredGraph(tok)
+    sep.eager()
+    torch.cuda.synchronize()
+    ref = [p["y"].clone() for p in tok.products]
+    fused = LayeredGraph(tok, fused=True)
+    assert fused.launches() * 2 == sep.launches()
+    for rep in range(3):
+        for p in tok.products:
+            p["y"].fill_(float("nan"))
+        tok.xqbuf.zero_()
+        tok.xsbuf.zero_()
+        torch.cuda.synchronize()
+        fused.graph.replay()
+        torch.cuda.synchronize()
+        for p, y0 in zip(tok.products, ref):
+            assert torch.equal(p["y"], y0), f"replay {rep}: {p['name']} layer {p['layer']} differs"
+        tok.step()  # eager work between replays
+        torch.cuda.synchronize()
+    fused.close()
+    sep.close()
+    tok.batch.close()
