@@ -29,6 +29,8 @@
 //    per-row / per-tensor scales are applied once at the end.
 #include "lowbit_internal.h"
 
+#include <atomic>
+
 namespace lb {
 
 namespace {
@@ -263,15 +265,21 @@ __device__ __forceinline__ void step_compute(const Lds &lds, int buf, int kab, i
     }
 }
 
-template <int FMT, bool EMIT>
-__global__ __launch_bounds__(GT, 2) void gemm_kernel(const uint8_t *__restrict__ W, int N, int K, float w_scale,
-                                                     const int8_t *__restrict__ X, const void *__restrict__ Xscale,
-                                                     int M, float *__restrict__ Y, int32_t *__restrict__ sums, int ntn)
+// KSPLIT = 2 (grids of fewer than two workgroups per CU): a workgroup of 16 waves, whose two 8-wave halves
+// walk alternate K-steps of the same output tile with their own LDS buffers and add their partial sums
+// at the end, so a CU holds 16 waves where the tile count alone would give it 8.
+template <int FMT, bool EMIT, int KSPLIT>
+__global__ __launch_bounds__(GT * KSPLIT, 2 * KSPLIT) void gemm_kernel(const uint8_t *__restrict__ W, int N, int K,
+                                                                       float w_scale, const int8_t *__restrict__ X,
+                                                                       const void *__restrict__ Xscale, int M,
+                                                                       float *__restrict__ Y, int32_t *__restrict__ sums,
+                                                                       int ntn)
 {
-    __shared__ Lds lds;
+    __shared__ Lds lds[KSPLIT];
 
     constexpr bool PLANAR = FMT == LB_TERNARY_PLANAR;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int half = KSPLIT == 1 ? 0 : (int)threadIdx.x / GT;
+    const int tid = (int)threadIdx.x % GT, lane = tid & 63, wave = tid >> 6;
     const int h = lane >> 5, l32 = lane & 31;
     // this wave's 32 x 32 output tile inside the 64 x 128 workgroup tile
     const int wn = wave & 1, wm = wave >> 1;
@@ -308,35 +316,67 @@ __global__ __launch_bounds__(GT, 2) void gemm_kernel(const uint8_t *__restrict__
     // at any moment the workgroups read different column ranges of the activation rows: with row strides
     // that are large powers of two, all workgroups reading the same column range at once pile onto a few
     // cache channels.  Integer block sums do not depend on the order; only the fp32 accumulation order
-    // of the weight blocks does.
+    // of the weight blocks does.  Half h of a split workgroup takes steps h, h + 2, ...
     const int nsteps = (K + KS - 1) / KS;
+    const int nsh = (nsteps + KSPLIT - 1) / KSPLIT; // steps of the first half (the second may have one fewer)
     const int rot = bn % nsteps;
-    auto step_k = [&](int s) { return ((s + rot) % nsteps) * KS; };
+    auto step_k = [&](int j) { // K offset of this half's j-th step, clamped to the last step
+        return ((min(j * KSPLIT + half, nsteps - 1) + rot) % nsteps) * KS;
+    };
 
-    // register ring: the loads of step s + PF are issued into the slot step s frees; the step loop is
+    // register ring: the loads of step j + PF are issued into the slot step j frees; the step loop is
     // unrolled by the ring length so every slot is a fixed set of registers and the compiler can wait
     // for exactly the oldest step's loads
     constexpr int PF = 2; // (3 measured slower: its registers cost the second workgroup per CU)
     StepRegs ring[PF];
 #pragma unroll
     for (int p = 0; p < PF; p++)
-        load_step<FMT>(ring[p], W, wsc, N, K, X, xsc, M, n0, m0, step_k(min(p, nsteps - 1)), tid);
+        load_step<FMT>(ring[p], W, wsc, N, K, X, xsc, M, n0, m0, step_k(p), tid);
 
-    for (int s0 = 0; s0 < nsteps; s0 += PF)
+    for (int j0 = 0; j0 < nsh; j0 += PF)
 #pragma unroll
     for (int q = 0; q < PF; q++) {
-        const int s = s0 + q;
-        if (s >= nsteps) // uniform
+        const int j = j0 + q;
+        if (j >= nsh) // uniform
             break;
-        const int buf = s & 1;
-        const int kk = step_k(s);
+        // the second half of a split workgroup may run one step short: it still meets every barrier
+        const bool active = j * KSPLIT + half < nsteps; // uniform per half
+        const int buf = j & 1;
+        const int kk = step_k(j);
         const int kab = min(KS, K - kk) / QK8;
-        store_step<FMT>(lds, buf, ring[q], K, kk, tid);
+        if (active)
+            store_step<FMT>(lds[half], buf, ring[q], K, kk, tid);
         __syncthreads();
         // unconditional (the last steps re-load the final step, unused): a load under a branch would make
         // the compiler wait for every outstanding load at the next store instead of only this slot's
-        load_step<FMT>(ring[q], W, wsc, N, K, X, xsc, M, n0, m0, step_k(min(s + PF, nsteps - 1)), tid);
-        step_compute<FMT, EMIT>(lds, buf, kab, h, l32, wn, wm, m0, n0, M, N, nab, kk, acc, iacc, cbias, sums);
+        load_step<FMT>(ring[q], W, wsc, N, K, X, xsc, M, n0, m0, step_k(j + PF), tid);
+        if (active)
+            step_compute<FMT, EMIT>(lds[half], buf, kab, h, l32, wn, wm, m0, n0, M, N, nab, kk, acc, iacc, cbias,
+                                    sums);
+    }
+
+    if (KSPLIT == 2) {
+        // the second half hands its partial sums to the first through LDS: 8 waves x 16 x 64 dwords = 32 KiB
+        // over the first half's buffers, free once every wave has passed this barrier
+        static_assert(sizeof(Lds) >= 8 * 16 * 64 * 4, "reduction area");
+        __syncthreads();
+        uint32_t *red = reinterpret_cast<uint32_t *>(&lds[0]);
+        if (half == 1) {
+#pragma unroll
+            for (int i = 0; i < 16; i++)
+                red[(wave * 16 + i) * 64 + lane] = PLANAR ? (uint32_t)iacc[i] : __float_as_uint(acc[i]);
+        }
+        __syncthreads();
+        if (half == 1)
+            return;
+#pragma unroll
+        for (int i = 0; i < 16; i++) {
+            const uint32_t o = red[(wave * 16 + i) * 64 + lane];
+            if (PLANAR)
+                iacc[i] += (int)o;
+            else
+                acc[i] += __uint_as_float(o);
+        }
     }
 
     // store: lane holds weight rows n = 32 wn + 8 (i / 4) + 4 h + i % 4 of activation row m = 32 wm + l32
@@ -362,6 +402,22 @@ __global__ __launch_bounds__(GT, 2) void gemm_kernel(const uint8_t *__restrict__
     }
 }
 
+// Compute units of the current device, cached per device.
+static int device_cus()
+{
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return 256;
+    int v = cache[dev].load(std::memory_order_relaxed);
+    if (v == 0) {
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v < 1)
+            v = 256;
+        cache[dev].store(v, std::memory_order_relaxed);
+    }
+    return v;
+}
+
 template <int FMT, bool EMIT>
 hipError_t launch_fmt(const uint8_t *W, int64_t N, int64_t K, float w_scale, const int8_t *Xq, const void *Xscale,
                       int64_t M, float *Y, int32_t *sums, hipStream_t s)
@@ -369,11 +425,20 @@ hipError_t launch_fmt(const uint8_t *W, int64_t N, int64_t K, float w_scale, con
     const int64_t ntn = (N + TN - 1) / TN, ntm = (M + TM - 1) / TM;
     if (ntn * ntm > INT32_MAX)
         return hipErrorInvalidValue;
-    hipLaunchKernelGGL((gemm_kernel<FMT, EMIT>), dim3((unsigned)(ntn * ntm)), dim3(GT), 0, s, W, (int)N, (int)K,
-                       w_scale, Xq, Xscale, (int)M, Y, sums, (int)ntn);
+    const dim3 grid((unsigned)(ntn * ntm));
+    // fewer tiles than two workgroups per CU: split K inside 16-wave workgroups (the block-sum instances
+    // need more than the 128 registers a 16-wave workgroup allows, and keep 8 waves)
+    if constexpr (!EMIT) {
+        if (ntn * ntm < 2 * (int64_t)device_cus()) {
+            hipLaunchKernelGGL((gemm_kernel<FMT, EMIT, 2>), grid, dim3(2 * GT), 0, s, W, (int)N, (int)K, w_scale, Xq,
+                               Xscale, (int)M, Y, sums, (int)ntn);
+            return hipGetLastError();
+        }
+    }
+    hipLaunchKernelGGL((gemm_kernel<FMT, EMIT, 1>), grid, dim3(GT), 0, s, W, (int)N, (int)K, w_scale, Xq, Xscale,
+                       (int)M, Y, sums, (int)ntn);
     return hipGetLastError();
 }
-
 } // namespace
 
 hipError_t launch_gemm(int fmt, const uint8_t *W, int64_t N, int64_t K, float w_scale, const int8_t *Xq,
