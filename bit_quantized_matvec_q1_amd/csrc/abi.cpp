@@ -236,6 +236,8 @@ static lb_status gemm_common(const char *fn, int fmt, const void *W, int64_t N, 
         return st;
     if (N * M >= (int64_t(1) << 31) / ((sums && fmt != LB_TERNARY_PLANAR) ? (K / 32 + 1) : 1))
         return fail(LB_ESHAPE, fn, "output of 2^31 elements or more");
+    if (M * K >= (int64_t(1) << 32))
+        return fail(LB_ESHAPE, fn, "activation matrix of 4 GiB or more");
     st = check_device(fn);
     if (st != LB_OK)
         return st;

@@ -88,6 +88,13 @@ struct StepRegs {
     uint2 c;
 };
 
+// Global-address-space views: loads take a scalar base and a 32-bit per-lane offset (the ABI keeps the
+// weight tensor and the activation matrix under 4 GiB), so no 64-bit address arithmetic per load.
+typedef __attribute__((address_space(1))) const uint8_t gu8;
+typedef __attribute__((address_space(1))) const v4u gv4u;
+typedef __attribute__((address_space(1))) const uint32_t gu32;
+typedef __attribute__((address_space(1))) const uint16_t gu16;
+
 template <int FMT>
 __device__ __forceinline__ void load_step(StepRegs &r, const uint8_t *__restrict__ W, const uint16_t *__restrict__ wsc,
                                           int N, int K, const int8_t *__restrict__ X, const uint16_t *__restrict__ xsc,
@@ -100,34 +107,34 @@ __device__ __forceinline__ void load_step(StepRegs &r, const uint8_t *__restrict
     // activation tile: 128 rows x kab blocks of 32 bytes; thread -> (row tid / 4, block tid % 4)
     {
         const int m = min(m0 + (tid >> 2), M - 1), ch = min(tid & 3, kab - 1);
-        const v4u *px = reinterpret_cast<const v4u *>(X + (int64_t)m * K + kk + 32 * ch);
-        r.b0 = px[0];
-        r.b1 = px[1];
+        const uint32_t xo = (uint32_t)m * (uint32_t)K + (uint32_t)(kk + 32 * ch);
+        r.b0 = *(gv4u *)((gu8 *)X + xo);
+        r.b1 = *(gv4u *)((gu8 *)X + (xo + 16u));
     }
     if (FMT != LB_TERNARY_PLANAR && tid < TM) { // one activation row's four block scales
         const int mm = min(m0 + (tid & (TM - 1)), M - 1);
-        const uint32_t *pp = reinterpret_cast<const uint32_t *>(xsc + (int64_t)mm * (K / QK8) + kk / QK8);
-        r.c.x = pp[0];                 // blocks 0, 1 (4-byte aligned: K / 32 and kk / 32 are even)
-        r.c.y = pp[kab > 2 ? 1 : 0];   // blocks 2, 3 (unused on a half step)
+        const uint32_t so = ((uint32_t)mm * (uint32_t)(K / QK8) + (uint32_t)(kk / QK8)) * 2u;
+        r.c.x = *(gu32 *)((gu8 *)xsc + so);                            // blocks 0, 1 (4-byte aligned: K / 32
+        r.c.y = *(gu32 *)((gu8 *)xsc + (so + (kab > 2 ? 4u : 0u)));    // and kk / 32 are even); 2, 3
     }
     const int row = min(n0 + (tid >> 3), N - 1), p = tid & 7;
     if (FMT == LB_Q1_0) {
         // one 128-weight record per row and step; thread p takes sign dword p / 2
-        const int64_t idx = (int64_t)row * (K / 128) + kk / 128;
-        r.a.x = *reinterpret_cast<const uint32_t *>(W + idx * 16 + 4 * (p >> 1));
-        r.a.z = wsc[idx];
+        const uint32_t idx = (uint32_t)row * (uint32_t)(K / 128) + (uint32_t)(kk / 128);
+        r.a.x = *(gu32 *)((gu8 *)W + (idx * 16u + 4u * (uint32_t)(p >> 1)));
+        r.a.z = *(gu16 *)((gu8 *)wsc + idx * 2u);
     } else if (FMT == LB_Q2_0_G64) {
         // two 64-weight records per row (one on a half step); thread p takes dword p % 4 of record p / 4
         const int bb = min(p >> 2, kab / 2 - 1), d = p & 3;
-        const int64_t idx = (int64_t)row * (K / 64) + kk / 64 + bb;
-        r.a.x = *reinterpret_cast<const uint32_t *>(W + idx * 16 + 4 * d);
-        r.a.z = wsc[idx];
+        const uint32_t idx = (uint32_t)row * (uint32_t)(K / 64) + (uint32_t)(kk / 64 + bb);
+        r.a.x = *(gu32 *)((gu8 *)W + (idx * 16u + 4u * (uint32_t)d));
+        r.a.z = *(gu16 *)((gu8 *)wsc + idx * 2u);
     } else {
         // two 64-column beats per row; thread p takes the (pos, neg) dword pair (p / 2) % 2 of beat p / 4
         const int bb = min(p >> 2, kab / 2 - 1), hh = (p >> 1) & 1;
-        const int64_t idx = (int64_t)row * (K / 64) + kk / 64 + bb;
-        r.a.x = *reinterpret_cast<const uint32_t *>(W + idx * 16 + 4 * hh);     // pos
-        r.a.y = *reinterpret_cast<const uint32_t *>(W + idx * 16 + 8 + 4 * hh); // neg
+        const uint32_t idx = (uint32_t)row * (uint32_t)(K / 64) + (uint32_t)(kk / 64 + bb);
+        r.a.x = *(gu32 *)((gu8 *)W + (idx * 16u + 4u * (uint32_t)hh));       // pos
+        r.a.y = *(gu32 *)((gu8 *)W + (idx * 16u + 8u + 4u * (uint32_t)hh)); // neg
     }
 }
 
@@ -278,7 +285,8 @@ __global__ __launch_bounds__(GT * KSPLIT, 2 * KSPLIT) void gemm_kernel(const uin
     __shared__ Lds lds[KSPLIT];
 
     constexpr bool PLANAR = FMT == LB_TERNARY_PLANAR;
-    const int half = KSPLIT == 1 ? 0 : (int)threadIdx.x / GT;
+    // (uniform per wave: readfirstlane keeps the step bookkeeping in scalar registers)
+    const int half = KSPLIT == 1 ? 0 : __builtin_amdgcn_readfirstlane((int)threadIdx.x / GT);
     const int tid = (int)threadIdx.x % GT, lane = tid & 63, wave = tid >> 6;
     const int h = lane >> 5, l32 = lane & 31;
     // this wave's 32 x 32 output tile inside the 64 x 128 workgroup tile

@@ -139,6 +139,7 @@ lb_status lowbit_matvec(int fmt, const void *W, int64_t N, int64_t K, float w_te
  * prefill runs compute-bound).
  *   Xq: device int8 [M][K], 16-byte aligned; Xscale: binary16 [M][K/32] (ggml formats) or fp32 [M].
  *   Y:  device fp32 [M][N], 4-byte aligned.
+ * Limits (else LB_ESHAPE): those of lowbit_matvec, M * N < 2^31 outputs, M * K < 2^32 activation bytes.
  */
 lb_status lowbit_gemm(int fmt, const void *W, int64_t N, int64_t K, float w_tensor_scale, int afmt,
                       const int8_t *Xq, const void *Xscale, int64_t M, float *Y, hipStream_t s);
