@@ -413,6 +413,60 @@ def prefill_tops(fmt, N, K, M, reps=100, seed=1004):
     return ms, 2.0 * M * N * K / (ms * 1e-3) / 1e12
 
 
+def single_launch(fmt, shapes, reps=30, seed=1011):
+    """One lowbit_matvec launch per shape (one product, batch 1): the median of `reps` launches timed with
+    HIP events, warm (the same weights launch after launch, resident in the 256 MB last-level cache when
+    they fit) and cold (a 512 MB buffer is rewritten before each launch, evicting every cache level).
+    Returns {shape: {...}}."""
+    import statistics
+
+    import torch
+
+    import bit_quantized_matvec_q1_amd.lowbit as L
+    import synth
+
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    out = {}
+    for i, (N, K) in enumerate(shapes):
+        raw = synth.device_ggml_blocks(fmt, N, K, seed + i)
+        W = torch.empty(L.lowbit_weight_bytes(fmt, N, K), dtype=torch.uint8, device="cuda")
+        L.lowbit_pack_weights(fmt, raw.reshape(-1), N, K, W)
+        del raw
+        g = torch.Generator(device="cuda")
+        g.manual_seed(seed + 100 + i)
+        x = torch.randn(K, generator=g, device="cuda")
+        xq = torch.empty(K, dtype=torch.int8, device="cuda")
+        xs = torch.empty(K // 32, dtype=torch.uint16, device="cuda")
+        L.lowbit_quantize_act(L.ACT_Q8_0, x, 1, K, xq, xs)
+        y = torch.empty(N, dtype=torch.float32, device="cuda")
+
+        def launch():
+            L.lowbit_matvec(fmt, W, N, K, 1.0, L.ACT_Q8_0, xq, xs, y)
+
+        warm_up(launch)
+        times = {}
+        for mode in ("warm", "cold"):
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+            # hold the GPU (a bounded spin) while the host queues every launch, so that warm launches run back
+            # to back instead of each waiting for the host's next call
+            torch.cuda._sleep(20_000_000)
+            for a, b in ev:
+                if mode == "cold":
+                    flush.fill_(1)
+                a.record()
+                launch()
+                b.record()
+            torch.cuda.synchronize()
+            times[mode] = statistics.median(a.elapsed_time(b) for a, b in ev)
+        nbytes = L.lowbit_weight_bytes(fmt, N, K)
+        out[f"{N}x{K}"] = {"weight_bytes": nbytes, "warm_us": round(times["warm"] * 1e3, 2),
+                           "cold_us": round(times["cold"] * 1e3, 2),
+                           "cold_gbs": round(nbytes / (times["cold"] * 1e-3) / 1e9, 1)}
+    del flush
+    torch.cuda.empty_cache()
+    return out
+
+
 def copy_probe_gbs(nbytes=1 << 31, reps=5):
     """Device-to-device copy of a buffer far larger than the 256 MB last-level cache: read+write GB/s."""
     import torch
@@ -440,8 +494,8 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle leg (profiling runs)")
-    ap.add_argument("--secondary", default="layered,q1,planar,b3,q8,prefill",
-                    help="comma list of extra workloads: layered, q1, planar, b3, q8, prefill, none")
+    ap.add_argument("--secondary", default="layered,q1,planar,b3,q8,prefill,single",
+                    help="comma list of extra workloads: layered, q1, planar, b3, q8, prefill, single, none")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU: this library has no multi-GPU path (asked for --gpus {args.gpus}). "
@@ -548,6 +602,14 @@ def main():
             }
             t1.batch.close()
             del t1
+        elif name == "single":
+            # one product per launch (no batching), warm and cold: the 1024x1024 parity case and the four
+            # distinct Qwen3-8B shapes
+            shapes = [(1024, 1024)] + sorted({(N, K) for _, N, K in synth.QWEN3_8B_LAYER})
+            secondary["q2_0_single_launch"] = {
+                "workload": "one Q2_0_g64 product per lowbit_matvec launch, batch 1: median of 30 launches, warm "
+                            "(weights resident in cache when they fit) and cold (every cache evicted first)",
+                **single_launch(synth.Q2_0_G64, shapes)}
         elif name == "planar":
             tp = DecodeToken(synth.TERNARY_PLANAR, synth.BITNET_2B_LAYER, synth.BITNET_2B_LAYERS, seed=1005,
                              head=synth.BITNET_HEAD)
