@@ -61,10 +61,16 @@ __device__ __forceinline__ uint32_t nibbles16(uint32_t x) // low nibbles of 4 by
 // per nibble-word pair (the 8 activation bytes it covers, one 8/16/32-byte load, gathered with byte
 // permutes where they are strided) and one per (slice, q8_0 block) for d_x and -sum(q).  Item loads are
 // issued four at a time.
-template <int FMT>
-__device__ __forceinline__ void stage_activation(const int8_t *__restrict__ xq, const void *__restrict__ xscale, int ns,
-                                                 uint32_t *__restrict__ lds)
+// The source sits in global memory (AS = 1) or, when the launch quantised it, in LDS (AS = 3); an explicit
+// address space gives global or LDS loads instead of flat ones.
+template <int AS, typename T> using src_t = __attribute__((address_space(AS))) const T;
+
+template <int FMT, int AS>
+__device__ __forceinline__ void stage_activation(const int8_t *__restrict__ xq_g, const void *__restrict__ xscale_g,
+                                                 int ns, uint32_t *__restrict__ lds)
 {
+    src_t<AS, int8_t> *xq = (src_t<AS, int8_t> *)xq_g;
+    src_t<AS, uint16_t> *xscale = (src_t<AS, uint16_t> *)xscale_g;
     constexpr int SW = F<FMT>::SW, NAB = F<FMT>::NAB, REC = F<FMT>::REC;
     constexpr int WPS = SW / 8; // nibble-word pairs per slice
     constexpr int UNR = 4;
@@ -76,15 +82,15 @@ __device__ __forceinline__ void stage_activation(const int8_t *__restrict__ xq, 
             const int it = base + q * WG;
             if (it < nw) {
                 const int sl = it / WPS, a = it % WPS;
-                const int8_t *sb = xq + (int64_t)sl * SW;
+                src_t<AS, int8_t> *sb = xq + sl * SW;
                 if (FMT == LB_Q1_0) { // 8 consecutive bytes
-                    const uint2 t = *reinterpret_cast<const uint2 *>(sb + 32 * (a & 3) + 8 * (a >> 2));
+                    const uint2 t = *(src_t<AS, uint2> *)(sb + 32 * (a & 3) + 8 * (a >> 2));
                     v[q][0] = make_uint4(t.x, t.y, 0u, 0u);
                 } else if (FMT == LB_Q2_0_G64) { // every other byte of 16
-                    v[q][0] = *reinterpret_cast<const uint4 *>(sb + 16 * (a >> 1));
+                    v[q][0] = *(src_t<AS, uint4> *)(sb + 16 * (a >> 1));
                 } else { // every fourth byte of 32
-                    v[q][0] = *reinterpret_cast<const uint4 *>(sb + 32 * (a >> 2));
-                    v[q][FMT == LB_TERNARY_PLANAR ? 1 : 0] = *reinterpret_cast<const uint4 *>(sb + 32 * (a >> 2) + 16);
+                    v[q][0] = *(src_t<AS, uint4> *)(sb + 32 * (a >> 2));
+                    v[q][FMT == LB_TERNARY_PLANAR ? 1 : 0] = *(src_t<AS, uint4> *)(sb + 32 * (a >> 2) + 16);
                 }
             }
         }
@@ -118,7 +124,7 @@ __device__ __forceinline__ void stage_activation(const int8_t *__restrict__ xq, 
     if (NAB > 0) {
         for (int it = threadIdx.x; it < ns * NAB; it += WG) {
             const int sl = it / (NAB > 0 ? NAB : 1), j = it % (NAB > 0 ? NAB : 1);
-            const uint4 *src = reinterpret_cast<const uint4 *>(xq + (int64_t)sl * SW + 32 * j);
+            src_t<AS, uint4> *src = (src_t<AS, uint4> *)(xq + sl * SW + 32 * j);
             const uint4 b0 = src[0], b1 = src[1];
             int sq = 0;
             sq = __builtin_amdgcn_sdot4((int)b0.x, 0x01010101, sq, false);
@@ -131,7 +137,7 @@ __device__ __forceinline__ void stage_activation(const int8_t *__restrict__ xq, 
             sq = __builtin_amdgcn_sdot4((int)b1.w, 0x01010101, sq, false);
             // Q1_0 keeps 2 d_x / 2^j (exact): its block sums are 2 S - sum(q), S = the sum of q where the
             // bit is 1, and its products deliver 2^j S (the nibble value of mask position j)
-            const float dx = half_bits_to_float(reinterpret_cast<const uint16_t *>(xscale)[it]);
+            const float dx = half_bits_to_float(xscale[it]);
             const float q1f = j == 0 ? 2.0f : j == 1 ? 1.0f : j == 2 ? 0.5f : 0.25f;
             uint32_t *rec = lds + sl * REC;
             rec[SW / 4 + j] = __float_as_uint(FMT == LB_Q1_0 ? q1f * dx : dx);
@@ -396,7 +402,7 @@ __device__ __forceinline__ void matvec_tile(const uint8_t *__restrict__ W, int N
 #pragma unroll
             for (int u = 0; u < QU; u++) {
                 const int c = c0 + u * WG;
-                v[u] = c < nc ? reinterpret_cast<const float4 *>(x)[c] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+                v[u] = c < nc ? (float4)((src_t<1, float4> *)x)[c] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
             }
 #pragma unroll
             for (int u = 0; u < QU; u++) {
@@ -410,9 +416,9 @@ __device__ __forceinline__ void matvec_tile(const uint8_t *__restrict__ W, int N
             }
         }
         __syncthreads();
-        stage_activation<FMT>(qb, qs, ns, lds);
+        stage_activation<FMT, 3>(qb, qs, ns, lds);
     } else {
-        stage_activation<FMT>(xq, xscale, ns, lds);
+        stage_activation<FMT, 1>(xq, xscale, ns, lds);
     }
     __syncthreads();
 
