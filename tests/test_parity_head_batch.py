@@ -137,7 +137,8 @@ def test_batched_fp32_activations_quantised_in_launch(fmt):
     """LB_ACT_F32_Q8_0: each product quantises its fp32 input inside its own launch.  Outputs are
     bit-identical to quantising first (lowbit_quantize_act) and running the same batch, and within the
     tolerance of the oracle on the oracle's q8_0 of the same x; two products share one x, as q/k/v do."""
-    shapes = [(300, 1024), (1024, 4096), (129, 12288), (1, 128), (517, 2560), (64, 4096)]
+    # the largest K stages 74 KiB of LDS per workgroup (the staged records plus the quantised row)
+    shapes = [(300, 1024), (1024, 4096), (129, 12288), (1, 128), (517, 2560), (5, 32768), (64, 4096)]
     say(f"case batched fp32 activations fmt={fmt} shapes={shapes}")
     fused, quantised, keep = [], [], []
     x_shared = None
