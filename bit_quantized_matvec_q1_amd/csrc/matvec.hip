@@ -64,6 +64,19 @@ __device__ __forceinline__ uint32_t nibbles16(uint32_t x) // low nibbles of 4 by
 // The source sits in global memory (AS = 1) or, when the launch quantised it, in LDS (AS = 3); an explicit
 // address space gives global or LDS loads instead of flat ones.
 template <int AS, typename T> using src_t = __attribute__((address_space(AS))) const T;
+typedef unsigned sv2u __attribute__((ext_vector_type(2))); // native vectors: loadable from any address space
+typedef unsigned sv4u __attribute__((ext_vector_type(4)));
+typedef float sv4f __attribute__((ext_vector_type(4)));
+template <int AS> __device__ __forceinline__ uint2 ld2(src_t<AS, int8_t> *p)
+{
+    const sv2u t = *(src_t<AS, sv2u> *)p;
+    return make_uint2(t.x, t.y);
+}
+template <int AS> __device__ __forceinline__ uint4 ld4(src_t<AS, int8_t> *p)
+{
+    const sv4u t = *(src_t<AS, sv4u> *)p;
+    return make_uint4(t.x, t.y, t.z, t.w);
+}
 
 template <int FMT, int AS>
 __device__ __forceinline__ void stage_activation(const int8_t *__restrict__ xq_g, const void *__restrict__ xscale_g,
@@ -84,13 +97,13 @@ __device__ __forceinline__ void stage_activation(const int8_t *__restrict__ xq_g
                 const int sl = it / WPS, a = it % WPS;
                 src_t<AS, int8_t> *sb = xq + sl * SW;
                 if (FMT == LB_Q1_0) { // 8 consecutive bytes
-                    const uint2 t = *(src_t<AS, uint2> *)(sb + 32 * (a & 3) + 8 * (a >> 2));
+                    const uint2 t = ld2<AS>(sb + 32 * (a & 3) + 8 * (a >> 2));
                     v[q][0] = make_uint4(t.x, t.y, 0u, 0u);
                 } else if (FMT == LB_Q2_0_G64) { // every other byte of 16
-                    v[q][0] = *(src_t<AS, uint4> *)(sb + 16 * (a >> 1));
+                    v[q][0] = ld4<AS>(sb + 16 * (a >> 1));
                 } else { // every fourth byte of 32
-                    v[q][0] = *(src_t<AS, uint4> *)(sb + 32 * (a >> 2));
-                    v[q][FMT == LB_TERNARY_PLANAR ? 1 : 0] = *(src_t<AS, uint4> *)(sb + 32 * (a >> 2) + 16);
+                    v[q][0] = ld4<AS>(sb + 32 * (a >> 2));
+                    v[q][FMT == LB_TERNARY_PLANAR ? 1 : 0] = ld4<AS>(sb + 32 * (a >> 2) + 16);
                 }
             }
         }
@@ -124,8 +137,7 @@ __device__ __forceinline__ void stage_activation(const int8_t *__restrict__ xq_g
     if (NAB > 0) {
         for (int it = threadIdx.x; it < ns * NAB; it += WG) {
             const int sl = it / (NAB > 0 ? NAB : 1), j = it % (NAB > 0 ? NAB : 1);
-            src_t<AS, uint4> *src = (src_t<AS, uint4> *)(xq + sl * SW + 32 * j);
-            const uint4 b0 = src[0], b1 = src[1];
+            const uint4 b0 = ld4<AS>(xq + sl * SW + 32 * j), b1 = ld4<AS>(xq + sl * SW + 32 * j + 16);
             int sq = 0;
             sq = __builtin_amdgcn_sdot4((int)b0.x, 0x01010101, sq, false);
             sq = __builtin_amdgcn_sdot4((int)b0.y, 0x01010101, sq, false);
@@ -402,7 +414,8 @@ __device__ __forceinline__ void matvec_tile(const uint8_t *__restrict__ W, int N
 #pragma unroll
             for (int u = 0; u < QU; u++) {
                 const int c = c0 + u * WG;
-                v[u] = c < nc ? (float4)((src_t<1, float4> *)x)[c] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+                const sv4f t = c < nc ? ((src_t<1, sv4f> *)x)[c] : sv4f{0.0f, 0.0f, 0.0f, 0.0f};
+                v[u] = make_float4(t.x, t.y, t.z, t.w);
             }
 #pragma unroll
             for (int u = 0; u < QU; u++) {
