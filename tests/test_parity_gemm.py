@@ -76,6 +76,14 @@ def test_gemm_odd_block_tail(fmt):
     check(fmt, 65, 129, 448, seed=6100)
 
 
+@pytest.mark.parametrize("fmt", [synth.Q2_0_G64, synth.TERNARY_PLANAR], ids=NAMES.get)
+@pytest.mark.parametrize("M,N,K", [(3, 70, 64), (130, 65, 192)])
+def test_gemm_single_and_three_half_steps(fmt, M, N, K):
+    # K = 64: one half step, so the second half of a split-K workgroup has no step at all; K = 192: one full
+    # step and one half step, split one per half
+    check(fmt, M, N, K, seed=6150 + K)
+
+
 def test_gemm_code3_and_minus_128():
     say("case gemm code3/-128")
     fmt, M, N, K = synth.Q2_0_G64, 64, 128, 512
