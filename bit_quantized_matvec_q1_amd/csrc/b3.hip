@@ -8,13 +8,17 @@
 //
 // Decode on CDNA4.  The device layout (lowbit_pack_weights) keeps the beat stream but stores each base-3
 // byte v as the 8-bit fraction b = ceil(256 v / 243): then the leading m base-3 digits of v are
-// F_m = floor(3^m b / 256), digit 5 - m is F_m - 3 F_(m-1), and for the five columns j0 .. j0 + 4 of a byte
-//     sum_t c_t q_(j0+t) = sum_(m=1..5) F_m * Q_m,   Q_m = q_(j0+5-m) - 3 q_(j0+4-m) (m <= 4),   Q_5 = q_j0,
-// so the activation (not the weights) carries the base-3 structure, rearranged once per workgroup.  Per
-// pair of bytes held in the 16-bit halves of a register (one byte permute per pair), each m costs one
-// multiply by 3, one byte permute (the two fields' high bytes are the floors) and one v_dot2_i32_i16
-// against a staged pair of Q_m: 15 operations per 10 weights, against 4 for the 2-bit planar beat.
-//
+// F_m = floor(3^m b / 256) (F_5 = v) and digit 5 - m is F_m - 3 F_(m-1).  For the five columns j0 .. j0 + 4
+// of a byte,
+//     sum_t c_t q_(j0+t) = sum_(m=1..4) F_m q_(j0+5-m) + d_0 q_j0 - 3 sum_(m=1..3) F_m q_(j0+4-m),
+// with d_0 = F_5 - 3 F_4 (the F_5 term and the m = 4 term of the second sum cancel down to d_0).  A
+// record dword's four bytes are split into the 16-bit halves of two registers (two byte permutes); per
+// m both are multiplied by 3 (products below 2^16, so the halves never carry into each other) and one
+// byte permute gathers the four floors F_m (< 81 for m <= 4) into one dword of int8, multiplied into two
+// int32 accumulators with v_dot4_i32_i8 against the activations, which the workgroup stages once,
+// transposed: per record dword five dwords P_o, byte k of P_o = q of column 5 k + o.  27 operations per
+// 20 weights, against 4 per 16 for the 2-bit planar beat.
+
 // Work split as in the other decode kernels: a row over L lanes, S beats per lane (strided by L so a
 // wave-wide 16-byte load is contiguous), the staged activation pairs held in registers for every row a
 // lane streams, the next row's loads in flight, a DPP tree per row; rows never split across workgroups.
@@ -26,10 +30,9 @@ namespace {
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(1))) const v4u gv4u;
 typedef __attribute__((address_space(1))) const uint8_t gu8;
-typedef short v2s __attribute__((ext_vector_type(2)));
 
 constexpr int BCOLS = 80; // columns per beat
-constexpr int REC = 40;   // staged dwords per beat: 4 dwords x {even, odd bytes} x 5 values of m
+constexpr int REC = 20;   // staged dwords per beat: 4 record dwords x 5 column offsets
 
 #define LB_B3_CFGS(X) X(0, 16, 1) X(1, 16, 2) X(2, 32, 1) X(3, 32, 2) X(4, 32, 3) X(5, 64, 1) X(6, 64, 2)
 
@@ -41,49 +44,49 @@ constexpr CfgLS kB3Cfgs[] = {LB_B3_CFGS(LB_B3_ENTRY)};
 #undef LB_B3_ENTRY
 constexpr int kB3NumCfgs = sizeof(kB3Cfgs) / sizeof(kB3Cfgs[0]);
 
-__device__ __forceinline__ int dot2(uint32_t a, uint32_t b, int c)
+__device__ __forceinline__ int dot4(uint32_t a, uint32_t b, int c)
 {
-    return __builtin_amdgcn_sdot2(__builtin_bit_cast(v2s, a), __builtin_bit_cast(v2s, b), c, false);
+    return __builtin_amdgcn_sdot4((int)a, (int)b, c, false);
 }
 
-// sum over the 4 bytes of one record dword: pairs (bytes 0, 2) and (bytes 1, 3), m = 1..5
-__device__ __forceinline__ int b3_dword(uint32_t d, const uint32_t *A, int acc)
+// The four bytes of one record dword: F_m of all four in one dword per m, int8 dot products against the
+// staged activation columns P[o] (byte k of P[o]: the activation of column 5 k + o of the dword's 20).
+__device__ __forceinline__ void b3_dword(uint32_t d, const uint32_t *P, int &acc_a, int &acc_b)
 {
+    uint32_t ye = __builtin_amdgcn_perm(0u, d, 0x0C020C00u); // bytes 0 and 2 in the low bytes of the halves
+    uint32_t yo = __builtin_amdgcn_perm(0u, d, 0x0C030C01u); // bytes 1 and 3
+    uint32_t f4 = 0;
 #pragma unroll
-    for (int h = 0; h < 2; h++) {
-        // bytes h and h + 2 of d into the low bytes of the two 16-bit halves
-        uint32_t y = __builtin_amdgcn_perm(0u, d, h ? 0x0C030C01u : 0x0C020C00u);
-#pragma unroll
-        for (int m = 0; m < 5; m++) {
-            y = y * 3u; // 3^(m+1) b per half: below 2^16, so the halves never carry into each other
-            const uint32_t f = __builtin_amdgcn_perm(0u, y, 0x0C030C01u); // floor(3^(m+1) b / 256) per half
-            acc = dot2(f, A[h * 5 + m], acc);
-        }
+    for (int m = 1; m <= 5; m++) {
+        ye *= 3u; // 3^m b per half: below 2^16, so the halves never carry into each other
+        yo *= 3u;
+        const uint32_t f = __builtin_amdgcn_perm(yo, ye, 0x07030501u); // the high bytes: F_m of bytes 0..3
+        if (m <= 4)
+            acc_a = dot4(f, P[5 - m], acc_a);
+        if (m <= 3)
+            acc_b = dot4(f, P[4 - m], acc_b);
+        if (m == 4)
+            f4 = f;
+        if (m == 5) // digit 0 of each byte, F_5 - 3 F_4 in 0..2: no byte borrows or carries
+            acc_a = dot4(f - 3u * f4, P[0], acc_a);
     }
-    return acc;
 }
 
-// Stage the activation once per workgroup: per beat, per record dword, per byte pair, the five Q_m pairs
+// Stage the activation once per workgroup: per beat and record dword, the five transposed column dwords
 // (columns past K read q = 0), and the row's sum of q.
 __device__ __forceinline__ void b3_stage(const int8_t *__restrict__ xq, int K, int nbt, uint32_t *__restrict__ lds,
                                          int *__restrict__ sumq)
 {
-    for (int it = threadIdx.x; it < nbt * 8; it += WG) {
-        const int bt = it >> 3, d = (it >> 1) & 3, h = it & 1;
-        uint32_t *rec = lds + bt * REC + d * 10 + h * 5;
+    for (int it = threadIdx.x; it < nbt * REC; it += WG) {
+        const int bt = it / REC, r = it % REC, dd = r / 5, o = r % 5;
+        const int c0 = bt * BCOLS + 20 * dd + o; // column of byte 0
+        uint32_t v = 0;
 #pragma unroll
-        for (int m = 1; m <= 5; m++) {
-            uint32_t pair = 0;
-#pragma unroll
-            for (int f = 0; f < 2; f++) {
-                const int byte = bt * 16 + 4 * d + h + 2 * f; // byte index within the row
-                const int j0 = 5 * byte;
-                auto qa = [&](int c) { return c < K ? (int)xq[c] : 0; };
-                const int Q = m == 5 ? qa(j0) : qa(j0 + 5 - m) - 3 * qa(j0 + 4 - m);
-                pair |= ((uint32_t)Q & 0xffffu) << (16 * f);
-            }
-            rec[m - 1] = pair;
+        for (int k = 0; k < 4; k++) {
+            const int c = c0 + 5 * k;
+            v |= (uint32_t)(uint8_t)(c < K ? xq[c] : (int8_t)0) << (8 * k);
         }
+        lds[it] = v;
     }
     // sum of q over the row (one wave)
     if (threadIdx.x < 64) {
@@ -161,15 +164,15 @@ __device__ __forceinline__ void b3_tile(const uint8_t *__restrict__ W, int K, fl
             if (cur + STEP < nrows) // uniform
                 issue(buf[p ^ 1], min(onext, last));
             onext += stepb;
-            int acc = 0;
+            int acc_a = 0, acc_b = 0;
 #pragma unroll
             for (int i = 0; i < S; i++) {
-                acc = b3_dword(buf[p].code[i].x, act[i] + 0, acc);
-                acc = b3_dword(buf[p].code[i].y, act[i] + 10, acc);
-                acc = b3_dword(buf[p].code[i].z, act[i] + 20, acc);
-                acc = b3_dword(buf[p].code[i].w, act[i] + 30, acc);
+                b3_dword(buf[p].code[i].x, act[i] + 0, acc_a, acc_b);
+                b3_dword(buf[p].code[i].y, act[i] + 5, acc_a, acc_b);
+                b3_dword(buf[p].code[i].z, act[i] + 10, acc_a, acc_b);
+                b3_dword(buf[p].code[i].w, act[i] + 15, acc_a, acc_b);
             }
-            acc = group_sum_i<L>(acc);
+            int acc = group_sum_i<L>(acc_a - 3 * acc_b);
             const int rl = cur + rbase;
             if (rl < nrows && li == L - 1) {
                 const int a = acc - sq; // sum (w + 1) q - sum q
