@@ -637,6 +637,23 @@ def main():
                 "ms": round(pms, 4), "gbs": round(pg, 1)}
             tp.batch.close()
             del tp
+            torch.cuda.empty_cache()
+            # the same model with grouped-query attention (k/v 640 x 2560): the body behind the pages' 2.5:1
+            tg = DecodeToken(synth.TERNARY_PLANAR, synth.BITNET_2B_GQA_LAYER, synth.BITNET_2B_LAYERS, seed=1012,
+                             head=synth.BITNET_HEAD)
+            msg, mlg = time_token(tg, max(50, args.steps // 2), warm_steps(tg))
+            secondary["planar_2b_gqa_token"] = {
+                "workload": "BitNet-b1.58-2B with grouped-query attention (k/v 640x2560), 30 layers x 7 planar "
+                            "products + the dense bf16 head 128256x2560; per-token int8 activations",
+                "weight_bytes": tg.weight_bytes, "ms_per_step": round(msg, 5),
+                "gbs": round(tg.weight_bytes / (msg * 1e-3) / 1e9, 1),
+                "pct_hbm_peak": round(100 * tg.weight_bytes / (msg * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+                "tokens_per_s_equiv": round(1e3 / msg, 1),
+                "products_launch_ms": round(mlg, 5),
+                "products_launch_gbs": round(tg.algorithmic_bytes / (mlg * 1e-3) / 1e9, 1),
+            }
+            tg.batch.close()
+            del tg
         elif name == "b3":
             tb = DecodeToken(synth.TERNARY_B3, synth.BITNET_2B_LAYER, synth.BITNET_2B_LAYERS, seed=1009,
                              head=synth.BITNET_HEAD)

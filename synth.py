@@ -244,6 +244,9 @@ BITNET_2B_LAYER = (
     ("ffn_down", 2560, 6912),
 )
 BITNET_2B_LAYERS = 30
+# The same block with grouped-query attention (k/v at 640 rows): the body the pages' 2.5:1 head-to-body
+# ratio implies.
+BITNET_2B_GQA_LAYER = tuple((n, 640 if n in ("attn_k", "attn_v") else N, K) for n, N, K in BITNET_2B_LAYER)
 BITNET_HEAD = (128256, 2560)
 
 PREFILL_M = 512

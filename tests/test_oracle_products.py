@@ -257,6 +257,8 @@ def test_int8_head_speedup_the_pages_quote():
     gqa = sum(oracle.weight_bytes(oracle.TERNARY_PLANAR, n, k) for n, k in
               ((2560, 2560), (640, 2560), (640, 2560), (2560, 2560), (6912, 2560), (6912, 2560), (2560, 6912))) * 30
     assert gqa == body and round(p["head_f32_bytes"] / body, 1) == 2.5
+    # the generator's GQA block (used by the benchmark) is that body
+    assert sum(oracle.weight_bytes(oracle.TERNARY_PLANAR, n, k) for _, n, k in synth.BITNET_2B_GQA_LAYER) * 30 == body
     int8_head = N * K + 4 * N
     assert round((p["head_f32_bytes"] + body) / (int8_head + body), 1) == p["head_int8_token_speedup"]
 
