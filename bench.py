@@ -684,7 +684,7 @@ def main():
             del t8
         elif name == "prefill":
             pre = {}
-            for fmt, fname in ((synth.Q2_0_G64, "q2_0_g64"), (synth.Q1_0, "q1_0")):
+            for fmt, fname in ((synth.Q2_0_G64, "q2_0_g64"), (synth.Q1_0, "q1_0"), (synth.Q8_0, "q8_0")):
                 for N, K in synth.PREFILL_SHAPES:
                     ms, tops = prefill_tops(fmt, N, K, synth.PREFILL_M)
                     pre[f"{fname}_{synth.PREFILL_M}x{N}x{K}"] = {

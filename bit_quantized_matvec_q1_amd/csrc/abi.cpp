@@ -238,6 +238,8 @@ static lb_status gemm_common(const char *fn, int fmt, const void *W, int64_t N, 
         return fail(LB_ESHAPE, fn, "output of 2^31 elements or more");
     if (M * K >= (int64_t(1) << 32))
         return fail(LB_ESHAPE, fn, "activation matrix of 4 GiB or more");
+    if (fmt == LB_Q8_0 && K % 128)
+        return fail(LB_ESHAPE, fn, "Q8_0 prefill needs K to be a multiple of 128");
     st = check_device(fn);
     if (st != LB_OK)
         return st;

@@ -11,7 +11,8 @@
 //    computes; at the top of a step they are written to double-buffered LDS -- the weights unpacked to
 //    int8 in natural column order (shift and mask, a 4x4 byte transpose with v_perm_b32, and a
 //    v_perm_b32 lookup from code to weight byte: Q2_0 c -> c - 1, Q1_0 bit -> +/-1, planar (pos, neg) ->
-//    pos - neg) -- and one barrier per step separates the writes from the reads.  Every thread loads and
+//    pos - neg; Q8_0 weights are int8 already and copied as they are) -- and one barrier per step
+//    separates the writes from the reads.  Every thread loads and
 //    unpacks an equal share of the weight tile and copies an equal share of the activation tile.
 //  * A workgroup is 8 waves (512 threads), two per SIMD, and two workgroups fit a CU.  Wave w computes
 //    the 32 x 32 output tile (weight rows 32 (w mod 2), activation rows 32 (w / 2)) over every step's
@@ -19,8 +20,8 @@
 //    operand (activations) from LDS, one MFMA, one exact int32 sum per (weight row, activation row,
 //    block).  The weight unpack is shared by the 128 activation rows of the tile and the activation copy
 //    by its 64 weight rows, so per MFMA the per-step work stays small next to the rescale below.
-//  * Q2_0: the accumulator input of every MFMA is a constant register tile holding 0x4B400000 (1.5 * 2^23),
-//    so each result, read as fp32, is 1.5 * 2^23 + isum exactly; one FMA with the block's activation
+//  * Q2_0 and Q8_0: the accumulator input of every MFMA is a constant register tile holding 0x4B400000
+//    (1.5 * 2^23), so each result, read as fp32, is 1.5 * 2^23 + isum exactly; one FMA with the block's activation
 //    scale and -d_x * 1.5 * 2^23 gives round(d_x * isum) without a conversion.  Q1_0: a zero accumulator,
 //    each exact int32 result converted and multiply-added into the weight block's sum (fewer registers,
 //    which keeps two workgroups per CU).  The weight block scale is then applied with one more FMA (bankml
@@ -86,6 +87,7 @@ struct StepRegs {
     uint4 a;
     v4u b0, b1; // native vectors: copied as registers, never through memory
     uint2 c;
+    uint32_t ws; // Q8_0: the binary16 scale of the thread's weight block
 };
 
 // Global-address-space views: loads take a scalar base and a 32-bit per-lane offset (the ABI keeps the
@@ -123,6 +125,13 @@ __device__ __forceinline__ void load_step(StepRegs &r, const uint8_t *__restrict
         const uint32_t idx = (uint32_t)row * (uint32_t)(K / 128) + (uint32_t)(kk / 128);
         r.a.x = *(gu32 *)((gu8 *)W + (idx * 16u + 4u * (uint32_t)(p >> 1)));
         r.a.z = *(gu16 *)((gu8 *)wsc + idx * 2u);
+    } else if (FMT == LB_Q8_0) {
+        // four 32-byte records per row (K is a whole number of steps); thread p takes half p % 2 of
+        // record p / 2, and its scale
+        const uint32_t idx = (uint32_t)row * (uint32_t)(K / 32) + (uint32_t)(kk / 32 + (p >> 1));
+        const v4u t = *(gv4u *)((gu8 *)W + (idx * 32u + 16u * (uint32_t)(p & 1)));
+        r.a = make_uint4(t.x, t.y, t.z, t.w);
+        r.ws = *(gu16 *)((gu8 *)wsc + idx * 2u);
     } else if (FMT == LB_Q2_0_G64) {
         // two 64-weight records per row (one on a half step); thread p takes dword p % 4 of record p / 4
         const int bb = min(p >> 2, kab / 2 - 1), d = p & 3;
@@ -141,7 +150,7 @@ __device__ __forceinline__ void load_step(StepRegs &r, const uint8_t *__restrict
 struct __attribute__((aligned(16))) Lds {
     uint32_t w[2][TN * WROW];
     uint32_t x[2][TM * XROW];
-    float dw[2][2 * TN]; // weight block scales: [block within step][row]
+    float dw[2][4 * TN]; // weight block scales: [block within step][row]
     float dx[2][4 * TM]; // activation scales: [block within step][row]
 };
 
@@ -180,6 +189,12 @@ __device__ __forceinline__ void store_step(Lds &lds, int buf, const StepRegs &r,
         }
         if (p == 0)
             lds.dw[buf][rr] = half_bits_to_float((uint16_t)r.a.z);
+    } else if (FMT == LB_Q8_0) {
+        // the weights are int8 already: copied as they are
+        const int j = p >> 1;
+        *reinterpret_cast<uint4 *>(wrow + 8 * j + 4 * (p & 1)) = r.a;
+        if ((p & 1) == 0)
+            lds.dw[buf][j * TN + rr] = half_bits_to_float((uint16_t)r.ws);
     } else if (FMT == LB_Q2_0_G64) {
         const int bb = p >> 2, d = p & 3;
         if (2 * bb < kab) {
@@ -218,8 +233,9 @@ __device__ __forceinline__ void step_compute(const Lds &lds, int buf, int kab, i
                                              const v16i &cbias, int32_t *__restrict__ sums)
 {
     constexpr bool PLANAR = FMT == LB_TERNARY_PLANAR;
-    constexpr bool BIASED = FMT == LB_Q2_0_G64; // accumulator preset to the bias (else zero)
-    constexpr int JW = FMT == LB_Q1_0 ? 4 : 2;  // activation blocks per weight block
+    // accumulator preset to the bias (else zero); exact while |isum| < 2^22 (Q8_0: at most 2^19)
+    constexpr bool BIASED = FMT == LB_Q2_0_G64 || FMT == LB_Q8_0;
+    constexpr int JW = FMT == LB_Q1_0 ? 4 : FMT == LB_Q8_0 ? 1 : 2; // activation blocks per weight block
     const uint32_t *wl = lds.w[buf] + (32 * wn + l32) * WROW + 4 * h;
     const uint32_t *xl = lds.x[buf] + (32 * wm + l32) * XROW + 4 * h;
     float t[16];
@@ -293,9 +309,9 @@ __global__ __launch_bounds__(GT * KSPLIT, 2 * KSPLIT) void gemm_kernel(const uin
     const int wn = wave & 1, wm = wave >> 1;
     const int bn = blockIdx.x % ntn, bm = blockIdx.x / ntn; // weight tiles vary fastest
     const int n0 = bn * TN, m0 = bm * TM;
-    const int nrec = FMT == LB_Q1_0 ? K / 128 : K / 64; // 16-byte records per weight row
-    const int nab = K / QK8;                             // activation blocks per row
-    const uint16_t *wsc = reinterpret_cast<const uint16_t *>(W + (int64_t)N * nrec * 16);
+    const int64_t rowcode = FMT == LB_Q1_0 ? K / 8 : FMT == LB_Q8_0 ? K : K / 4; // code bytes per weight row
+    const int nab = K / QK8;                                                  // activation blocks per row
+    const uint16_t *wsc = reinterpret_cast<const uint16_t *>(W + (int64_t)N * rowcode);
     const uint16_t *xsc = reinterpret_cast<const uint16_t *>(Xscale);
 
     // Q2_0: 16 registers of the bias, each made opaque to the compiler: a tile it knows to be uniform it
@@ -306,7 +322,7 @@ __global__ __launch_bounds__(GT * KSPLIT, 2 * KSPLIT) void gemm_kernel(const uin
 #pragma unroll
     for (int i = 0; i < 16; i++) {
         int b = (int)BIAS;
-        if (FMT == LB_Q2_0_G64)
+        if (FMT == LB_Q2_0_G64 || FMT == LB_Q8_0)
             asm volatile("; opaque bias %0" : "+v"(b));
         else
             b = 0;
@@ -464,6 +480,8 @@ hipError_t launch_gemm(int fmt, const uint8_t *W, int64_t N, int64_t K, float w_
         return emit ? launch_fmt<LB_TERNARY_PLANAR, true>(W, N, K, w_scale, Xq, Xscale, M, Y, sums, s)
                     : launch_fmt<LB_TERNARY_PLANAR, false>(W, N, K, w_scale, Xq, Xscale, M, Y, sums, s);
     case LB_Q8_0:
+        return emit ? launch_fmt<LB_Q8_0, true>(W, N, K, w_scale, Xq, Xscale, M, Y, sums, s)
+                    : launch_fmt<LB_Q8_0, false>(W, N, K, w_scale, Xq, Xscale, M, Y, sums, s);
     case LB_TERNARY_B3:
         return hipErrorNotSupported; // decode only
     }

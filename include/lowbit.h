@@ -15,8 +15,8 @@
  *   LB_Q8_0           ggml Q8_0 weights: 34-byte blocks of 32 weights, binary16 scale d then 32 signed
  *                     bytes; weight = d * byte.  The q8_0 block of the bankml technical report, section
  *                     III.2, used for weights ("Q8_0 weights" and vec_dot_q8_0_q8_0 for the KV cache in
- *                     the bankml build history's 0.3.9 entry).  Decode (lowbit_matvec, the batch and
- *                     lowbit_block_sums with M = 1) only; lowbit_gemm returns LB_EUNSUPPORTED.
+ *                     the bankml build history's 0.3.9 entry).  Decode takes K up to 16384; prefill
+ *                     (lowbit_gemm, lowbit_block_sums with M > 1) also needs K % 128 == 0 (LB_ESHAPE).
  *   LB_TERNARY_B3     base-3 ternary beats: 16 bytes per 80 consecutive columns of one row, byte j holding
  *                     columns 5j..5j+4 as the integer sum_t (w + 1) * 3^t, lowest digit first (0..242);
  *                     a row of K columns (K % 64 == 0) takes ceil(K/80) beats, the columns past K coded 0.
@@ -139,7 +139,8 @@ lb_status lowbit_matvec(int fmt, const void *W, int64_t N, int64_t K, float w_te
  * prefill runs compute-bound).
  *   Xq: device int8 [M][K], 16-byte aligned; Xscale: binary16 [M][K/32] (ggml formats) or fp32 [M].
  *   Y:  device fp32 [M][N], 4-byte aligned.
- * Limits (else LB_ESHAPE): those of lowbit_matvec, M * N < 2^31 outputs, M * K < 2^32 activation bytes.
+ * Limits (else LB_ESHAPE): those of lowbit_matvec, M * N < 2^31 outputs, M * K < 2^32 activation bytes,
+ * and K % 128 == 0 for LB_Q8_0.  LB_TERNARY_B3 has no prefill kernel (LB_EUNSUPPORTED).
  */
 lb_status lowbit_gemm(int fmt, const void *W, int64_t N, int64_t K, float w_tensor_scale, int afmt,
                       const int8_t *Xq, const void *Xscale, int64_t M, float *Y, hipStream_t s);

@@ -85,6 +85,9 @@ def test_other_entry_points_validate():
     assert lib.lowbit_gemm(L.Q2_0_G64, A16, 8, 64, 1.0, L.ACT_Q8_0, A16, A16, -1, A16, None) == L.LB_ESHAPE
     assert lib.lowbit_gemm(L.Q2_0_G64, A16, 8, 64, 1.0, L.ACT_I8_ROW, A16, A16, 4, A16, None) == L.LB_EINVAL
     assert lib.lowbit_gemm(L.Q2_0_G64, A16, 1, 4096, 1.0, L.ACT_Q8_0, A16, A16, 1 << 20, A16, None) == L.LB_ESHAPE
+    # Q8_0 prefill walks whole 128-column steps; decode of the same K is allowed (M = 1 goes to decode)
+    assert lib.lowbit_gemm(L.Q8_0, A16, 8, 96, 1.0, L.ACT_Q8_0, A16, A16, 4, A16, None) == L.LB_ESHAPE
+    assert lib.lowbit_block_sums(L.Q8_0, A16, 8, 160, L.ACT_Q8_0, A16, A16, 2, A16, None) == L.LB_ESHAPE
     assert lib.lowbit_block_sums(L.Q2_0_G64, A16, 8, 64, L.ACT_Q8_0, A16, A16, 1, None, None) == L.LB_EINVAL
     assert lib.dense_head_matvec(A16, 8, 12, A16, A16, None) == L.LB_ESHAPE
     assert lib.dense_head_matvec(A16, 8, 8192, A16, A16, None) == L.LB_ESHAPE

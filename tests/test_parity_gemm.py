@@ -11,7 +11,8 @@ from gpu_util import assert_close, dev, host, packed_weights, say
 
 pytestmark = pytest.mark.gpu
 
-NAMES = {synth.Q1_0: "Q1_0", synth.Q2_0_G64: "Q2_0_g64", synth.TERNARY_PLANAR: "planar"}
+NAMES = {synth.Q1_0: "Q1_0", synth.Q2_0_G64: "Q2_0_g64", synth.TERNARY_PLANAR: "planar", synth.Q8_0: "Q8_0"}
+QK = {synth.Q1_0: 128, synth.Q2_0_G64: 64, synth.Q8_0: 32}
 
 
 def acts(fmt, M, K, seed):
@@ -64,7 +65,7 @@ def check(fmt, M, N, K, seed, p=synth.TERNARY_P, sums=True, m_rows=None, n_rows=
             assert np.array_equal(S[m, ns], ref), f"block sums of activation row {m} differ"
 
 
-@pytest.mark.parametrize("fmt", [synth.Q1_0, synth.Q2_0_G64, synth.TERNARY_PLANAR], ids=NAMES.get)
+@pytest.mark.parametrize("fmt", [synth.Q1_0, synth.Q2_0_G64, synth.TERNARY_PLANAR, synth.Q8_0], ids=NAMES.get)
 @pytest.mark.parametrize("M,N,K", [(2, 1, 128), (64, 128, 128), (70, 130, 384), (33, 300, 640), (128, 256, 4096)])
 def test_gemm_shapes(fmt, M, N, K):
     check(fmt, M, N, K, seed=6000 + M + N + K)
@@ -99,14 +100,39 @@ def test_gemm_code3_and_minus_128():
         assert np.array_equal(S[m], oracle.block_sums(fmt, Wt.raw, N, K, Q[m]))
 
 
-@pytest.mark.parametrize("fmt", [synth.Q1_0, synth.Q2_0_G64], ids=NAMES.get)
+def test_gemm_q8_0_extreme_bytes():
+    """Q8_0 bytes -128 and +127 against activations -128 with unit scales: block sums of +2^19 and
+    -32 * 16256, the largest the format allows, still exact through the biased accumulator."""
+    say("case gemm Q8_0 extreme bytes")
+    M, N, K = 70, 130, 512
+    w = np.broadcast_to(np.where(np.arange(N)[:, None] % 2 == 0, -128, 127), (N, K)).astype(np.int8)
+    ones = np.full((N, K // 32), 1.0, np.float16)
+    Wt = synth.Weights(synth.Q8_0, N, K, synth.lay_out_q8_0(w, ones), w)
+    Q = np.full((M, K), -128, np.int8)
+    Q[1::2, ::7] = 127
+    XS = np.full((M, K // 32), 0x3C00, np.uint16)
+    packed = packed_weights(Wt)
+    S = gpu_gemm_sums(synth.Q8_0, packed, N, K, Q, XS, M)
+    for m in (0, 1, M - 1):
+        assert np.array_equal(S[m], oracle.block_sums(synth.Q8_0, Wt.raw, N, K, Q[m]))
+    assert S.max() == 32 * 16384 and S.min() == -32 * 16256
+    Y = gpu_gemm(synth.Q8_0, packed, N, K, Q, XS, M)
+    Yr, _ = oracle.gemm_q(synth.Q8_0, Wt.raw, N, K, Q, XS)
+    assert np.array_equal(Y.astype(np.float64), Yr)
+
+
+@pytest.mark.parametrize("fmt", [synth.Q1_0, synth.Q2_0_G64, synth.Q8_0], ids=NAMES.get)
 def test_gemm_unit_scales_bit_exact(fmt):
     say(f"case gemm unit scales {NAMES[fmt]}")
     M, N, K = 64, 256, 2048
     Wt = synth.make_weights(fmt, N, K, 6300)
-    qk = 128 if fmt == synth.Q1_0 else 64
-    raw = oracle.encode(fmt, Wt.w, np.full((N, K // qk), 0x3C00, np.uint16), N, K)
-    Wu = synth.Weights(fmt, N, K, raw.reshape(N, K // qk, 18), Wt.w)
+    qk = QK[fmt]
+    if fmt == synth.Q8_0:
+        Wu = synth.Weights(fmt, N, K, synth.lay_out_q8_0(Wt.w, np.full((N, K // qk), 1.0, np.float16)), Wt.w)
+        raw = Wu.raw
+    else:
+        raw = oracle.encode(fmt, Wt.w, np.full((N, K // qk), 0x3C00, np.uint16), N, K)
+        Wu = synth.Weights(fmt, N, K, raw.reshape(N, K // qk, 18), Wt.w)
     Q, _ = acts(fmt, M, K, 6301)
     ones = np.full((M, K // 32), 0x3C00, np.uint16)
     Y = gpu_gemm(fmt, packed_weights(Wu), N, K, Q, ones, M)
@@ -114,7 +140,7 @@ def test_gemm_unit_scales_bit_exact(fmt):
     assert np.array_equal(Y.astype(np.float64), Yr)
 
 
-@pytest.mark.parametrize("fmt", [synth.Q1_0, synth.Q2_0_G64], ids=NAMES.get)
+@pytest.mark.parametrize("fmt", [synth.Q1_0, synth.Q2_0_G64, synth.Q8_0], ids=NAMES.get)
 @pytest.mark.parametrize("N", [4096, 12288])
 def test_gemm_full_size_sampled(fmt, N):
     """The prefill workload at full size (512 activation rows x N x 4096); the oracle checks a seeded
