@@ -457,14 +457,57 @@ def single_launch(fmt, shapes, reps=30, seed=1011):
                 launch()
                 b.record()
             torch.cuda.synchronize()
-            times[mode] = statistics.median(a.elapsed_time(b) for a, b in ev)
+            el = [a.elapsed_time(b) for a, b in ev]
+            times[mode] = statistics.median(el)
+            times[mode + "_min"] = min(el)
         nbytes = L.lowbit_weight_bytes(fmt, N, K)
         out[f"{N}x{K}"] = {"weight_bytes": nbytes, "warm_us": round(times["warm"] * 1e3, 2),
+                           "warm_min_us": round(times["warm_min"] * 1e3, 2),
                            "cold_us": round(times["cold"] * 1e3, 2),
+                           "cold_min_us": round(times["cold_min"] * 1e3, 2),
                            "cold_gbs": round(nbytes / (times["cold"] * 1e-3) / 1e9, 1)}
     del flush
     torch.cuda.empty_cache()
     return out
+
+
+def read_probe_gbs(nbytes=1 << 31, reps=5):
+    """A stream read of a buffer far larger than the 256 MB last-level cache: torch's fp32 sum, read GB/s."""
+    import torch
+
+    a = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    a.sum()
+    torch.cuda.synchronize()
+    best = 0.0
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        a.sum()
+        e1.record()
+        torch.cuda.synchronize()
+        best = max(best, nbytes / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+    del a
+    torch.cuda.empty_cache()
+    return best
+
+
+def device_clocks():
+    """The current shader and memory clocks as rocm-smi reports them (a child process; None if unavailable)."""
+    import shutil
+    import subprocess
+
+    exe = shutil.which("rocm-smi") or ("/opt/rocm/bin/rocm-smi" if os.path.exists("/opt/rocm/bin/rocm-smi") else None)
+    if exe is None:
+        return None
+    try:
+        r = subprocess.run([exe, "--showclocks", "--json"], capture_output=True, text=True, timeout=20)
+        data = json.loads(r.stdout)
+    except (OSError, ValueError, subprocess.SubprocessError):
+        return None
+    card = next((v for k, v in data.items() if k.startswith("card")), None)
+    if not isinstance(card, dict):
+        return None
+    return {k: v for k, v in card.items() if "sclk" in k.lower() or "mclk" in k.lower() or "fclk" in k.lower()}
 
 
 def copy_probe_gbs(nbytes=1 << 31, reps=5):
@@ -512,6 +555,10 @@ def main():
 
     probe = copy_probe_gbs()
     log(f"copy probe: {probe:.0f} GB/s (read+write)")
+    rprobe = read_probe_gbs()
+    log(f"read probe: {rprobe:.0f} GB/s (torch fp32 sum)")
+    clocks = device_clocks()
+    log(f"clocks: {clocks}")
 
     tok = DecodeToken(synth.Q2_0_G64, synth.QWEN3_8B_LAYER, synth.QWEN3_8B_LAYERS, seed=1003,
                       keep_blocks_layers=0 if args.no_cpu_baseline else synth.QWEN3_8B_LAYERS)
@@ -546,6 +593,9 @@ def main():
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "tokens_per_s_equiv": round(1e3 / ms_step, 1),
         "copy_probe_gbs": round(probe, 1),
+        "read_probe_gbs": round(rprobe, 1),
+        "device": {"name": dev.name, "arch": getattr(dev, "gcnArchName", None), "cus": dev.multi_processor_count,
+                   "clocks": clocks},
         "roofline": {
             "bound": "hbm",
             "achieved": round(achieved, 2),
