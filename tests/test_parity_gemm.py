@@ -71,6 +71,13 @@ def test_gemm_shapes(fmt, M, N, K):
     check(fmt, M, N, K, seed=6000 + M + N + K)
 
 
+@pytest.mark.parametrize("fmt", [synth.Q1_0, synth.Q2_0_G64, synth.TERNARY_PLANAR, synth.Q8_0], ids=NAMES.get)
+def test_gemm_largest_k(fmt):
+    # the largest K the ABI takes (32768; 16384 for Q8_0), ragged in both M and N: every K-step rotation
+    # of the walk and, for the 16-wave split workgroups, the longest per-half step count
+    check(fmt, 70, 65, 16384 if fmt == synth.Q8_0 else 32768, seed=6050)
+
+
 @pytest.mark.parametrize("fmt", [synth.Q2_0_G64, synth.TERNARY_PLANAR], ids=NAMES.get)
 def test_gemm_odd_block_tail(fmt):
     # K = 7 blocks of 64: the last K-step of the kernel is half full
