@@ -10,24 +10,26 @@
 #include <queue>
 #include <cstdio>
 #include <cstring>
-#include <string>
+#include <memory>
+#include <new>
 #include <vector>
 
 #include "lowbit_internal.h"
 
 namespace {
 
-thread_local std::string g_last_error;
+// fixed storage: recording an error never allocates (nothing may throw through the C ABI)
+thread_local char g_last_error[512];
 
 lb_status fail(lb_status st, const char *fn, const char *what)
 {
-    g_last_error = std::string(fn) + ": " + what;
+    std::snprintf(g_last_error, sizeof(g_last_error), "%s: %s", fn, what);
     return st;
 }
 
 lb_status hip_fail(const char *fn, hipError_t e)
 {
-    g_last_error = std::string(fn) + ": " + hipGetErrorName(e) + ": " + hipGetErrorString(e);
+    std::snprintf(g_last_error, sizeof(g_last_error), "%s: %s: %s", fn, hipGetErrorName(e), hipGetErrorString(e));
     return LB_EDEVICE;
 }
 
@@ -123,14 +125,16 @@ const char *lowbit_status_str(lb_status st)
     case LB_EALIGN:
         return "LB_EALIGN: misaligned pointer";
     case LB_EUNSUPPORTED:
-        return "LB_EUNSUPPORTED: unsupported device";
+        return "LB_EUNSUPPORTED: unsupported device or format";
     case LB_EDEVICE:
         return "LB_EDEVICE: HIP runtime error";
+    case LB_ENOMEM:
+        return "LB_ENOMEM: host memory exhausted";
     }
     return "unknown lb_status";
 }
 
-const char *lowbit_last_error(void) { return g_last_error.c_str(); }
+const char *lowbit_last_error(void) { return g_last_error; }
 
 int64_t lowbit_weight_bytes(int fmt, int64_t N, int64_t K)
 {
@@ -430,7 +434,7 @@ struct lb_batch {
     int device = -1;
 };
 
-lb_status lowbit_batch_create(const lb_matvec_desc *list, int32_t n, lb_batch **out)
+static lb_status batch_create(const lb_matvec_desc *list, int32_t n, lb_batch **out)
 {
     const char *fn = "lowbit_batch_create";
     if (!out)
@@ -519,13 +523,12 @@ lb_status lowbit_batch_create(const lb_matvec_desc *list, int32_t n, lb_batch **
     for (size_t gi = 0; gi < keys.size(); gi++)
         bytes += (descs[gi].size() * sizeof(lb::DevDesc) + 255) / 256 * 256 +
                  (tiles[gi].size() * sizeof(lb::TileRef) + 255) / 256 * 256;
-    lb_batch *b = new lb_batch();
+    std::unique_ptr<lb_batch> b(new lb_batch());
     b->device = device;
+    b->groups.reserve(keys.size()); // nothing below allocates host memory once the device memory is held
     hipError_t e = hipMalloc(&b->dev, bytes);
-    if (e != hipSuccess) {
-        delete b;
+    if (e != hipSuccess)
         return hip_fail(fn, e);
-    }
     size_t off = 0;
     char *base = static_cast<char *>(b->dev);
     for (size_t gi = 0; gi < keys.size(); gi++) {
@@ -544,15 +547,24 @@ lb_status lowbit_batch_create(const lb_matvec_desc *list, int32_t n, lb_batch **
             off += (tiles[gi].size() * sizeof(lb::TileRef) + 255) / 256 * 256;
         }
         if (e != hipSuccess) {
-            hipFree(b->dev);
-            delete b;
+            (void)hipFree(b->dev);
             return hip_fail(fn, e);
         }
         grp.lds = lds[gi];
         b->groups.push_back(grp);
     }
-    *out = b;
+    *out = b.release();
     return LB_OK;
+}
+
+lb_status lowbit_batch_create(const lb_matvec_desc *list, int32_t n, lb_batch **out)
+{
+    // the plan is built in host containers: an allocation failure is reported, not thrown through C
+    try {
+        return batch_create(list, n, out);
+    } catch (const std::bad_alloc &) {
+        return fail(LB_ENOMEM, "lowbit_batch_create", "host allocation failed while planning the batch");
+    }
 }
 
 lb_status lowbit_matvec_batched(const lb_batch *b, hipStream_t s)

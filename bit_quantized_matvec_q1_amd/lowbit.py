@@ -14,7 +14,7 @@ import torch
 
 Q1_0, Q2_0_G64, TERNARY_PLANAR, Q8_0, TERNARY_B3 = 1, 2, 3, 4, 5
 ACT_Q8_0, ACT_I8_ROW, ACT_F32_Q8_0 = 1, 2, 3
-LB_OK, LB_EINVAL, LB_ESHAPE, LB_EALIGN, LB_EUNSUPPORTED, LB_EDEVICE = range(6)
+LB_OK, LB_EINVAL, LB_ESHAPE, LB_EALIGN, LB_EUNSUPPORTED, LB_EDEVICE, LB_ENOMEM = range(7)
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblowbit.so")
 if not os.path.exists(LIB_PATH):

@@ -68,13 +68,15 @@ typedef enum {
     LB_ESHAPE = 2,       /* negative size, K not a multiple of the weight block (128, 64, 64, 32, 64), or over a limit */
     LB_EALIGN = 3,       /* a pointer is not aligned as its argument requires */
     LB_EUNSUPPORTED = 4, /* the current device is not gfx950, or the entry point has no kernel for the format */
-    LB_EDEVICE = 5       /* a HIP call failed; lowbit_last_error() holds the runtime's message */
+    LB_EDEVICE = 5,      /* a HIP call failed; lowbit_last_error() holds the runtime's message */
+    LB_ENOMEM = 6        /* host memory for a set-up object (lowbit_batch_create) could not be allocated */
 } lb_status;
 
 /* Human-readable name of a status code (static string). */
 const char *lowbit_status_str(lb_status st);
 
-/* Message of the last error raised by this library on the calling thread ("" if none). */
+/* Message of the last error raised by this library on the calling thread ("" if none; at most 511
+ * characters, valid until the thread's next failing call). */
 const char *lowbit_last_error(void);
 
 /*
@@ -208,7 +210,8 @@ typedef struct {
 
 typedef struct lb_batch lb_batch;
 
-/* list: HOST array of n descriptors (n >= 1).  On success *out owns device memory until destroyed.
+/* list: HOST array of n descriptors (n >= 1).  On success *out owns device memory until destroyed;
+ * lowbit_batch_destroy frees it (hipFree, which waits for the device), so no launch may use it after.
  * The buffers the descriptors point to must stay valid while the batch is used.  A descriptor with
  * afmt LB_ACT_F32_Q8_0 takes its activations from x and needs fmt LB_Q1_0 or LB_Q2_0_G64 (else
  * LB_EUNSUPPORTED); null x is LB_EINVAL, x not 16-byte aligned LB_EALIGN. */

@@ -29,9 +29,18 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_status_strings():
-    for st in range(6):
-        assert L.lib.lowbit_status_str(st)
+    for st in range(7):
+        assert L.lib.lowbit_status_str(st).startswith(b"LB_")
     assert L.lib.lowbit_status_str(0) == b"LB_OK"
+    assert L.lib.lowbit_status_str(L.LB_ENOMEM).startswith(b"LB_ENOMEM")
+    assert L.lib.lowbit_status_str(99) == b"unknown lb_status"
+
+
+def test_last_error_is_bounded_and_names_the_call():
+    # a failing call records "<function>: <reason>" in fixed per-thread storage
+    assert L.lib.lowbit_gemm(L.Q2_0_G64, A16, 8, 64, 1.0, L.ACT_Q8_0, A16, A16, -1, A16, None) == L.LB_ESHAPE
+    msg = L.lib.lowbit_last_error()
+    assert msg.startswith(b"lowbit_gemm: ") and len(msg) < 512
 
 
 def test_weight_bytes():
