@@ -71,10 +71,16 @@ class lb_matvec_desc(ctypes.Structure):
 
 
 def _ptr(t):
+    """A device tensor's address (ints pass through as raw addresses).  Host tensors and strided views are
+    refused: the kernels take dense device buffers, and a host address in a kernel is a memory fault."""
     if t is None:
         return None
     if isinstance(t, int):
         return t
+    if not t.is_cuda:
+        raise ValueError(f"device tensor required, got one on {t.device}")
+    if not t.is_contiguous():
+        raise ValueError("contiguous tensor required (the C ABI takes dense row-major buffers)")
     return t.data_ptr()
 
 

@@ -142,3 +142,12 @@ def test_no_device_is_refused_without_launch():
     assert b"gfx950" in L.lib.lowbit_last_error()
     with pytest.raises(L.LowbitError):
         L.lowbit_matvec(L.Q2_0_G64, A16, 8, 128, 1.0, L.ACT_Q8_0, A16, A16, A16, stream=0)
+
+
+def test_binding_refuses_host_tensors():
+    # a host address handed to a kernel would be a memory fault: the binding refuses it before the call
+    import torch
+
+    host = torch.zeros(64, dtype=torch.int8)
+    with pytest.raises(ValueError, match="device tensor required"):
+        L.lowbit_matvec(L.Q2_0_G64, A16, 8, 64, 1.0, L.ACT_Q8_0, host, A16, A16)
