@@ -491,23 +491,32 @@ def read_probe_gbs(nbytes=1 << 31, reps=5):
     return best
 
 
-def device_clocks():
-    """The current shader and memory clocks as rocm-smi reports them (a child process; None if unavailable)."""
-    import shutil
-    import subprocess
+def device_clocks(props):
+    """The current shader, memory and fabric clock levels of this GPU, read from sysfs (the DPM table line
+    marked current), with no child process.  The card is matched on the PCI bus number torch reports; None
+    when nothing matches or the files are not readable."""
+    import glob
 
-    exe = shutil.which("rocm-smi") or ("/opt/rocm/bin/rocm-smi" if os.path.exists("/opt/rocm/bin/rocm-smi") else None)
-    if exe is None:
-        return None
-    try:
-        r = subprocess.run([exe, "--showclocks", "--json"], capture_output=True, text=True, timeout=20)
-        data = json.loads(r.stdout)
-    except (OSError, ValueError, subprocess.SubprocessError):
-        return None
-    card = next((v for k, v in data.items() if k.startswith("card")), None)
-    if not isinstance(card, dict):
-        return None
-    return {k: v for k, v in card.items() if "sclk" in k.lower() or "mclk" in k.lower() or "fclk" in k.lower()}
+    bus = getattr(props, "pci_bus_id", None)
+    for dev_dir in sorted(glob.glob("/sys/class/drm/card*/device")):
+        try:
+            with open(os.path.join(dev_dir, "uevent")) as f:
+                slot = next((l.split("=", 1)[1].strip() for l in f if l.startswith("PCI_SLOT_NAME=")), "")
+        except OSError:
+            continue
+        if bus is None or not slot or int(slot.split(":")[1], 16) != bus:
+            continue
+        out = {"pci": slot}
+        for name in ("sclk", "mclk", "fclk"):
+            try:
+                with open(os.path.join(dev_dir, f"pp_dpm_{name}")) as f:
+                    cur = [l.split(":", 1)[1].replace("*", "").strip() for l in f if l.rstrip().endswith("*")]
+            except OSError:
+                continue
+            if cur:
+                out[name] = cur[0]
+        return out
+    return None
 
 
 def copy_probe_gbs(nbytes=1 << 31, reps=5):
@@ -557,7 +566,7 @@ def main():
     log(f"copy probe: {probe:.0f} GB/s (read+write)")
     rprobe = read_probe_gbs()
     log(f"read probe: {rprobe:.0f} GB/s (torch fp32 sum)")
-    clocks = device_clocks()
+    clocks = device_clocks(dev)
     log(f"clocks: {clocks}")
 
     tok = DecodeToken(synth.Q2_0_G64, synth.QWEN3_8B_LAYER, synth.QWEN3_8B_LAYERS, seed=1003,
