@@ -551,7 +551,8 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU: this library has no multi-GPU path (asked for --gpus {args.gpus}). "
-              "Each product shards by rows; see the design notes.", file=sys.stderr)
+              "Each product would shard by rows: N / G rows per GPU, the activation replicated, one all-gather "
+              "of y.", file=sys.stderr)
         sys.exit(2)
 
     import torch
