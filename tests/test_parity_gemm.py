@@ -175,3 +175,23 @@ def test_gemm_rows_match_decode():
         yr, A = oracle.matvec_q(fmt, Wt.raw, N, K, Q[m], XS[m])
         assert_close(host(y), yr, A, K // 32, "decode row")
         assert_close(Y[m], yr, A, K // 32, "prefill row")
+
+
+# --- seeded shape sweep: ragged M and N (partial tiles on both sides), K from one step to several, and grids
+# on both sides of the split-K threshold ---------------------------------------------------------------------
+
+def _sweep_cases(n=16, seed=9500):
+    g = synth.rng(seed)
+    fmts = [synth.Q1_0, synth.Q2_0_G64, synth.TERNARY_PLANAR, synth.Q8_0]
+    cases = []
+    for i in range(n):
+        fmt = fmts[int(g.integers(0, len(fmts)))]
+        blk = 128 if fmt in (synth.Q1_0, synth.Q8_0) else 64
+        K = blk * int(g.integers(1, 2048 // blk + 1))
+        cases.append((fmt, int(g.integers(1, 161)), int(g.integers(1, 201)), K, seed + 1 + i))
+    return cases
+
+
+@pytest.mark.parametrize("fmt,M,N,K,seed", _sweep_cases(), ids=lambda v: str(v))
+def test_gemm_seeded_shape_sweep(fmt, M, N, K, seed):
+    check(fmt, M, N, K, seed=seed)

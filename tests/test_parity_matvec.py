@@ -284,3 +284,25 @@ def test_quantize_i8_row_bytes(M, K):
     L.lowbit_quantize_act(L.ACT_I8_ROW, dev(x), M, K, xq, xs)
     assert np.array_equal(host(xq), q_ref)
     assert np.array_equal(host(xs), s_ref)
+
+
+# --- seeded shape sweep: every K the decode kernels take is a configuration choice (lanes per row, records
+# per lane, a full or clamped last lane); a seeded draw of formats, row counts and K covers the choices the
+# hand-picked shapes above do not ---------------------------------------------------------------------------
+
+def _sweep_cases(n=24, seed=9000):
+    g = synth.rng(seed)
+    cases = []
+    for i in range(n):
+        fmt = ALL_FMTS[int(g.integers(0, len(ALL_FMTS)))]
+        blk = {synth.Q1_0: 128, synth.Q8_0: 32}.get(fmt, 64)
+        kmax = min(MAX_K.get(fmt, 32768), 8192)
+        K = blk * int(g.integers(1, kmax // blk + 1))
+        N = int(g.integers(1, 400))
+        cases.append((fmt, N, K, seed + 1 + i))
+    return cases
+
+
+@pytest.mark.parametrize("fmt,N,K,seed", _sweep_cases(), ids=lambda v: str(v))
+def test_matvec_seeded_shape_sweep(fmt, N, K, seed):
+    check_product(fmt, N, K, seed=seed)
