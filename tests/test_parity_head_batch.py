@@ -115,20 +115,39 @@ def test_batched_matches_single_and_oracle(fmt):
 
 
 def test_batched_mixed_formats():
+    """One work list over all five formats, two configurations of one format, an empty product and a product
+    that quantises its fp32 input in the launch: one launch group per (format, configuration, input kind),
+    each product bit-identical to its own single launch."""
     say("case batched mixed formats")
-    items = [(synth.Q2_0_G64, 256, 4096), (synth.Q1_0, 256, 4096), (synth.TERNARY_PLANAR, 256, 2560)]
+    items = [(synth.Q2_0_G64, 256, 4096), (synth.Q1_0, 256, 4096), (synth.TERNARY_PLANAR, 256, 2560),
+             (synth.Q8_0, 200, 4096), (synth.TERNARY_B3, 130, 2560), (synth.Q2_0_G64, 96, 12288)]
     descs, keep = [], []
     for i, (fmt, N, K) in enumerate(items):
         Wt, packed, q, xs = _product(fmt, N, K, 5500 + i)
         qd, xsd = dev(q), dev(xs)
-        y = torch.empty(N, dtype=torch.float32, device="cuda")
+        y = torch.full((N,), float("nan"), dtype=torch.float32, device="cuda")
         keep.append((fmt, N, K, Wt, packed, q, xs, qd, xsd, y))
         descs.append(L.desc(fmt, packed, N, K, qd, xsd, y, w_tensor_scale=Wt.s_w if Wt.s_w is not None else 1.0))
+    # an empty product (nothing to do, nothing written) and an fp32-input product beside its quantised twin
+    Wt0, packed0, q0, xs0 = _product(synth.Q1_0, 8, 1024, 5590)
+    descs.append(L.desc(synth.Q1_0, packed0, 0, 1024, dev(q0), dev(xs0), torch.empty(1, device="cuda")))
+    Wf, packedf, _, _ = _product(synth.Q2_0_G64, 150, 4096, 5595)
+    xf = synth.activations(synth.rng(5596), 1, 4096)[0]
+    xfd = dev(xf)
+    xq = torch.empty(4096, dtype=torch.int8, device="cuda")
+    xsq = torch.empty(128, dtype=torch.uint16, device="cuda")
+    L.lowbit_quantize_act(L.ACT_Q8_0, xfd, 1, 4096, xq, xsq)
+    yf = torch.full((150,), float("nan"), dtype=torch.float32, device="cuda")
+    descs.append(L.desc(synth.Q2_0_G64, packedf, 150, 4096, None, None, yf, x=xfd))
     b = L.Batch(descs)
     b.run()
+    torch.cuda.synchronize()
     for fmt, N, K, Wt, packed, q, xs, _, _, y in keep:
         ref = gpu_matvec(fmt, packed, N, K, q, xs, w_scale=Wt.s_w if Wt.s_w is not None else 1.0)
-        assert np.array_equal(host(y), ref)
+        assert np.array_equal(host(y), ref), f"format {fmt} {N}x{K} differs from its single launch"
+    yq = torch.empty(150, dtype=torch.float32, device="cuda")
+    L.lowbit_matvec(synth.Q2_0_G64, packedf, 150, 4096, 1.0, L.ACT_Q8_0, xq, xsq, yq)
+    assert np.array_equal(host(yf), host(yq)), "in-launch quantisation differs from quantising first"
     b.close()
 
 
