@@ -194,3 +194,45 @@ def test_batched_fp32_activations_quantised_in_launch(fmt):
         assert_close(host(yf), y_ref, A, K // 32, f"fp32-activation batch {N}x{K}")
     bf.close()
     bq.close()
+
+
+def test_concurrent_threads_and_streams():
+    """Four host threads, each on its own stream, launch single products and a batch at once (the library
+    keeps no launch state between calls: per-device caches are atomics, error text is per thread); every
+    output equals the one a sequential run gives."""
+    import threading
+
+    say("case concurrent threads and streams")
+    work = []
+    for i, (fmt, N, K) in enumerate([(synth.Q2_0_G64, 512, 4096), (synth.Q1_0, 300, 4096),
+                                     (synth.TERNARY_PLANAR, 700, 2560), (synth.Q8_0, 256, 4096)]):
+        Wt, packed, q, xs = _product(fmt, N, K, 5700 + i)
+        w_scale = Wt.s_w if Wt.s_w is not None else 1.0
+        ref = gpu_matvec(fmt, packed, N, K, q, xs, w_scale=w_scale)
+        qd, xsd = dev(q), dev(xs)
+        ys = [torch.full((N,), float("nan"), dtype=torch.float32, device="cuda") for _ in range(2)]
+        batch = L.Batch([L.desc(fmt, packed, N, K, qd, xsd, ys[1], w_tensor_scale=w_scale)])
+        work.append((fmt, N, K, packed, qd, xsd, w_scale, ys, batch, ref, torch.cuda.Stream()))
+    torch.cuda.synchronize()
+    errors = []
+
+    def run(item):
+        fmt, N, K, packed, qd, xsd, w_scale, ys, batch, _, stream = item
+        try:
+            for _ in range(20):
+                L.lowbit_matvec(fmt, packed, N, K, w_scale, L.ACT_I8_ROW if fmt == synth.TERNARY_PLANAR else L.ACT_Q8_0,
+                                qd, xsd, ys[0], stream=stream)
+                batch.run(stream=stream)
+        except Exception as e:  # reported below, after every thread has joined
+            errors.append(e)
+
+    threads = [threading.Thread(target=run, args=(item,)) for item in work]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for fmt, N, K, _, _, _, _, ys, batch, ref, _ in work:
+        assert np.array_equal(host(ys[0]), ref) and np.array_equal(host(ys[1]), ref), f"format {fmt} differs"
+        batch.close()
