@@ -72,6 +72,14 @@ def test_bitnet_token_full_size(fmt):
     tok.batch.close()
 
 
+def test_bitnet_gqa_token_full_size():
+    """The grouped-query BitNet token bench.py times (k/v 640x2560 in every layer), planar, at full size."""
+    say("case full 2B GQA token")
+    tok = _run_token(synth.TERNARY_PLANAR, synth.BITNET_2B_GQA_LAYER, synth.BITNET_2B_LAYERS, seed=7400)
+    _check_token(tok, seed=7401)
+    tok.batch.close()
+
+
 @pytest.mark.parametrize("fmt", [synth.Q2_0_G64, synth.TERNARY_PLANAR], ids=["Q2_0_g64", "planar"])
 def test_layered_graph_replays_match_eager_and_oracle(fmt):
     """The dependency-ordered token captured as one HIP graph: every replay (with eager work and a clobber of
