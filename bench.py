@@ -9,9 +9,11 @@ Inputs are synthetic (seeded), with the shapes and value distributions of the wo
 HBM before timing starts.
 
 Prints ONE JSON line: the effective weight GB/s of the step (weight bytes / step time), the roofline of
-the dominant kernel (the batched decode launch) measured with HIP events on the stream it runs on, and
-the CPU oracle timed on a bounded sample of the same bytes.  ``--gpus`` above 1 exits: this library
-runs on one GPU.
+the dominant kernel (the batched decode launch) measured with HIP events on the stream it runs on, the
+same token in dependency order (layer by layer, as one HIP graph), a streaming-read probe run in the same
+process (the bound the decode kernels are reported against beside the HBM peak), the shader clock while
+the step runs, and the CPU oracle timed on the host's cores (rows split over threads, never a reduction)
+on a bounded sample of the same bytes.  ``--gpus`` above 1 exits: this library runs on one GPU.
 """
 from __future__ import annotations
 
@@ -265,35 +267,125 @@ def stored_traffic(kernel_name, algorithmic_bytes):
     return float(m_bytes.group(1))
 
 
-def cpu_baseline(tok, budget_s=12.0):
-    """The oracle, as it stands, on the same bytes: layers in order (quantise + all 7 products each) until
-    the time budget is spent.  Single-threaded."""
+def host_info():
+    """The host the oracle runs on: CPU model (/proc/cpuinfo), logical CPUs, the CPUs this process may use,
+    and the worker threads the oracle legs use (the machine's CPU share per GPU is 16)."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), None)
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = os.cpu_count() or 1
+    return {"cpu_model": model, "nproc": os.cpu_count(), "usable_cpus": usable, "threads": max(1, min(usable, 16))}
+
+
+def oracle_rows(fn, n_rows, threads):
+    """Run fn(r0, r1) -> array over contiguous row chunks on `threads` host threads (the oracle's C calls
+    release the GIL) and concatenate: rows are split, never a reduction, so the result does not depend on
+    the thread count."""
+    import concurrent.futures as cf
+
     import numpy as np
-    import torch
+
+    chunks = [(n_rows * t // threads, n_rows * (t + 1) // threads) for t in range(threads)]
+    chunks = [(a, b) for a, b in chunks if b > a]
+    if len(chunks) == 1:
+        return fn(*chunks[0])
+    with cf.ThreadPoolExecutor(max_workers=len(chunks)) as ex:
+        parts = list(ex.map(lambda c: fn(*c), chunks))
+    return np.concatenate(parts)
+
+
+def oracle_matvec_rows(fmt, raw, N, K, q, xs, s_w, threads):
+    """The oracle's product of one weight tensor, rows split over threads -> y."""
+    import numpy as np
 
     import oracle
 
+    if fmt == 3:  # planar: per-token activations, ((float)acc * s_x) * s_w
+        return oracle_rows(lambda a, b: oracle.matvec_planar(raw, N, K, q, xs[0], s_w, rows=np.arange(a, b))[1],
+                           N, threads)
+    return oracle_rows(lambda a, b: oracle.matvec_q(fmt, raw, N, K, q, xs, rows=np.arange(a, b))[0], N, threads)
+
+
+def oracle_thread_identity(threads):
+    """The 1024 x 1024 Q2_0_g64 product (the small parity workload) by the oracle on one thread and on
+    `threads` threads: True when the outputs are bit-identical."""
+    import numpy as np
+
+    import oracle
+    import synth
+
+    Wt = synth.make_weights(synth.Q2_0_G64, 1024, 1024, seed=1001)
+    q, dh = oracle.quantize_q8_0(synth.activations(synth.rng(1002), 1, 1024))
+    y1 = oracle_matvec_rows(synth.Q2_0_G64, Wt.raw, 1024, 1024, q[0], dh[0], 1.0, 1)
+    yt = oracle_matvec_rows(synth.Q2_0_G64, Wt.raw, 1024, 1024, q[0], dh[0], 1.0, threads)
+    return bool(np.array_equal(y1.view(np.uint64), yt.view(np.uint64)))
+
+
+def cpu_baseline(tok, threads, budget_s=12.0):
+    """The oracle, as it stands, on the same bytes as the GPU step: layers in order (quantise the layer's
+    activations, then all of its products, each product's rows split over `threads` host threads) until
+    the time budget is spent or the token is done.  Returns (seconds, weight bytes, layers)."""
+    import oracle
+
+    planar = tok.fmt == 3
     t_total, wbytes, layers_done = 0.0, 0, 0
+    xs_host = {K: x.cpu().numpy() for K, x in tok.x.items()}
     for l in range(tok.layers):
         if (l, 0) not in tok.blocks:
             break
-        xs_host = {K: x.cpu().numpy() for K, x in tok.x.items()}
         raws = [(p, tok.blocks[(l, j)].cpu().numpy().reshape(-1))
                 for j, p in enumerate([p for p in tok.products if p["layer"] == l])]
+        head = None
+        if tok.head is not None and l == tok.layers - 1:  # the token's dense head follows its last layer
+            import numpy as np
+
+            h = tok.head
+            head = (h["W"].cpu().numpy().view(np.uint16), h["N"], h["K"], h["x"].cpu().numpy())
         t0 = time.perf_counter()
         qcache = {}
         for p, raw in raws:
             K, r = p["feed"]
             if (K, r) not in qcache:
-                qcache[(K, r)] = oracle.quantize_q8_0(xs_host[K][r:r + 1])
-            q, dh = qcache[(K, r)]
-            oracle.matvec_q(tok.fmt, raw, p["N"], p["K"], q[0], dh[0])
+                x = xs_host[K][r:r + 1]
+                qcache[(K, r)] = oracle.quantize_i8_row(x) if planar else oracle.quantize_q8_0(x)
+            q, sc = qcache[(K, r)]
+            oracle_matvec_rows(tok.fmt, raw, p["N"], p["K"], q[0], sc if planar else sc[0], p["w_scale"], threads)
             wbytes += raw.size
+        if head is not None:
+            W, hn, hk, xh = head
+            oracle_rows(lambda a, b: oracle.head_matvec(W, hn, hk, xh, rows=range(a, b))[0], hn, threads)
+            wbytes += W.nbytes
         t_total += time.perf_counter() - t0
         layers_done += 1
         if t_total >= budget_s:
             break
     return t_total, wbytes, layers_done
+
+
+def cpu_prefill(fmt, N, K, M, threads, seed=1004):
+    """The oracle's prefill product on a bounded sample: the first activation rows of the M-row workload,
+    all N weight rows each, rows of W split over threads, until ~4 s are spent.  -> (TOPS, rows done)."""
+    import numpy as np
+
+    import oracle
+    import synth
+
+    Wt = synth.make_weights(fmt, N, K, seed)
+    X = synth.activations(synth.rng(seed + 1), M, K)
+    Q, DH = oracle.quantize_q8_0(X)
+    t0, m = time.perf_counter(), 0
+    while m < M and time.perf_counter() - t0 < 4.0:
+        oracle_rows(lambda a, b: oracle.matvec_q(fmt, Wt.raw, N, K, Q[m], DH[m], rows=np.arange(a, b))[0], N,
+                    threads)
+        m += 1
+    dt = time.perf_counter() - t0
+    return 2.0 * m * N * K / dt / 1e12, m
 
 
 def warm_up(fn, ms=100.0):
@@ -540,6 +632,94 @@ def copy_probe_gbs(nbytes=1 << 31, reps=5):
     return best
 
 
+def hip_read_probe_gbs(nbytes=4 << 30, reps=5):
+    """The library's streaming-read probe (16-byte non-temporal loads, the decode kernels' weight access
+    pattern) over a buffer 16x the 256 MB last-level cache: best of `reps` by HIP events, GB/s."""
+    import torch
+
+    import bit_quantized_matvec_q1_amd.lowbit as L
+
+    a = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(65536, dtype=torch.int32, device="cuda")
+    warm_up(lambda: L.lowbit_read_probe(a, nbytes, sink), ms=50.0)
+    best = 0.0
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        L.lowbit_read_probe(a, nbytes, sink)
+        e1.record()
+        torch.cuda.synchronize()
+        best = max(best, nbytes / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+    del a, sink
+    torch.cuda.empty_cache()
+    return best
+
+
+def _sysfs_card(props):
+    """The sysfs device directory of this GPU (matched on the PCI bus number torch reports), or None."""
+    import glob
+
+    bus = getattr(props, "pci_bus_id", None)
+    for dev_dir in sorted(glob.glob("/sys/class/drm/card*/device")):
+        try:
+            with open(os.path.join(dev_dir, "uevent")) as f:
+                slot = next((l.split("=", 1)[1].strip() for l in f if l.startswith("PCI_SLOT_NAME=")), "")
+        except OSError:
+            continue
+        if bus is not None and slot and int(slot.split(":")[1], 16) == bus:
+            return dev_dir
+    return None
+
+
+def _read_sclk_mhz(dev_dir):
+    """The shader clock now, in MHz: the hwmon frequency input if there is one, else the DPM level sysfs
+    marks as current."""
+    import glob
+
+    for f in sorted(glob.glob(os.path.join(dev_dir, "hwmon", "hwmon*", "freq1_input"))):
+        try:
+            with open(f) as fh:
+                return int(fh.read().strip()) / 1e6
+        except (OSError, ValueError):
+            pass
+    try:
+        with open(os.path.join(dev_dir, "pp_dpm_sclk")) as fh:
+            for line in fh:
+                if line.rstrip().endswith("*"):
+                    v = line.split(":", 1)[1].replace("*", "").strip().lower().replace("mhz", "")
+                    return float(v)
+    except (OSError, ValueError):
+        pass
+    return None
+
+
+def clocks_under_load(props, fn, n):
+    """The shader clock while this leg's work runs: enqueue fn() n times (tens of milliseconds of GPU
+    work), then sample the clock every ~2 ms until the stream drains.  A pass of its own, outside every
+    timed region.  -> {"sclk_mhz_median", "sclk_mhz_max", "samples"} or None."""
+    import statistics
+
+    import torch
+
+    dev_dir = _sysfs_card(props)
+    if dev_dir is None:
+        return None
+    torch.cuda.synchronize()
+    for _ in range(n):
+        fn()
+    stream = torch.cuda.current_stream()
+    samples = []
+    while not stream.query():
+        v = _read_sclk_mhz(dev_dir)
+        if v is not None:
+            samples.append(v)
+        time.sleep(0.002)
+    torch.cuda.synchronize()
+    if not samples:
+        return None
+    return {"sclk_mhz_median": statistics.median(samples), "sclk_mhz_max": max(samples), "samples": len(samples)}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -562,23 +742,51 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs an MI355X"
     dev = torch.cuda.get_device_properties(0)
     log(f"device: {dev.name} ({getattr(dev, 'gcnArchName', '?')}), {dev.multi_processor_count} CUs")
+    host = host_info()
+    log(f"host: {host}")
 
+    hprobe = hip_read_probe_gbs()
+    log(f"streaming-read probe (16-byte non-temporal loads, 4 GiB, best of 5): {hprobe:.0f} GB/s")
     probe = copy_probe_gbs()
     log(f"copy probe: {probe:.0f} GB/s (read+write)")
     rprobe = read_probe_gbs()
     log(f"read probe: {rprobe:.0f} GB/s (torch fp32 sum)")
     clocks = device_clocks(dev)
-    log(f"clocks: {clocks}")
+    log(f"clocks (idle, between legs): {clocks}")
 
     tok = DecodeToken(synth.Q2_0_G64, synth.QWEN3_8B_LAYER, synth.QWEN3_8B_LAYERS, seed=1003,
                       keep_blocks_layers=0 if args.no_cpu_baseline else synth.QWEN3_8B_LAYERS)
     log(f"Q2_0_g64 token: {len(tok.products)} products, {tok.weight_bytes} weight bytes")
-    ms_step, ms_launch = time_token(tok, args.steps, args.warmup)
+    warm = max(args.warmup, warm_steps(tok))
+    ms_step, ms_launch = time_token(tok, args.steps, warm)
     value = tok.weight_bytes / (ms_step * 1e-3) / 1e9
     achieved = tok.algorithmic_bytes / (ms_launch * 1e-3) / 1e9
     traffic = stored_traffic("matvec_batched_kernel", tok.algorithmic_bytes)
     log(f"step {ms_step:.4f} ms, batched launch {ms_launch:.4f} ms -> {value:.0f} GB/s weights, "
         f"launch {achieved:.0f} GB/s algorithmic")
+    clk = clocks_under_load(dev, tok.step, max(50, int(100.0 / ms_step)))
+    log(f"shader clock while the step runs: {clk}")
+
+    # the same token in dependency order (per layer q/k/v, o, gate/up, down), replayed as one HIP graph
+    layered = {}
+    for fused, key, what in ((True, "fused", "each phase one batched launch that quantises its fp32 input to "
+                                             "q8_0 itself"),
+                             (False, "separate_quantise", "each phase a q8_0 quantise launch plus one batched "
+                                                          "launch")):
+        if not fused and "layered" not in args.secondary.split(","):
+            continue
+        lg = LayeredGraph(tok, fused=fused)
+        msg = time_graph(lg, args.steps, warm)
+        layered[key] = {
+            "workload": "the headline token in dependency order: per layer q/k/v, o, gate/up, down, " + what +
+                        ", captured as one HIP graph",
+            "launches": lg.launches(), "ms_per_token": round(msg, 5),
+            "tokens_per_s": round(1e3 / msg, 1),
+            "gbs": round(tok.weight_bytes / (msg * 1e-3) / 1e9, 1),
+            "pct_hbm_peak": round(100 * tok.weight_bytes / (msg * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+        }
+        lg.close()
+        log(f"dependency-ordered token ({key}): {msg:.4f} ms")
 
     out = {
         "metric": METRIC,
@@ -587,6 +795,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_steps_run": warm,
         "ms_per_step": round(ms_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -595,17 +804,23 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": "Q2_0_g64 decode token, Qwen3-8B shapes: 36 layers x {q 4096x4096, k/v 1024x4096, "
-                        "o 4096x4096, gate/up 12288x4096, down 4096x12288}, batch 1, q8_0 activations",
+                        "o 4096x4096, gate/up 12288x4096, down 4096x12288}, batch 1, q8_0 activations; a step "
+                        "quantises the token's 144 activation rows and runs all 252 products as independent "
+                        "work in one batched launch (layer order not enforced: the dependency-ordered figures "
+                        "are under dependency_ordered_token)",
             "products": len(tok.products),
             "weight_bytes": tok.weight_bytes,
             "parallelism": "single GPU",
         },
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
-        "tokens_per_s_equiv": round(1e3 / ms_step, 1),
+        "pct_of_read_probe": round(100.0 * value / hprobe, 2),
+        "token_products_per_s_equiv": round(1e3 / ms_step, 1),
+        "dependency_ordered_token": layered.get("fused"),
+        "read_probe_hip_gbs": round(hprobe, 1),
         "copy_probe_gbs": round(probe, 1),
-        "read_probe_gbs": round(rprobe, 1),
+        "read_probe_torch_sum_gbs": round(rprobe, 1),
         "device": {"name": dev.name, "arch": getattr(dev, "gcnArchName", None), "cus": dev.multi_processor_count,
-                   "clocks": clocks},
+                   "clocks_idle": clocks, "clock_during_step": clk},
         "roofline": {
             "bound": "hbm",
             "achieved": round(achieved, 2),
@@ -616,50 +831,54 @@ def main():
             "kernel": "matvec_batched_kernel<Q2_0_g64>",
             "algorithmic_bytes_per_launch": tok.algorithmic_bytes,
             "launch_ms": round(ms_launch, 5),
+            "frac_of_read_probe": round(achieved / hprobe, 4),
         },
     }
 
+    threads = host["threads"]
     if not args.no_cpu_baseline:
-        t_cpu, wb, layers = cpu_baseline(tok)
+        same = oracle_thread_identity(threads)
+        t_cpu, wb, layers = cpu_baseline(tok, threads)
         out["cpu_baseline"] = {
             "value": round(wb / t_cpu / 1e9, 4),
             "unit": "GB/s",
-            "cores": 1,
+            "cores": threads,
             "kind": "oracle",
             "sample": f"first {layers} of 36 layers (all 7 products each, q8_0 quantise included), the same "
-                      f"bytes as the GPU run: {wb} weight bytes in {t_cpu:.2f} s on one host thread",
+                      f"bytes as the GPU run: {wb} weight bytes in {t_cpu:.2f} s, rows split over {threads} "
+                      f"host threads",
+            "tokens_per_s": round((wb / tok.weight_bytes) / t_cpu, 3),
+            "host": host,
+            "bit_identical_to_one_thread": same,
         }
+        log(f"cpu baseline: {out['cpu_baseline']}")
     secondary = {}
     if "layered" in args.secondary.split(","):
-        # the same token in dependency order (per layer q/k/v, o, gate/up, down), replayed as one HIP graph
-        for fused, key, what in ((True, "q2_0_8b_token_layered_graph",
-                                  "each phase one batched launch that quantises its fp32 input to q8_0 itself"),
-                                 (False, "q2_0_8b_token_layered_graph_separate_quantise",
-                                  "each phase a q8_0 quantise launch plus one batched launch")):
-            lg = LayeredGraph(tok, fused=fused)
-            msg = time_graph(lg, args.steps, args.warmup)
-            secondary[key] = {
-                "workload": "the headline token in dependency order: per layer q/k/v, o, gate/up, down, " + what +
-                            ", captured as one HIP graph",
-                "launches": lg.launches(), "ms_per_token": round(msg, 5),
-                "gbs": round(tok.weight_bytes / (msg * 1e-3) / 1e9, 1),
-                "pct_hbm_peak": round(100 * tok.weight_bytes / (msg * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
-            }
-            lg.close()
+        for key, v in layered.items():
+            secondary["q2_0_8b_token_layered_graph" + ("" if key == "fused" else "_" + key)] = v
     tok.batch.close()
     del tok
     torch.cuda.empty_cache()
 
     for name in [s for s in args.secondary.split(",") if s and s != "none"]:
         if name == "q1":
-            t1 = DecodeToken(synth.Q1_0, synth.QWEN3_8B_LAYER, synth.QWEN3_8B_LAYERS, seed=1002)
+            t1 = DecodeToken(synth.Q1_0, synth.QWEN3_8B_LAYER, synth.QWEN3_8B_LAYERS, seed=1002,
+                             keep_blocks_layers=0 if args.no_cpu_baseline else synth.QWEN3_8B_LAYERS)
             ms1, ml1 = time_token(t1, max(50, args.steps // 2), warm_steps(t1))
             secondary["q1_0_8b_token"] = {
                 "weight_bytes": t1.weight_bytes, "ms_per_step": round(ms1, 5),
                 "gbs": round(t1.weight_bytes / (ms1 * 1e-3) / 1e9, 1),
                 "launch_gbs": round(t1.algorithmic_bytes / (ml1 * 1e-3) / 1e9, 1),
                 "pct_hbm_peak": round(100 * t1.weight_bytes / (ms1 * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+                "pct_of_read_probe": round(100 * t1.weight_bytes / (ms1 * 1e-3) / 1e9 / hprobe, 2),
+                "token_products_per_s_equiv": round(1e3 / ms1, 1),
             }
+            if not args.no_cpu_baseline:
+                tc, wb, nl = cpu_baseline(t1, threads, budget_s=4.0)
+                secondary["q1_0_8b_token"]["cpu_baseline"] = {
+                    "value": round(wb / tc / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+                    "sample": f"first {nl} of 36 layers, {wb} weight bytes in {tc:.2f} s",
+                    "tokens_per_s": round((wb / t1.weight_bytes) / tc, 3)}
             t1.batch.close()
             del t1
         elif name == "single":
@@ -672,7 +891,8 @@ def main():
                 **single_launch(synth.Q2_0_G64, shapes)}
         elif name == "planar":
             tp = DecodeToken(synth.TERNARY_PLANAR, synth.BITNET_2B_LAYER, synth.BITNET_2B_LAYERS, seed=1005,
-                             head=synth.BITNET_HEAD)
+                             head=synth.BITNET_HEAD,
+                             keep_blocks_layers=0 if args.no_cpu_baseline else synth.BITNET_2B_LAYERS)
             msp, mlp = time_token(tp, max(50, args.steps // 2), warm_steps(tp))
             secondary["planar_2b_token"] = {
                 "workload": "BitNet-b1.58-2B shapes, 30 layers x 7 planar products + the dense bf16 head "
@@ -680,9 +900,18 @@ def main():
                 "weight_bytes": tp.weight_bytes, "ms_per_step": round(msp, 5),
                 "gbs": round(tp.weight_bytes / (msp * 1e-3) / 1e9, 1),
                 "pct_hbm_peak": round(100 * tp.weight_bytes / (msp * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+                "pct_of_read_probe": round(100 * tp.weight_bytes / (msp * 1e-3) / 1e9 / hprobe, 2),
+                "tokens_per_s_equiv": round(1e3 / msp, 1),
                 "products_launch_ms": round(mlp, 5),
                 "products_launch_gbs": round(tp.algorithmic_bytes / (mlp * 1e-3) / 1e9, 1),
             }
+            if not args.no_cpu_baseline:
+                tc, wb, nl = cpu_baseline(tp, threads, budget_s=4.0)
+                secondary["planar_2b_token"]["cpu_baseline"] = {
+                    "value": round(wb / tc / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+                    "sample": f"first {nl} of 30 layers (the head after the last), {wb} weight bytes in "
+                              f"{tc:.2f} s",
+                    "tokens_per_s": round((wb / tp.weight_bytes) / tc, 3)}
             hms, hg = head_gbs(*synth.BITNET_HEAD)
             secondary["head_bf16_128256x2560"] = {"ms": round(hms, 4), "gbs": round(hg, 1),
                                                   "pct_hbm_peak": round(100 * hg / HBM_PEAK_GBS, 2)}
@@ -750,6 +979,13 @@ def main():
                     pre[f"{fname}_{synth.PREFILL_M}x{N}x{K}"] = {
                         "ms": round(ms, 4), "tops": round(tops, 1),
                         "frac_int8_mfma_peak": round(tops / MFMA_I8_PEAK_TOPS, 4)}
+            if not args.no_cpu_baseline:
+                N, K = synth.PREFILL_SHAPES[0]
+                ctops, rows = cpu_prefill(synth.Q2_0_G64, N, K, synth.PREFILL_M, threads)
+                pre["cpu_baseline"] = {
+                    "value": round(ctops, 6), "unit": "TOPS", "cores": threads, "kind": "oracle",
+                    "sample": f"Q2_0_g64 {N}x{K}: the first {rows} of the {synth.PREFILL_M} activation rows (one "
+                              "oracle product of all N weight rows per activation row)"}
             secondary["prefill"] = pre
         torch.cuda.empty_cache()
     if secondary:

@@ -14,7 +14,7 @@ CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "liblowbit.so")
 BUILD = os.path.join(HERE, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-SOURCES = ["abi.cpp", "quantize.hip", "matvec.hip", "q8.hip", "b3.hip", "popcount.hip", "head.hip", "gemm.hip"]
+SOURCES = ["abi.cpp", "quantize.hip", "matvec.hip", "q8.hip", "b3.hip", "popcount.hip", "head.hip", "gemm.hip", "probe.hip"]
 
 FLAGS = [
     "--offload-arch=gfx950",

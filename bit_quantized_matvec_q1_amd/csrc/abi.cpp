@@ -212,9 +212,9 @@ static lb_status matvec_common(const char *fn, int fmt, const void *W, int64_t N
         return st;
     hipError_t e;
     if (K == 0) {
-        // an empty sum: y = 0 (and no per-block sums exist; planar row sums are 0)
+        // an empty sum: y = 0 (and no per-block sums exist; planar and base-3 row sums are 0)
         if (sums)
-            e = fmt == LB_TERNARY_PLANAR ? lb::launch_fill_zero_i32(sums, N, s) : hipSuccess;
+            e = fmt == LB_TERNARY_PLANAR || fmt == LB_TERNARY_B3 ? lb::launch_fill_zero_i32(sums, N, s) : hipSuccess;
         else
             e = lb::launch_fill_zero(y, N, s);
     } else {
@@ -349,6 +349,24 @@ lb_status dense_head_matvec_i8(const int8_t *W, const float *row_scale, int64_t 
     return e == hipSuccess ? LB_OK : hip_fail(fn, e);
 }
 
+lb_status lowbit_read_probe(const void *buf, int64_t nbytes, uint32_t *sink, hipStream_t s)
+{
+    const char *fn = "lowbit_read_probe";
+    if (nbytes < 0 || nbytes % 16)
+        return fail(LB_ESHAPE, fn, "nbytes must be a non-negative multiple of 16");
+    if (nbytes == 0)
+        return LB_OK;
+    if (!buf || !sink)
+        return fail(LB_EINVAL, fn, "null pointer");
+    if (!aligned(buf, 16) || !aligned(sink, 4))
+        return fail(LB_EALIGN, fn, "buf needs 16-byte alignment, sink 4-byte alignment");
+    lb_status st = check_device(fn);
+    if (st != LB_OK)
+        return st;
+    hipError_t e = lb::launch_read_probe(buf, nbytes, sink, s);
+    return e == hipSuccess ? LB_OK : hip_fail(fn, e);
+}
+
 // ---- batched decode ------------------------------------------------------------------------------
 
 // Tile plan of one launch group.  Every product is cut into row tiles (whole row iterations of the
@@ -434,12 +452,57 @@ struct lb_batch {
     int device = -1;
 };
 
-static lb_status batch_create(const lb_matvec_desc *list, int32_t n, lb_batch **out)
+namespace {
+
+// A validated work list cut into launch groups with their device tables, still in host memory.
+struct BatchPlan {
+    struct Key {
+        int fmt, cfg, qin;
+    };
+    std::vector<Key> keys;
+    std::vector<std::vector<lb::DevDesc>> descs;
+    std::vector<std::vector<lb::TileRef>> tiles;
+    std::vector<int> full;
+    std::vector<size_t> lds;
+    int device = 0;
+
+    static size_t padded(size_t b) { return (b + 255) / 256 * 256; }
+    // bytes of the device tables: per group its descriptors, then its tiles, each padded to 256 bytes
+    size_t table_bytes() const
+    {
+        size_t bytes = 0;
+        for (size_t gi = 0; gi < keys.size(); gi++)
+            bytes += padded(descs[gi].size() * sizeof(lb::DevDesc)) + padded(tiles[gi].size() * sizeof(lb::TileRef));
+        return bytes;
+    }
+    // Lay the tables out at `host` (table_bytes() bytes) for device address `dev`, and describe the launch
+    // groups that read them there.
+    void emit(char *host, char *dev, std::vector<lb_batch::Group> &groups) const
+    {
+        size_t off = 0;
+        groups.clear();
+        for (size_t gi = 0; gi < keys.size(); gi++) {
+            lb_batch::Group grp;
+            grp.g.fmt = keys[gi].fmt;
+            grp.g.cfg_a = keys[gi].cfg;
+            grp.g.full = full[gi];
+            grp.g.qin = keys[gi].qin;
+            grp.g.ntiles = (int32_t)tiles[gi].size();
+            grp.g.desc = reinterpret_cast<const lb::DevDesc *>(dev + off);
+            std::memcpy(host + off, descs[gi].data(), descs[gi].size() * sizeof(lb::DevDesc));
+            off += padded(descs[gi].size() * sizeof(lb::DevDesc));
+            grp.g.tiles = reinterpret_cast<const lb::TileRef *>(dev + off);
+            std::memcpy(host + off, tiles[gi].data(), tiles[gi].size() * sizeof(lb::TileRef));
+            off += padded(tiles[gi].size() * sizeof(lb::TileRef));
+            grp.lds = lds[gi];
+            groups.push_back(grp);
+        }
+    }
+};
+
+// Validate a host work list and plan its launches (no device memory is touched).
+lb_status batch_plan(const char *fn, const lb_matvec_desc *list, int32_t n, BatchPlan &plan)
 {
-    const char *fn = "lowbit_batch_create";
-    if (!out)
-        return fail(LB_EINVAL, fn, "null output pointer");
-    *out = nullptr;
     if (!list || n < 1)
         return fail(LB_EINVAL, fn, "empty or null work list");
     for (int32_t i = 0; i < n; i++) {
@@ -470,12 +533,6 @@ static lb_status batch_create(const lb_matvec_desc *list, int32_t n, lb_batch **
         return st;
 
     // one launch group per (weight format, kernel configuration) present, products in list order
-    struct Key {
-        int fmt, cfg, qin;
-    };
-    std::vector<Key> keys;
-    std::vector<std::vector<lb::DevDesc>> descs;
-    std::vector<size_t> lds;
     for (int32_t i = 0; i < n; i++) {
         const lb_matvec_desc &d = list[i];
         if (d.N == 0)
@@ -483,12 +540,13 @@ static lb_status batch_create(const lb_matvec_desc *list, int32_t n, lb_batch **
         const int cfg = lb::matvec_config(d.fmt, d.K);
         const int qin = d.afmt == LB_ACT_F32_Q8_0 ? 1 : 0;
         size_t gi = 0;
-        while (gi < keys.size() && !(keys[gi].fmt == d.fmt && keys[gi].cfg == cfg && keys[gi].qin == qin))
+        while (gi < plan.keys.size() &&
+               !(plan.keys[gi].fmt == d.fmt && plan.keys[gi].cfg == cfg && plan.keys[gi].qin == qin))
             gi++;
-        if (gi == keys.size()) {
-            keys.push_back({d.fmt, cfg, qin});
-            descs.emplace_back();
-            lds.push_back(0);
+        if (gi == plan.keys.size()) {
+            plan.keys.push_back({d.fmt, cfg, qin});
+            plan.descs.emplace_back();
+            plan.lds.push_back(0);
         }
         lb::DevDesc dd;
         dd.W = static_cast<const uint8_t *>(d.W);
@@ -501,57 +559,62 @@ static lb_status batch_create(const lb_matvec_desc *list, int32_t n, lb_batch **
         dd.cfg = cfg;
         dd.tile_rows = 0; // set by the tile plan
         dd.x = qin ? d.x : nullptr;
-        descs[gi].push_back(dd);
-        lds[gi] = std::max(lds[gi], (size_t)lb::matvec_stage_bytes(d.fmt, d.K) +
-                                        (qin ? (size_t)lb::q8_0_lds_bytes(d.K) : 0));
+        plan.descs[gi].push_back(dd);
+        plan.lds[gi] = std::max(plan.lds[gi], (size_t)lb::matvec_stage_bytes(d.fmt, d.K) +
+                                                  (qin ? (size_t)lb::q8_0_lds_bytes(d.K) : 0));
     }
-    int device = 0, cus = 0;
-    hipGetDevice(&device);
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess || cus < 1)
+    int cus = 0;
+    (void)hipGetDevice(&plan.device); // succeeded in check_device
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, plan.device) != hipSuccess || cus < 1)
         cus = 1;
-    std::vector<std::vector<lb::TileRef>> tiles(keys.size());
-    std::vector<int> full(keys.size(), 1);
-    for (size_t gi = 0; gi < keys.size(); gi++) {
-        for (const lb::DevDesc &dd : descs[gi])
-            full[gi] &= lb::matvec_config_full(keys[gi].fmt, keys[gi].cfg, dd.K) ? 1 : 0;
+    plan.tiles.resize(plan.keys.size());
+    plan.full.assign(plan.keys.size(), 1);
+    for (size_t gi = 0; gi < plan.keys.size(); gi++) {
+        const BatchPlan::Key &k = plan.keys[gi];
+        for (const lb::DevDesc &dd : plan.descs[gi])
+            plan.full[gi] &= lb::matvec_config_full(k.fmt, k.cfg, dd.K) ? 1 : 0;
         const int64_t slots =
-            (int64_t)cus * lb::matvec_batched_blocks_per_cu(keys[gi].fmt, keys[gi].cfg, full[gi] != 0,
-                                                            keys[gi].qin != 0, lds[gi]);
-        plan_tiles(keys[gi].fmt, keys[gi].cfg, descs[gi], slots, tiles[gi]);
+            (int64_t)cus * lb::matvec_batched_blocks_per_cu(k.fmt, k.cfg, plan.full[gi] != 0, k.qin != 0, plan.lds[gi]);
+        plan_tiles(k.fmt, k.cfg, plan.descs[gi], slots, plan.tiles[gi]);
     }
-    size_t bytes = 256;
-    for (size_t gi = 0; gi < keys.size(); gi++)
-        bytes += (descs[gi].size() * sizeof(lb::DevDesc) + 255) / 256 * 256 +
-                 (tiles[gi].size() * sizeof(lb::TileRef) + 255) / 256 * 256;
+    return LB_OK;
+}
+
+lb_status launch_groups(const char *fn, const std::vector<lb_batch::Group> &groups, hipStream_t s)
+{
+    for (const auto &grp : groups) {
+        hipError_t e = lb::launch_matvec_batched(grp.g, s, grp.lds);
+        if (e != hipSuccess)
+            return hip_fail(fn, e);
+    }
+    return LB_OK;
+}
+
+} // namespace
+
+static lb_status batch_create(const lb_matvec_desc *list, int32_t n, lb_batch **out)
+{
+    const char *fn = "lowbit_batch_create";
+    if (!out)
+        return fail(LB_EINVAL, fn, "null output pointer");
+    *out = nullptr;
+    BatchPlan plan;
+    lb_status st = batch_plan(fn, list, n, plan);
+    if (st != LB_OK)
+        return st;
+    const size_t bytes = std::max<size_t>(plan.table_bytes(), 256);
+    std::vector<char> host(bytes);
     std::unique_ptr<lb_batch> b(new lb_batch());
-    b->device = device;
-    b->groups.reserve(keys.size()); // nothing below allocates host memory once the device memory is held
+    b->device = plan.device;
+    b->groups.reserve(plan.keys.size()); // nothing below allocates host memory once the device memory is held
     hipError_t e = hipMalloc(&b->dev, bytes);
     if (e != hipSuccess)
         return hip_fail(fn, e);
-    size_t off = 0;
-    char *base = static_cast<char *>(b->dev);
-    for (size_t gi = 0; gi < keys.size(); gi++) {
-        lb_batch::Group grp;
-        grp.g.fmt = keys[gi].fmt;
-        grp.g.cfg_a = keys[gi].cfg;
-        grp.g.full = full[gi];
-        grp.g.qin = keys[gi].qin;
-        grp.g.ntiles = (int32_t)tiles[gi].size();
-        grp.g.desc = reinterpret_cast<const lb::DevDesc *>(base + off);
-        e = hipMemcpy(base + off, descs[gi].data(), descs[gi].size() * sizeof(lb::DevDesc), hipMemcpyHostToDevice);
-        off += (descs[gi].size() * sizeof(lb::DevDesc) + 255) / 256 * 256;
-        if (e == hipSuccess) {
-            grp.g.tiles = reinterpret_cast<const lb::TileRef *>(base + off);
-            e = hipMemcpy(base + off, tiles[gi].data(), tiles[gi].size() * sizeof(lb::TileRef), hipMemcpyHostToDevice);
-            off += (tiles[gi].size() * sizeof(lb::TileRef) + 255) / 256 * 256;
-        }
-        if (e != hipSuccess) {
-            (void)hipFree(b->dev);
-            return hip_fail(fn, e);
-        }
-        grp.lds = lds[gi];
-        b->groups.push_back(grp);
+    plan.emit(host.data(), static_cast<char *>(b->dev), b->groups);
+    e = hipMemcpy(b->dev, host.data(), bytes, hipMemcpyHostToDevice);
+    if (e != hipSuccess) {
+        (void)hipFree(b->dev);
+        return hip_fail(fn, e);
     }
     *out = b.release();
     return LB_OK;
@@ -576,15 +639,10 @@ lb_status lowbit_matvec_batched(const lb_batch *b, hipStream_t s)
     if (st != LB_OK)
         return st;
     int dev = -1;
-    hipGetDevice(&dev);
+    (void)hipGetDevice(&dev); // succeeded in check_device
     if (dev != b->device)
         return fail(LB_EINVAL, fn, "the batch was created on another device");
-    for (const auto &grp : b->groups) {
-        hipError_t e = lb::launch_matvec_batched(grp.g, s, grp.lds);
-        if (e != hipSuccess)
-            return hip_fail(fn, e);
-    }
-    return LB_OK;
+    return launch_groups(fn, b->groups, s);
 }
 
 void lowbit_batch_destroy(lb_batch *b)

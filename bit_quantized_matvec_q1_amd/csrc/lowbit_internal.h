@@ -94,6 +94,8 @@ bool matvec_supported_k(int fmt, int64_t K);
 hipError_t launch_gemm(int fmt, const uint8_t *W, int64_t N, int64_t K, float w_scale, const int8_t *Xq,
                        const void *Xscale, int64_t M, float *Y, int32_t *sums, hipStream_t s);
 
+hipError_t launch_read_probe(const void *buf, int64_t nbytes, uint32_t *sink, hipStream_t s);
+
 hipError_t launch_head(const uint16_t *W, int64_t N, int64_t K, const float *x, float *y, hipStream_t s);
 hipError_t launch_head_i8(const int8_t *W, const float *sw, int64_t N, int64_t K, const float *x, float *y,
                           hipStream_t s);

@@ -42,6 +42,7 @@ SIGNATURES = {
     "lowbit_batch_create": (_I, [_P, ctypes.c_int32, _P]),
     "lowbit_matvec_batched": (_I, [_P, _P]),
     "lowbit_batch_destroy": (None, [_P]),
+    "lowbit_read_probe": (_I, [_P, _I64, _P, _P]),
 }
 for _name, (_res, _args) in SIGNATURES.items():
     _f = getattr(lib, _name)
@@ -71,8 +72,9 @@ class lb_matvec_desc(ctypes.Structure):
 
 
 def _ptr(t):
-    """A device tensor's address (ints pass through as raw addresses).  Host tensors and strided views are
-    refused: the kernels take dense device buffers, and a host address in a kernel is a memory fault."""
+    """A device tensor's address (ints pass through as raw addresses, unchecked).  Host tensors and strided
+    views are refused: the kernels take dense device buffers, and a host address in a kernel is a memory
+    fault."""
     if t is None:
         return None
     if isinstance(t, int):
@@ -82,6 +84,56 @@ def _ptr(t):
     if not t.is_contiguous():
         raise ValueError("contiguous tensor required (the C ABI takes dense row-major buffers)")
     return t.data_ptr()
+
+
+_F16_BITS = (torch.uint16, torch.int16, torch.float16)  # binary16 scales travel as their 16-bit patterns
+_BF16_BITS = (torch.uint16, torch.int16, torch.bfloat16)
+
+
+def _check_arg(t, name, count, dtypes=None):
+    """Check that tensor t holds at least `count` elements of one of `dtypes` (or, with dtypes None, at
+    least `count` bytes of any dtype).  The kernels read and write exactly the extents the sizes imply, so
+    a short buffer would be a read or write past its end: refused with ValueError.  None and raw int
+    addresses are not checked (raw addresses are the caller's responsibility)."""
+    if t is None or isinstance(t, int):
+        return
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name}: a torch tensor, an int address or None is required")
+    if dtypes is not None and t.dtype not in dtypes:
+        raise ValueError(f"{name}: dtype {t.dtype} not accepted (expected one of {[str(d) for d in dtypes]})")
+    have = t.numel() if dtypes is not None else t.numel() * t.element_size()
+    if count > 0 and have < count:
+        unit = "elements" if dtypes is not None else "bytes"
+        raise ValueError(f"{name}: needs at least {count} {unit}, has {have}")
+
+
+def _args(*specs):
+    """Addresses of the arguments (t, name, count[, dtypes]) after checking every one of them: all sizes and
+    dtypes first, then the device and layout checks of _ptr."""
+    for spec in specs:
+        _check_arg(*spec)
+    return [_ptr(spec[0]) for spec in specs]
+
+
+def _pos(*vals):
+    """Sizes as the C ABI sees them, for the extents checks: negative ones are left for the library to refuse
+    (LB_ESHAPE), and a product with no rows (any size 0 but K) touches no buffer, so all extents are 0."""
+    v = [max(int(x), 0) for x in vals]
+    if len(v) > 1 and (v[0] == 0 or (len(v) > 2 and v[2] == 0)):  # (N, K[, M]): N == 0 or M == 0
+        return [0] * len(v)
+    return v
+
+
+def _wbytes(fmt, N, K):
+    n = lib.lowbit_weight_bytes(fmt, N, K)
+    return max(n, 0)
+
+
+def _scale_spec(t, name, afmt, M, K):
+    """Activation scales: binary16 [M][K/32] for q8_0, fp32 [M] for per-row int8."""
+    if afmt == ACT_I8_ROW:
+        return (t, name, M, (torch.float32,))
+    return (t, name, M * (K // 32), _F16_BITS)
 
 
 def _stream(stream, *tensors):
@@ -103,51 +155,80 @@ def lowbit_weight_bytes(fmt: int, N: int, K: int) -> int:
 
 
 def lowbit_pack_weights(fmt, blocks, N, K, packed, stream=None):
-    _check(lib.lowbit_pack_weights(fmt, _ptr(blocks), N, K, _ptr(packed), _stream(stream, packed)),
-           "lowbit_pack_weights")
+    nb = _wbytes(fmt, N, K)  # the ggml block stream and the device layout have the same byte count
+    pb, pp = _args((blocks, "blocks", nb), (packed, "packed", nb))
+    _check(lib.lowbit_pack_weights(fmt, pb, N, K, pp, _stream(stream, packed)), "lowbit_pack_weights")
 
 
 def lowbit_unpack_weights(fmt, packed, N, K, blocks, stream=None):
-    _check(lib.lowbit_unpack_weights(fmt, _ptr(packed), N, K, _ptr(blocks), _stream(stream, packed)),
-           "lowbit_unpack_weights")
+    nb = _wbytes(fmt, N, K)
+    pp, pb = _args((packed, "packed", nb), (blocks, "blocks", nb))
+    _check(lib.lowbit_unpack_weights(fmt, pp, N, K, pb, _stream(stream, packed)), "lowbit_unpack_weights")
 
 
 def lowbit_quantize_act(afmt, x, M, K, xq, xscale, stream=None):
-    _check(lib.lowbit_quantize_act(afmt, _ptr(x), M, K, _ptr(xq), _ptr(xscale), _stream(stream, x)),
-           "lowbit_quantize_act")
+    m, k = _pos(M, K)
+    px, pq, ps = _args((x, "x", m * k, (torch.float32,)), (xq, "xq", m * k, (torch.int8,)),
+                       _scale_spec(xscale, "xscale", afmt, m, k))
+    _check(lib.lowbit_quantize_act(afmt, px, M, K, pq, ps, _stream(stream, x)), "lowbit_quantize_act")
 
 
 def lowbit_matvec(fmt, W, N, K, w_tensor_scale, afmt, xq, xscale, y, stream=None):
-    _check(lib.lowbit_matvec(fmt, _ptr(W), N, K, float(w_tensor_scale), afmt, _ptr(xq), _ptr(xscale), _ptr(y),
-                             _stream(stream, y)), "lowbit_matvec")
+    n, k = _pos(N, K)
+    pw, pq, ps, py = _args((W, "W", _wbytes(fmt, n, k)), (xq, "xq", k, (torch.int8,)),
+                           _scale_spec(xscale, "xscale", afmt, 1, k), (y, "y", n, (torch.float32,)))
+    _check(lib.lowbit_matvec(fmt, pw, N, K, float(w_tensor_scale), afmt, pq, ps, py, _stream(stream, y)),
+           "lowbit_matvec")
 
 
 def lowbit_gemm(fmt, W, N, K, w_tensor_scale, afmt, Xq, Xscale, M, Y, stream=None):
-    _check(lib.lowbit_gemm(fmt, _ptr(W), N, K, float(w_tensor_scale), afmt, _ptr(Xq), _ptr(Xscale), M, _ptr(Y),
-                           _stream(stream, Y)), "lowbit_gemm")
+    n, k, m = _pos(N, K, M)
+    pw, pq, ps, py = _args((W, "W", _wbytes(fmt, n, k)), (Xq, "Xq", m * k, (torch.int8,)),
+                           _scale_spec(Xscale, "Xscale", afmt, m, k), (Y, "Y", m * n, (torch.float32,)))
+    _check(lib.lowbit_gemm(fmt, pw, N, K, float(w_tensor_scale), afmt, pq, ps, M, py, _stream(stream, Y)),
+           "lowbit_gemm")
 
 
 def lowbit_block_sums(fmt, W, N, K, afmt, Xq, Xscale, M, sums, stream=None):
-    _check(lib.lowbit_block_sums(fmt, _ptr(W), N, K, afmt, _ptr(Xq), _ptr(Xscale), M, _ptr(sums),
-                                 _stream(stream, sums)), "lowbit_block_sums")
+    n, k, m = _pos(N, K, M)
+    per_row = fmt in (TERNARY_PLANAR, TERNARY_B3)  # one sum per row; else one per 32-block of K
+    pw, pq, ps, pz = _args((W, "W", _wbytes(fmt, n, k)), (Xq, "Xq", m * k, (torch.int8,)),
+                           _scale_spec(Xscale, "Xscale", afmt, m, k),
+                           (sums, "sums", m * n * (1 if per_row else k // 32), (torch.int32,)))
+    _check(lib.lowbit_block_sums(fmt, pw, N, K, afmt, pq, ps, M, pz, _stream(stream, sums)), "lowbit_block_sums")
 
 
 def dense_head_matvec(W, N, K, x, y, stream=None):
-    _check(lib.dense_head_matvec(_ptr(W), N, K, _ptr(x), _ptr(y), _stream(stream, y)), "dense_head_matvec")
+    n, k = _pos(N, K)
+    pw, px, py = _args((W, "W", n * k, _BF16_BITS), (x, "x", k, (torch.float32,)), (y, "y", n, (torch.float32,)))
+    _check(lib.dense_head_matvec(pw, N, K, px, py, _stream(stream, y)), "dense_head_matvec")
 
 
 def lowbit_matvec_popcount(W, N, K, w_tensor_scale, xq, xscale, y, row_sums=None, stream=None):
-    _check(lib.lowbit_matvec_popcount(_ptr(W), N, K, float(w_tensor_scale), _ptr(xq), _ptr(xscale), _ptr(y),
-                                      _ptr(row_sums), _stream(stream, xq)), "lowbit_matvec_popcount")
+    n, k = _pos(N, K)
+    pw, pq, ps, py, pr = _args((W, "W", _wbytes(TERNARY_PLANAR, n, k)), (xq, "xq", k, (torch.int8,)),
+                               (xscale, "xscale", 1, (torch.float32,)), (y, "y", n, (torch.float32,)),
+                               (row_sums, "row_sums", n, (torch.int32,)))
+    _check(lib.lowbit_matvec_popcount(pw, N, K, float(w_tensor_scale), pq, ps, py, pr, _stream(stream, xq)),
+           "lowbit_matvec_popcount")
 
 
 def dense_head_matvec_i8(W, row_scale, N, K, x, y, stream=None):
-    _check(lib.dense_head_matvec_i8(_ptr(W), _ptr(row_scale), N, K, _ptr(x), _ptr(y), _stream(stream, y)),
-           "dense_head_matvec_i8")
+    n, k = _pos(N, K)
+    pw, pr, px, py = _args((W, "W", n * k, (torch.int8,)), (row_scale, "row_scale", n, (torch.float32,)),
+                           (x, "x", k, (torch.float32,)), (y, "y", n, (torch.float32,)))
+    _check(lib.dense_head_matvec_i8(pw, pr, N, K, px, py, _stream(stream, y)), "dense_head_matvec_i8")
+
+
+def lowbit_read_probe(buf, nbytes, sink, stream=None):
+    pb, ps = _args((buf, "buf", nbytes), (sink, "sink", 65536, (torch.int32, torch.uint32)))
+    _check(lib.lowbit_read_probe(pb, nbytes, ps, _stream(stream, buf)), "lowbit_read_probe")
 
 
 class Batch:
-    """A work list of decode products prepared once (lowbit_batch_create) and launched by run()."""
+    """A work list of decode products prepared once (lowbit_batch_create) and launched by run().  The batch
+    holds the tensors its descriptors point to until close(), so none of them can be freed (and its memory
+    handed to another tensor) while the batch can still write into it."""
 
     def __init__(self, descs):
         arr = (lb_matvec_desc * len(descs))(*descs)
@@ -155,8 +236,11 @@ class Batch:
         _check(lib.lowbit_batch_create(ctypes.cast(arr, ctypes.c_void_p), len(descs), ctypes.byref(handle)),
                "lowbit_batch_create")
         self._h = handle
+        self._keep = [getattr(d, "_tensors", ()) for d in descs]
 
     def run(self, stream=None):
+        if not self._h:
+            raise ValueError("batch is closed")
         s = _stream(stream) if stream is not None else torch.cuda.current_stream().cuda_stream
         _check(lib.lowbit_matvec_batched(self._h, s), "lowbit_matvec_batched")
 
@@ -164,6 +248,7 @@ class Batch:
         if self._h:
             lib.lowbit_batch_destroy(self._h)
             self._h = None
+        self._keep = []
 
     def __del__(self):
         try:
@@ -173,8 +258,20 @@ class Batch:
 
 
 def desc(fmt, W, N, K, xq, xscale, y, w_tensor_scale=1.0, afmt=None, x=None) -> lb_matvec_desc:
-    """One work-list entry.  With x (fp32 activations) and afmt ACT_F32_Q8_0 the product quantises x to
-    q8_0 in its own launch; xq and xscale are then ignored (pass None)."""
+    """One work-list entry, its buffers checked against the sizes like lowbit_matvec's.  With x (fp32
+    activations) and afmt ACT_F32_Q8_0 the product quantises x to q8_0 in its own launch; xq and xscale
+    are then ignored (pass None).  The entry keeps references to its tensors (a Batch built from it holds
+    them)."""
     if afmt is None:
         afmt = ACT_F32_Q8_0 if x is not None else ACT_I8_ROW if fmt in (TERNARY_PLANAR, TERNARY_B3) else ACT_Q8_0
-    return lb_matvec_desc(fmt, afmt, N, K, _ptr(W), float(w_tensor_scale), _ptr(xq), _ptr(xscale), _ptr(y), _ptr(x))
+    n, k = _pos(N, K)
+    if afmt == ACT_F32_Q8_0:
+        pw, py, px = _args((W, "W", _wbytes(fmt, n, k)), (y, "y", n, (torch.float32,)), (x, "x", k, (torch.float32,)))
+        pq, ps = _ptr(xq), _ptr(xscale)
+    else:
+        pw, py, pq, ps = _args((W, "W", _wbytes(fmt, n, k)), (y, "y", n, (torch.float32,)),
+                               (xq, "xq", k, (torch.int8,)), _scale_spec(xscale, "xscale", afmt, 1, k))
+        px = _ptr(x)
+    d = lb_matvec_desc(fmt, afmt, N, K, pw, float(w_tensor_scale), pq, ps, py, px)
+    d._tensors = tuple(t for t in (W, xq, xscale, y, x) if isinstance(t, torch.Tensor))
+    return d

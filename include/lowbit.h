@@ -219,6 +219,16 @@ lb_status lowbit_batch_create(const lb_matvec_desc *list, int32_t n, lb_batch **
 lb_status lowbit_matvec_batched(const lb_batch *b, hipStream_t s);
 void lowbit_batch_destroy(lb_batch *b);
 
+/*
+ * Measurement helper, not a product: a streaming read of `nbytes` (a multiple of 16, 16-byte aligned) of
+ * device memory by 16-byte non-temporal loads, the access pattern of the decode kernels' weight stream,
+ * so its rate bounds theirs (tritium "Architecture", section 3: the roofline is measured with a
+ * streaming-read probe in the same run).  `sink` (device uint32, at least 65536 entries, 4-byte aligned) is
+ * written only when a workgroup's checksum of the bytes equals a fixed constant, so the loads cannot be
+ * removed and almost nothing is written.
+ */
+lb_status lowbit_read_probe(const void *buf, int64_t nbytes, uint32_t *sink, hipStream_t s);
+
 #ifdef __cplusplus
 }
 #endif

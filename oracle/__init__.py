@@ -24,15 +24,28 @@ Q1_0, Q2_0_G64, TERNARY_PLANAR, Q8_0, TERNARY_B3 = 1, 2, 3, 4, 5
 QK8 = 32
 
 CFLAGS = ["-O2", "-std=c99", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared", "-Wall"]
+# LOWBIT_ORACLE_SANITIZE=1: a separate build with AddressSanitizer and UBSan (any report aborts the run).
+# Python must then load the ASan runtime first:
+#   LOWBIT_ORACLE_SANITIZE=1 LD_PRELOAD=$(gcc -print-file-name=libasan.so) ASAN_OPTIONS=detect_leaks=0 \
+#       python -m pytest tests/test_oracle_formats.py tests/test_oracle_quant.py \
+#       tests/test_oracle_products.py tests/test_oracle_b3.py -q
+SANITIZE_FLAGS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined", "-fno-omit-frame-pointer", "-g"]
+
+
+def _sanitized() -> bool:
+    return os.environ.get("LOWBIT_ORACLE_SANITIZE", "") not in ("", "0")
 
 
 def build(force: bool = False) -> str:
     """Compile the oracle with gcc (a few seconds).  Called by __graft_entry__.build() and on first use."""
-    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
-        tmp = _LIB + f".tmp{os.getpid()}"
-        subprocess.run(["gcc", *CFLAGS, _SRC, "-o", tmp, "-lm"], check=True)
-        os.replace(tmp, _LIB)
-    return _LIB
+    lib_path, flags = _LIB, CFLAGS
+    if _sanitized():
+        lib_path, flags = _LIB.replace(".so", "_san.so"), CFLAGS + SANITIZE_FLAGS
+    if force or not os.path.exists(lib_path) or os.path.getmtime(lib_path) < os.path.getmtime(_SRC):
+        tmp = lib_path + f".tmp{os.getpid()}"
+        subprocess.run(["gcc", *flags, _SRC, "-o", tmp, "-lm"], check=True)
+        os.replace(tmp, lib_path)
+    return lib_path
 
 
 _lib = None

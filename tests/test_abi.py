@@ -151,3 +151,58 @@ def test_binding_refuses_host_tensors():
     host = torch.zeros(64, dtype=torch.int8)
     with pytest.raises(ValueError, match="device tensor required"):
         L.lowbit_matvec(L.Q2_0_G64, A16, 8, 64, 1.0, L.ACT_Q8_0, host, A16, A16)
+
+
+def test_binding_checks_sizes_and_dtypes():
+    # a buffer shorter than the sizes imply would be read or written past its end by the kernels: the
+    # binding refuses it (ValueError) before the C call, as it does a wrong dtype; these checks come before
+    # the device check, so host tensors exercise them without a GPU
+    import torch
+
+    N, K = 8, 128
+    W = torch.zeros(L.lowbit_weight_bytes(L.Q2_0_G64, N, K), dtype=torch.uint8)
+    xq = torch.zeros(K, dtype=torch.int8)
+    xs = torch.zeros(K // 32, dtype=torch.uint16)
+    y = torch.zeros(N, dtype=torch.float32)
+    with pytest.raises(ValueError, match="W: needs at least"):
+        L.lowbit_matvec(L.Q2_0_G64, W[:-1], N, K, 1.0, L.ACT_Q8_0, xq, xs, y)
+    with pytest.raises(ValueError, match="xq: needs at least"):
+        L.lowbit_matvec(L.Q2_0_G64, W, N, K, 1.0, L.ACT_Q8_0, xq[:64], xs, y)
+    with pytest.raises(ValueError, match="xscale: needs at least"):
+        L.lowbit_matvec(L.Q2_0_G64, W, N, K, 1.0, L.ACT_Q8_0, xq, xs[:3], y)
+    with pytest.raises(ValueError, match="y: needs at least"):
+        L.lowbit_matvec(L.Q2_0_G64, W, N, K, 1.0, L.ACT_Q8_0, xq, xs, y[:7])
+    with pytest.raises(ValueError, match="y: dtype"):
+        L.lowbit_matvec(L.Q2_0_G64, W, N, K, 1.0, L.ACT_Q8_0, xq, xs, y.double())
+    with pytest.raises(ValueError, match="xscale: dtype"):  # per-row int8 activations take one fp32 scale
+        L.lowbit_matvec(L.TERNARY_PLANAR, W, N, K, 1.0, L.ACT_I8_ROW, xq, xs, y)
+    with pytest.raises(ValueError, match="Y: needs at least"):
+        L.lowbit_gemm(L.Q2_0_G64, W, N, K, 1.0, L.ACT_Q8_0, xq.repeat(2), xs.repeat(2), 2, y)
+    with pytest.raises(ValueError, match="sums: needs at least"):  # [M][N][K/32] for the ggml formats
+        L.lowbit_block_sums(L.Q2_0_G64, W, N, K, L.ACT_Q8_0, xq, xs, 1, torch.zeros(N, dtype=torch.int32))
+    with pytest.raises(ValueError, match="xq: needs at least"):
+        L.lowbit_quantize_act(L.ACT_Q8_0, torch.zeros(2 * K), 2, K, xq, xs.repeat(2))
+    with pytest.raises(ValueError, match="W: needs at least"):
+        L.dense_head_matvec(torch.zeros(N * K - 1, dtype=torch.int16), N, K, torch.zeros(K), y)
+    with pytest.raises(ValueError, match="row_scale: needs at least"):
+        L.dense_head_matvec_i8(torch.zeros(N * K, dtype=torch.int8), torch.zeros(N - 1), N, K, torch.zeros(K), y)
+    with pytest.raises(ValueError, match="packed: needs at least"):
+        L.lowbit_pack_weights(L.Q1_0, W, N, K, W[:16])
+    with pytest.raises(ValueError, match="x: needs at least"):
+        L.desc(L.Q2_0_G64, W, N, K, None, None, y, x=torch.zeros(K - 32))
+    # sizes that fit get as far as the device check: a host tensor is refused there
+    with pytest.raises(ValueError, match="device tensor required"):
+        L.lowbit_matvec(L.Q2_0_G64, W, N, K, 1.0, L.ACT_Q8_0, xq, xs, y)
+
+
+def test_desc_keeps_its_tensors():
+    # a batch holds the tensors of its entries, so none can be freed and reused while it can write them
+    import torch
+
+    N, K = 8, 128
+    W = torch.zeros(L.lowbit_weight_bytes(L.Q2_0_G64, N, K), dtype=torch.uint8)
+    y = torch.zeros(N)
+    with pytest.raises(ValueError, match="device tensor required"):
+        L.desc(L.Q2_0_G64, W, N, K, torch.zeros(K, dtype=torch.int8), torch.zeros(K // 32, dtype=torch.uint16), y)
+    d = L.desc(L.Q2_0_G64, 1 << 12, N, K, 1 << 12, 1 << 12, 1 << 12)  # raw addresses pass through
+    assert d._tensors == ()
