@@ -590,6 +590,68 @@ lb_status launch_groups(const char *fn, const std::vector<lb_batch::Group> &grou
     return LB_OK;
 }
 
+// ---- the allocation-free variant: its tables live in a fixed device array -------------------------
+
+// The work-list tables of lowbit_matvec_batched_static, one copy per GPU (each device holds its own
+// instance of a __device__ array).  Host code never names it as an address: its device address is looked
+// up once per device with hipGetSymbolAddress.
+static __device__ __align__(256) unsigned char scratch[LB_STATIC_TABLE_BYTES];
+
+std::atomic<void *> g_scratch_ptr[kMaxDevices];
+std::atomic<int> g_scratch_state[kMaxDevices]; // 0 not looked up, 1 looked up, 2 lookup failed
+
+lb_status scratch_address(const char *fn, int dev, char **out)
+{
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(LB_EINVAL, fn, "device index out of range");
+    int st = g_scratch_state[dev].load(std::memory_order_acquire);
+    if (st == 0) {
+        void *ptr = nullptr;
+        hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)); // the current device's copy
+        if (e != hipSuccess || ptr == nullptr) {
+            (void)hipGetLastError();
+            g_scratch_state[dev].store(2, std::memory_order_release);
+            return hip_fail(fn, e == hipSuccess ? hipErrorInvalidSymbol : e);
+        }
+        g_scratch_ptr[dev].store(ptr, std::memory_order_relaxed);
+        g_scratch_state[dev].store(1, std::memory_order_release);
+        st = 1;
+    }
+    if (st != 1)
+        return fail(LB_EDEVICE, fn, "the device address of the static table could not be found");
+    *out = static_cast<char *>(g_scratch_ptr[dev].load(std::memory_order_relaxed));
+    return LB_OK;
+}
+
+lb_status batched_static(const lb_matvec_desc *list, int32_t n, hipStream_t s)
+{
+    const char *fn = "lowbit_matvec_batched_static";
+    BatchPlan plan;
+    lb_status st = batch_plan(fn, list, n, plan);
+    if (st != LB_OK)
+        return st;
+    const size_t bytes = plan.table_bytes();
+    if (bytes > (size_t)LB_STATIC_TABLE_BYTES) {
+        char what[160];
+        std::snprintf(what, sizeof(what), "the work list's tables need %zu bytes, above the static table's %d "
+                                          "(use lowbit_batch_create)", bytes, (int)LB_STATIC_TABLE_BYTES);
+        return fail(LB_ESHAPE, fn, what);
+    }
+    char *dev = nullptr;
+    st = scratch_address(fn, plan.device, &dev);
+    if (st != LB_OK)
+        return st;
+    std::vector<char> host(bytes);
+    std::vector<lb_batch::Group> groups;
+    plan.emit(host.data(), dev, groups);
+    // ordered on s after every earlier use of the table on s (a pageable source is staged by the runtime
+    // before the call returns, so `host` may go away afterwards)
+    hipError_t e = hipMemcpyAsync(dev, host.data(), bytes, hipMemcpyHostToDevice, s);
+    if (e != hipSuccess)
+        return hip_fail(fn, e);
+    return launch_groups(fn, groups, s);
+}
+
 } // namespace
 
 static lb_status batch_create(const lb_matvec_desc *list, int32_t n, lb_batch **out)
@@ -643,6 +705,16 @@ lb_status lowbit_matvec_batched(const lb_batch *b, hipStream_t s)
     if (dev != b->device)
         return fail(LB_EINVAL, fn, "the batch was created on another device");
     return launch_groups(fn, b->groups, s);
+}
+
+lb_status lowbit_matvec_batched_static(const lb_matvec_desc *list, int32_t n, hipStream_t s)
+{
+    // the plan is built in host containers: an allocation failure is reported, not thrown through C
+    try {
+        return batched_static(list, n, s);
+    } catch (const std::bad_alloc &) {
+        return fail(LB_ENOMEM, "lowbit_matvec_batched_static", "host allocation failed while planning the batch");
+    }
 }
 
 void lowbit_batch_destroy(lb_batch *b)

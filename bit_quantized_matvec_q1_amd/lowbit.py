@@ -42,6 +42,7 @@ SIGNATURES = {
     "lowbit_batch_create": (_I, [_P, ctypes.c_int32, _P]),
     "lowbit_matvec_batched": (_I, [_P, _P]),
     "lowbit_batch_destroy": (None, [_P]),
+    "lowbit_matvec_batched_static": (_I, [_P, ctypes.c_int32, _P]),
     "lowbit_read_probe": (_I, [_P, _I64, _P, _P]),
 }
 for _name, (_res, _args) in SIGNATURES.items():

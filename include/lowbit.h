@@ -220,6 +220,25 @@ lb_status lowbit_matvec_batched(const lb_batch *b, hipStream_t s);
 void lowbit_batch_destroy(lb_batch *b);
 
 /*
+ * For callers that cannot allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the work list of lowbit_batch_create run in one call, with its
+ * descriptor and tile tables held in a fixed device array of LB_STATIC_TABLE_BYTES bytes inside the library
+ * instead of memory the library allocates.  Calls no hipMalloc / hipFree; the tile plan is built in host
+ * memory on every call.
+ *   list: HOST array of n descriptors, validated exactly as by lowbit_batch_create (same status codes);
+ *         the same products give the same kernels and bit-identical outputs as a batch of that list.
+ *   A list whose tables exceed LB_STATIC_TABLE_BYTES (64 bytes per product plus 8 per row tile: for
+ *   example 14,000 single-tile products, or 130,000 tiles -- about 32 GB of weights in 256 KiB tiles) is
+ *   refused with LB_ESHAPE before anything is enqueued.
+ * The tables are copied into the array on `s` (stream-ordered after earlier work on `s`), then the kernels
+ * run on `s`.  Every call on one GPU shares that GPU's array, which keeps the last call's tables: calls
+ * that overlap on one GPU -- on different streams, or from different host threads without ordering --
+ * race and may compute with another call's tables.  Calls queued on one stream are safe.
+ */
+#define LB_STATIC_TABLE_BYTES (1 << 20)
+lb_status lowbit_matvec_batched_static(const lb_matvec_desc *list, int32_t n, hipStream_t s);
+
+/*
  * Measurement helper, not a product: a streaming read of `nbytes` (a multiple of 16, 16-byte aligned) of
  * device memory by 16-byte non-temporal loads, the access pattern of the decode kernels' weight stream,
  * so its rate bounds theirs (tritium "Architecture", section 3: the roofline is measured with a
