@@ -41,7 +41,7 @@ constexpr int TN = 64;           // weight rows per workgroup
 constexpr int TM = 128;          // activation rows per workgroup
 constexpr int KS = 128;          // columns per K-step
 constexpr int WROW = KS / 4 + 4; // LDS dwords per unpacked weight row (padded against bank conflicts)
-constexpr int XROW = KS / 4 + 4; // LDS dwords per activation row
+constexpr int XCH = KS / 16;     // 16-byte chunks per activation tile row
 constexpr uint32_t BIAS = 0x4B400000u; // 1.5 * 2^23 as fp32 bits
 constexpr float BIASF = 12582912.0f;
 
@@ -77,17 +77,15 @@ __device__ __forceinline__ void unpack_q2_dword(uint32_t v, uint32_t *out)
     transpose4(e[0], e[1], e[2], e[3], out);
 }
 
-// What one thread carries from global memory into a K-step.  Every thread takes one share of the weight
-// tile -- Q2_0: one code dword (16 weights); Q1_0: one sign dword, of which it builds two of the four
-// activation blocks; planar: one (pos, neg) dword pair, of which it builds half -- in a.x (planar neg in
-// a.y, the weight block scale's binary16 in a.z where the thread stores it), 32 activation bytes (one
-// q8_0 block of one activation row) in b0, b1, and, for the first TM threads, the four binary16
-// activation scales of one activation row in c.
+// What one thread carries from global memory into a K-step's weight tile.  Every thread takes one share of
+// it -- Q2_0: one code dword (16 weights); Q1_0: one sign dword, of which it builds two of the four
+// activation blocks; planar: one (pos, neg) dword pair, of which it builds half; Q8_0: 16 weight bytes --
+// in a (planar neg in a.y, the weight block scale's binary16 in a.z where the thread stores it; Q8_0's in
+// ws), and, for the first TM threads, the four binary16 activation scales of one activation row in c.
 struct StepRegs {
     uint4 a;
-    v4u b0, b1; // native vectors: copied as registers, never through memory
     uint2 c;
-    uint32_t ws; // Q8_0: the binary16 scale of the thread's weight block
+    uint32_t ws;
 };
 
 // Global-address-space views: loads take a scalar base and a 32-bit per-lane offset (the ABI keeps the
@@ -96,76 +94,152 @@ typedef __attribute__((address_space(1))) const uint8_t gu8;
 typedef __attribute__((address_space(1))) const v4u gv4u;
 typedef __attribute__((address_space(1))) const uint32_t gu32;
 typedef __attribute__((address_space(1))) const uint16_t gu16;
+typedef unsigned v2u_a4 __attribute__((ext_vector_type(2), aligned(4)));
+typedef __attribute__((address_space(1))) const v2u_a4 gv2u;
+typedef __attribute__((address_space(1))) void gvoid;
+typedef __attribute__((address_space(3))) void lvoid;
+
+// Per-thread load offsets, fixed for the whole K walk: every load of a step is a per-step scalar base (the
+// tensor's address plus the step's offset, kept in scalar registers) plus one of these 32-bit lane offsets,
+// so a step's loads cost no vector arithmetic.  Rows past N or M are clamped to the last row (re-read,
+// never stored).
+struct LaneOffs {
+    uint32_t w;     // the thread's share of the weight codes (Q8_0: of the weight bytes)
+    uint32_t ws;    // its weight block scale
+    uint32_t dx;    // the four activation scales of activation row tid mod TM
+    uint32_t x[2];  // its two activation-tile slots: row offset + 16 x chunk (x_slot)
+};
+
+// Bytes a step advances each base by: weight records (16 bytes per 64 Q2_0 / planar or 128 Q1_0 weights, 32
+// per 32 Q8_0 weights), their binary16 scales, the activation scales (binary16 per 32) and the activation
+// bytes themselves.
+template <int FMT> __device__ __forceinline__ uint32_t step_wbytes(int kk)
+{
+    return FMT == LB_Q1_0 ? (uint32_t)(kk / 128) * 16u : FMT == LB_Q8_0 ? (uint32_t)kk : (uint32_t)(kk / 64) * 16u;
+}
+template <int FMT> __device__ __forceinline__ uint32_t step_sbytes(int kk)
+{
+    return FMT == LB_Q1_0 ? (uint32_t)(kk / 128) * 2u : FMT == LB_Q8_0 ? (uint32_t)(kk / 32) * 2u : (uint32_t)(kk / 64) * 2u;
+}
 
 template <int FMT>
-__device__ __forceinline__ void load_step(StepRegs &r, const uint8_t *__restrict__ W, const uint16_t *__restrict__ wsc,
-                                          int N, int K, const int8_t *__restrict__ X, const uint16_t *__restrict__ xsc,
-                                          int M, int n0, int m0, int kk, int tid)
+__device__ __forceinline__ LaneOffs lane_offsets(int N, int K, int M, int n0, int m0, int tid)
 {
-    // Every load is unconditional, its index clamped into the tensor: on a half step (the K tail) the
-    // shares past the row's end re-read its last block and are not stored.  The registers are filled
-    // straight from memory, so nothing waits on them until the step is stored.
-    const int kab = min(KS, K - kk) / QK8; // activation blocks in this step
-    // activation tile: 128 rows x kab blocks of 32 bytes; thread -> (row tid / 4, block tid % 4)
-    {
-        const int m = min(m0 + (tid >> 2), M - 1), ch = min(tid & 3, kab - 1);
-        const uint32_t xo = (uint32_t)m * (uint32_t)K + (uint32_t)(kk + 32 * ch);
-        r.b0 = *(gv4u *)((gu8 *)X + xo);
-        r.b1 = *(gv4u *)((gu8 *)X + (xo + 16u));
-    }
-    if (FMT != LB_TERNARY_PLANAR && tid < TM) { // one activation row's four block scales
-        const int mm = min(m0 + (tid & (TM - 1)), M - 1);
-        const uint32_t so = ((uint32_t)mm * (uint32_t)(K / QK8) + (uint32_t)(kk / QK8)) * 2u;
-        r.c.x = *(gu32 *)((gu8 *)xsc + so);                            // blocks 0, 1 (4-byte aligned: K / 32
-        r.c.y = *(gu32 *)((gu8 *)xsc + (so + (kab > 2 ? 4u : 0u)));    // and kk / 32 are even); 2, 3
-    }
+    LaneOffs o;
     const int row = min(n0 + (tid >> 3), N - 1), p = tid & 7;
-    if (FMT == LB_Q1_0) {
-        // one 128-weight record per row and step; thread p takes sign dword p / 2
-        const uint32_t idx = (uint32_t)row * (uint32_t)(K / 128) + (uint32_t)(kk / 128);
-        r.a.x = *(gu32 *)((gu8 *)W + (idx * 16u + 4u * (uint32_t)(p >> 1)));
-        r.a.z = *(gu16 *)((gu8 *)wsc + idx * 2u);
-    } else if (FMT == LB_Q8_0) {
-        // four 32-byte records per row (K is a whole number of steps); thread p takes half p % 2 of
-        // record p / 2, and its scale
-        const uint32_t idx = (uint32_t)row * (uint32_t)(K / 32) + (uint32_t)(kk / 32 + (p >> 1));
-        const v4u t = *(gv4u *)((gu8 *)W + (idx * 32u + 16u * (uint32_t)(p & 1)));
+    if (FMT == LB_Q1_0) { // one 128-weight record per row and step; thread p takes sign dword p / 2
+        o.w = (uint32_t)row * (uint32_t)(K / 128) * 16u + 4u * (uint32_t)(p >> 1);
+        o.ws = (uint32_t)row * (uint32_t)(K / 128) * 2u;
+    } else if (FMT == LB_Q8_0) { // four 32-byte records per row; thread p takes half p % 2 of record p / 2
+        o.w = (uint32_t)row * (uint32_t)K + 32u * (uint32_t)(p >> 1) + 16u * (uint32_t)(p & 1);
+        o.ws = ((uint32_t)row * (uint32_t)(K / 32) + (uint32_t)(p >> 1)) * 2u;
+    } else if (FMT == LB_Q2_0_G64) { // two 64-weight records per row; thread p takes dword p % 4 of record p / 4
+        o.w = ((uint32_t)row * (uint32_t)(K / 64) + (uint32_t)(p >> 2)) * 16u + 4u * (uint32_t)(p & 3);
+        o.ws = ((uint32_t)row * (uint32_t)(K / 64) + (uint32_t)(p >> 2)) * 2u;
+    } else { // two 64-column beats per row; thread p takes the (pos, neg) dword pair (p / 2) % 2 of beat p / 4
+        o.w = ((uint32_t)row * (uint32_t)(K / 64) + (uint32_t)(p >> 2)) * 16u + 4u * (uint32_t)((p >> 1) & 1);
+        o.ws = 0;
+    }
+    o.dx = (uint32_t)min(m0 + (tid & (TM - 1)), M - 1) * (uint32_t)(K / QK8) * 2u;
+    const int wave = tid >> 6, lane = tid & 63;
+#pragma unroll
+    for (int u = 0; u < 2; u++) {
+        const int slot = 128 * wave + 64 * u + lane, r = slot / XCH;
+        o.x[u] = (uint32_t)min(m0 + r, M - 1) * (uint32_t)K + 16u * (uint32_t)((slot % XCH) ^ ((r >> 1) & 7));
+    }
+    return o;
+}
+
+// One step's weight codes / scales and activation scales into registers.  A full step (128 columns) reads
+// exactly the step's blocks.  The half step that ends a Q2_0 / planar row of an odd number of 64-column
+// blocks (only one step of the walk) takes a branch whose lanes of the missing second block re-read the
+// first.  Every thread loads the activation scales of activation row tid mod TM (the first TM threads
+// store them).
+template <int FMT>
+__device__ __forceinline__ void load_step(StepRegs &r, const LaneOffs &o, const uint8_t *__restrict__ W,
+                                          const uint8_t *__restrict__ wsc, const uint8_t *__restrict__ xsc, int kk,
+                                          bool half_step, int tid)
+{
+    uint32_t ow = o.w + step_wbytes<FMT>(kk), os = o.ws + step_sbytes<FMT>(kk);
+    const uint32_t odx = o.dx + (uint32_t)(kk / QK8) * 2u;
+    if (half_step) { // uniform
+        const uint32_t second = (uint32_t)((tid >> 2) & 1); // the lane's record / beat index within the step
+        ow -= 16u * second;
+        os -= 2u * second;
+    }
+    if (FMT != LB_TERNARY_PLANAR && tid < TM) {
+        // one 8-byte load per activation row (4-byte aligned: K / 32 and kk / 32 are even); the half step has
+        // two blocks only
+        if (half_step) {
+            r.c.x = r.c.y = *(const gu32 *)((const gu8 *)xsc + odx);
+        } else {
+            const v2u_a4 t = *(const gv2u *)((const gu8 *)xsc + odx);
+            r.c.x = t.x, r.c.y = t.y;
+        }
+    }
+    if (FMT == LB_Q8_0) {
+        const v4u t = *(const gv4u *)((const gu8 *)W + ow);
         r.a = make_uint4(t.x, t.y, t.z, t.w);
-        r.ws = *(gu16 *)((gu8 *)wsc + idx * 2u);
-    } else if (FMT == LB_Q2_0_G64) {
-        // two 64-weight records per row (one on a half step); thread p takes dword p % 4 of record p / 4
-        const int bb = min(p >> 2, kab / 2 - 1), d = p & 3;
-        const uint32_t idx = (uint32_t)row * (uint32_t)(K / 64) + (uint32_t)(kk / 64 + bb);
-        r.a.x = *(gu32 *)((gu8 *)W + (idx * 16u + 4u * (uint32_t)d));
-        r.a.z = *(gu16 *)((gu8 *)wsc + idx * 2u);
+        r.ws = *(const gu16 *)((const gu8 *)wsc + os);
+    } else if (FMT == LB_TERNARY_PLANAR) {
+        r.a.x = *(const gu32 *)((const gu8 *)W + ow);        // pos
+        r.a.y = *(const gu32 *)((const gu8 *)W + (ow + 8u)); // neg
     } else {
-        // two 64-column beats per row; thread p takes the (pos, neg) dword pair (p / 2) % 2 of beat p / 4
-        const int bb = min(p >> 2, kab / 2 - 1), hh = (p >> 1) & 1;
-        const uint32_t idx = (uint32_t)row * (uint32_t)(K / 64) + (uint32_t)(kk / 64 + bb);
-        r.a.x = *(gu32 *)((gu8 *)W + (idx * 16u + 4u * (uint32_t)hh));       // pos
-        r.a.y = *(gu32 *)((gu8 *)W + (idx * 16u + 8u + 4u * (uint32_t)hh)); // neg
+        r.a.x = *(const gu32 *)((const gu8 *)W + ow);
+        r.a.z = *(const gu16 *)((const gu8 *)wsc + os);
     }
 }
 
+// The activation tile of a step (TM rows x KS bytes) goes HBM -> LDS through the load unit, without
+// registers: one global_load_lds_dwordx4 writes lane i's 16 bytes at the wave's LDS base + 16 i, so each
+// instruction fills 64 consecutive 16-byte slots and each thread issues two.  Chunk c (16 bytes) of tile
+// row r sits in slot r * XCH + (c ^ ((r >> 1) & 7)), so the operand reads (16 lanes, one chunk of 16
+// consecutive rows each) meet 16 different bank groups; the lane that fills a slot loads the chunk that
+// belongs there.  On the half step the lanes of the chunks past K load nothing (each wave holds whole
+// rows, so every wave still issues both instructions).
+__device__ __forceinline__ int x_slot(int r, int c) { return r * XCH + (c ^ ((r >> 1) & 7)); }
+
+__device__ __forceinline__ void issue_x(uint32_t *lds_tile, const int8_t *__restrict__ X, const LaneOffs &o, int kk,
+                                       bool half_step, int wave, int lane)
+{
+#pragma unroll
+    for (int u = 0; u < 2; u++) {
+        uint32_t *dst = lds_tile + 4 * (128 * wave + 64 * u); // the wave's 64 slots
+        if (!half_step || ((64 * u + lane) % XCH ^ (((128 * wave + 64 * u + lane) / XCH >> 1) & 7)) < 4)
+            __builtin_amdgcn_global_load_lds((gvoid *)((const gu8 *)X + (o.x[u] + (uint32_t)kk)), (lvoid *)dst, 16, 0, 0);
+    }
+}
+
+// s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
+constexpr int waitcnt(int vm, int lgkm) { return (vm & 15) | (7 << 4) | ((lgkm & 15) << 8) | ((vm >> 4) << 14); }
+constexpr int wait_vmcnt(int n) { return waitcnt(n, 15); }
+constexpr int WAIT_LGKM0 = waitcnt(63, 0);
+static_assert(wait_vmcnt(0) == 0x0F70 && WAIT_LGKM0 == 0xC07F, "s_waitcnt encoding");
+
+// A workgroup barrier for the step loop.  __syncthreads() would also fence memory, which makes every thread
+// wait for all of its outstanding loads -- the activation tiles of the next steps included -- so the
+// loop takes its waits explicitly: this thread's LDS writes (lgkmcnt 0) before the barrier, and the loads a
+// step reads (a vmcnt wait at the top of the step).  The empty asm statements keep the compiler from moving
+// LDS accesses across the barrier.
+__device__ __forceinline__ void step_barrier()
+{
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(WAIT_LGKM0);
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 struct __attribute__((aligned(16))) Lds {
-    uint32_t w[2][TN * WROW];
-    uint32_t x[2][TM * XROW];
-    float dw[2][4 * TN]; // weight block scales: [block within step][row]
-    float dx[2][4 * TM]; // activation scales: [block within step][row]
+    uint32_t w[2][TN * WROW];   // unpacked int8 weight tiles, padded rows
+    float dw[2][4 * TN];        // weight block scales: [block within step][row]
+    float dx[2][4 * TM];        // activation scales: [block within step][row]
 };
+constexpr int XTILE = TM * KS / 4; // dwords of an activation tile, swizzled 16-byte chunks (x_slot)
 
 template <int FMT>
 __device__ __forceinline__ void store_step(Lds &lds, int buf, const StepRegs &r, int K, int kk, int tid)
 {
     const int kab = min(KS, K - kk) / QK8;
-    {
-        const int mr = tid >> 2, ch = tid & 3;
-        if (ch < kab) {
-            v4u *dst = reinterpret_cast<v4u *>(lds.x[buf] + mr * XROW + 8 * ch);
-            dst[0] = r.b0;
-            dst[1] = r.b1;
-        }
-    }
     if (FMT != LB_TERNARY_PLANAR && tid < TM) {
         // (on a half step the values of blocks 2 and 3 are not read)
         lds.dx[buf][0 * TM + tid] = half_bits_to_float((uint16_t)(r.c.x & 0xffffu));
@@ -225,45 +299,52 @@ __device__ __forceinline__ void store_step(Lds &lds, int buf, const StepRegs &r,
     }
 }
 
-// One wave's share of a K-step: its 32 x 32 output tile over the step's kab q8_0 blocks (4, or 2 on the
-// half step that ends a Q2_0 / planar row of an odd number of weight blocks).
-template <int FMT, bool EMIT>
-__device__ __forceinline__ void step_compute(const Lds &lds, int buf, int kab, int h, int l32, int wn, int wm, int m0,
-                                             int n0, int M, int N, int nab, int kk, float (&acc)[16], v16i &iacc,
-                                             const v16i &cbias, int32_t *__restrict__ sums)
+// One wave's share of a K-step: its 32 x 32 output tile over the step's KAB q8_0 blocks (4, or 2 on the
+// half step that ends a Q2_0 / planar row of an odd number of weight blocks).  Each block's result is
+// scaled as soon as it is ready: the other waves of the SIMD keep the vector ALU busy meanwhile.
+template <int FMT, bool EMIT, int KAB>
+__device__ __forceinline__ void step_compute(const Lds &lds, int buf, const uint32_t *xt, const uint32_t (&xb)[4], int h,
+                                             int l32, int wn, int wm, int m0, int n0, int M, int N, int nab, int kk,
+                                             float (&acc)[16], v16i &iacc, const v16i &cbias,
+                                             int32_t *__restrict__ sums)
 {
     constexpr bool PLANAR = FMT == LB_TERNARY_PLANAR;
-    // accumulator preset to the bias (else zero); exact while |isum| < 2^22 (Q8_0: at most 2^19)
-    constexpr bool BIASED = FMT == LB_Q2_0_G64 || FMT == LB_Q8_0;
     constexpr int JW = FMT == LB_Q1_0 ? 4 : FMT == LB_Q8_0 ? 1 : 2; // activation blocks per weight block
     const uint32_t *wl = lds.w[buf] + (32 * wn + l32) * WROW + 4 * h;
-    const uint32_t *xl = lds.x[buf] + (32 * wm + l32) * XROW + 4 * h;
-    float t[16];
-#pragma unroll
-    for (int j = 0; j < KS / QK8; j++) {
-        if (j >= kab) // uniform
-            break;
+    auto mfma = [&](int j, const v16i &c) {
         const uint4 a4 = *reinterpret_cast<const uint4 *>(wl + 8 * j);
-        const uint4 b4 = *reinterpret_cast<const uint4 *>(xl + 8 * j);
+        const uint4 b4 = *reinterpret_cast<const uint4 *>(xt + xb[j]); // chunk 2 j + h of the lane's row
         const v4i A = {(int)a4.x, (int)a4.y, (int)a4.z, (int)a4.w};
         const v4i B = {(int)b4.x, (int)b4.y, (int)b4.z, (int)b4.w};
-        if (PLANAR) {
-            iacc = __builtin_amdgcn_mfma_i32_32x32x32_i8(A, B, iacc, 0, 0, 0);
-            continue;
+        return __builtin_amdgcn_mfma_i32_32x32x32_i8(A, B, c, 0, 0, 0);
+    };
+    if (PLANAR) {
+#pragma unroll
+        for (int j = 0; j < KAB; j++)
+            iacc = mfma(j, iacc);
+        return;
+    }
+    // the step's activation scales of this lane's activation row
+    float dx[KAB];
+#pragma unroll
+    for (int j = 0; j < KAB; j++)
+        dx[j] = lds.dx[buf][j * TM + 32 * wm + l32];
+    // every result is read as fp32 through the bias: 1.5 * 2^23 + isum exactly (|isum| < 2^22)
+#pragma unroll
+    for (int j = 0; j < KAB; j++) {
+        const v16i Dj = mfma(j, cbias);
+        // the weight block's scales of this lane's 16 weight rows
+        float dwv[16];
+#pragma unroll
+        for (int g = 0; g < 4; g++) {
+            const float4 dw = *reinterpret_cast<const float4 *>(lds.dw[buf] + (j / JW) * TN + 32 * wn + 8 * g + 4 * h);
+            dwv[4 * g] = dw.x, dwv[4 * g + 1] = dw.y, dwv[4 * g + 2] = dw.z, dwv[4 * g + 3] = dw.w;
         }
-        const v16i D = __builtin_amdgcn_mfma_i32_32x32x32_i8(A, B, cbias, 0, 0, 0);
-        const float dx = lds.dx[buf][j * TM + 32 * wm + l32];
-        if (BIASED) {
-            const float c = -dx * BIASF; // exact: an 11-bit significand times 3 * 2^22
+        const float c = -dx[j] * BIASF; // exact: an 11-bit significand times 3 * 2^22
 #pragma unroll
-            for (int i = 0; i < 16; i++) {
-                const float v = fmaf(dx, __int_as_float(D[i]), c); // round(d_x * isum)
-                t[i] = j % JW == 0 ? v : t[i] + v;
-            }
-        } else {
-#pragma unroll
-            for (int i = 0; i < 16; i++) // (float)isum is exact: |isum| < 2^24
-                t[i] = j % JW == 0 ? dx * (float)D[i] : fmaf(dx, (float)D[i], t[i]);
+        for (int i = 0; i < 16; i++) {
+            const float v = fmaf(dx[j], __int_as_float(Dj[i]), c); // round(d_x * isum)
+            acc[i] = fmaf(dwv[i], v, acc[i]);
         }
         if (EMIT) {
             const int m = m0 + 32 * wm + l32, kb = kk / QK8 + j;
@@ -271,18 +352,7 @@ __device__ __forceinline__ void step_compute(const Lds &lds, int buf, int kab, i
             for (int i = 0; i < 16; i++) {
                 const int n = n0 + 32 * wn + 8 * (i >> 2) + 4 * h + (i & 3);
                 if (m < M && n < N)
-                    sums[((int64_t)m * N + n) * nab + kb] = BIASED ? D[i] - (int)BIAS : D[i];
-            }
-        }
-        if (j % JW == JW - 1) { // the weight block is complete
-            const int b = j / JW;
-#pragma unroll
-            for (int g = 0; g < 4; g++) {
-                const float4 dw = *reinterpret_cast<const float4 *>(lds.dw[buf] + b * TN + 32 * wn + 8 * g + 4 * h);
-                const float dwv[4] = {dw.x, dw.y, dw.z, dw.w};
-#pragma unroll
-                for (int q = 0; q < 4; q++)
-                    acc[4 * g + q] = fmaf(dwv[q], t[4 * g + q], acc[4 * g + q]);
+                    sums[((int64_t)m * N + n) * nab + kb] = Dj[i] - (int)BIAS;
             }
         }
     }
@@ -292,18 +362,20 @@ __device__ __forceinline__ void step_compute(const Lds &lds, int buf, int kab, i
 // walk alternate K-steps of the same output tile with their own LDS buffers and add their partial sums
 // at the end, so a CU holds 16 waves where the tile count alone would give it 8.
 template <int FMT, bool EMIT, int KSPLIT>
-__global__ __launch_bounds__(GT * KSPLIT, 2 * KSPLIT) void gemm_kernel(const uint8_t *__restrict__ W, int N, int K,
+__global__ __launch_bounds__(GT * KSPLIT, EMIT ? 2 * KSPLIT : 4) void gemm_kernel(const uint8_t *__restrict__ W, int N, int K,
                                                                        float w_scale, const int8_t *__restrict__ X,
                                                                        const void *__restrict__ Xscale, int M,
                                                                        float *__restrict__ Y, int32_t *__restrict__ sums,
                                                                        int ntn)
 {
     __shared__ Lds lds[KSPLIT];
+    __shared__ uint32_t xt0[KSPLIT][XTILE], xt1[KSPLIT][XTILE];
 
     constexpr bool PLANAR = FMT == LB_TERNARY_PLANAR;
     // (uniform per wave: readfirstlane keeps the step bookkeeping in scalar registers)
     const int half = KSPLIT == 1 ? 0 : __builtin_amdgcn_readfirstlane((int)threadIdx.x / GT);
-    const int tid = (int)threadIdx.x % GT, lane = tid & 63, wave = tid >> 6;
+    const int tid = (int)threadIdx.x % GT, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int h = lane >> 5, l32 = lane & 31;
     // this wave's 32 x 32 output tile inside the 64 x 128 workgroup tile
     const int wn = wave & 1, wm = wave >> 1;
@@ -311,8 +383,8 @@ __global__ __launch_bounds__(GT * KSPLIT, 2 * KSPLIT) void gemm_kernel(const uin
     const int n0 = bn * TN, m0 = bm * TM;
     const int64_t rowcode = FMT == LB_Q1_0 ? K / 8 : FMT == LB_Q8_0 ? K : K / 4; // code bytes per weight row
     const int nab = K / QK8;                                                  // activation blocks per row
-    const uint16_t *wsc = reinterpret_cast<const uint16_t *>(W + (int64_t)N * rowcode);
-    const uint16_t *xsc = reinterpret_cast<const uint16_t *>(Xscale);
+    const uint8_t *wsc = W + (int64_t)N * rowcode;
+    const uint8_t *xsc = reinterpret_cast<const uint8_t *>(Xscale);
 
     // Q2_0: 16 registers of the bias, each made opaque to the compiler: a tile it knows to be uniform it
     // rebuilds before every MFMA (16 moves each) instead of keeping it live.  Q1_0: a zero accumulator
@@ -322,7 +394,7 @@ __global__ __launch_bounds__(GT * KSPLIT, 2 * KSPLIT) void gemm_kernel(const uin
 #pragma unroll
     for (int i = 0; i < 16; i++) {
         int b = (int)BIAS;
-        if (FMT == LB_Q2_0_G64 || FMT == LB_Q8_0)
+        if (FMT != LB_TERNARY_PLANAR)
             asm volatile("; opaque bias %0" : "+v"(b));
         else
             b = 0;
@@ -343,48 +415,61 @@ __global__ __launch_bounds__(GT * KSPLIT, 2 * KSPLIT) void gemm_kernel(const uin
     // of the weight blocks does.  Half h of a split workgroup takes steps h, h + 2, ...
     const int nsteps = (K + KS - 1) / KS;
     const int nsh = (nsteps + KSPLIT - 1) / KSPLIT; // steps of the first half (the second may have one fewer)
-    const int rot = bn % nsteps;
-    auto step_k = [&](int j) { // K offset of this half's j-th step, clamped to the last step
-        return ((min(j * KSPLIT + half, nsteps - 1) + rot) % nsteps) * KS;
-    };
+    const int kend = nsteps * KS;                   // the walk's K offsets are taken modulo this
+    const int kfirst = ((bn % nsteps + half) % nsteps) * KS;
 
-    // register ring: the loads of step j + PF are issued into the slot step j frees; the step loop is
-    // unrolled by the ring length so every slot is a fixed set of registers and the compiler can wait
-    // for exactly the oldest step's loads
-    constexpr int PF = 2; // (3 measured slower: its registers cost the second workgroup per CU)
-    StepRegs ring[PF];
+    const LaneOffs lo = lane_offsets<FMT>(N, K, M, n0, m0, tid);
+    uint32_t xb[4]; // dword offsets in a tile of chunk 2 j + h of activation row 32 wm + l32
 #pragma unroll
-    for (int p = 0; p < PF; p++)
-        load_step<FMT>(ring[p], W, wsc, N, K, X, xsc, M, n0, m0, step_k(p), tid);
+    for (int j = 0; j < 4; j++)
+        xb[j] = 4u * (uint32_t)x_slot(32 * wm + l32, 2 * j + h);
 
-    for (int j0 = 0; j0 < nsh; j0 += PF)
+    // Step j's weight codes and scales are loaded into registers, and its activation tile into LDS, while
+    // step j - 1 computes; at the top of step j the thread waits for its own loads, unpacks the weights into
+    // LDS, and a barrier makes every thread's share visible.  The step loop is unrolled by two so that the
+    // LDS tiles of every step are fixed objects.
+    StepRegs ring;
+    int kk = kfirst;
+    load_step<FMT>(ring, lo, W, wsc, xsc, kk, K - kk < KS, tid);
+    issue_x(xt0[half], X, lo, kk, K - kk < KS, wave, lane);
+
+    for (int j0 = 0; j0 < nsh; j0 += 2)
 #pragma unroll
-    for (int q = 0; q < PF; q++) {
+    for (int q = 0; q < 2; q++) {
         const int j = j0 + q;
         if (j >= nsh) // uniform
             break;
         // the second half of a split workgroup may run one step short: it still meets every barrier
         const bool active = j * KSPLIT + half < nsteps; // uniform per half
-        const int buf = j & 1;
-        const int kk = step_k(j);
-        const int kab = min(KS, K - kk) / QK8;
+        const bool half_step = K - kk < KS;
+        __builtin_amdgcn_s_waitcnt(wait_vmcnt(0)); // this thread's loads of step j have landed
         if (active)
-            store_step<FMT>(lds[half], buf, ring[q], K, kk, tid);
-        __syncthreads();
-        // unconditional (the last steps re-load the final step, unused): a load under a branch would make
-        // the compiler wait for every outstanding load at the next store instead of only this slot's
-        load_step<FMT>(ring[q], W, wsc, N, K, X, xsc, M, n0, m0, step_k(j + PF), tid);
-        if (active)
-            step_compute<FMT, EMIT>(lds[half], buf, kab, h, l32, wn, wm, m0, n0, M, N, nab, kk, acc, iacc, cbias,
-                                    sums);
+            store_step<FMT>(lds[half], q, ring, K, kk, tid);
+        step_barrier();
+        // the next step's loads (past the last step the walk wraps: valid addresses, unused)
+        int kn = kk + KSPLIT * KS;
+        kn = kn >= kend ? kn - kend : kn;
+        load_step<FMT>(ring, lo, W, wsc, xsc, kn, K - kn < KS, tid);
+        issue_x(q ? xt0[half] : xt1[half], X, lo, kn, K - kn < KS, wave, lane);
+        if (active) {
+            if (!half_step)
+                step_compute<FMT, EMIT, 4>(lds[half], q, q ? xt1[half] : xt0[half], xb, h, l32, wn, wm, m0, n0, M, N,
+                                           nab, kk, acc, iacc, cbias, sums);
+            else // the half step that ends a row of an odd number of 64-column blocks
+                step_compute<FMT, EMIT, 2>(lds[half], q, q ? xt1[half] : xt0[half], xb, h, l32, wn, wm, m0, n0, M, N,
+                                           nab, kk, acc, iacc, cbias, sums);
+        }
+        kk = kn;
     }
+    // the last (unused) activation loads must land before the workgroup's LDS is reused or released
+    __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
 
-    if (KSPLIT == 2) {
+    if constexpr (KSPLIT == 2) {
         // the second half hands its partial sums to the first through LDS: 8 waves x 16 x 64 dwords = 32 KiB
-        // over the first half's buffers, free once every wave has passed this barrier
-        static_assert(sizeof(Lds) >= 8 * 16 * 64 * 4, "reduction area");
+        // over both halves' first activation tiles, free once every wave has passed this barrier
+        static_assert(KSPLIT * sizeof(uint32_t) * XTILE >= 8 * 16 * 64 * 4, "reduction area");
         __syncthreads();
-        uint32_t *red = reinterpret_cast<uint32_t *>(&lds[0]);
+        uint32_t *red = xt0[0];
         if (half == 1) {
 #pragma unroll
             for (int i = 0; i < 16; i++)
@@ -403,26 +488,43 @@ __global__ __launch_bounds__(GT * KSPLIT, 2 * KSPLIT) void gemm_kernel(const uin
         }
     }
 
-    // store: lane holds weight rows n = 32 wn + 8 (i / 4) + 4 h + i % 4 of activation row m = 32 wm + l32
+    // The wave's 32 x 32 tile of Y.  Lane (h, l32) holds weight rows n = 32 wn + 8 (i / 4) + 4 h + i % 4 of
+    // activation row m = 32 wm + l32; the tile goes through LDS (a 32 x 32 fp32 area per wave, element
+    // [m][n] at m * 32 + (n ^ m): the XOR keeps the column writes and the row reads free of bank conflicts)
+    // so that every store writes two whole 128-byte row segments of Y.
     const int m = m0 + 32 * wm + l32;
-    if (m >= M)
+    float out[16];
+    if (PLANAR) {
+        const float sx = reinterpret_cast<const float *>(Xscale)[min(m, M - 1)];
+#pragma unroll
+        for (int i = 0; i < 16; i++) {
+            const int n = n0 + 32 * wn + 8 * (i >> 2) + 4 * h + (i & 3);
+            if (EMIT && m < M && n < N)
+                sums[(int64_t)m * N + n] = iacc[i];
+            out[i] = ((float)iacc[i] * sx) * w_scale;
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 16; i++)
+            out[i] = acc[i];
+    }
+    if (EMIT && Y == nullptr)
         return;
-    const float sx = PLANAR ? reinterpret_cast<const float *>(Xscale)[m] : 0.0f;
+    if constexpr (KSPLIT == 1)
+        __syncthreads(); // every wave is done with the activation tiles
+    uint32_t *t = (wave < 4 ? xt0[0] : xt1[0]) + 1024 * (wave & 3);
 #pragma unroll
     for (int i = 0; i < 16; i++) {
-        const int n = n0 + 32 * wn + 8 * (i >> 2) + 4 * h + (i & 3);
-        if (n >= N)
-            continue;
-        if (PLANAR) {
-            if (EMIT)
-                sums[(int64_t)m * N + n] = iacc[i];
-            if (!EMIT || Y != nullptr) {
-                const float ys = (float)iacc[i] * sx;
-                Y[(int64_t)m * N + n] = ys * w_scale;
-            }
-        } else if (!EMIT || Y != nullptr) {
-            Y[(int64_t)m * N + n] = acc[i];
-        }
+        const int nl = 8 * (i >> 2) + 4 * h + (i & 3);
+        t[32 * l32 + (nl ^ l32)] = __float_as_uint(out[i]);
+    }
+    const int nc = lane & 31, n = n0 + 32 * wn + nc;
+#pragma unroll
+    for (int k = 0; k < 16; k++) {
+        const int r = 2 * k + (lane >> 5), mm = m0 + 32 * wm + r;
+        const float v = __uint_as_float(t[32 * r + (nc ^ r)]);
+        if (mm < M && n < N)
+            Y[(int64_t)mm * N + n] = v;
     }
 }
 
