@@ -80,12 +80,13 @@ __device__ __forceinline__ void unpack_q2_dword(uint32_t v, uint32_t *out)
 // What one thread carries from global memory into a K-step's weight tile.  Every thread takes one share of
 // it -- Q2_0: one code dword (16 weights); Q1_0: one sign dword, of which it builds two of the four
 // activation blocks; planar: one (pos, neg) dword pair, of which it builds half; Q8_0: 16 weight bytes --
-// in a (planar neg in a.y, the weight block scale's binary16 in a.z where the thread stores it; Q8_0's in
-// ws), and, for the first TM threads, the four binary16 activation scales of one activation row in c.
+// in a (planar neg in a.y; the weight block scale's binary16 where the thread stores it in
+// sc, sh), and, for the first TM threads, the four binary16 activation scales of one activation row in c.
 struct StepRegs {
     uint4 a;
     uint2 c;
-    uint32_t ws;
+    uint32_t sc; // the aligned dword holding the thread's weight block scale (binary16) ...
+    uint32_t sh; // ... at this bit offset (0 or 16)
 };
 
 // Global-address-space views: loads take a scalar base and a 32-bit per-lane offset (the ABI keeps the
@@ -170,8 +171,8 @@ __device__ __forceinline__ void load_step(StepRegs &r, const LaneOffs &o, const 
     if (FMT != LB_TERNARY_PLANAR && tid < TM) {
         // one 8-byte load per activation row (4-byte aligned: K / 32 and kk / 32 are even); the half step has
         // two blocks only
-        if (half_step) {
-            r.c.x = r.c.y = *(const gu32 *)((const gu8 *)xsc + odx);
+        if (half_step) { // (blocks 2 and 3 are stored as zero)
+            r.c.x = *(const gu32 *)((const gu8 *)xsc + odx);
         } else {
             const v2u_a4 t = *(const gv2u *)((const gu8 *)xsc + odx);
             r.c.x = t.x, r.c.y = t.y;
@@ -180,13 +181,17 @@ __device__ __forceinline__ void load_step(StepRegs &r, const LaneOffs &o, const 
     if (FMT == LB_Q8_0) {
         const v4u t = *(const gv4u *)((const gu8 *)W + ow);
         r.a = make_uint4(t.x, t.y, t.z, t.w);
-        r.ws = *(const gu16 *)((const gu8 *)wsc + os);
     } else if (FMT == LB_TERNARY_PLANAR) {
         r.a.x = *(const gu32 *)((const gu8 *)W + ow);        // pos
         r.a.y = *(const gu32 *)((const gu8 *)W + (ow + 8u)); // neg
     } else {
         r.a.x = *(const gu32 *)((const gu8 *)W + ow);
-        r.a.z = *(const gu16 *)((const gu8 *)wsc + os);
+    }
+    if (FMT != LB_TERNARY_PLANAR) {
+        // the scale's aligned dword (a 2-byte load would be widened by an instruction of its own, which makes the
+        // compiler wait for the load as soon as it is issued)
+        r.sc = *(const gu32 *)((const gu8 *)wsc + (os & ~3u));
+        r.sh = (os & 2u) * 8u;
     }
 }
 
@@ -239,13 +244,16 @@ constexpr int XTILE = TM * KS / 4; // dwords of an activation tile, swizzled 16-
 template <int FMT>
 __device__ __forceinline__ void store_step(Lds &lds, int buf, const StepRegs &r, int K, int kk, int tid)
 {
+    // On the half step that ends a row of an odd number of 64-column blocks, blocks 2 and 3 of the step get
+    // zero weights and zero scales: every step then runs the same four-block compute, and the missing blocks
+    // add exactly +0 (the MFMA gives the bias, the rescale 0 * bias - 0 * bias = +0, times a zero scale).
     const int kab = min(KS, K - kk) / QK8;
     if (FMT != LB_TERNARY_PLANAR && tid < TM) {
-        // (on a half step the values of blocks 2 and 3 are not read)
+        const uint32_t hi = kab == 4 ? r.c.y : 0u;
         lds.dx[buf][0 * TM + tid] = half_bits_to_float((uint16_t)(r.c.x & 0xffffu));
         lds.dx[buf][1 * TM + tid] = half_bits_to_float((uint16_t)(r.c.x >> 16));
-        lds.dx[buf][2 * TM + tid] = half_bits_to_float((uint16_t)(r.c.y & 0xffffu));
-        lds.dx[buf][3 * TM + tid] = half_bits_to_float((uint16_t)(r.c.y >> 16));
+        lds.dx[buf][2 * TM + tid] = half_bits_to_float((uint16_t)(hi & 0xffffu));
+        lds.dx[buf][3 * TM + tid] = half_bits_to_float((uint16_t)(hi >> 16));
     }
     const int rr = tid >> 3, p = tid & 7;
     uint32_t *wrow = lds.w[buf] + rr * WROW;
@@ -262,46 +270,45 @@ __device__ __forceinline__ void store_step(Lds &lds, int buf, const StepRegs &r,
                 make_uint2(__builtin_amdgcn_perm(e1, e0, 0x05010400u), __builtin_amdgcn_perm(e1, e0, 0x07030602u));
         }
         if (p == 0)
-            lds.dw[buf][rr] = half_bits_to_float((uint16_t)r.a.z);
+            lds.dw[buf][rr] = half_bits_to_float((uint16_t)(r.sc >> r.sh));
     } else if (FMT == LB_Q8_0) {
         // the weights are int8 already: copied as they are
         const int j = p >> 1;
         *reinterpret_cast<uint4 *>(wrow + 8 * j + 4 * (p & 1)) = r.a;
         if ((p & 1) == 0)
-            lds.dw[buf][j * TN + rr] = half_bits_to_float((uint16_t)r.ws);
+            lds.dw[buf][j * TN + rr] = half_bits_to_float((uint16_t)(r.sc >> r.sh));
     } else if (FMT == LB_Q2_0_G64) {
         const int bb = p >> 2, d = p & 3;
-        if (2 * bb < kab) {
-            uint32_t o[4];
-            unpack_q2_dword(r.a.x, o);
-            *reinterpret_cast<uint4 *>(wrow + 16 * bb + 4 * d) = make_uint4(o[0], o[1], o[2], o[3]);
-            if (d == 0)
-                lds.dw[buf][bb * TN + rr] = half_bits_to_float((uint16_t)r.a.z);
-        }
+        const bool live = 2 * bb < kab;
+        uint32_t o[4];
+        unpack_q2_dword(live ? r.a.x : 0x55555555u, o); // code 1 = weight 0
+        *reinterpret_cast<uint4 *>(wrow + 16 * bb + 4 * d) = make_uint4(o[0], o[1], o[2], o[3]);
+        if (d == 0)
+            lds.dw[buf][bb * TN + rr] = live ? half_bits_to_float((uint16_t)(r.sc >> r.sh)) : 0.0f;
     } else {
         const int bb = p >> 2, hh = (p >> 1) & 1, sub = p & 1;
-        if (2 * bb < kab) {
-            // bits 4 sub .. 4 sub + 3 of each byte: weights 8 t + 4 sub + s of the dword pair's 32
-            const uint32_t lut = 0x00FF0100u; // (pos, neg): 00 -> 0, 01 -> +1, 10 -> -1, 11 -> 0
-            uint32_t e[4];
+        const bool live = 2 * bb < kab;
+        const uint32_t pos = live ? r.a.x : 0u, neg = live ? r.a.y : 0u;
+        // bits 4 sub .. 4 sub + 3 of each byte: weights 8 t + 4 sub + s of the dword pair's 32
+        const uint32_t lut = 0x00FF0100u; // (pos, neg): 00 -> 0, 01 -> +1, 10 -> -1, 11 -> 0
+        uint32_t e[4];
 #pragma unroll
-            for (int s = 0; s < 4; s++) {
-                const int rb = 4 * sub + s;
-                e[s] = __builtin_amdgcn_perm(0u, lut, ((r.a.x >> rb) & 0x01010101u) | (((r.a.y >> rb) & 0x01010101u) << 1));
-            }
-            uint32_t t[4];
-            transpose4(e[0], e[1], e[2], e[3], t);
-            uint32_t *dst = wrow + 16 * bb + 8 * hh;
-#pragma unroll
-            for (int q = 0; q < 4; q++)
-                dst[2 * q + sub] = t[q];
+        for (int s = 0; s < 4; s++) {
+            const int rb = 4 * sub + s;
+            e[s] = __builtin_amdgcn_perm(0u, lut, ((pos >> rb) & 0x01010101u) | (((neg >> rb) & 0x01010101u) << 1));
         }
+        uint32_t t[4];
+        transpose4(e[0], e[1], e[2], e[3], t);
+        uint32_t *dst = wrow + 16 * bb + 8 * hh;
+#pragma unroll
+        for (int q = 0; q < 4; q++)
+            dst[2 * q + sub] = t[q];
     }
 }
 
-// One wave's share of a K-step: its 32 x 32 output tile over the step's KAB q8_0 blocks (4, or 2 on the
-// half step that ends a Q2_0 / planar row of an odd number of weight blocks).  Each block's result is
-// scaled as soon as it is ready: the other waves of the SIMD keep the vector ALU busy meanwhile.
+// One wave's share of a K-step: its 32 x 32 output tile over the step's KAB = 4 q8_0 blocks (on a half step
+// the last two carry zero weights and scales).  Each block's result is scaled as soon as it is ready: the
+// other waves of the SIMD keep the vector ALU busy meanwhile.
 template <int FMT, bool EMIT, int KAB>
 __device__ __forceinline__ void step_compute(const Lds &lds, int buf, const uint32_t *xt, const uint32_t (&xb)[4], int h,
                                              int l32, int wn, int wm, int m0, int n0, int M, int N, int nab, int kk,
@@ -351,7 +358,7 @@ __device__ __forceinline__ void step_compute(const Lds &lds, int buf, const uint
 #pragma unroll
             for (int i = 0; i < 16; i++) {
                 const int n = n0 + 32 * wn + 8 * (i >> 2) + 4 * h + (i & 3);
-                if (m < M && n < N)
+                if (m < M && n < N && kb < nab) // (the zero blocks of a half step have no sums)
                     sums[((int64_t)m * N + n) * nab + kb] = Dj[i] - (int)BIAS;
             }
         }
@@ -440,8 +447,7 @@ __global__ __launch_bounds__(GT * KSPLIT, EMIT ? 2 * KSPLIT : 4) void gemm_kerne
         if (j >= nsh) // uniform
             break;
         // the second half of a split workgroup may run one step short: it still meets every barrier
-        const bool active = j * KSPLIT + half < nsteps; // uniform per half
-        const bool half_step = K - kk < KS;
+        const bool active = KSPLIT == 1 || j * KSPLIT + half < nsteps; // uniform per half
         __builtin_amdgcn_s_waitcnt(wait_vmcnt(0)); // this thread's loads of step j have landed
         if (active)
             store_step<FMT>(lds[half], q, ring, K, kk, tid);
@@ -451,14 +457,9 @@ __global__ __launch_bounds__(GT * KSPLIT, EMIT ? 2 * KSPLIT : 4) void gemm_kerne
         kn = kn >= kend ? kn - kend : kn;
         load_step<FMT>(ring, lo, W, wsc, xsc, kn, K - kn < KS, tid);
         issue_x(q ? xt0[half] : xt1[half], X, lo, kn, K - kn < KS, wave, lane);
-        if (active) {
-            if (!half_step)
-                step_compute<FMT, EMIT, 4>(lds[half], q, q ? xt1[half] : xt0[half], xb, h, l32, wn, wm, m0, n0, M, N,
-                                           nab, kk, acc, iacc, cbias, sums);
-            else // the half step that ends a row of an odd number of 64-column blocks
-                step_compute<FMT, EMIT, 2>(lds[half], q, q ? xt1[half] : xt0[half], xb, h, l32, wn, wm, m0, n0, M, N,
-                                           nab, kk, acc, iacc, cbias, sums);
-        }
+        if (active)
+            step_compute<FMT, EMIT, 4>(lds[half], q, q ? xt1[half] : xt0[half], xb, h, l32, wn, wm, m0, n0, M, N, nab,
+                                       kk, acc, iacc, cbias, sums);
         kk = kn;
     }
     // the last (unused) activation loads must land before the workgroup's LDS is reused or released
