@@ -773,7 +773,8 @@ def main():
                                              "q8_0 itself"),
                              (False, "separate_quantise", "each phase a q8_0 quantise launch plus one batched "
                                                           "launch")):
-        if not fused and "layered" not in args.secondary.split(","):
+        # both legs replay a HIP graph: left out unless asked for ("layered"), e.g. under counter collection
+        if "layered" not in args.secondary.split(","):
             continue
         lg = LayeredGraph(tok, fused=fused)
         msg = time_graph(lg, args.steps, warm)

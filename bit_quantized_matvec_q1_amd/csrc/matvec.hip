@@ -166,6 +166,22 @@ __device__ __forceinline__ int udot8(uint32_t a, uint32_t b, int c)
 {
     return (int)__builtin_amdgcn_udot8(a, b, (uint32_t)c, false);
 }
+// The first signed product of an accumulator chain, with the zero accumulator as an inline constant.  (The
+// compiler would start the chain in the two-operand form that accumulates into its destination, which
+// costs a move of zero into that register first: one VALU instruction per chain.)
+__device__ __forceinline__ int sdot8z(uint32_t a, uint32_t b)
+{
+    int r;
+    asm("v_dot8_i32_i4 %0, %1, %2, 0" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
+// l - 16 h in one instruction (|h| < 2^23): the block whose mask bit reads as -8 in the signed product
+__device__ __forceinline__ int sub16(int l, int h)
+{
+    int r;
+    asm("v_mad_i32_i24 %0, %1, -16, %2" : "=v"(r) : "v"(h), "v"(l));
+    return r;
+}
 
 // ------------------------------------------------------------------------------------------------
 // Per-slice arithmetic.  Q formats return the slice's scaled contribution and (EMIT) its two exact
@@ -177,13 +193,13 @@ __device__ __forceinline__ void q2_isums(uint4 c, const uint32_t *A, int &i0, in
 {
     const uint32_t cw[4] = {c.x, c.y, c.z, c.w};
     // the low-nibble accumulators start at -sum(q) (modular), so each block sum is one shift-add
-    int h[2] = {0, 0}, l[2] = {(int)A[18], (int)A[19]};
+    int h[2], l[2] = {(int)A[18], (int)A[19]};
 #pragma unroll
     for (int k = 0; k < 4; k++) {
         const uint32_t e0 = cw[k] & 0x33333333u;
         const uint32_t e1 = (cw[k] >> 2) & 0x33333333u;
         const int j = k >> 1;
-        h[j] = sdot8(e0, A[(2 * k + 0) * 2 + 1], h[j]);
+        h[j] = (k & 1) ? sdot8(e0, A[(2 * k + 0) * 2 + 1], h[j]) : sdot8z(e0, A[(2 * k + 0) * 2 + 1]);
         l[j] = udot8(e0, A[(2 * k + 0) * 2 + 0], l[j]);
         h[j] = sdot8(e1, A[(2 * k + 1) * 2 + 1], h[j]);
         l[j] = udot8(e1, A[(2 * k + 1) * 2 + 0], l[j]);
@@ -200,19 +216,19 @@ __device__ __forceinline__ void q1_group_sums(uint4 b, const uint32_t *A, int (&
     const uint32_t bw[4] = {b.x, b.y, b.z, b.w};
     // the eight accumulator chains advance together (dword by dword), so consecutive dot products are
     // independent
-    int h[4] = {0, 0, 0, 0}, l[4] = {0, 0, 0, 0};
+    int h[4], l[4];
 #pragma unroll
     for (int m = 0; m < 4; m++) {
 #pragma unroll
         for (int r = 0; r < 4; r++) {
             const uint32_t e = bw[m] & (0x11111111u << r);
-            h[r] = sdot8(e, A[(4 * m + r) * 2 + 1], h[r]);
-            l[r] = udot8(e, A[(4 * m + r) * 2 + 0], l[r]);
+            h[r] = m ? sdot8(e, A[(4 * m + r) * 2 + 1], h[r]) : sdot8z(e, A[(4 * m + r) * 2 + 1]);
+            l[r] = udot8(e, A[(4 * m + r) * 2 + 0], m ? l[r] : 0);
         }
     }
 #pragma unroll
     for (int r = 0; r < 4; r++)
-        C[r] = r < 3 ? h[r] * 16 + l[r] : l[r] - h[r] * 16;
+        C[r] = r < 3 ? h[r] * 16 + l[r] : sub16(l[r], h[r]);
 }
 
 // Planar: plane words {pos0, pos1, neg0, neg1}.  Masking without a shift leaves bit r of a nibble in
@@ -300,11 +316,20 @@ __device__ __forceinline__ void issue_row(RowRegs<FMT, S> &r, const uint8_t *__r
     }
 }
 
+// The row result of the product instantiations (no sums): every lane issues the store, and a lane that
+// does not hold a stored result (not the row's last lane, or a row past the tile) addresses past the
+// end of the tile's output range, where the buffer unit drops it.  No branch surrounds the store, so the
+// compiler can count the loads still in flight exactly and waits only for the row it computes next.
+__device__ __forceinline__ void store_row_result(__amdgpu_buffer_rsrc_t yt, bool keep, int rl, float v)
+{
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), yt, keep ? (uint32_t)rl * 4u : 0x80000000u, 0, 0);
+}
+
 template <int FMT, int L, int S, bool EMIT, bool FULL>
 __device__ __forceinline__ void compute_row(const uint4 (&code)[S], const uint32_t (&sc)[S],
                                             const uint32_t (&act)[S][F<FMT>::REC], const float (&cfold)[S], int ns, int li,
                                             bool valid, int row, float w_scale, float sx, float *__restrict__ y,
-                                            int32_t *__restrict__ sums)
+                                            int32_t *__restrict__ sums, __amdgpu_buffer_rsrc_t yt, int rl)
 {
     constexpr int NAB = F<FMT>::NAB, DX = F<FMT>::SW / 4;
     if (FMT == LB_TERNARY_PLANAR) {
@@ -313,15 +338,18 @@ __device__ __forceinline__ void compute_row(const uint4 (&code)[S], const uint32
         for (int i = 0; i < S; i++)
             planar_accumulate(code[i], act[i], acc);
         const int t = group_sum_i<L>(planar_total8(acc));
-        if (valid && li == L - 1) {
-            const int a = t >> 3; // exact: the total is a multiple of 8
-            if (EMIT)
+        const int a = t >> 3; // exact: the total is a multiple of 8
+        // tritium "Architecture", section 5: activation scale and weight scale are applied as two fp32
+        // multiplies, in that order
+        const float ys = (float)a * sx;
+        if constexpr (EMIT) {
+            if (valid && li == L - 1) {
                 sums[row] = a;
-            // tritium "Architecture", section 5: activation scale and weight scale are applied as two
-            // fp32 multiplies, in that order
-            const float ys = (float)a * sx;
-            if (!EMIT || y != nullptr) // the sums instantiation may be called without an output vector
-                y[row] = ys * w_scale;
+                if (y != nullptr) // the sums instantiation may be called without an output vector
+                    y[row] = ys * w_scale;
+            }
+        } else {
+            store_row_result(yt, valid && li == L - 1, rl, ys * w_scale);
         }
     } else {
         float part = 0.0f;
@@ -357,8 +385,12 @@ __device__ __forceinline__ void compute_row(const uint4 (&code)[S], const uint32
             }
         }
         part = group_sum_f<L>(part);
-        if (valid && li == L - 1 && (!EMIT || y != nullptr))
-            *(gf32 *)((gu8 *)y + (uint32_t)row * 4u) = part;
+        if constexpr (EMIT) {
+            if (valid && li == L - 1 && y != nullptr)
+                *(gf32 *)((gu8 *)y + (uint32_t)row * 4u) = part;
+        } else {
+            store_row_result(yt, valid && li == L - 1, rl, part);
+        }
     }
 }
 
@@ -395,8 +427,7 @@ __device__ __forceinline__ void matvec_tile(const uint8_t *__restrict__ W, int N
     RowRegs<FMT, S> buf[NB];
 #pragma unroll
     for (int b = 0; b < NB - 1; b++) {
-        if (b * STEP < nrows) // uniform
-            issue_row<FMT, L, S, FULL>(buf[b], W, scales, min(onext, last), slo, sls);
+        issue_row<FMT, L, S, FULL>(buf[b], W, scales, min(onext, last), slo, sls);
         onext += stepb;
     }
 
@@ -470,18 +501,23 @@ __device__ __forceinline__ void matvec_tile(const uint8_t *__restrict__ W, int N
         cfold[i] = c;
     }
 
+    // the tile's outputs y[row0, row0 + nrows) as a buffer range (the sums instantiation may run without y)
+    const __amdgpu_buffer_rsrc_t yt =
+        __builtin_amdgcn_make_buffer_rsrc(EMIT ? nullptr : y + row0, 0, EMIT ? 0 : nrows * 4, 0x00020000);
     for (int it = 0; it < nrows; it += NB * STEP) {
 #pragma unroll
         for (int b = 0; b < NB; b++) {
+            // No branch inside the ring: a row past the tile's end is computed from the clamped loads
+            // and never stored.  With a branch here the compiler would sink each half's loads into the
+            // half that uses them, after this row's arithmetic, and that half would wait for loads only
+            // just issued.
             const int cur = it + b * STEP;
-            if (cur >= nrows) // uniform
-                break;
-            if (cur + (NB - 1) * STEP < nrows) // uniform
-                issue_row<FMT, L, S, FULL>(buf[(b + NB - 1) % NB], W, scales, min(onext, last), slo, sls);
+            issue_row<FMT, L, S, FULL>(buf[(b + NB - 1) % NB], W, scales, min(onext, last), slo, sls);
+            __builtin_amdgcn_sched_barrier(0); // the next row's loads go out before this row's arithmetic
             onext += stepb;
             const int rl = cur + rbase;
             compute_row<FMT, L, S, EMIT, FULL>(buf[b].code, buf[b].sc, act, cfold, ns, li, rl < nrows, row0 + rl, w_scale,
-                                         sx, y, sums);
+                                               sx, y, sums, yt, rl);
         }
     }
 }
