@@ -92,8 +92,8 @@ lb_status check_product(const char *fn, int fmt, const void *W, int64_t N, int64
         return fail(LB_ESHAPE, fn, "negative size");
     if (K % block_weights(fmt))
         return fail(LB_ESHAPE, fn, "K is not a multiple of the weight block (128 for Q1_0, 32 for Q8_0, 64 otherwise)");
-    if (fmt == LB_TERNARY_B3 && K > 10240) // a row is at most 64 lanes of two beats
-        return fail(LB_ESHAPE, fn, "K above 10240 for base-3 beats");
+    if (fmt == LB_TERNARY_B3 && K > 30720) // a row is at most 64 lanes of six 80-column beats
+        return fail(LB_ESHAPE, fn, "K above 30720 for base-3 beats");
     if (K > 32768 || N > INT32_MAX)
         return fail(LB_ESHAPE, fn, "K above 32768 or N above 2^31-1");
     if (fmt == LB_Q8_0 && K > 16384) // a row is at most one wave of lanes with 8 blocks each

@@ -34,7 +34,9 @@ typedef __attribute__((address_space(1))) const uint8_t gu8;
 constexpr int BCOLS = 80; // columns per beat
 constexpr int REC = 20;   // staged dwords per beat: 4 record dwords x 5 column offsets
 
-#define LB_B3_CFGS(X) X(0, 16, 1) X(1, 16, 2) X(2, 32, 1) X(3, 32, 2) X(4, 32, 3) X(5, 64, 1) X(6, 64, 2)
+#define LB_B3_CFGS(X)                                                                                         \
+    X(0, 16, 1) X(1, 16, 2) X(2, 32, 1) X(3, 32, 2) X(4, 32, 3) X(5, 64, 1) X(6, 64, 2) X(7, 32, 5) X(8, 64, 3)     \
+    X(9, 64, 4) X(10, 64, 6)
 
 struct CfgLS {
     int L, S;
@@ -133,6 +135,9 @@ __device__ __forceinline__ void b3_tile(const uint8_t *__restrict__ W, int K, fl
     B3Row<S> buf[2];
     issue(buf[0], min(onext, last));
     onext += stepb;
+    // the tile's outputs y[row0, row0 + nrows) as a buffer range (the sums instantiation may run without y)
+    const __amdgpu_buffer_rsrc_t yt =
+        __builtin_amdgcn_make_buffer_rsrc(EMIT ? nullptr : y + row0, 0, EMIT ? 0 : nrows * 4, 0x00020000);
 
     int *sumq = reinterpret_cast<int *>(lds + nbt * REC);
     b3_stage(xq, K, nbt, lds, sumq);
@@ -158,11 +163,12 @@ __device__ __forceinline__ void b3_tile(const uint8_t *__restrict__ W, int K, fl
     for (int it = 0; it < nrows; it += 2 * STEP) {
 #pragma unroll
         for (int p = 0; p < 2; p++) {
+            // no branch inside the pair: a row past the tile's end is computed from the clamped loads and
+            // never stored, so the next row's loads are issued every time, ahead of this row's arithmetic,
+            // and the load counter waits only for the row computed next
             const int cur = it + p * STEP;
-            if (cur >= nrows) // uniform
-                break;
-            if (cur + STEP < nrows) // uniform
-                issue(buf[p ^ 1], min(onext, last));
+            issue(buf[p ^ 1], min(onext, last));
+            __builtin_amdgcn_sched_barrier(0);
             onext += stepb;
             int acc_a = 0, acc_b = 0;
 #pragma unroll
@@ -174,14 +180,21 @@ __device__ __forceinline__ void b3_tile(const uint8_t *__restrict__ W, int K, fl
             }
             int acc = group_sum_i<L>(acc_a - 3 * acc_b);
             const int rl = cur + rbase;
-            if (rl < nrows && li == L - 1) {
-                const int a = acc - sq; // sum (w + 1) q - sum q
-                if (EMIT)
+            const int a = acc - sq; // sum (w + 1) q - sum q
+            // tritium "Architecture", section 5: activation scale, then weight scale, in fp32
+            const float ys = (float)a * sx;
+            if constexpr (EMIT) {
+                if (rl < nrows && li == L - 1) {
                     sums[row0 + rl] = a;
-                // tritium "Architecture", section 5: activation scale, then weight scale, in fp32
-                const float ys = (float)a * sx;
-                if (!EMIT || y != nullptr)
-                    y[row0 + rl] = ys * w_scale;
+                    if (y != nullptr)
+                        y[row0 + rl] = ys * w_scale;
+                }
+            } else {
+                // every lane stores; a lane without a result addresses past the tile's output range, where
+                // the buffer unit drops it (no branch around the store)
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(ys * w_scale), yt,
+                                                      rl < nrows && li == L - 1 ? (uint32_t)rl * 4u : 0x80000000u,
+                                                      0, 0);
             }
         }
     }
@@ -210,8 +223,8 @@ __global__ __launch_bounds__(WG) void b3_batched_kernel(const DevDesc *__restric
 
 } // namespace
 
-// Choice: the fewest idle lane slots among the configurations whose staged activation fits 120 registers
-// per lane; then fewer lanes per row.
+// Choice: the fewest idle lane slots among the configurations (their staged activation fits 120 registers
+// per lane: at most 6 beats, so K up to 64 x 6 x 80 = 30720); then fewer lanes per row.
 int b3_config(int64_t K)
 {
     if (K <= 0 || K % 64)

@@ -59,14 +59,16 @@ __global__ __launch_bounds__(WG) void head_kernel(const uint16_t *__restrict__ W
     };
     issue(buf[0], min(onext, last));
     onext += STEP * rowb;
+    const __amdgpu_buffer_rsrc_t yt = __builtin_amdgcn_make_buffer_rsrc(y + row0, 0, nrows * 4, 0x00020000);
     for (int it = 0; it < nrows; it += 2 * STEP) {
 #pragma unroll
         for (int b = 0; b < 2; b++) {
+            // no branch inside the pair: a row past the tile's end is computed from the clamped loads and
+            // never stored, so the next row's loads are issued every time, ahead of this row's arithmetic,
+            // and the load counter waits only for the row computed next
             const int cur = it + b * STEP;
-            if (cur >= nrows) // uniform
-                break;
-            if (cur + STEP < nrows) // uniform
-                issue(buf[b ^ 1], min(onext, last));
+            issue(buf[b ^ 1], min(onext, last));
+            __builtin_amdgcn_sched_barrier(0);
             onext += STEP * rowb;
             if (ragged && lane + 64 * (S - 1) >= nch)
                 buf[b][S - 1] = make_uint4(0u, 0u, 0u, 0u);
@@ -82,8 +84,10 @@ __global__ __launch_bounds__(WG) void head_kernel(const uint16_t *__restrict__ W
             }
             acc = group_sum_f<64>(acc);
             const int rl = cur + wave;
-            if (rl < nrows && lane == 63)
-                y[row0 + rl] = acc;
+            // every lane stores; a lane without the row's total addresses past the tile's output range,
+            // where the buffer unit drops it (no branch around the store)
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc), yt,
+                                                  rl < nrows && lane == 63 ? (uint32_t)rl * 4u : 0x80000000u, 0, 0);
         }
     }
 }
@@ -118,18 +122,22 @@ __global__ __launch_bounds__(WG) void head_i8_kernel(const int8_t *__restrict__ 
     // fastest: 2 leaves HBM idle, 4 costs occupancy)
     constexpr int NB = 3;
     uint4 buf[NB][S];
-    auto issue = [&](uint4 (&w)[S], uint32_t off) {
+    float sbuf[NB]; // the row's scale travels with its weights
+    const int rlast = row0 + nrows - 1;
+    int rnext = row0 + min(rbase, nrows - 1);
+    auto issue = [&](uint4 (&w)[S], float &s, uint32_t off, int row) {
 #pragma unroll
         for (int i = 0; i < S; i++) {
             const hv4u t = __builtin_nontemporal_load((ghv4u *)((ghu8 *)W + (off + co[i])));
             w[i] = make_uint4(t.x, t.y, t.z, t.w);
         }
+        s = sw[row];
     };
 #pragma unroll
     for (int b = 0; b < NB - 1; b++) {
-        if (b * STEP < nrows) // uniform
-            issue(buf[b], min(onext, last));
+        issue(buf[b], sbuf[b], min(onext, last), min(rnext, rlast));
         onext += STEP * rowb;
+        rnext += STEP;
     }
     // x into registers while the first rows stream in (columns past K read zero)
     float xr[S][16];
@@ -142,15 +150,18 @@ __global__ __launch_bounds__(WG) void head_i8_kernel(const int8_t *__restrict__ 
             xr[i][4 * q + 0] = a.x, xr[i][4 * q + 1] = a.y, xr[i][4 * q + 2] = a.z, xr[i][4 * q + 3] = a.w;
         }
     }
+    const __amdgpu_buffer_rsrc_t yt = __builtin_amdgcn_make_buffer_rsrc(y + row0, 0, nrows * 4, 0x00020000);
     for (int it = 0; it < nrows; it += NB * STEP) {
 #pragma unroll
         for (int b = 0; b < NB; b++) {
+            // no branch inside the ring: a row past the tile's end is computed from the clamped loads and
+            // never stored, so the next row's loads are issued every time, ahead of this row's arithmetic,
+            // and the load counter waits only for the row computed next
             const int cur = it + b * STEP;
-            if (cur >= nrows) // uniform
-                break;
-            if (cur + (NB - 1) * STEP < nrows) // uniform
-                issue(buf[(b + NB - 1) % NB], min(onext, last));
+            issue(buf[(b + NB - 1) % NB], sbuf[(b + NB - 1) % NB], min(onext, last), min(rnext, rlast));
+            __builtin_amdgcn_sched_barrier(0);
             onext += STEP * rowb;
+            rnext += STEP;
             // a lane's chunk past the row's end re-read the last chunk; its x is zero, so it adds nothing;
             // a lane past the tile's last row re-read that row, and its sum is not stored
             float acc = 0.0f;
@@ -165,8 +176,10 @@ __global__ __launch_bounds__(WG) void head_i8_kernel(const int8_t *__restrict__ 
             }
             acc = group_sum_f<L>(acc);
             const int rl = cur + rbase;
-            if (rl < nrows && li == L - 1)
-                y[row0 + rl] = sw[row0 + rl] * acc;
+            // every lane stores; a lane without the row's total addresses past the tile's output range,
+            // where the buffer unit drops it (no branch around the store)
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sbuf[b] * acc), yt,
+                                                  rl < nrows && li == L - 1 ? (uint32_t)rl * 4u : 0x80000000u, 0, 0);
         }
     }
 }

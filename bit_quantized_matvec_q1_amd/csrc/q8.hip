@@ -114,14 +114,18 @@ __device__ __forceinline__ void q8_tile(const uint8_t *__restrict__ W, int N, in
         dx[i] = in ? dl[u >> 1] : 0.0f;
     }
 
+    // the tile's outputs y[row0, row0 + nrows) as a buffer range (the sums instantiation may run without y)
+    const __amdgpu_buffer_rsrc_t yt =
+        __builtin_amdgcn_make_buffer_rsrc(EMIT ? nullptr : y + row0, 0, EMIT ? 0 : nrows * 4, 0x00020000);
     for (int it = 0; it < nrows; it += 2 * STEP) {
 #pragma unroll
         for (int p = 0; p < 2; p++) {
+            // no branch inside the pair: a row past the tile's end is computed from the clamped loads and
+            // never stored, so the next row's loads are issued every time, ahead of this row's arithmetic,
+            // and the load counter waits only for the row computed next
             const int cur = it + p * STEP;
-            if (cur >= nrows) // uniform
-                break;
-            if (cur + STEP < nrows) // uniform
-                q8_issue<L, S>(buf[p ^ 1], W, scales, min(onext, last), uo);
+            q8_issue<L, S>(buf[p ^ 1], W, scales, min(onext, last), uo);
+            __builtin_amdgcn_sched_barrier(0);
             onext += stepb;
             const int rl = cur + rbase;
             const bool valid = rl < nrows;
@@ -142,8 +146,15 @@ __device__ __forceinline__ void q8_tile(const uint8_t *__restrict__ W, int N, in
                 }
             }
             part = group_sum_f<L>(part);
-            if (valid && li == L - 1 && (!EMIT || y != nullptr))
-                y[row0 + rl] = part;
+            if constexpr (EMIT) {
+                if (valid && li == L - 1 && y != nullptr)
+                    y[row0 + rl] = part;
+            } else {
+                // every lane stores; a lane without a result addresses past the tile's output range, where
+                // the buffer unit drops it (no branch around the store)
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(part), yt,
+                                                      valid && li == L - 1 ? (uint32_t)rl * 4u : 0x80000000u, 0, 0);
+            }
         }
     }
 }

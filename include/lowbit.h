@@ -127,7 +127,7 @@ lb_status lowbit_quantize_act(int afmt, const float *x, int64_t M, int64_t K, in
  *   afmt:   LB_ACT_Q8_0 for the ggml formats, LB_ACT_I8_ROW for planar and base-3 beats.
  *   xq:     device int8 [K], 16-byte aligned.  xscale: binary16 [K/32] or one fp32, 4-byte aligned.
  *   y:      device fp32 [N], 4-byte aligned.
- * Limits: K <= 32768 (16384 for LB_Q8_0, 10240 for LB_TERNARY_B3) and N <= 2^31 - 1; the weight tensor must
+ * Limits: K <= 32768 (16384 for LB_Q8_0, 30720 for LB_TERNARY_B3) and N <= 2^31 - 1; the weight tensor must
  * be smaller than 4 GiB.
  */
 lb_status lowbit_matvec(int fmt, const void *W, int64_t N, int64_t K, float w_tensor_scale, int afmt,

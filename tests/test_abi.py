@@ -72,7 +72,7 @@ def test_matvec_validation_codes():
     assert mv(K=32768 + 64) == L.LB_ESHAPE
     assert mv(fmt=L.Q8_0, K=16384 + 32) == L.LB_ESHAPE  # Q8_0 rows are at most 16384 weights
     assert mv(fmt=L.Q8_0, K=48) == L.LB_ESHAPE  # not a multiple of 32
-    assert mv(fmt=L.TERNARY_B3, afmt=L.ACT_I8_ROW, K=10240 + 64) == L.LB_ESHAPE  # base-3 rows <= 10240
+    assert mv(fmt=L.TERNARY_B3, afmt=L.ACT_I8_ROW, K=30720 + 64) == L.LB_ESHAPE  # base-3 rows <= 30720
     assert mv(fmt=L.TERNARY_B3, afmt=L.ACT_Q8_0) == L.LB_EINVAL  # base-3 takes per-token activations
     assert mv(W=None) == L.LB_EINVAL
     assert mv(y=None) == L.LB_EINVAL

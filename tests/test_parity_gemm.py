@@ -55,7 +55,7 @@ def check(fmt, M, N, K, seed, p=synth.TERNARY_P, sums=True, m_rows=None, n_rows=
             for m in ms:
                 acc, _ = oracle.matvec_planar(Wt.raw, N, K, Q[m], XS[m], Wt.s_w, rows=ns)
                 assert np.array_equal(S[m, ns], acc)
-        return
+        return Wt, packed, Q, XS
     Yr, A = oracle.gemm_q(fmt, Wt.raw, N, K, Q, XS, m_rows=ms, n_rows=ns)
     assert_close(Y[np.ix_(ms, ns)].ravel(), Yr.ravel(), A.ravel(), K // 32, f"{NAMES[fmt]} prefill {M}x{N}x{K}")
     if sums:
@@ -63,6 +63,7 @@ def check(fmt, M, N, K, seed, p=synth.TERNARY_P, sums=True, m_rows=None, n_rows=
         for m in ms:
             ref = oracle.block_sums(fmt, Wt.raw, N, K, Q[m], rows=ns)
             assert np.array_equal(S[m, ns], ref), f"block sums of activation row {m} differ"
+    return Wt, packed, Q, XS
 
 
 @pytest.mark.parametrize("fmt", [synth.Q1_0, synth.Q2_0_G64, synth.TERNARY_PLANAR, synth.Q8_0], ids=NAMES.get)
@@ -151,12 +152,22 @@ def test_gemm_unit_scales_bit_exact(fmt):
 @pytest.mark.parametrize("N", [4096, 12288])
 def test_gemm_full_size_sampled(fmt, N):
     """The prefill workload at full size (512 activation rows x N x 4096); the oracle checks a seeded
-    sample of (row, column) pairs: every 64th activation row against 300 weight rows."""
+    sample of (row, column) pairs: every 64th activation row against 300 weight rows, outputs within the
+    tolerance and the block sums of the same pairs bit-exact (taken from the device at full size, the
+    sample gathered there)."""
     M, K = synth.PREFILL_M, 4096
     g = synth.rng(6400 + N)
     n_rows = np.unique(np.concatenate([g.integers(0, N, 300), [0, N - 1]]))
     m_rows = np.unique(np.concatenate([np.arange(0, M, 64), [M - 1]]))
-    check(fmt, M, N, K, seed=6401 + N, sums=False, m_rows=m_rows, n_rows=n_rows)
+    Wt, packed, Q, XS = check(fmt, M, N, K, seed=6401 + N, sums=False, m_rows=m_rows, n_rows=n_rows)
+    S = torch.empty((M, N, K // 32), dtype=torch.int32, device="cuda")
+    L.lowbit_block_sums(fmt, packed, N, K, L.ACT_Q8_0, dev(Q), dev(XS), M, S)
+    mi, ni = torch.from_numpy(m_rows).cuda(), torch.from_numpy(n_rows).cuda()
+    Ss = host(S[mi][:, ni])
+    del S
+    for a, m in enumerate(m_rows):
+        ref = oracle.block_sums(fmt, Wt.raw, N, K, Q[m], rows=n_rows)
+        assert np.array_equal(Ss[a], ref), f"full-size block sums of activation row {m} differ"
 
 
 def test_gemm_rows_match_decode():

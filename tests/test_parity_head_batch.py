@@ -81,7 +81,7 @@ def _product(fmt, N, K, seed):
 
 @pytest.mark.parametrize("fmt", [synth.Q1_0, synth.Q2_0_G64, synth.TERNARY_PLANAR, synth.Q8_0, synth.TERNARY_B3])
 def test_batched_matches_single_and_oracle(fmt):
-    shapes = [(300, 1024), (1024, 4096), (129, 12288 if fmt != synth.TERNARY_B3 else 10240), (1, 128), (517, 2560)]
+    shapes = [(300, 1024), (1024, 4096), (129, 12288), (1, 128), (517, 2560)]
     if fmt != synth.Q1_0:
         shapes.append((70, 6912 // 64 * 64))
     say(f"case batched fmt={fmt} shapes={shapes}")
@@ -111,6 +111,35 @@ def test_batched_matches_single_and_oracle(fmt):
     torch.cuda.synchronize()
     assert np.array_equal(host(ys[1]), gpu_matvec(fmt, prods[1][1], shapes[1][0], shapes[1][1], prods[1][2],
                                                   prods[1][3], w_scale=prods[1][0].s_w or 1.0))
+    b.close()
+
+
+@pytest.mark.parametrize("fmt", [synth.Q1_0, synth.Q2_0_G64], ids=["Q1_0", "Q2_0_g64"])
+def test_batched_unit_scales_bit_exact_full_configs(fmt):
+    """Every binary16 scale 1.0, on the weights and on the activations: each output is an integer below
+    2^24, computed exactly in any order, so the batched launch must equal the oracle bit for bit.  K = 4096
+    and K = 12288 are the token's two configurations (every lane slot of a row filled), several tiles per
+    product and a ragged last tile."""
+    qk = synth.BLOCK_WEIGHTS[fmt]
+    shapes = [(1024, 4096), (512, 12288), (77, 4096), (33, 12288)]
+    say(f"case batched unit scales fmt={fmt} shapes={shapes}")
+    descs, keep = [], []
+    for i, (N, K) in enumerate(shapes):
+        Wt = synth.make_weights(fmt, N, K, seed=5700 + i)
+        raw = oracle.encode(fmt, Wt.w, np.full((N, K // qk), 0x3C00, np.uint16), N, K)
+        Wu = synth.Weights(fmt, N, K, raw.reshape(N, K // qk, synth.BLOCK_BYTES[fmt]), Wt.w)
+        q, _, _ = act_for(fmt, K, 5750 + i)
+        ones = np.full(K // 32, 0x3C00, np.uint16)
+        packed, qd, xsd = packed_weights(Wu), dev(q), dev(ones)
+        y = torch.full((N,), float("nan"), dtype=torch.float32, device="cuda")
+        keep.append((N, K, raw, q, ones, packed, qd, xsd, y))
+        descs.append(L.desc(fmt, packed, N, K, qd, xsd, y))
+    b = L.Batch(descs)
+    b.run()
+    torch.cuda.synchronize()
+    for N, K, raw, q, ones, _, _, _, y in keep:
+        y_ref, _ = oracle.matvec_q(fmt, raw, N, K, q, ones)
+        assert np.array_equal(host(y).astype(np.float64), y_ref), f"batched unit-scale {N}x{K} differs"
     b.close()
 
 

@@ -17,7 +17,7 @@ ALL_FMTS = Q_FMTS + [synth.TERNARY_PLANAR, synth.TERNARY_B3]
 ROW_FMTS = (synth.TERNARY_PLANAR, synth.TERNARY_B3)  # per-token activations, per-tensor scale, row sums
 NAMES = {synth.Q1_0: "Q1_0", synth.Q2_0_G64: "Q2_0_g64", synth.TERNARY_PLANAR: "planar", synth.Q8_0: "Q8_0",
          synth.TERNARY_B3: "base3"}
-MAX_K = {synth.Q8_0: 16384, synth.TERNARY_B3: 10240}
+MAX_K = {synth.Q8_0: 16384, synth.TERNARY_B3: 30720}
 QK = {synth.Q1_0: 128, synth.Q2_0_G64: 64, synth.Q8_0: 32}
 
 

@@ -22,7 +22,7 @@ def _run_token(fmt, layer, layers, seed):
     return tok
 
 
-def _check_token(tok, rows_per_product=6, seed=0):
+def _check_token(tok, rows_per_product=64, seed=0):
     g = synth.rng(seed)
     planar = tok.fmt in (synth.TERNARY_PLANAR, synth.TERNARY_B3)
     # every activation row of the token, byte for byte
