@@ -29,10 +29,12 @@ inline __device__ float half_bits_to_float(uint16_t h) { return __half2float(__u
 // library goes through these two functions, so they all give the same bytes.
 inline __device__ float q8_0_block_amax8(float4 v)
 {
+    // maximum over the 8 lanes by DPP: swap neighbours, swap pairs (each quad then holds its maximum), then
+    // mirror within the 8 (lane i meets lane 7 - i of the other quad)
     float amax = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
-#pragma unroll
-    for (int o = 1; o < 8; o <<= 1)
-        amax = fmaxf(amax, __shfl_xor(amax, o, 8));
+    amax = fmaxf(amax, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(amax), 0xB1, 0xF, 0xF, false)));
+    amax = fmaxf(amax, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(amax), 0x4E, 0xF, 0xF, false)));
+    amax = fmaxf(amax, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(amax), 0x141, 0xF, 0xF, false)));
     return amax;
 }
 inline __device__ uint32_t q8_0_pack4(float4 v, float amax)

@@ -78,84 +78,140 @@ template <int AS> __device__ __forceinline__ uint4 ld4(src_t<AS, int8_t> *p)
     return make_uint4(t.x, t.y, t.z, t.w);
 }
 
+// Loads of one item (one nibble-word pair: 8, 16 or 32 activation bytes) and of one (slice, q8_0 block)
+// item (its 32 bytes and binary16 scale).
+template <int FMT, int AS> struct StageLoads {
+    uint4 v[FMT == LB_TERNARY_PLANAR ? 2 : 1];
+};
 template <int FMT, int AS>
+__device__ __forceinline__ StageLoads<FMT, AS> stage_load_item(src_t<AS, int8_t> *xq, int it)
+{
+    constexpr int SW = F<FMT>::SW, WPS = SW / 8;
+    StageLoads<FMT, AS> r;
+    const int sl = it / WPS, a = it % WPS;
+    src_t<AS, int8_t> *sb = xq + sl * SW;
+    if (FMT == LB_Q1_0) { // 8 consecutive bytes
+        const uint2 t = ld2<AS>(sb + 32 * (a & 3) + 8 * (a >> 2));
+        r.v[0] = make_uint4(t.x, t.y, 0u, 0u);
+    } else if (FMT == LB_Q2_0_G64) { // every other byte of 16
+        r.v[0] = ld4<AS>(sb + 16 * (a >> 1));
+    } else { // every fourth byte of 32
+        r.v[0] = ld4<AS>(sb + 32 * (a >> 2));
+        r.v[FMT == LB_TERNARY_PLANAR ? 1 : 0] = ld4<AS>(sb + 32 * (a >> 2) + 16);
+    }
+    return r;
+}
+template <int FMT, int AS>
+__device__ __forceinline__ void stage_store_item(const StageLoads<FMT, AS> &t, int it, uint32_t *__restrict__ lds)
+{
+    constexpr int WPS = F<FMT>::SW / 8, REC = F<FMT>::REC;
+    const int sl = it / WPS, a = it % WPS;
+    uint32_t u0, u1;
+    if (FMT == LB_Q1_0) {
+        u0 = t.v[0].x;
+        u1 = t.v[0].y;
+    } else if (FMT == LB_Q2_0_G64) {
+        const uint32_t sel = (a & 1) ? 0x07050301u : 0x06040200u;
+        u0 = __builtin_amdgcn_perm(t.v[0].y, t.v[0].x, sel);
+        u1 = __builtin_amdgcn_perm(t.v[0].w, t.v[0].z, sel);
+    } else {
+        const uint32_t r = (uint32_t)(a & 3), sel = r | ((4u + r) << 8);
+        const uint4 lo4 = t.v[0], hi4 = t.v[FMT == LB_TERNARY_PLANAR ? 1 : 0];
+        u0 = __builtin_amdgcn_perm(__builtin_amdgcn_perm(lo4.w, lo4.z, sel), __builtin_amdgcn_perm(lo4.y, lo4.x, sel),
+                                   0x05040100u);
+        u1 = __builtin_amdgcn_perm(__builtin_amdgcn_perm(hi4.w, hi4.z, sel), __builtin_amdgcn_perm(hi4.y, hi4.x, sel),
+                                   0x05040100u);
+    }
+    uint32_t *rec = lds + sl * REC;
+    rec[2 * a + 0] = nibbles16(u0) | (nibbles16(u1) << 16);
+    rec[2 * a + 1] = nibbles16(u0 >> 4) | (nibbles16(u1 >> 4) << 16);
+}
+struct BlockLoads {
+    uint4 b0, b1;
+    uint32_t sc;
+};
+template <int FMT, int AS>
+__device__ __forceinline__ BlockLoads stage_load_block(src_t<AS, int8_t> *xq, src_t<AS, uint16_t> *xscale, int it)
+{
+    constexpr int SW = F<FMT>::SW, NAB = F<FMT>::NAB > 0 ? F<FMT>::NAB : 1;
+    const int sl = it / NAB, j = it % NAB;
+    return {ld4<AS>(xq + sl * SW + 32 * j), ld4<AS>(xq + sl * SW + 32 * j + 16), (uint32_t)xscale[it]};
+}
+template <int FMT>
+__device__ __forceinline__ void stage_store_block(const BlockLoads &t, int it, uint32_t *__restrict__ lds)
+{
+    constexpr int SW = F<FMT>::SW, NAB = F<FMT>::NAB > 0 ? F<FMT>::NAB : 1, REC = F<FMT>::REC;
+    const int sl = it / NAB, j = it % NAB;
+    int sq = 0;
+    const uint32_t w[8] = {t.b0.x, t.b0.y, t.b0.z, t.b0.w, t.b1.x, t.b1.y, t.b1.z, t.b1.w};
+#pragma unroll
+    for (int k = 0; k < 8; k++)
+        sq = __builtin_amdgcn_sdot4((int)w[k], 0x01010101, sq, false);
+    // Q1_0 keeps 2 d_x / 2^j (exact): its block sums are 2 S - sum(q), S = the sum of q where the bit is 1,
+    // and its products deliver 2^j S (the nibble value of mask position j)
+    const float dx = half_bits_to_float((uint16_t)t.sc);
+    const float q1f = j == 0 ? 2.0f : j == 1 ? 1.0f : j == 2 ? 0.5f : 0.25f;
+    uint32_t *rec = lds + sl * REC;
+    rec[SW / 4 + j] = __float_as_uint(FMT == LB_Q1_0 ? q1f * dx : dx);
+    rec[SW / 4 + F<FMT>::NAB + j] = (uint32_t)(-sq);
+}
+
+// The whole activation vector, staged by all threads of the workgroup as independent items: one item
+// per nibble-word pair (the 8 activation bytes it covers, one 8/16/32-byte load, gathered with byte
+// permutes where they are strided) and one per (slice, q8_0 block) for d_x and -sum(q).  A thread's
+// first items (UNR0 of the first kind, covering K up to 12288 for the ggml formats, and two of the
+// second) are loaded before pre() runs -- the caller issues its first weight rows there -- so the waits
+// for these loads never include the weights.  The source sits in global memory (AS = 1) or, when the
+// launch quantised it, in LDS (AS = 3); an explicit address space gives global or LDS loads instead of
+// flat ones.
+template <int FMT, int AS, typename Pre>
 __device__ __forceinline__ void stage_activation(const int8_t *__restrict__ xq_g, const void *__restrict__ xscale_g,
-                                                 int ns, uint32_t *__restrict__ lds)
+                                                 int ns, uint32_t *__restrict__ lds, Pre &&pre)
 {
     src_t<AS, int8_t> *xq = (src_t<AS, int8_t> *)xq_g;
     src_t<AS, uint16_t> *xscale = (src_t<AS, uint16_t> *)xscale_g;
-    constexpr int SW = F<FMT>::SW, NAB = F<FMT>::NAB, REC = F<FMT>::REC;
+    constexpr int SW = F<FMT>::SW, NAB = F<FMT>::NAB;
     constexpr int WPS = SW / 8; // nibble-word pairs per slice
-    constexpr int UNR = 4;
-    const int nw = ns * WPS;
-    for (int base = threadIdx.x; base < nw; base += UNR * WG) {
-        uint4 v[UNR][FMT == LB_TERNARY_PLANAR ? 2 : 1];
+    constexpr int UNR0 = 6, NB0 = 2, UNR = 4;
+    const int nw = ns * WPS, nblk = ns * NAB;
+    const int t = threadIdx.x;
+    StageLoads<FMT, AS> v0[UNR0];
 #pragma unroll
-        for (int q = 0; q < UNR; q++) {
-            const int it = base + q * WG;
-            if (it < nw) {
-                const int sl = it / WPS, a = it % WPS;
-                src_t<AS, int8_t> *sb = xq + sl * SW;
-                if (FMT == LB_Q1_0) { // 8 consecutive bytes
-                    const uint2 t = ld2<AS>(sb + 32 * (a & 3) + 8 * (a >> 2));
-                    v[q][0] = make_uint4(t.x, t.y, 0u, 0u);
-                } else if (FMT == LB_Q2_0_G64) { // every other byte of 16
-                    v[q][0] = ld4<AS>(sb + 16 * (a >> 1));
-                } else { // every fourth byte of 32
-                    v[q][0] = ld4<AS>(sb + 32 * (a >> 2));
-                    v[q][FMT == LB_TERNARY_PLANAR ? 1 : 0] = ld4<AS>(sb + 32 * (a >> 2) + 16);
-                }
-            }
-        }
+    for (int q = 0; q < UNR0; q++)
+        if (t + q * WG < nw)
+            v0[q] = stage_load_item<FMT, AS>(xq, t + q * WG);
+    // (unconditional, the index clamped to the last block: the scale's conversion then stays with its use,
+    // after the weight rows, instead of joining the load under a branch and waiting for it here)
+    BlockLoads k0[NB0];
 #pragma unroll
-        for (int q = 0; q < UNR; q++) {
-            const int it = base + q * WG;
-            if (it < nw) {
-                const int sl = it / WPS, a = it % WPS;
-                uint32_t u0, u1;
-                if (FMT == LB_Q1_0) {
-                    u0 = v[q][0].x;
-                    u1 = v[q][0].y;
-                } else if (FMT == LB_Q2_0_G64) {
-                    const uint32_t sel = (a & 1) ? 0x07050301u : 0x06040200u;
-                    u0 = __builtin_amdgcn_perm(v[q][0].y, v[q][0].x, sel);
-                    u1 = __builtin_amdgcn_perm(v[q][0].w, v[q][0].z, sel);
-                } else {
-                    const uint32_t r = (uint32_t)(a & 3), sel = r | ((4u + r) << 8);
-                    const uint4 lo4 = v[q][0], hi4 = v[q][FMT == LB_TERNARY_PLANAR ? 1 : 0];
-                    u0 = __builtin_amdgcn_perm(__builtin_amdgcn_perm(lo4.w, lo4.z, sel), __builtin_amdgcn_perm(lo4.y, lo4.x, sel),
-                                               0x05040100u);
-                    u1 = __builtin_amdgcn_perm(__builtin_amdgcn_perm(hi4.w, hi4.z, sel), __builtin_amdgcn_perm(hi4.y, hi4.x, sel),
-                                               0x05040100u);
-                }
-                uint32_t *rec = lds + sl * REC;
-                rec[2 * a + 0] = nibbles16(u0) | (nibbles16(u1) << 16);
-                rec[2 * a + 1] = nibbles16(u0 >> 4) | (nibbles16(u1 >> 4) << 16);
-            }
-        }
+    for (int q = 0; q < NB0; q++)
+        if (NAB > 0)
+            k0[q] = stage_load_block<FMT, AS>(xq, xscale, min(t + q * WG, nblk - 1));
+    __builtin_amdgcn_sched_barrier(0);
+    pre();
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int q = 0; q < UNR0; q++)
+        if (t + q * WG < nw)
+            stage_store_item<FMT, AS>(v0[q], t + q * WG, lds);
+#pragma unroll
+    for (int q = 0; q < NB0; q++)
+        if (NAB > 0 && t + q * WG < nblk)
+            stage_store_block<FMT>(k0[q], t + q * WG, lds);
+    for (int base = t + UNR0 * WG; base < nw; base += UNR * WG) {
+        StageLoads<FMT, AS> v[UNR];
+#pragma unroll
+        for (int q = 0; q < UNR; q++)
+            if (base + q * WG < nw)
+                v[q] = stage_load_item<FMT, AS>(xq, base + q * WG);
+#pragma unroll
+        for (int q = 0; q < UNR; q++)
+            if (base + q * WG < nw)
+                stage_store_item<FMT, AS>(v[q], base + q * WG, lds);
     }
-    if (NAB > 0) {
-        for (int it = threadIdx.x; it < ns * NAB; it += WG) {
-            const int sl = it / (NAB > 0 ? NAB : 1), j = it % (NAB > 0 ? NAB : 1);
-            const uint4 b0 = ld4<AS>(xq + sl * SW + 32 * j), b1 = ld4<AS>(xq + sl * SW + 32 * j + 16);
-            int sq = 0;
-            sq = __builtin_amdgcn_sdot4((int)b0.x, 0x01010101, sq, false);
-            sq = __builtin_amdgcn_sdot4((int)b0.y, 0x01010101, sq, false);
-            sq = __builtin_amdgcn_sdot4((int)b0.z, 0x01010101, sq, false);
-            sq = __builtin_amdgcn_sdot4((int)b0.w, 0x01010101, sq, false);
-            sq = __builtin_amdgcn_sdot4((int)b1.x, 0x01010101, sq, false);
-            sq = __builtin_amdgcn_sdot4((int)b1.y, 0x01010101, sq, false);
-            sq = __builtin_amdgcn_sdot4((int)b1.z, 0x01010101, sq, false);
-            sq = __builtin_amdgcn_sdot4((int)b1.w, 0x01010101, sq, false);
-            // Q1_0 keeps 2 d_x / 2^j (exact): its block sums are 2 S - sum(q), S = the sum of q where the
-            // bit is 1, and its products deliver 2^j S (the nibble value of mask position j)
-            const float dx = half_bits_to_float(xscale[it]);
-            const float q1f = j == 0 ? 2.0f : j == 1 ? 1.0f : j == 2 ? 0.5f : 0.25f;
-            uint32_t *rec = lds + sl * REC;
-            rec[SW / 4 + j] = __float_as_uint(FMT == LB_Q1_0 ? q1f * dx : dx);
-            rec[SW / 4 + NAB + j] = (uint32_t)(-sq);
-        }
-    }
+    if (NAB > 0)
+        for (int it = t + NB0 * WG; it < nblk; it += WG)
+            stage_store_block<FMT>(stage_load_block<FMT, AS>(xq, xscale, it), it, lds);
 }
 
 __device__ __forceinline__ int sdot8(uint32_t a, uint32_t b, int c)
@@ -425,44 +481,60 @@ __device__ __forceinline__ void matvec_tile(const uint8_t *__restrict__ W, int N
     uint32_t onext = (uint32_t)(row0 + min(rbase, nrows - 1)) * rowbytes;
 
     RowRegs<FMT, S> buf[NB];
+    // the first weight rows, requested once the activation's first loads are out (see stage_activation)
+    auto first_rows = [&]() {
 #pragma unroll
-    for (int b = 0; b < NB - 1; b++) {
-        issue_row<FMT, L, S, FULL>(buf[b], W, scales, min(onext, last), slo, sls);
-        onext += stepb;
-    }
+        for (int b = 0; b < NB - 1; b++) {
+            issue_row<FMT, L, S, FULL>(buf[b], W, scales, min(onext, last), slo, sls);
+            onext += stepb;
+        }
+    };
 
     if (QIN) {
         // fp32 activations (LB_ACT_F32_Q8_0): quantised to q8_0 into LDS past the staged records with the
-        // arithmetic of the quantise kernel, then staged from there like quantised ones
+        // arithmetic of the quantise kernel, then staged from there like quantised ones.  K / 4 float4
+        // chunks, eight per block; WG is a multiple of 8, so a block's eight lanes are all in range or all
+        // out.  A thread's first QPRE chunks (K up to 12288) are loaded before the first weight rows.
         int8_t *qb = reinterpret_cast<int8_t *>(lds + ns * REC);
         uint16_t *qs = reinterpret_cast<uint16_t *>(qb + K);
-        // K / 4 float4 chunks, eight per block, four chunks per thread in flight at once; WG is a
-        // multiple of 8, so a block's eight lanes are all in range or all out
-        constexpr int QU = 4;
+        constexpr int QPRE = 12, QU = 4;
         const int nc = K / 4;
-        for (int c0 = threadIdx.x; c0 < nc; c0 += QU * WG) {
-            float4 v[QU];
-#pragma unroll
-            for (int u = 0; u < QU; u++) {
-                const int c = c0 + u * WG;
-                const sv4f t = c < nc ? ((src_t<1, sv4f> *)x)[c] : sv4f{0.0f, 0.0f, 0.0f, 0.0f};
-                v[u] = make_float4(t.x, t.y, t.z, t.w);
+        const int npre = min((nc + WG - 1) / WG, QPRE); // uniform
+        auto ldx = [&](int c) {
+            const sv4f t = ((src_t<1, sv4f> *)x)[min(c, nc - 1)];
+            return make_float4(t.x, t.y, t.z, t.w);
+        };
+        auto quant = [&](float4 v, int c) {
+            const float amax = q8_0_block_amax8(v);
+            if (c < nc) {
+                reinterpret_cast<uint32_t *>(qb)[c] = q8_0_pack4(v, amax);
+                if ((c & 7) == 0)
+                    qs[c >> 3] = q8_0_scale_bits(amax);
             }
+        };
+        float4 v[QPRE];
 #pragma unroll
-            for (int u = 0; u < QU; u++) {
-                const int c = c0 + u * WG;
-                const float amax = q8_0_block_amax8(v[u]);
-                if (c < nc) {
-                    reinterpret_cast<uint32_t *>(qb)[c] = q8_0_pack4(v[u], amax);
-                    if ((c & 7) == 0)
-                        qs[c >> 3] = q8_0_scale_bits(amax);
-                }
-            }
+        for (int u = 0; u < QPRE; u++)
+            if (u < npre)
+                v[u] = ldx(threadIdx.x + u * WG);
+        first_rows();
+#pragma unroll
+        for (int u = 0; u < QPRE; u++)
+            if (u < npre)
+                quant(v[u], threadIdx.x + u * WG);
+        for (int c0 = threadIdx.x + QPRE * WG; c0 < nc; c0 += QU * WG) {
+            float4 w[QU];
+#pragma unroll
+            for (int u = 0; u < QU; u++)
+                w[u] = ldx(c0 + u * WG);
+#pragma unroll
+            for (int u = 0; u < QU; u++)
+                quant(w[u], c0 + u * WG);
         }
         __syncthreads();
-        stage_activation<FMT, 3>(qb, qs, ns, lds);
+        stage_activation<FMT, 3>(qb, qs, ns, lds, [] {});
     } else {
-        stage_activation<FMT, 1>(xq, xscale, ns, lds);
+        stage_activation<FMT, 1>(xq, xscale, ns, lds, first_rows);
     }
     __syncthreads();
 
