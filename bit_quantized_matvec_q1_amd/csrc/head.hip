@@ -210,10 +210,10 @@ static hipError_t launch_head_i8_cfg(const int8_t *W, const float *sw, int N, in
 {
     // one workgroup per resident slot, each streaming one contiguous range of rows with x loaded once:
     // no second, partly filled round of workgroups, and x is read from L2 once per slot
-    constexpr int STEP = (64 / L) * (WG / 64);
+    constexpr int PASS = 3 * (64 / L) * (WG / 64); // rows of one pass of the three-row ring
     const int slots = head_i8_slots<L, S>();
     int tile = (N + slots - 1) / slots;
-    tile = (tile + STEP - 1) / STEP * STEP;
+    tile = (tile + PASS - 1) / PASS * PASS;
     const int grid = (N + tile - 1) / tile;
     hipLaunchKernelGGL((head_i8_kernel<L, S>), dim3(grid), dim3(WG), 0, s, W, sw, N, K, x, y, tile);
     return hipGetLastError();

@@ -576,6 +576,18 @@ __device__ __forceinline__ void matvec_tile(const uint8_t *__restrict__ W, int N
     // the tile's outputs y[row0, row0 + nrows) as a buffer range (the sums instantiation may run without y)
     const __amdgpu_buffer_rsrc_t yt =
         __builtin_amdgcn_make_buffer_rsrc(EMIT ? nullptr : y + row0, 0, EMIT ? 0 : nrows * 4, 0x00020000);
+    // A tile of at most NB - 1 passes has all its rows' loads in flight already (the first passes were
+    // requested before the staging): compute exactly its passes, no ring.
+    if (nrows <= (NB - 1) * STEP) { // uniform
+#pragma unroll
+        for (int b = 0; b < NB - 1; b++) {
+            const int rl = b * STEP + rbase;
+            if (b == 0 || b * STEP < nrows) // uniform
+                compute_row<FMT, L, S, EMIT, FULL>(buf[b].code, buf[b].sc, act, cfold, ns, li, rl < nrows, row0 + rl,
+                                                   w_scale, sx, y, sums, yt, rl);
+        }
+        return;
+    }
     for (int it = 0; it < nrows; it += NB * STEP) {
 #pragma unroll
         for (int b = 0; b < NB; b++) {
