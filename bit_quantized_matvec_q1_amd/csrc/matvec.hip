@@ -577,8 +577,10 @@ __device__ __forceinline__ void matvec_tile(const uint8_t *__restrict__ W, int N
     const __amdgpu_buffer_rsrc_t yt =
         __builtin_amdgcn_make_buffer_rsrc(EMIT ? nullptr : y + row0, 0, EMIT ? 0 : nrows * 4, 0x00020000);
     // A tile of at most NB - 1 passes has all its rows' loads in flight already (the first passes were
-    // requested before the staging): compute exactly its passes, no ring.
-    if (nrows <= (NB - 1) * STEP) { // uniform
+    // requested before the staging): compute exactly its passes, no ring.  Such tiles are what a small
+    // batch (one dependency phase of a token, fp32 inputs) is cut into; the instantiations for quantised
+    // inputs leave the path out (a second copy of the row arithmetic costs them registers).
+    if (QIN && nrows <= (NB - 1) * STEP) { // uniform
 #pragma unroll
         for (int b = 0; b < NB - 1; b++) {
             const int rl = b * STEP + rbase;
