@@ -283,8 +283,8 @@ lb_status dense_head_matvec(const uint16_t *W, int64_t N, int64_t K, const float
     const char *fn = "dense_head_matvec";
     if (N < 0 || K < 0 || N > INT32_MAX)
         return fail(LB_ESHAPE, fn, "negative size");
-    if (K % 8 || K > 4096)
-        return fail(LB_ESHAPE, fn, "K must be a multiple of 8 and at most 4096");
+    if (K % 8 || K > 32768)
+        return fail(LB_ESHAPE, fn, "K must be a multiple of 8 and at most 32768");
     if (N * K * 2 >= (int64_t(1) << 32))
         return fail(LB_ESHAPE, fn, "weight tensor of 4 GiB or more");
     if (N == 0)
@@ -332,8 +332,8 @@ lb_status dense_head_matvec_i8(const int8_t *W, const float *row_scale, int64_t 
     const char *fn = "dense_head_matvec_i8";
     if (N < 0 || K < 0 || N > INT32_MAX)
         return fail(LB_ESHAPE, fn, "negative size");
-    if (K % 16 || K > 8192)
-        return fail(LB_ESHAPE, fn, "K must be a multiple of 16 and at most 8192");
+    if (K % 16 || K > 32768)
+        return fail(LB_ESHAPE, fn, "K must be a multiple of 16 and at most 32768");
     if (N * K >= (int64_t(1) << 32))
         return fail(LB_ESHAPE, fn, "weight tensor of 4 GiB or more");
     if (N == 0)

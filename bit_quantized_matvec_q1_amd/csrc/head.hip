@@ -4,9 +4,13 @@
 // Purely bandwidth-bound: each weight byte is read once with 16-byte loads (8 bf16), widened to fp32
 // exactly (bf16 is the top half of a binary32), and multiply-added against x held in VGPRs.  A row is
 // spread over one wave (each lane owns S chunks of 8 columns, strided so every wave-wide load is
-// contiguous) and closed with a cross-lane tree.
+// contiguous) and closed with a cross-lane tree.  Rows longer than the registers hold x for (4096 columns
+// here, 8192 for the int8 head) run as column segments, one launch each in stream order: the first
+// stores its partial sums, every later one adds its own to them (one atomic add per row and segment, in a
+// fixed order, so the result does not depend on timing).
 #include "lowbit_internal.h"
 
+#include <algorithm>
 #include <atomic>
 
 namespace lb {
@@ -19,8 +23,20 @@ typedef __attribute__((address_space(1))) const uint8_t ghu8;
 // (chunk offsets clamped to the row's last chunk, row offsets to the tile's last row -- both in bounds,
 // their results never stored or multiplied by a zero x), non-temporal (the weights are read once), and
 // issued one row ahead into a second register buffer.
-template <int S>
-__global__ __launch_bounds__(WG) void head_kernel(const uint16_t *__restrict__ W, int N, int K,
+// The store of a row's total: the first segment writes it, later ones add to it.  Every lane issues it; a
+// lane without the total addresses past the tile's output range, where the buffer unit drops it.
+template <bool ADD> __device__ __forceinline__ void put_row(__amdgpu_buffer_rsrc_t yt, bool keep, int rl, float v)
+{
+    const uint32_t off = keep ? (uint32_t)rl * 4u : 0x80000000u;
+    if constexpr (ADD)
+        __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(v, yt, off, 0, 0);
+    else
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), yt, off, 0, 0);
+}
+
+// One column segment [0, K) of the rows (W and x already offset to it); ldw: the full row length.
+template <int S, bool ADD>
+__global__ __launch_bounds__(WG) void head_kernel(const uint16_t *__restrict__ W, int N, int K, int ldw,
                                                   const float *__restrict__ x, float *__restrict__ y, int tile_rows)
 {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -46,7 +62,7 @@ __global__ __launch_bounds__(WG) void head_kernel(const uint16_t *__restrict__ W
     const int row0 = blockIdx.x * tile_rows;
     const int nrows = min(tile_rows, N - row0);
     constexpr int STEP = WG / 64;
-    const uint32_t rowb = (uint32_t)K * 2u;
+    const uint32_t rowb = (uint32_t)ldw * 2u;
     const uint32_t last = (uint32_t)(row0 + nrows - 1) * rowb;
     uint32_t onext = (uint32_t)(row0 + min(wave, nrows - 1)) * rowb;
     uint4 buf[2][S];
@@ -84,10 +100,7 @@ __global__ __launch_bounds__(WG) void head_kernel(const uint16_t *__restrict__ W
             }
             acc = group_sum_f<64>(acc);
             const int rl = cur + wave;
-            // every lane stores; a lane without the row's total addresses past the tile's output range,
-            // where the buffer unit drops it (no branch around the store)
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc), yt,
-                                                  rl < nrows && lane == 63 ? (uint32_t)rl * 4u : 0x80000000u, 0, 0);
+            put_row<ADD>(yt, rl < nrows && lane == 63, rl, acc); // no branch around the store
         }
     }
 }
@@ -98,10 +111,10 @@ __global__ __launch_bounds__(WG) void head_kernel(const uint16_t *__restrict__ W
 // multiply-added against x held in VGPRs; the row's scale multiplies the finished sum.  A row takes L
 // lanes (64 / L rows per wave) and each lane S chunks, L chosen so that L * S covers the row's chunks with
 // the fewest idle lane slots (K = 2560: 160 chunks = 32 lanes x 5).
-template <int L, int S>
+template <int L, int S, bool ADD>
 __global__ __launch_bounds__(WG) void head_i8_kernel(const int8_t *__restrict__ W, const float *__restrict__ sw, int N,
-                                                     int K, const float *__restrict__ x, float *__restrict__ y,
-                                                     int tile_rows)
+                                                     int K, int ldw, const float *__restrict__ x,
+                                                     float *__restrict__ y, int tile_rows)
 {
     constexpr int G = 64 / L;            // rows per wave
     constexpr int STEP = G * (WG / 64);  // rows per workgroup iteration
@@ -115,7 +128,7 @@ __global__ __launch_bounds__(WG) void head_i8_kernel(const int8_t *__restrict__ 
     const int row0 = blockIdx.x * tile_rows;
     const int nrows = min(tile_rows, N - row0);
     const int rbase = wave * G + g; // this lane's row within an iteration
-    const uint32_t rowb = (uint32_t)K;
+    const uint32_t rowb = (uint32_t)ldw;
     const uint32_t last = (uint32_t)(row0 + nrows - 1) * rowb;
     uint32_t onext = (uint32_t)(row0 + min(rbase, nrows - 1)) * rowb;
     // a ring of NB register buffers: NB - 1 rows' loads in flight while a row is computed (3 measured
@@ -176,10 +189,7 @@ __global__ __launch_bounds__(WG) void head_i8_kernel(const int8_t *__restrict__ 
             }
             acc = group_sum_f<L>(acc);
             const int rl = cur + rbase;
-            // every lane stores; a lane without the row's total addresses past the tile's output range,
-            // where the buffer unit drops it (no branch around the store)
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sbuf[b] * acc), yt,
-                                                  rl < nrows && li == L - 1 ? (uint32_t)rl * 4u : 0x80000000u, 0, 0);
+            put_row<ADD>(yt, rl < nrows && li == L - 1, rl, sbuf[b] * acc); // no branch around the store
         }
     }
 }
@@ -196,7 +206,8 @@ template <int L, int S> static int head_i8_slots()
         int cus = 0, nb = 0;
         if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
             cus = 1;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, head_i8_kernel<L, S>, WG, 0) != hipSuccess || nb < 1)
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, head_i8_kernel<L, S, false>, WG, 0) != hipSuccess ||
+            nb < 1)
             nb = 1;
         v = cus * nb;
         cache[dev].store(v, std::memory_order_relaxed);
@@ -205,8 +216,8 @@ template <int L, int S> static int head_i8_slots()
 }
 
 template <int L, int S>
-static hipError_t launch_head_i8_cfg(const int8_t *W, const float *sw, int N, int K, const float *x, float *y,
-                                     hipStream_t s)
+static hipError_t launch_head_i8_cfg(const int8_t *W, const float *sw, int N, int K, int ldw, bool add,
+                                     const float *x, float *y, hipStream_t s)
 {
     // one workgroup per resident slot, each streaming one contiguous range of rows with x loaded once:
     // no second, partly filled round of workgroups, and x is read from L2 once per slot
@@ -215,11 +226,16 @@ static hipError_t launch_head_i8_cfg(const int8_t *W, const float *sw, int N, in
     int tile = (N + slots - 1) / slots;
     tile = (tile + PASS - 1) / PASS * PASS;
     const int grid = (N + tile - 1) / tile;
-    hipLaunchKernelGGL((head_i8_kernel<L, S>), dim3(grid), dim3(WG), 0, s, W, sw, N, K, x, y, tile);
+    if (add)
+        hipLaunchKernelGGL((head_i8_kernel<L, S, true>), dim3(grid), dim3(WG), 0, s, W, sw, N, K, ldw, x, y, tile);
+    else
+        hipLaunchKernelGGL((head_i8_kernel<L, S, false>), dim3(grid), dim3(WG), 0, s, W, sw, N, K, ldw, x, y, tile);
     return hipGetLastError();
 }
 
-hipError_t launch_head_i8(const int8_t *W, const float *sw, int64_t N, int64_t K, const float *x, float *y, hipStream_t s)
+// One column segment (at most 8192 columns) of the int8 head.
+static hipError_t launch_head_i8_seg(const int8_t *W, const float *sw, int64_t N, int64_t K, int64_t ldw, bool add,
+                                     const float *x, float *y, hipStream_t s)
 {
     const int nch = (int)(K / 16);
     // lanes per row: the fewest idle lane slots (L * S - nch) with S <= 8, then the most lanes
@@ -231,11 +247,11 @@ hipError_t launch_head_i8(const int8_t *W, const float *sw, int64_t N, int64_t K
             S = sl;
         }
     }
-    const int n = (int)N, k = (int)K;
+    const int n = (int)N, k = (int)K, ld = (int)ldw;
     switch (L * 16 + S) {
 #define LB_HEAD_I8(l, sv)                                                                                     \
     case l * 16 + sv:                                                                                         \
-        return launch_head_i8_cfg<l, sv>(W, sw, n, k, x, y, s);
+        return launch_head_i8_cfg<l, sv>(W, sw, n, k, ld, add, x, y, s);
 #define LB_HEAD_I8_L(l)                                                                                       \
     LB_HEAD_I8(l, 1) LB_HEAD_I8(l, 2) LB_HEAD_I8(l, 3) LB_HEAD_I8(l, 4) LB_HEAD_I8(l, 5) LB_HEAD_I8(l, 6)       \
     LB_HEAD_I8(l, 7) LB_HEAD_I8(l, 8)
@@ -247,23 +263,46 @@ hipError_t launch_head_i8(const int8_t *W, const float *sw, int64_t N, int64_t K
     }
 }
 
+hipError_t launch_head_i8(const int8_t *W, const float *sw, int64_t N, int64_t K, const float *x, float *y, hipStream_t s)
+{
+    constexpr int64_t SEG = 8192; // the columns one launch holds x for
+    for (int64_t k0 = 0; k0 < K; k0 += SEG) {
+        const hipError_t e = launch_head_i8_seg(W + k0, sw, N, std::min(SEG, K - k0), K, k0 > 0, x + k0, y, s);
+        if (e != hipSuccess)
+            return e;
+    }
+    return hipSuccess;
+}
+
 hipError_t launch_head(const uint16_t *W, int64_t N, int64_t K, const float *x, float *y, hipStream_t s)
 {
-    const int nch = (int)(K / 8);
-    const int S = (nch + 63) / 64;
+    constexpr int64_t SEG = 4096; // the columns one launch holds x for
     const int tile = 64;
     const int grid = (int)((N + tile - 1) / tile);
-    switch (S) {
+    for (int64_t k0 = 0; k0 < K; k0 += SEG) {
+        const int kseg = (int)std::min(SEG, K - k0);
+        const int S = (kseg / 8 + 63) / 64;
+        const bool add = k0 > 0;
+        switch (S) {
 #define LB_HEAD(n)                                                                                            \
     case n:                                                                                                   \
-        hipLaunchKernelGGL(head_kernel<n>, dim3(grid), dim3(WG), 0, s, W, (int)N, (int)K, x, y, tile);        \
+        if (add)                                                                                              \
+            hipLaunchKernelGGL((head_kernel<n, true>), dim3(grid), dim3(WG), 0, s, W + k0, (int)N, kseg, (int)K,   \
+                               x + k0, y, tile);                                                              \
+        else                                                                                                  \
+            hipLaunchKernelGGL((head_kernel<n, false>), dim3(grid), dim3(WG), 0, s, W + k0, (int)N, kseg, (int)K,  \
+                               x + k0, y, tile);                                                              \
         break;
-        LB_HEAD(1) LB_HEAD(2) LB_HEAD(3) LB_HEAD(4) LB_HEAD(5) LB_HEAD(6) LB_HEAD(7) LB_HEAD(8)
+            LB_HEAD(1) LB_HEAD(2) LB_HEAD(3) LB_HEAD(4) LB_HEAD(5) LB_HEAD(6) LB_HEAD(7) LB_HEAD(8)
 #undef LB_HEAD
-    default:
-        return hipErrorInvalidValue;
+        default:
+            return hipErrorInvalidValue;
+        }
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess)
+            return e;
     }
-    return hipGetLastError();
+    return hipSuccess;
 }
 
 } // namespace lb

@@ -160,8 +160,9 @@ lb_status lowbit_block_sums(int fmt, const void *W, int64_t N, int64_t K, int af
  * Dense bf16 head matvec y[N] = sum_k bf16_to_f32(W[n][k]) * x[k], accumulated in fp32
  * (tritium "Architecture", section 3: the dense head is the largest single stream; bf16 storage).
  *   W: device uint16 bf16 bits [N][K], 16-byte aligned, K % 8 == 0; x: device fp32 [K], 16-byte aligned;
- *   y: device fp32 [N].  K must be a multiple of 8 and at most 4096 (the activation vector is held in
- *   registers) and the weights smaller than 4 GiB; otherwise LB_ESHAPE.
+ *   y: device fp32 [N].  K must be a multiple of 8 and at most 32768 and the weights smaller than 4 GiB;
+ *   otherwise LB_ESHAPE.  Rows longer than 4096 columns run as column segments of 4096, one launch each on
+ *   `s`: the first writes y, each later one adds its partial sums to it (in that fixed order).
  */
 lb_status dense_head_matvec(const uint16_t *W, int64_t N, int64_t K, const float *x, float *y, hipStream_t s);
 
@@ -182,8 +183,10 @@ lb_status lowbit_matvec_popcount(const void *W, int64_t N, int64_t K, float w_te
  * "Architecture", section 10: int8 is the obvious move for the head, at half the bf16 head's bytes; the
  * reading taken: symmetric int8 weights with one fp32 scale per row).
  *   W: device int8 [N][K], 16-byte aligned; row_scale: device fp32 [N], 4-byte aligned; x: device fp32 [K],
- *   16-byte aligned; y: device fp32 [N], 4-byte aligned.  K must be a multiple of 16 and at most 8192
- *   (the activation vector is held in registers) and the weights smaller than 4 GiB; otherwise LB_ESHAPE.
+ *   16-byte aligned; y: device fp32 [N], 4-byte aligned.  K must be a multiple of 16 and at most 32768 and
+ *   the weights smaller than 4 GiB; otherwise LB_ESHAPE.  Rows longer than 8192 columns run as column
+ *   segments of 8192, one launch each on `s`: the first writes row_scale[n] times its partial sum, each
+ *   later one adds its own (in that fixed order).
  */
 lb_status dense_head_matvec_i8(const int8_t *W, const float *row_scale, int64_t N, int64_t K, const float *x, float *y,
                                hipStream_t s);

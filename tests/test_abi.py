@@ -99,7 +99,7 @@ def test_other_entry_points_validate():
     assert lib.lowbit_block_sums(L.Q8_0, A16, 8, 160, L.ACT_Q8_0, A16, A16, 2, A16, None) == L.LB_ESHAPE
     assert lib.lowbit_block_sums(L.Q2_0_G64, A16, 8, 64, L.ACT_Q8_0, A16, A16, 1, None, None) == L.LB_EINVAL
     assert lib.dense_head_matvec(A16, 8, 12, A16, A16, None) == L.LB_ESHAPE
-    assert lib.dense_head_matvec(A16, 8, 8192, A16, A16, None) == L.LB_ESHAPE
+    assert lib.dense_head_matvec(A16, 8, 32768 + 8, A16, A16, None) == L.LB_ESHAPE
     assert lib.dense_head_matvec(A16, 1 << 20, 2048, A16, A16, None) == L.LB_ESHAPE  # 4 GiB of weights
     assert lib.dense_head_matvec(A16 + 2, 8, 64, A16, A16, None) == L.LB_EALIGN
     assert lib.lowbit_matvec_popcount(A16, 8, 8192 + 64, 1.0, A16, A16, A16, None, None) == L.LB_ESHAPE
@@ -107,7 +107,7 @@ def test_other_entry_points_validate():
     assert lib.lowbit_matvec_popcount(A16, 8, 128, 1.0, A16, A16, None, None, None) == L.LB_EINVAL  # no output
     assert lib.lowbit_matvec_popcount(A16, 8, 128, 1.0, A16, A16, None, A16 + 2, None) == L.LB_EALIGN
     assert lib.dense_head_matvec_i8(A16, A16, 8, 24, A16, A16, None) == L.LB_ESHAPE  # K % 16
-    assert lib.dense_head_matvec_i8(A16, A16, 8, 8192 + 16, A16, A16, None) == L.LB_ESHAPE
+    assert lib.dense_head_matvec_i8(A16, A16, 8, 32768 + 16, A16, A16, None) == L.LB_ESHAPE
     assert lib.dense_head_matvec_i8(A16, A16, 1 << 20, 4096, A16, A16, None) == L.LB_ESHAPE  # 4 GiB of weights
     assert lib.dense_head_matvec_i8(A16 + 8, A16, 8, 64, A16, A16, None) == L.LB_EALIGN
     assert lib.dense_head_matvec_i8(A16, None, 8, 64, A16, A16, None) == L.LB_EINVAL

@@ -17,7 +17,8 @@ def gpu_head(W, N, K, x):
     return host(y)
 
 
-@pytest.mark.parametrize("N,K", [(1, 8), (3, 64), (77, 520), (65, 1032), (1000, 2560), (300, 4096)])
+@pytest.mark.parametrize("N,K", [(1, 8), (3, 64), (77, 520), (65, 1032), (1000, 2560), (300, 4096), (129, 4104),
+                                 (65, 8192), (33, 12296), (20, 32768)])
 def test_head_shapes(N, K):
     say(f"case head N={N} K={K}")
     W = synth.head_weights(N, K, 4000 + N)
@@ -46,7 +47,7 @@ def gpu_head_i8(W, s, N, K, x):
 
 
 @pytest.mark.parametrize("N,K", [(1, 16), (3, 64), (77, 528), (65, 1040), (1000, 2560), (300, 4096), (17, 8192),
-                                 (129, 6912)])
+                                 (129, 6912), (65, 8208), (33, 16384), (20, 32768)])
 def test_head_i8_shapes(N, K):
     say(f"case head int8 N={N} K={K}")
     W, s = synth.head_weights_i8(N, K, 4200 + N)
@@ -71,6 +72,24 @@ def test_head_i8_full_size_sampled_and_extremes():
     xi = synth.rng(4304).integers(-64, 64, 1024).astype(np.float32)
     yi = gpu_head_i8(Wx, np.ones(64, np.float32), 64, 1024, xi)
     assert np.array_equal(yi.astype(np.float64), (Wx.astype(np.int64) @ xi.astype(np.int64)).astype(np.float64))
+
+
+def test_heads_column_segments_exact():
+    """Rows longer than one launch holds x for run as column segments whose partial sums are added in a fixed
+    order: with integer weights and activations every partial sum and their total stay below 2^24, so both
+    heads must give the integer dot products exactly (a ragged last segment included)."""
+    g = synth.rng(4400)
+    N, K = 33, 12296  # bf16: three 4096-column segments and one of 8
+    Wi = g.integers(-2, 3, (N, K))
+    Wb = (Wi.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)  # small integers are exact in bf16
+    xi = g.integers(-3, 4, K).astype(np.float32)
+    y = gpu_head(Wb, N, K, xi)
+    assert np.array_equal(y.astype(np.float64), (Wi @ xi.astype(np.int64)).astype(np.float64))
+    N, K = 32, 16400  # int8: two 8192-column segments and one of 16
+    W8 = np.where(g.integers(0, 2, (N, K)) == 1, 127, -128).astype(np.int8)
+    xi = g.integers(-3, 4, K).astype(np.float32)
+    y = gpu_head_i8(W8, np.ones(N, np.float32), N, K, xi)
+    assert np.array_equal(y.astype(np.float64), (W8.astype(np.int64) @ xi.astype(np.int64)).astype(np.float64))
 
 
 def _product(fmt, N, K, seed):
