@@ -20,12 +20,11 @@
 //    operand (activations) from LDS, one MFMA, one exact int32 sum per (weight row, activation row,
 //    block).  The weight unpack is shared by the 128 activation rows of the tile and the activation copy
 //    by its 64 weight rows, so per MFMA the per-step work stays small next to the rescale below.
-//  * Q2_0 and Q8_0: the accumulator input of every MFMA is a constant register tile holding 0x4B400000
-//    (1.5 * 2^23), so each result, read as fp32, is 1.5 * 2^23 + isum exactly; one FMA with the block's activation
-//    scale and -d_x * 1.5 * 2^23 gives round(d_x * isum) without a conversion.  Q1_0: a zero accumulator,
-//    each exact int32 result converted and multiply-added into the weight block's sum (fewer registers,
-//    which keeps two workgroups per CU).  The weight block scale is then applied with one more FMA (bankml
-//    technical report, section III.3: one multiply-add per q8_0 block, then one per weight block).
+//  * Q1_0, Q2_0 and Q8_0: the accumulator input of every MFMA is a constant register tile holding
+//    0x4B400000 (1.5 * 2^23), so each result, read as fp32, is 1.5 * 2^23 + isum exactly; one FMA with the
+//    block's activation scale and -d_x * 1.5 * 2^23 gives round(d_x * isum) without a conversion.  The
+//    weight block scale is then applied with one more FMA (bankml technical report, section III.3: one
+//    multiply-add per q8_0 block, then one per weight block).
 //  * Planar weights have no block scales: the MFMA accumulates int32 over the whole row and the two
 //    per-row / per-tensor scales are applied once at the end.
 #include "lowbit_internal.h"
@@ -393,10 +392,8 @@ __global__ __launch_bounds__(GT * KSPLIT, EMIT ? 2 * KSPLIT : 4) void gemm_kerne
     const uint8_t *wsc = W + (int64_t)N * rowcode;
     const uint8_t *xsc = reinterpret_cast<const uint8_t *>(Xscale);
 
-    // Q2_0: 16 registers of the bias, each made opaque to the compiler: a tile it knows to be uniform it
-    // rebuilds before every MFMA (16 moves each) instead of keeping it live.  Q1_0: a zero accumulator
-    // (its results are converted instead: the bias registers would push it past 128 VGPRs, and so to one
-    // workgroup per CU)
+    // 16 registers of the bias, each made opaque to the compiler: a tile it knows to be uniform it rebuilds
+    // before every MFMA (16 moves each) instead of keeping it live.  Planar: a zero accumulator.
     v16i cbias;
 #pragma unroll
     for (int i = 0; i < 16; i++) {
