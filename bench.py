@@ -32,7 +32,8 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 MFMA_I8_PEAK_TOPS = 5000.0  # MI355X dense int8, published
 METRIC = "effective weight GB/s & % HBM peak, 8B-shape batch-1 ternary matvec; prefill TOPS"
 PROFILE_PMC = os.path.join(ROOT, "profiles", "matvec_batched_q2_8b_token.pmc.txt")
-KERNEL_SRC = os.path.join(ROOT, "bit_quantized_matvec_q1_amd", "csrc", "matvec.hip")
+# the decode kernel and the batch tile planner: both decide the batched launch's traffic
+KERNEL_SRCS = [os.path.join(ROOT, "bit_quantized_matvec_q1_amd", "csrc", f) for f in ("matvec.hip", "abi.cpp")]
 
 
 def log(*a):
@@ -255,11 +256,14 @@ def time_token(tok, steps, warmup):
 
 def stored_traffic(kernel_name, algorithmic_bytes):
     """HBM bytes per launch from the committed rocprofv3 --pmc summary, if it was taken on the current
-    kernel source; otherwise None."""
+    kernel and tile-planner sources (sha256 over matvec.hip then abi.cpp); otherwise None."""
     if not os.path.exists(PROFILE_PMC):
         return None
     text = open(PROFILE_PMC).read()
-    src_hash = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
+    h = hashlib.sha256()
+    for f in KERNEL_SRCS:
+        h.update(open(f, "rb").read())
+    src_hash = h.hexdigest()
     m_hash = re.search(r"kernel_source_sha256:\s*([0-9a-f]{64})", text)
     m_bytes = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
     if not m_hash or not m_bytes or m_hash.group(1) != src_hash:

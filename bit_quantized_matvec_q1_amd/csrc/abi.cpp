@@ -369,27 +369,41 @@ lb_status lowbit_read_probe(const void *buf, int64_t nbytes, uint32_t *sink, hip
 
 // ---- batched decode ------------------------------------------------------------------------------
 
+// The tile size a large batch keeps, measured per format on whole tokens (the 8B shapes for Q1_0, Q2_0 and
+// Q8_0, the 2B shapes for planar and base-3; launch times with every size from 32 to 384 KiB forced): the
+// two nibble-product formats run fastest with small tiles, 64 KiB (96 KiB for rows above 8192 columns, which
+// stage three times the activation per tile) -- 3 % faster than 256 KiB for both --, planar and Q8_0 with
+// 256 KiB and base-3 with 224 KiB.
+static int64_t default_tile_bytes(int fmt, int64_t K)
+{
+    if (fmt == LB_Q1_0 || fmt == LB_Q2_0_G64)
+        return (K > 8192 ? 96 : 64) * 1024;
+    return (fmt == LB_TERNARY_B3 ? 224 : 256) * 1024;
+}
+
 // Tile plan of one launch group.  Every product is cut into row tiles (whole row iterations of the
-// configuration) of about the same weight bytes, between 16 and 384 KiB; the size is the one whose
-// in-order dispatch onto the group's resident workgroup slots (CUs x workgroups per CU) has the shortest
-// simulated makespan, each tile costing its weight bytes plus a fixed start-up share; among sizes within
-// 0.5 % of the best, the largest -- but 256 KiB unless the simulation predicts a makespan at least 5 %
-// shorter.  A whole token's products (gigabytes) keep 256 KiB tiles (smaller tiles pay more for their
-// activation staging, larger ones leave a ragged tail: both measured slower); a small batch -- one
-// dependency phase of a token, a few tens of MB -- gets tiles small enough to occupy every CU instead of
-// a few dozen workgroups.  Tiles are emitted largest first, so the partial tiles of every product fill
-// the tail of the launch.
+// configuration) of about the same weight bytes, between 16 and 384 KiB.  A large batch (four or more
+// rounds of the group's resident workgroup slots at the default size -- a whole token's products) keeps
+// the format's default size.  A smaller one -- one dependency phase of a token, a few tens of MB -- takes
+// the size whose in-order dispatch onto the slots (CUs x workgroups per CU) has the shortest simulated
+// makespan, each tile costing its weight bytes plus a fixed start-up share, if that beats the default by at
+// least 5 % (among sizes within 0.5 % of the best, the largest): tiles small enough to occupy every CU
+// instead of a few dozen workgroups.  Tiles are emitted largest first, so the partial tiles of every
+// product fill the tail of the launch.
 static void plan_tiles(int fmt, int cfg, std::vector<lb::DevDesc> &ds, int64_t slots, std::vector<lb::TileRef> &out)
 {
     constexpr int64_t kStartup = 24 * 1024; // bytes-equivalent of one workgroup's staging and start-up
-    constexpr int64_t kDefault = 256 * 1024; // the best fixed size measured on the 8B-shape tokens
+    int64_t maxk = 0;
+    for (const lb::DevDesc &d : ds)
+        maxk = std::max<int64_t>(maxk, d.K);
+    const int64_t kDefault = default_tile_bytes(fmt, maxk);
     const int64_t rpi = lb::matvec_config_rows_per_iter(fmt, cfg);
     auto rows_for = [&](int64_t tb, const lb::DevDesc &d) {
         const int64_t rb = lowbit_weight_bytes(fmt, 1, d.K);
         const int64_t want = std::max<int64_t>(1, (tb + rb - 1) / rb);
         return rpi * ((want + rpi - 1) / rpi);
     };
-    std::vector<int64_t> cand, span;
+    std::vector<int64_t> cand, span, ntiles;
     std::vector<int64_t> costs;
     std::vector<int64_t> sizes = {16 * 1024, 24 * 1024, 32 * 1024, 48 * 1024, 64 * 1024, 96 * 1024, 128 * 1024,
                                   160 * 1024};
@@ -415,13 +429,15 @@ static void plan_tiles(int fmt, int cfg, std::vector<lb::DevDesc> &ds, int64_t s
         }
         cand.push_back(tb);
         span.push_back(make);
+        ntiles.push_back((int64_t)costs.size());
     }
     const int64_t best = *std::min_element(span.begin(), span.end());
-    int64_t tb = kDefault, at_default = 0;
+    int64_t tb = kDefault, at_default = 0, tiles_default = 0;
     for (size_t i = 0; i < cand.size(); i++)
         if (cand[i] == kDefault)
-            at_default = span[i];
-    if (best * 100 < at_default * 95) // the model is coarse: leave the default unless it predicts >= 5 %
+            at_default = span[i], tiles_default = ntiles[i];
+    // the model is coarse: leave the default unless the batch is small and it predicts >= 5 %
+    if (tiles_default < 4 * slots && best * 100 < at_default * 95)
         for (size_t i = 0; i < cand.size(); i++)
             if (span[i] * 1000 <= best * 1005)
                 tb = cand[i];
