@@ -199,7 +199,7 @@ class LayeredGraph:
             b.run()
 
     def launches(self):
-        return (1 if self.fused else 2) * len(self.phases)
+        return sum(b.launches() for _, _, b in self.phases) + (0 if self.fused else len(self.phases))
 
     def close(self):
         for _, _, b in self.phases:

@@ -463,6 +463,15 @@ struct lb_batch {
         lb::BatchGroup g;
         size_t lds;
     };
+    // an fp32 activation row quantised to q8_0 by a launch of its own ahead of the groups, into the batch's
+    // device memory
+    struct Quant {
+        const float *x;
+        int64_t K;
+        int8_t *xq;
+        uint16_t *xs;
+    };
+    std::vector<Quant> quants;
     std::vector<Group> groups;
     void *dev = nullptr;
     int device = -1;
@@ -470,13 +479,30 @@ struct lb_batch {
 
 namespace {
 
+// fp32 activation rows (LB_ACT_F32_Q8_0) longer than this are quantised by one launch of their own ahead of
+// the products instead of inside every product workgroup: each workgroup would read and quantise the whole
+// row for a tile of a few rows.  Measured on the dependency-ordered 8B token's down projection (K = 12288,
+// 14 MB): 9.1 us per phase quantised in the launch, 7.5 us with a quantise launch first; at K = 4096 the
+// in-launch form is 1.3-1.7 us faster per phase.
+constexpr int64_t kQinMaxK = 8192;
+
 // A validated work list cut into launch groups with their device tables, still in host memory.
 struct BatchPlan {
     struct Key {
         int fmt, cfg, qin;
     };
+    // an fp32 row quantised ahead of the groups; its q8_0 bytes then binary16 scales sit `off` bytes past the
+    // tables, each part padded to 256 bytes
+    struct PreQ {
+        const float *x;
+        int64_t K;
+        size_t off;
+    };
     std::vector<Key> keys;
     std::vector<std::vector<lb::DevDesc>> descs;
+    std::vector<std::vector<int>> preq_of; // per descriptor: its row in preq, or -1
+    std::vector<PreQ> preq;
+    size_t preq_bytes = 0;
     std::vector<std::vector<lb::TileRef>> tiles;
     std::vector<int> full;
     std::vector<size_t> lds;
@@ -491,12 +517,19 @@ struct BatchPlan {
             bytes += padded(descs[gi].size() * sizeof(lb::DevDesc)) + padded(tiles[gi].size() * sizeof(lb::TileRef));
         return bytes;
     }
+    static size_t q8_bytes(int64_t K) { return padded((size_t)K) + padded((size_t)(K / 32) * 2); }
     // Lay the tables out at `host` (table_bytes() bytes) for device address `dev`, and describe the launch
-    // groups that read them there.
-    void emit(char *host, char *dev, std::vector<lb_batch::Group> &groups) const
+    // groups that read them there and the quantise launches that precede them (their q8_0 rows at
+    // dev + table_bytes(), preq_bytes more bytes of device memory).
+    void emit(char *host, char *dev, std::vector<lb_batch::Group> &groups, std::vector<lb_batch::Quant> &quants) const
     {
         size_t off = 0;
         groups.clear();
+        quants.clear();
+        char *const qbase = dev + table_bytes();
+        for (const PreQ &q : preq)
+            quants.push_back({q.x, q.K, reinterpret_cast<int8_t *>(qbase + q.off),
+                              reinterpret_cast<uint16_t *>(qbase + q.off + padded((size_t)q.K))});
         for (size_t gi = 0; gi < keys.size(); gi++) {
             lb_batch::Group grp;
             grp.g.fmt = keys[gi].fmt;
@@ -506,6 +539,13 @@ struct BatchPlan {
             grp.g.ntiles = (int32_t)tiles[gi].size();
             grp.g.desc = reinterpret_cast<const lb::DevDesc *>(dev + off);
             std::memcpy(host + off, descs[gi].data(), descs[gi].size() * sizeof(lb::DevDesc));
+            lb::DevDesc *hd = reinterpret_cast<lb::DevDesc *>(host + off);
+            for (size_t j = 0; j < descs[gi].size(); j++)
+                if (preq_of[gi][j] >= 0) { // reads the row its quantise launch writes
+                    const lb_batch::Quant &q = quants[(size_t)preq_of[gi][j]];
+                    hd[j].xq = q.xq;
+                    hd[j].xscale = q.xs;
+                }
             off += padded(descs[gi].size() * sizeof(lb::DevDesc));
             grp.g.tiles = reinterpret_cast<const lb::TileRef *>(dev + off);
             std::memcpy(host + off, tiles[gi].data(), tiles[gi].size() * sizeof(lb::TileRef));
@@ -516,8 +556,10 @@ struct BatchPlan {
     }
 };
 
-// Validate a host work list and plan its launches (no device memory is touched).
-lb_status batch_plan(const char *fn, const lb_matvec_desc *list, int32_t n, BatchPlan &plan)
+// Validate a host work list and plan its launches (no device memory is touched).  prequant: fp32 rows above
+// kQinMaxK columns get a quantise launch of their own (the batch object holds their q8_0 rows); without it
+// every fp32 row is quantised inside its products' launches.
+lb_status batch_plan(const char *fn, const lb_matvec_desc *list, int32_t n, BatchPlan &plan, bool prequant)
 {
     if (!list || n < 1)
         return fail(LB_EINVAL, fn, "empty or null work list");
@@ -554,7 +596,19 @@ lb_status batch_plan(const char *fn, const lb_matvec_desc *list, int32_t n, Batc
         if (d.N == 0)
             continue;
         const int cfg = lb::matvec_config(d.fmt, d.K);
-        const int qin = d.afmt == LB_ACT_F32_Q8_0 ? 1 : 0;
+        const bool pre = prequant && d.afmt == LB_ACT_F32_Q8_0 && d.K > kQinMaxK;
+        const int qin = d.afmt == LB_ACT_F32_Q8_0 && !pre ? 1 : 0;
+        int pi = -1;
+        if (pre) { // one quantise launch per distinct (x, K)
+            for (size_t j = 0; j < plan.preq.size() && pi < 0; j++)
+                if (plan.preq[j].x == d.x && plan.preq[j].K == d.K)
+                    pi = (int)j;
+            if (pi < 0) {
+                pi = (int)plan.preq.size();
+                plan.preq.push_back({d.x, d.K, plan.preq_bytes});
+                plan.preq_bytes += BatchPlan::q8_bytes(d.K);
+            }
+        }
         size_t gi = 0;
         while (gi < plan.keys.size() &&
                !(plan.keys[gi].fmt == d.fmt && plan.keys[gi].cfg == cfg && plan.keys[gi].qin == qin))
@@ -562,6 +616,7 @@ lb_status batch_plan(const char *fn, const lb_matvec_desc *list, int32_t n, Batc
         if (gi == plan.keys.size()) {
             plan.keys.push_back({d.fmt, cfg, qin});
             plan.descs.emplace_back();
+            plan.preq_of.emplace_back();
             plan.lds.push_back(0);
         }
         lb::DevDesc dd;
@@ -576,6 +631,7 @@ lb_status batch_plan(const char *fn, const lb_matvec_desc *list, int32_t n, Batc
         dd.tile_rows = 0; // set by the tile plan
         dd.x = qin ? d.x : nullptr;
         plan.descs[gi].push_back(dd);
+        plan.preq_of[gi].push_back(pi);
         plan.lds[gi] = std::max(plan.lds[gi], (size_t)lb::matvec_stage_bytes(d.fmt, d.K) +
                                                   (qin ? (size_t)lb::q8_0_lds_bytes(d.K) : 0));
     }
@@ -596,8 +652,14 @@ lb_status batch_plan(const char *fn, const lb_matvec_desc *list, int32_t n, Batc
     return LB_OK;
 }
 
-lb_status launch_groups(const char *fn, const std::vector<lb_batch::Group> &groups, hipStream_t s)
+lb_status launch_groups(const char *fn, const std::vector<lb_batch::Quant> &quants,
+                        const std::vector<lb_batch::Group> &groups, hipStream_t s)
 {
+    for (const auto &q : quants) {
+        hipError_t e = lb::launch_quantize_q8_0(q.x, 1, q.K, q.xq, q.xs, s);
+        if (e != hipSuccess)
+            return hip_fail(fn, e);
+    }
     for (const auto &grp : groups) {
         hipError_t e = lb::launch_matvec_batched(grp.g, s, grp.lds);
         if (e != hipSuccess)
@@ -643,7 +705,7 @@ lb_status batched_static(const lb_matvec_desc *list, int32_t n, hipStream_t s)
 {
     const char *fn = "lowbit_matvec_batched_static";
     BatchPlan plan;
-    lb_status st = batch_plan(fn, list, n, plan);
+    lb_status st = batch_plan(fn, list, n, plan, false); // every fp32 row quantised in its products' launches
     if (st != LB_OK)
         return st;
     const size_t bytes = plan.table_bytes();
@@ -659,13 +721,14 @@ lb_status batched_static(const lb_matvec_desc *list, int32_t n, hipStream_t s)
         return st;
     std::vector<char> host(bytes);
     std::vector<lb_batch::Group> groups;
-    plan.emit(host.data(), dev, groups);
+    std::vector<lb_batch::Quant> quants; // (none without pre-quantisation)
+    plan.emit(host.data(), dev, groups, quants);
     // ordered on s after every earlier use of the table on s (a pageable source is staged by the runtime
     // before the call returns, so `host` may go away afterwards)
     hipError_t e = hipMemcpyAsync(dev, host.data(), bytes, hipMemcpyHostToDevice, s);
     if (e != hipSuccess)
         return hip_fail(fn, e);
-    return launch_groups(fn, groups, s);
+    return launch_groups(fn, quants, groups, s);
 }
 
 } // namespace
@@ -677,19 +740,23 @@ static lb_status batch_create(const lb_matvec_desc *list, int32_t n, lb_batch **
         return fail(LB_EINVAL, fn, "null output pointer");
     *out = nullptr;
     BatchPlan plan;
-    lb_status st = batch_plan(fn, list, n, plan);
+    lb_status st = batch_plan(fn, list, n, plan, true);
     if (st != LB_OK)
         return st;
-    const size_t bytes = std::max<size_t>(plan.table_bytes(), 256);
-    std::vector<char> host(bytes);
+    const size_t tbytes = std::max<size_t>(plan.table_bytes(), 256);
+    std::vector<char> host(tbytes);
     std::unique_ptr<lb_batch> b(new lb_batch());
     b->device = plan.device;
-    b->groups.reserve(plan.keys.size()); // nothing below allocates host memory once the device memory is held
-    hipError_t e = hipMalloc(&b->dev, bytes);
+    // nothing below allocates host memory once the device memory is held
+    b->groups.reserve(plan.keys.size());
+    b->quants.reserve(plan.preq.size());
+    // the tables, then the q8_0 rows of the quantise launches at table_bytes() (written on the device by those
+    // launches, not copied; there are none when the tables take fewer than 256 bytes)
+    hipError_t e = hipMalloc(&b->dev, tbytes + plan.preq_bytes);
     if (e != hipSuccess)
         return hip_fail(fn, e);
-    plan.emit(host.data(), static_cast<char *>(b->dev), b->groups);
-    e = hipMemcpy(b->dev, host.data(), bytes, hipMemcpyHostToDevice);
+    plan.emit(host.data(), static_cast<char *>(b->dev), b->groups, b->quants);
+    e = hipMemcpy(b->dev, host.data(), tbytes, hipMemcpyHostToDevice);
     if (e != hipSuccess) {
         (void)hipFree(b->dev);
         return hip_fail(fn, e);
@@ -720,7 +787,7 @@ lb_status lowbit_matvec_batched(const lb_batch *b, hipStream_t s)
     (void)hipGetDevice(&dev); // succeeded in check_device
     if (dev != b->device)
         return fail(LB_EINVAL, fn, "the batch was created on another device");
-    return launch_groups(fn, b->groups, s);
+    return launch_groups(fn, b->quants, b->groups, s);
 }
 
 lb_status lowbit_matvec_batched_static(const lb_matvec_desc *list, int32_t n, hipStream_t s)
@@ -731,6 +798,11 @@ lb_status lowbit_matvec_batched_static(const lb_matvec_desc *list, int32_t n, hi
     } catch (const std::bad_alloc &) {
         return fail(LB_ENOMEM, "lowbit_matvec_batched_static", "host allocation failed while planning the batch");
     }
+}
+
+int32_t lowbit_batch_launches(const lb_batch *b)
+{
+    return b ? (int32_t)(b->quants.size() + b->groups.size()) : -1;
 }
 
 void lowbit_batch_destroy(lb_batch *b)

@@ -41,6 +41,7 @@ SIGNATURES = {
     "lowbit_matvec_popcount": (_I, [_P, _I64, _I64, ctypes.c_float, _P, _P, _P, _P, _P]),
     "lowbit_batch_create": (_I, [_P, ctypes.c_int32, _P]),
     "lowbit_matvec_batched": (_I, [_P, _P]),
+    "lowbit_batch_launches": (ctypes.c_int32, [_P]),
     "lowbit_batch_destroy": (None, [_P]),
     "lowbit_matvec_batched_static": (_I, [_P, ctypes.c_int32, _P]),
     "lowbit_read_probe": (_I, [_P, _I64, _P, _P]),
@@ -244,6 +245,12 @@ class Batch:
             raise ValueError("batch is closed")
         s = _stream(stream) if stream is not None else torch.cuda.current_stream().cuda_stream
         _check(lib.lowbit_matvec_batched(self._h, s), "lowbit_matvec_batched")
+
+    def launches(self):
+        """Kernel launches one run() makes (lowbit_batch_launches)."""
+        if not self._h:
+            raise ValueError("batch is closed")
+        return int(lib.lowbit_batch_launches(self._h))
 
     def close(self):
         if self._h:

@@ -31,10 +31,13 @@
  *                     two ggml weight formats.
  *   LB_ACT_I8_ROW     int8 xq[M][K] plus one fp32 scale per row (per token), xscale[M] (tritium
  *                     "Architecture", section 1: activations are int8).  Used with the planar format.
- *   LB_ACT_F32_Q8_0   fp32 x[K], quantised to q8_0 inside the product's own launch, with exactly the
- *                     arithmetic of lowbit_quantize_act(LB_ACT_Q8_0) (so the results are bit-identical
- *                     to quantising first).  Batched decode of LB_Q1_0 and LB_Q2_0_G64 only: a product
- *                     that depends on the previous one's output then costs one launch instead of two.
+ *   LB_ACT_F32_Q8_0   fp32 x[K], quantised to q8_0 by the batch itself, with exactly the arithmetic of
+ *                     lowbit_quantize_act(LB_ACT_Q8_0) (so the results are bit-identical to quantising
+ *                     first).  Batched decode of LB_Q1_0 and LB_Q2_0_G64 only: a product that depends on the
+ *                     previous one's output then needs no quantise call of its own.  Rows of at most 8192
+ *                     columns are quantised inside the products' own launch (every workgroup quantises
+ *                     the row it stages); a batch from lowbit_batch_create quantises longer rows with one
+ *                     launch per distinct (x, K) ahead of its products, into device memory it owns.
  *
  * Conventions for every entry point:
  *   - Tensor pointers are DEVICE pointers unless stated otherwise; the caller owns every buffer.  No
@@ -220,6 +223,9 @@ typedef struct lb_batch lb_batch;
  * LB_EUNSUPPORTED); null x is LB_EINVAL, x not 16-byte aligned LB_EALIGN. */
 lb_status lowbit_batch_create(const lb_matvec_desc *list, int32_t n, lb_batch **out);
 lb_status lowbit_matvec_batched(const lb_batch *b, hipStream_t s);
+/* Kernel launches one lowbit_matvec_batched call makes (the quantise launches of long fp32 rows plus one
+ * per weight format and kernel configuration present); -1 for a null batch. */
+int32_t lowbit_batch_launches(const lb_batch *b);
 void lowbit_batch_destroy(lb_batch *b);
 
 /*
@@ -229,10 +235,11 @@ void lowbit_batch_destroy(lb_batch *b);
  * instead of memory the library allocates.  Calls no hipMalloc / hipFree; the tile plan is built in host
  * memory on every call.
  *   list: HOST array of n descriptors, validated exactly as by lowbit_batch_create (same status codes);
- *         the same products give the same kernels and bit-identical outputs as a batch of that list.
+ *         the same products give bit-identical outputs as a batch of that list (here every fp32 row,
+ *         however long, is quantised inside its products' launches).
  *   A list whose tables exceed LB_STATIC_TABLE_BYTES (64 bytes per product plus 8 per row tile: for
- *   example 14,000 single-tile products, or 130,000 tiles -- about 32 GB of weights in 256 KiB tiles) is
- *   refused with LB_ESHAPE before anything is enqueued.
+ *   example 14,000 single-tile products, or 130,000 tiles -- about 8 GB of Q1_0 / Q2_0 weights in their
+ *   64 KiB tiles, 32 GB in 256 KiB tiles) is refused with LB_ESHAPE before anything is enqueued.
  * The tables are copied into the array on `s` (stream-ordered after earlier work on `s`), then the kernels
  * run on `s`.  Every call on one GPU shares that GPU's array, which keeps the last call's tables: calls
  * that overlap on one GPU -- on different streams, or from different host threads without ordering --

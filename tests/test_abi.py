@@ -85,6 +85,7 @@ def test_matvec_validation_codes():
 
 def test_other_entry_points_validate():
     lib = L.lib
+    assert lib.lowbit_batch_launches(None) == -1
     assert lib.lowbit_quantize_act(3, A16, 1, 64, A16, A16, None) == L.LB_EINVAL
     assert lib.lowbit_quantize_act(L.ACT_Q8_0, A16, 1, 48, A16, A16, None) == L.LB_ESHAPE
     assert lib.lowbit_quantize_act(L.ACT_Q8_0, A16 + 4, 1, 64, A16, A16, None) == L.LB_EALIGN

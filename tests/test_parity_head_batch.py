@@ -201,9 +201,10 @@ def test_batched_mixed_formats():
 
 @pytest.mark.parametrize("fmt", [synth.Q1_0, synth.Q2_0_G64])
 def test_batched_fp32_activations_quantised_in_launch(fmt):
-    """LB_ACT_F32_Q8_0: each product quantises its fp32 input inside its own launch.  Outputs are
-    bit-identical to quantising first (lowbit_quantize_act) and running the same batch, and within the
-    tolerance of the oracle on the oracle's q8_0 of the same x; two products share one x, as q/k/v do."""
+    """LB_ACT_F32_Q8_0: each product's fp32 input is quantised by the batch (inside the product's own launch,
+    or for rows above 8192 columns by a quantise launch ahead of the products).  Outputs are bit-identical to
+    quantising first (lowbit_quantize_act) and running the same batch, and within the tolerance of the
+    oracle on the oracle's q8_0 of the same x; two products share one x, as q/k/v do."""
     # the largest K stages 74 KiB of LDS per workgroup (the staged records plus the quantised row)
     shapes = [(300, 1024), (1024, 4096), (129, 12288), (1, 128), (517, 2560), (5, 32768), (64, 4096)]
     say(f"case batched fp32 activations fmt={fmt} shapes={shapes}")
@@ -229,6 +230,8 @@ def test_batched_fp32_activations_quantised_in_launch(fmt):
         quantised.append(L.desc(fmt, packed, N, K, xq, xs, yq))
         keep.append((N, K, Wt, packed, x, xd, xq, xs, yf, yq))
     bf, bq = L.Batch(fused), L.Batch(quantised)
+    # the 12288- and 32768-column rows get a quantise launch each, ahead of the product launches
+    assert bf.launches() == bq.launches() + 2
     for _ in range(2):  # a second launch of the same plans gives the same bits
         bf.run()
         bq.run()
