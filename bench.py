@@ -160,8 +160,9 @@ FEEDS = {"attn_q": 0, "attn_k": 0, "attn_v": 0, "attn_output": 1, "ffn_gate": 2,
 class LayeredGraph:
     """A token in dependency order: per layer, the q/k/v products, then o, then gate/up, then down, captured
     once as a HIP graph and replayed.  Each phase is one batched launch after the quantisation of its own
-    input row (288 launches for 36 layers), or, fused (ggml formats), one batched launch that quantises its
-    fp32 input itself (144 launches)."""
+    input row (288 launches for 36 layers), or, fused (ggml formats), one batched launch whose fp32 input
+    the batch quantises itself (inside the launch; the long down-projection row by a quantise launch the
+    batch makes ahead of it: 180 launches)."""
 
     def __init__(self, tok, fused=False):
         import torch
@@ -773,8 +774,9 @@ def main():
 
     # the same token in dependency order (per layer q/k/v, o, gate/up, down), replayed as one HIP graph
     layered = {}
-    for fused, key, what in ((True, "fused", "each phase one batched launch that quantises its fp32 input to "
-                                             "q8_0 itself"),
+    for fused, key, what in ((True, "fused", "each phase one batched launch whose fp32 input the batch "
+                                             "quantises to q8_0 (inside the launch; the 12288-column down "
+                                             "input by a quantise launch of the batch's own ahead of it)"),
                              (False, "separate_quantise", "each phase a q8_0 quantise launch plus one batched "
                                                           "launch")):
         # both legs replay a HIP graph: left out unless asked for ("layered"), e.g. under counter collection
