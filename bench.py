@@ -207,6 +207,39 @@ class LayeredGraph:
             b.close()
 
 
+def graph_launch_floor(n, steps=50, warmup=10):
+    """ms per replay of a HIP graph of n dependent launches that do (almost) nothing: a one-element fill each.
+    It prices the graph's own launch chain, which any n-phase dependency-ordered token pays."""
+    import torch
+
+    t = torch.zeros(1, device="cuda")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for i in range(n):
+            t.fill_(float(i))
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(n):
+            t.fill_(float(i))
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    best = float("inf")
+    for _ in range(3):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(steps):
+            g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        best = min(best, a.elapsed_time(b) / steps)
+    del g
+    return best
+
+
 def time_graph(lg, steps, warmup):
     """ms per replay of the layered token graph, by HIP events on the replay stream."""
     import torch
@@ -784,10 +817,13 @@ def main():
             continue
         lg = LayeredGraph(tok, fused=fused)
         msg = time_graph(lg, args.steps, warm)
+        floor = graph_launch_floor(lg.launches())
         layered[key] = {
             "workload": "the headline token in dependency order: per layer q/k/v, o, gate/up, down, " + what +
                         ", captured as one HIP graph",
             "launches": lg.launches(), "ms_per_token": round(msg, 5),
+            # the same number of dependent launches of a one-element fill in one graph: the chain's own cost
+            "launch_floor_ms": round(floor, 5),
             "tokens_per_s": round(1e3 / msg, 1),
             "gbs": round(tok.weight_bytes / (msg * 1e-3) / 1e9, 1),
             "pct_hbm_peak": round(100 * tok.weight_bytes / (msg * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
