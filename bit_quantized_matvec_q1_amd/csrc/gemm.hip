@@ -106,7 +106,6 @@ typedef __attribute__((address_space(3))) void lvoid;
 struct LaneOffs {
     uint32_t w;     // the thread's share of the weight codes (Q8_0: of the weight bytes)
     uint32_t ws;    // its weight block scale
-    uint32_t dx;    // the four activation scales of activation row tid mod TM
     uint32_t x[2];  // its two activation-tile slots: row offset + 16 x chunk (x_slot)
 };
 
@@ -140,7 +139,6 @@ __device__ __forceinline__ LaneOffs lane_offsets(int N, int K, int M, int n0, in
         o.w = ((uint32_t)row * (uint32_t)(K / 64) + (uint32_t)(p >> 2)) * 16u + 4u * (uint32_t)((p >> 1) & 1);
         o.ws = 0;
     }
-    o.dx = (uint32_t)min(m0 + (tid & (TM - 1)), M - 1) * (uint32_t)(K / QK8) * 2u;
     const int wave = tid >> 6, lane = tid & 63;
 #pragma unroll
     for (int u = 0; u < 2; u++) {
@@ -158,16 +156,20 @@ __device__ __forceinline__ LaneOffs lane_offsets(int N, int K, int M, int n0, in
 template <int FMT>
 __device__ __forceinline__ void load_step(StepRegs &r, const LaneOffs &o, const uint8_t *__restrict__ W,
                                           const uint8_t *__restrict__ wsc, const uint8_t *__restrict__ xsc, int kk,
-                                          bool half_step, int tid)
+                                          bool half_step, int tid, int m0, int M, int K)
 {
     uint32_t ow = o.w + step_wbytes<FMT>(kk), os = o.ws + step_sbytes<FMT>(kk);
-    const uint32_t odx = o.dx + (uint32_t)(kk / QK8) * 2u;
     if (half_step) { // uniform
         const uint32_t second = (uint32_t)((tid >> 2) & 1); // the lane's record / beat index within the step
         ow -= 16u * second;
         os -= 2u * second;
     }
     if (FMT != LB_TERNARY_PLANAR && tid < TM) {
+        // the row offset is rebuilt at every step (an opaque copy of tid stops the compiler from keeping it
+        // live across the loop, where it costs a register that the compute needs)
+        int t = tid;
+        asm volatile("; activation-scale row %0" : "+v"(t));
+        const uint32_t odx = (uint32_t)min(m0 + t, M - 1) * (uint32_t)(K / QK8) * 2u + (uint32_t)(kk / QK8) * 2u;
         // one 8-byte load per activation row (4-byte aligned: K / 32 and kk / 32 are even); the half step has
         // two blocks only
         if (half_step) { // (blocks 2 and 3 are stored as zero)
@@ -306,8 +308,8 @@ __device__ __forceinline__ void store_step(Lds &lds, int buf, const StepRegs &r,
 }
 
 // One wave's share of a K-step: its 32 x 32 output tile over the step's KAB = 4 q8_0 blocks (on a half step
-// the last two carry zero weights and scales).  Each block's result is scaled as soon as it is ready: the
-// other waves of the SIMD keep the vector ALU busy meanwhile.
+// the last two carry zero weights and scales).  Each block's result is scaled as soon as it is ready; the
+// next block's MFMA runs meanwhile (Q1_0, Q2_0), and the other waves of the SIMD fill the rest.
 template <int FMT, bool EMIT, int KAB>
 __device__ __forceinline__ void step_compute(const Lds &lds, int buf, const uint32_t *xt, const uint32_t (&xb)[4], int h,
                                              int l32, int wn, int wm, int m0, int n0, int M, int N, int nab, int kk,
@@ -335,10 +337,18 @@ __device__ __forceinline__ void step_compute(const Lds &lds, int buf, const uint
 #pragma unroll
     for (int j = 0; j < KAB; j++)
         dx[j] = lds.dx[buf][j * TM + 32 * wm + l32];
-    // every result is read as fp32 through the bias: 1.5 * 2^23 + isum exactly (|isum| < 2^22)
+    // every result is read as fp32 through the bias: 1.5 * 2^23 + isum exactly (|isum| < 2^22).  Q1_0 and
+    // Q2_0 issue each block's MFMA before the previous block's rescale, so the wave's own rescale covers the
+    // MFMA latency (Q8_0, whose weight scales change with every block, measured slower that way).
+    constexpr bool AHEAD = FMT != LB_Q8_0;
+    v16i Dn;
+    if (AHEAD)
+        Dn = mfma(0, cbias);
 #pragma unroll
     for (int j = 0; j < KAB; j++) {
-        const v16i Dj = mfma(j, cbias);
+        const v16i Dj = AHEAD ? Dn : mfma(j, cbias);
+        if (AHEAD && j + 1 < KAB)
+            Dn = mfma(j + 1, cbias);
         // the weight block's scales of this lane's 16 weight rows
         float dwv[16];
 #pragma unroll
@@ -434,7 +444,7 @@ __global__ __launch_bounds__(GT * KSPLIT, EMIT ? 2 * KSPLIT : 4) void gemm_kerne
     // LDS tiles of every step are fixed objects.
     StepRegs ring;
     int kk = kfirst;
-    load_step<FMT>(ring, lo, W, wsc, xsc, kk, K - kk < KS, tid);
+    load_step<FMT>(ring, lo, W, wsc, xsc, kk, K - kk < KS, tid, m0, M, K);
     issue_x(xt0[half], X, lo, kk, K - kk < KS, wave, lane);
 
     for (int j0 = 0; j0 < nsh; j0 += 2)
@@ -449,10 +459,12 @@ __global__ __launch_bounds__(GT * KSPLIT, EMIT ? 2 * KSPLIT : 4) void gemm_kerne
         if (active)
             store_step<FMT>(lds[half], q, ring, K, kk, tid);
         step_barrier();
-        // the next step's loads (past the last step the walk wraps: valid addresses, unused)
+        // the next step's loads (past the last step the walk wraps: valid addresses, unused).  With one
+        // step in all and two halves, the stride is twice the walk, so the offset may need two wraps.
         int kn = kk + KSPLIT * KS;
         kn = kn >= kend ? kn - kend : kn;
-        load_step<FMT>(ring, lo, W, wsc, xsc, kn, K - kn < KS, tid);
+        kn = kn >= kend ? kn - kend : kn;
+        load_step<FMT>(ring, lo, W, wsc, xsc, kn, K - kn < KS, tid, m0, M, K);
         issue_x(q ? xt0[half] : xt1[half], X, lo, kn, K - kn < KS, wave, lane);
         if (active)
             step_compute<FMT, EMIT, 4>(lds[half], q, q ? xt1[half] : xt0[half], xb, h, l32, wn, wm, m0, n0, M, N, nab,
