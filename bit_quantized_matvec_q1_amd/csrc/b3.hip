@@ -7,17 +7,22 @@
 // c = w + 1 of each trit, acc = sum c q - sum q, exactly.
 //
 // Decode on CDNA4.  The device layout (lowbit_pack_weights) keeps the beat stream but stores each base-3
-// byte v as the 8-bit fraction b = ceil(256 v / 243): then the leading m base-3 digits of v are
-// F_m = floor(3^m b / 256) (F_5 = v) and digit 5 - m is F_m - 3 F_(m-1).  For the five columns j0 .. j0 + 4
-// of a byte,
-//     sum_t c_t q_(j0+t) = sum_(m=1..4) F_m q_(j0+5-m) + d_0 q_j0 - 3 sum_(m=1..3) F_m q_(j0+4-m),
-// with d_0 = F_5 - 3 F_4 (the F_5 term and the m = 4 term of the second sum cancel down to d_0).  A
-// record dword's four bytes are split into the 16-bit halves of two registers (two byte permutes); per
-// m both are multiplied by 3 (products below 2^16, so the halves never carry into each other) and one
-// byte permute gathers the four floors F_m (< 81 for m <= 4) into one dword of int8, multiplied into two
-// int32 accumulators with v_dot4_i32_i8 against the activations, which the workgroup stages once,
-// transposed: per record dword five dwords P_o, byte k of P_o = q of column 5 k + o.  27 operations per
-// 20 weights, against 4 per 16 for the 2-bit planar beat.
+// byte v as the 8-bit fraction b = ceil(256 v / 243) (v = 243 b >> 8).  A 16-byte record is four dwords of
+// four bytes (20 trits each), decoded two ways so that the vector ALU and the LDS share the work:
+//  * the first three dwords by table: per byte one 8-byte LDS entry indexed by b (one SDWA shift forms the
+//    address), holding the byte's five codes c_t = w + 1 -- c_0 .. c_3 as the bytes of its first dword,
+//    multiplied with v_dot4_i32_i8 against the activations of the byte's first four columns, and c_4 in
+//    byte k (the byte's position in its dword) of the second, ORed over the dword's four bytes and
+//    multiplied once against the four fifth columns: 11 operations and 4 LDS reads per 20 trits;
+//  * the fourth dword arithmetically: the leading m base-3 digits of v are F_m = floor(3^m b / 256)
+//    (F_5 = v), digit 5 - m is F_m - 3 F_(m-1), and for the five columns j0 .. j0 + 4 of a byte
+//        sum_t c_t q_(j0+t) = sum_(m=1..4) F_m q_(j0+5-m) + d_0 q_j0 - 3 sum_(m=1..3) F_m q_(j0+4-m),
+//    with d_0 = F_5 - 3 F_4.  The dword's bytes go to the 16-bit halves of two registers (two byte
+//    permutes); per m both are multiplied by 3 (products below 2^16, so the halves never carry into each
+//    other) and one permute gathers the four F_m into one int8 dword for v_dot4_i32_i8: 27 operations.
+// All table reads alone left the LDS as the limit (most of its busy cycles bank conflicts), the arithmetic
+// alone the vector ALU; three to one measured fastest.  The activations are staged once per workgroup in
+// the order each form reads (five dwords per record dword either way).
 
 // Work split as in the other decode kernels: a row over L lanes, S beats per lane (strided by L so a
 // wave-wide 16-byte load is contiguous), the staged activation pairs held in registers for every row a
@@ -51,9 +56,59 @@ __device__ __forceinline__ int dot4(uint32_t a, uint32_t b, int c)
     return __builtin_amdgcn_sdot4((int)a, (int)b, c, false);
 }
 
-// The four bytes of one record dword: F_m of all four in one dword per m, int8 dot products against the
-// staged activation columns P[o] (byte k of P[o]: the activation of column 5 k + o of the dword's 20).
-__device__ __forceinline__ void b3_dword(uint32_t d, const uint32_t *P, int &acc_a, int &acc_b)
+// The LDS table: for each byte position k of a record dword and each stored byte b, the digits c_t (the
+// codes w + 1, lowest digit first) of the base-3 value v = 243 b >> 8 -- c_0 .. c_3 as the four bytes of
+// the entry's first dword, c_4 in byte k of its second (zero elsewhere), so that the second dwords of a
+// record dword's four bytes combine by OR.  4 x 256 entries of 8 bytes, built by every workgroup.
+__device__ __forceinline__ void b3_build_lut(uint2 *__restrict__ lut)
+{
+    for (int e = threadIdx.x; e < 4 * 256; e += WG) {
+        const int k = e >> 8, b = e & 255;
+        uint32_t v = (243u * (uint32_t)b) >> 8, lo = 0;
+#pragma unroll
+        for (int t = 0; t < 4; t++) {
+            lo |= (v % 3u) << (8 * t);
+            v /= 3u;
+        }
+        lut[e] = make_uint2(lo, v << (8 * k)); // v is digit 4 now
+    }
+}
+
+// Byte k of d times 8, in one instruction (the byte selected by the operand's own SDWA field).
+template <int k> __device__ __forceinline__ uint32_t byte_x8(uint32_t d)
+{
+    uint32_t r;
+    if (k == 0)
+        asm("v_lshlrev_b32_sdwa %0, 3, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_0" : "=v"(r) : "v"(d));
+    else if (k == 1)
+        asm("v_lshlrev_b32_sdwa %0, 3, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_1" : "=v"(r) : "v"(d));
+    else if (k == 2)
+        asm("v_lshlrev_b32_sdwa %0, 3, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_2" : "=v"(r) : "v"(d));
+    else
+        asm("v_lshlrev_b32_sdwa %0, 3, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_3" : "=v"(r) : "v"(d));
+    return r;
+}
+
+// The four bytes of one record dword by table: per byte k one entry, whose first dword is multiplied against
+// the activations of the byte's first four columns (A[k]) and whose second dwords, ORed over the four
+// bytes, against those of their fifth columns (A[4]).
+__device__ __forceinline__ void b3_dword(uint32_t d, const uint32_t *A, const uint2 *__restrict__ lut, int &acc)
+{
+    uint32_t hi = 0;
+    const uint32_t a[4] = {byte_x8<0>(d), byte_x8<1>(d), byte_x8<2>(d), byte_x8<3>(d)};
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+        const uint2 e = *reinterpret_cast<const uint2 *>(reinterpret_cast<const char *>(lut + 256 * k) + a[k]);
+        acc = dot4(e.x, A[k], acc);
+        hi |= e.y;
+    }
+    acc = dot4(hi, A[4], acc);
+}
+
+// The four bytes of one record dword arithmetically: F_m of all four in one dword per m, int8 dot products
+// against the staged activation columns P[o] (byte k of P[o]: the activation of column 5 k + o of the
+// dword's 20).
+__device__ __forceinline__ void b3_dword_arith(uint32_t d, const uint32_t *P, int &acc_a, int &acc_b)
 {
     uint32_t ye = __builtin_amdgcn_perm(0u, d, 0x0C020C00u); // bytes 0 and 2 in the low bytes of the halves
     uint32_t yo = __builtin_amdgcn_perm(0u, d, 0x0C030C01u); // bytes 1 and 3
@@ -74,19 +129,22 @@ __device__ __forceinline__ void b3_dword(uint32_t d, const uint32_t *P, int &acc
     }
 }
 
-// Stage the activation once per workgroup: per beat and record dword, the five transposed column dwords
-// (columns past K read q = 0), and the row's sum of q.
+// Stage the activation once per workgroup: per beat and record dword five dwords (columns past K read
+// q = 0) -- for the table-decoded dwords 0..2, per byte k (columns c0 + 5 k .. c0 + 5 k + 4) the activations
+// of its first four columns, then one dword whose byte k is that of its fifth column; for dword 3 the
+// transposed columns P[o] -- and the row's sum of q.
 __device__ __forceinline__ void b3_stage(const int8_t *__restrict__ xq, int K, int nbt, uint32_t *__restrict__ lds,
                                          int *__restrict__ sumq)
 {
     for (int it = threadIdx.x; it < nbt * REC; it += WG) {
         const int bt = it / REC, r = it % REC, dd = r / 5, o = r % 5;
-        const int c0 = bt * BCOLS + 20 * dd + o; // column of byte 0
+        const int c0 = bt * BCOLS + 20 * dd; // column of byte 0's first trit
         uint32_t v = 0;
 #pragma unroll
-        for (int k = 0; k < 4; k++) {
-            const int c = c0 + 5 * k;
-            v |= (uint32_t)(uint8_t)(c < K ? xq[c] : (int8_t)0) << (8 * k);
+        for (int t = 0; t < 4; t++) {
+            // record dword 3 (decoded arithmetically): byte t of dword o = q of column 5 t + o
+            const int c = dd == 3 ? c0 + 5 * t + o : o < 4 ? c0 + 5 * o + t : c0 + 5 * t + 4;
+            v |= (uint32_t)(uint8_t)(c < K ? xq[c] : (int8_t)0) << (8 * t);
         }
         lds[it] = v;
     }
@@ -139,6 +197,9 @@ __device__ __forceinline__ void b3_tile(const uint8_t *__restrict__ W, int K, fl
     const __amdgpu_buffer_rsrc_t yt =
         __builtin_amdgcn_make_buffer_rsrc(EMIT ? nullptr : y + row0, 0, EMIT ? 0 : nrows * 4, 0x00020000);
 
+    __shared__ uint2 lut_s[4 * 256]; // (static: its address is a constant, folded into the reads' offsets)
+    const uint2 *lut = lut_s;
+    b3_build_lut(lut_s);
     int *sumq = reinterpret_cast<int *>(lds + nbt * REC);
     b3_stage(xq, K, nbt, lds, sumq);
     __syncthreads();
@@ -170,15 +231,15 @@ __device__ __forceinline__ void b3_tile(const uint8_t *__restrict__ W, int K, fl
             issue(buf[p ^ 1], min(onext, last));
             __builtin_amdgcn_sched_barrier(0);
             onext += stepb;
-            int acc_a = 0, acc_b = 0;
+            int acc = 0, acc_a = 0, acc_b = 0;
 #pragma unroll
             for (int i = 0; i < S; i++) {
-                b3_dword(buf[p].code[i].x, act[i] + 0, acc_a, acc_b);
-                b3_dword(buf[p].code[i].y, act[i] + 5, acc_a, acc_b);
-                b3_dword(buf[p].code[i].z, act[i] + 10, acc_a, acc_b);
-                b3_dword(buf[p].code[i].w, act[i] + 15, acc_a, acc_b);
+                b3_dword(buf[p].code[i].x, act[i] + 0, lut, acc);
+                b3_dword(buf[p].code[i].y, act[i] + 5, lut, acc);
+                b3_dword(buf[p].code[i].z, act[i] + 10, lut, acc);
+                b3_dword_arith(buf[p].code[i].w, act[i] + 15, acc_a, acc_b);
             }
-            int acc = group_sum_i<L>(acc_a - 3 * acc_b);
+            acc = group_sum_i<L>(acc + acc_a - 3 * acc_b);
             const int rl = cur + rbase;
             const int a = acc - sq; // sum (w + 1) q - sum q
             // tritium "Architecture", section 5: activation scale, then weight scale, in fp32
