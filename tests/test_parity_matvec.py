@@ -204,6 +204,35 @@ def test_b3_pack_round_trip():
     assert np.array_equal(host(back), Wt.raw.reshape(-1))
 
 
+@pytest.mark.parametrize("K", [320, 2560, 6912])
+def test_b3_every_byte_value_at_every_position(K):
+    """Base-3 decode covers all 243 byte values at every byte position of a beat: row r holds value
+    (r + 7 j) mod 243 at byte j, so each of the 16 positions (three of every four record dwords decoded by
+    table, the fourth by digit arithmetic) meets every value across the 243 rows.  Row sums and outputs
+    bit for bit against the oracle, with random activations including -128 and +127."""
+    N = 243
+    nbt = -(-K // 80)
+    say(f"case base3 all bytes K={K}")
+    j = np.arange(nbt * 16)
+    v = ((np.arange(N)[:, None] + 7 * j[None, :]) % 243).astype(np.int64)
+    digits = np.stack([(v // 3 ** t) % 3 for t in range(5)], axis=-1).reshape(N, nbt * 80)
+    w = (digits[:, :K] - 1).astype(np.int8)
+    raw = synth.lay_out_b3(w)  # columns past K are coded 0, so the last beat's tail bytes differ from v
+    assert np.array_equal(raw.reshape(N, -1)[:, : K // 5], v[:, : K // 5].astype(np.uint8))
+    Wt = synth.Weights(synth.TERNARY_B3, N, K, raw, w, s_w=np.float32(0.75))
+    g = synth.rng(2600 + K)
+    q = g.integers(-128, 128, size=K).astype(np.int8)
+    q[:: 97] = -128
+    q[1:: 89] = 127
+    xs = np.array([0.03125], np.float32)
+    packed = packed_weights(Wt)
+    y = gpu_matvec(synth.TERNARY_B3, packed, N, K, q, xs, w_scale=0.75)
+    sums = gpu_sums(synth.TERNARY_B3, packed, N, K, q[None, :], xs)[0]
+    acc, y_ref = oracle.matvec_b3(raw, N, K, q, xs[0], np.float32(0.75))
+    assert np.array_equal(sums, acc), "row sums differ"
+    assert np.array_equal(y, y_ref), "outputs differ"
+
+
 @pytest.mark.parametrize("fmt", Q_FMTS, ids=NAMES.get)
 def test_pack_round_trip(fmt):
     say(f"case pack {NAMES[fmt]}")
