@@ -132,31 +132,55 @@ __device__ __forceinline__ void b3_dword_arith(uint32_t d, const uint32_t *P, in
 // Stage the activation once per workgroup: per beat and record dword five dwords (columns past K read
 // q = 0) -- for the table-decoded dwords 0..2, per byte k (columns c0 + 5 k .. c0 + 5 k + 4) the activations
 // of its first four columns, then one dword whose byte k is that of its fifth column; for dword 3 the
-// transposed columns P[o] -- and the row's sum of q.
+// transposed columns P[o], byte k = column 5 k + o.  One item per record dword: its 20 columns as five
+// dword loads (K is a multiple of 64, so a dword is wholly in or past the row), rearranged with byte
+// selects.  The row's sum of q comes from the same loads: each wave's total at sumq[wave], summed by the
+// reader after the workgroup's barrier.
+template <int i> __device__ __forceinline__ uint32_t qbyte(const uint32_t (&s)[5])
+{
+    return (s[i / 4] >> (8 * (i % 4))) & 0xFFu;
+}
+template <int a, int b, int c, int d> __device__ __forceinline__ uint32_t gather4(const uint32_t (&s)[5])
+{
+    return qbyte<a>(s) | qbyte<b>(s) << 8 | qbyte<c>(s) << 16 | qbyte<d>(s) << 24;
+}
+
 __device__ __forceinline__ void b3_stage(const int8_t *__restrict__ xq, int K, int nbt, uint32_t *__restrict__ lds,
                                          int *__restrict__ sumq)
 {
-    for (int it = threadIdx.x; it < nbt * REC; it += WG) {
-        const int bt = it / REC, r = it % REC, dd = r / 5, o = r % 5;
-        const int c0 = bt * BCOLS + 20 * dd; // column of byte 0's first trit
-        uint32_t v = 0;
+    int part = 0;
+    for (int it = threadIdx.x; it < nbt * 4; it += WG) {
+        const int bt = it >> 2, dd = it & 3;
+        const int c0 = bt * BCOLS + 20 * dd;
+        uint32_t s[5];
 #pragma unroll
-        for (int t = 0; t < 4; t++) {
-            // record dword 3 (decoded arithmetically): byte t of dword o = q of column 5 t + o
-            const int c = dd == 3 ? c0 + 5 * t + o : o < 4 ? c0 + 5 * o + t : c0 + 5 * t + 4;
-            v |= (uint32_t)(uint8_t)(c < K ? xq[c] : (int8_t)0) << (8 * t);
+        for (int u = 0; u < 5; u++)
+            s[u] = c0 + 4 * u < K ? *reinterpret_cast<const uint32_t *>(xq + c0 + 4 * u) : 0u;
+#pragma unroll
+        for (int u = 0; u < 5; u++)
+            part = __builtin_amdgcn_sdot4((int)s[u], 0x01010101, part, false);
+        uint4 o03;
+        uint32_t o4;
+        if (dd == 3) {
+            o03 = make_uint4(gather4<0, 5, 10, 15>(s), gather4<1, 6, 11, 16>(s), gather4<2, 7, 12, 17>(s),
+                             gather4<3, 8, 13, 18>(s));
+            o4 = gather4<4, 9, 14, 19>(s);
+        } else {
+            o03 = make_uint4(gather4<0, 1, 2, 3>(s), gather4<5, 6, 7, 8>(s), gather4<10, 11, 12, 13>(s),
+                             gather4<15, 16, 17, 18>(s));
+            o4 = gather4<4, 9, 14, 19>(s);
         }
-        lds[it] = v;
+        uint32_t *dst = lds + bt * REC + 5 * dd;
+        dst[0] = o03.x;
+        dst[1] = o03.y;
+        dst[2] = o03.z;
+        dst[3] = o03.w;
+        dst[4] = o4;
     }
-    // sum of q over the row (one wave)
-    if (threadIdx.x < 64) {
-        int s = 0;
-        for (int c = threadIdx.x; c < K; c += 64)
-            s += xq[c];
-        s = group_sum_i<64>(s);
-        if (threadIdx.x == 63)
-            *sumq = s;
-    }
+    static_assert(WG == 256, "four per-wave partial sums (the 16 bytes past the staged activation)");
+    part = group_sum_i<64>(part);
+    if ((threadIdx.x & 63) == 63)
+        sumq[threadIdx.x >> 6] = part;
 }
 
 template <int S> struct B3Row {
@@ -219,7 +243,7 @@ __device__ __forceinline__ void b3_tile(const uint8_t *__restrict__ W, int K, fl
             act[i][4 * q + 3] = in ? t.w : 0u;
         }
     }
-    const int sq = *sumq;
+    const int sq = sumq[0] + sumq[1] + sumq[2] + sumq[3];
 
     for (int it = 0; it < nrows; it += 2 * STEP) {
 #pragma unroll
