@@ -106,6 +106,7 @@ typedef __attribute__((address_space(3))) void lvoid;
 struct LaneOffs {
     uint32_t w;     // the thread's share of the weight codes (Q8_0: of the weight bytes)
     uint32_t ws;    // its weight block scale
+    uint32_t dx;    // Q8_0: the four activation scales of activation row tid mod TM (the other formats rebuild it)
     uint32_t x[2];  // its two activation-tile slots: row offset + 16 x chunk (x_slot)
 };
 
@@ -145,6 +146,7 @@ __device__ __forceinline__ LaneOffs lane_offsets(int N, int K, int M, int n0, in
         const int slot = 128 * wave + 64 * u + lane, r = slot / XCH;
         o.x[u] = (uint32_t)min(m0 + r, M - 1) * (uint32_t)K + 16u * (uint32_t)((slot % XCH) ^ ((r >> 1) & 7));
     }
+    o.dx = (uint32_t)min(m0 + (tid & (TM - 1)), M - 1) * (uint32_t)(K / QK8) * 2u;
     return o;
 }
 
@@ -165,11 +167,16 @@ __device__ __forceinline__ void load_step(StepRegs &r, const LaneOffs &o, const 
         os -= 2u * second;
     }
     if (FMT != LB_TERNARY_PLANAR && tid < TM) {
-        // the row offset is rebuilt at every step (an opaque copy of tid stops the compiler from keeping it
-        // live across the loop, where it costs a register that the compute needs)
-        int t = tid;
-        asm volatile("; activation-scale row %0" : "+v"(t));
-        const uint32_t odx = (uint32_t)min(m0 + t, M - 1) * (uint32_t)(K / QK8) * 2u + (uint32_t)(kk / QK8) * 2u;
+        // Q1_0 and Q2_0 rebuild the row offset at every step (an opaque copy of tid stops the compiler from
+        // keeping it live across the loop, where it costs a register that their two result tiles need);
+        // Q8_0 keeps it
+        uint32_t odx = o.dx;
+        if (FMT != LB_Q8_0) {
+            int t = tid;
+            asm volatile("; activation-scale row %0" : "+v"(t));
+            odx = (uint32_t)min(m0 + t, M - 1) * (uint32_t)(K / QK8) * 2u;
+        }
+        odx += (uint32_t)(kk / QK8) * 2u;
         // one 8-byte load per activation row (4-byte aligned: K / 32 and kk / 32 are even); the half step has
         // two blocks only
         if (half_step) { // (blocks 2 and 3 are stored as zero)
