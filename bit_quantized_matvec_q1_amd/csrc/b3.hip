@@ -62,15 +62,17 @@ __device__ __forceinline__ int dot4(uint32_t a, uint32_t b, int c)
 // record dword's four bytes combine by OR.  4 x 256 entries of 8 bytes, built by every workgroup.
 __device__ __forceinline__ void b3_build_lut(uint2 *__restrict__ lut)
 {
-    for (int e = threadIdx.x; e < 4 * 256; e += WG) {
-        const int k = e >> 8, b = e & 255;
+    // one stored byte per thread, its entry written for all four byte positions
+    for (int b = threadIdx.x; b < 256; b += WG) {
         uint32_t v = (243u * (uint32_t)b) >> 8, lo = 0;
 #pragma unroll
         for (int t = 0; t < 4; t++) {
             lo |= (v % 3u) << (8 * t);
             v /= 3u;
         }
-        lut[e] = make_uint2(lo, v << (8 * k)); // v is digit 4 now
+#pragma unroll
+        for (int k = 0; k < 4; k++)
+            lut[256 * k + b] = make_uint2(lo, v << (8 * k)); // v is digit 4 now
     }
 }
 
