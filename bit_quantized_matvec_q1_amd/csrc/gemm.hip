@@ -6,14 +6,14 @@
 //
 // Mapping to CDNA4:
 //  * A workgroup owns a tile of TN = 64 weight rows x TM = 128 activation rows and walks K in steps of
-//    128 columns.  Each step is software-pipelined: the packed weight codes, activation tile and
-//    activation scales of the step two ahead are loaded into a register ring while the current step
-//    computes; at the top of a step they are written to double-buffered LDS -- the weights unpacked to
-//    int8 in natural column order (shift and mask, a 4x4 byte transpose with v_perm_b32, and a
-//    v_perm_b32 lookup from code to weight byte: Q2_0 c -> c - 1, Q1_0 bit -> +/-1, planar (pos, neg) ->
-//    pos - neg; Q8_0 weights are int8 already and copied as they are) -- and one barrier per step
-//    separates the writes from the reads.  Every thread loads and
-//    unpacks an equal share of the weight tile and copies an equal share of the activation tile.
+//    128 columns.  Each step is software-pipelined: while a step computes, the next step's packed weight
+//    codes, weight scales and activation scales are loaded into registers and its activation tile
+//    streams HBM -> LDS through the load unit; at the top of a step the registers are written to
+//    double-buffered LDS -- the weights unpacked to int8 in natural column order (shift and mask, a 4x4
+//    byte transpose with v_perm_b32, and a v_perm_b32 lookup from code to weight byte: Q2_0 c -> c - 1,
+//    Q1_0 bit -> +/-1, planar (pos, neg) -> pos - neg; Q8_0 weights are int8 already and copied as they
+//    are) -- and one barrier per step separates the writes from the reads.  Every thread loads and
+//    unpacks an equal share of the weight tile and issues an equal share of the activation tile.
 //  * A workgroup is 8 waves (512 threads), two per SIMD, and two workgroups fit a CU.  Wave w computes
 //    the 32 x 32 output tile (weight rows 32 (w mod 2), activation rows 32 (w / 2)) over every step's
 //    four q8_0 blocks (32 columns each, the MFMA's K depth): per block one A operand (weights) and one B
